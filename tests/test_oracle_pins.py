@@ -1,0 +1,341 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+Sources: Pie docs "The forward pass" (Lanes, State geometry, Attention masks,
+Readouts) and the two Pie reviews, section 2.1/2.2, Eqs. (1) and (2), and
+section 4 (whole prompt == prefix then continuation through the cache).
+"""
+
+import itertools
+import json
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+
+import bruteforce as bf
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------- Eq. (1), Eq. (2)
+
+def test_eq1_worked_example():
+    for c in _load("eq1_kv_bytes.json")["cases"]:
+        assert oracle.kv_bytes(c["L"], c["H_kv"], c["d"], c["T"], c["b"]) == c["bytes"]
+    assert oracle.kv_bytes(32, 8, 128, 1, 2) == 128 * 1024
+    assert oracle.kv_bytes(32, 8, 128, 8192, 2) == 1 << 30
+
+
+def test_eq2_golden_and_exhaustive():
+    for c in _load("eq2_page_waste.json")["cases"]:
+        assert oracle.pages_for(c["T"], c["P"]) == c["pages"]
+        assert oracle.page_waste(c["T"], c["P"]) == c["waste"]
+    for P in (1, 8, 16, 32):
+        for T in range(0, 65537):
+            w = oracle.page_waste(T, P)
+            assert 0 <= w < P
+            assert (T + w) % P == 0 and oracle.pages_for(T, P) * P == T + w
+
+
+def test_pool_bytes_match_eq1_per_page():
+    wl = W.make_config(1)
+    pool = oracle.Pool(wl.num_pages, wl.P, wl.H_kv, wl.d, wl.page_indptr, wl.page_ids)
+    assert pool.nbytes == wl.num_pages * oracle.kv_bytes(1, wl.H_kv, wl.d, wl.P, 2)
+    # 37 tokens in pages of 16: 3 pages, 11 unused slots (Eq. 2)
+    assert pool.nbytes == oracle.kv_bytes(1, 2, 64, 37, 2) + oracle.page_waste(37, 16) * 2 * 2 * 64 * 2
+    assert pool.nbytes == 24576
+
+
+# ----------------------------------------------------------------------------- bf16 rounding
+
+def test_bf16_rounding_matches_exact_rationals():
+    rng = np.random.default_rng(1)
+    xs = list(rng.standard_normal(3000) * np.exp(rng.uniform(-20, 20, 3000)))
+    # exact bf16 midpoints and their neighbours (tie cases and one-ulp-off cases)
+    for bits in rng.integers(0x0080, 0x7F00, size=400):
+        lo = bf16_value = struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+        hi = struct.unpack("<f", struct.pack("<I", (int(bits) + 1) << 16))[0]
+        mid = (lo + hi) / 2.0
+        xs += [mid, -mid, np.nextafter(mid, 0.0), np.nextafter(mid, np.inf), lo, hi]
+    xs = np.array(xs, dtype=np.float64)
+    got = oracle.f64_to_bf16(xs)
+    want = np.array([bf.bf16_round_exact(float(x)) for x in xs], dtype=np.uint16)
+    assert np.array_equal(got, want)
+    # exact round trip for bf16 values
+    b = rng.integers(0, 0x7F80, size=1000).astype(np.uint16)
+    assert np.array_equal(oracle.f64_to_bf16(oracle.bf16_to_f64(b)), b)
+
+
+# ----------------------------------------------------------------------------- RoPE
+
+def test_rope_identity_at_position_zero_and_norm():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((5, 3, 64))
+    assert np.array_equal(oracle.rope(x, np.zeros(5, int), 10000.0), x)
+    y = oracle.rope(x, rng.integers(0, 100000, 5), 10000.0)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+
+
+def test_rope_equals_complex_rotation():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 1, 16))
+    pos = np.array([0, 1, 17, 81234])
+    y = oracle.rope(x, pos, 10000.0)
+    for i in range(4):
+        ref = bf.rope_complex(list(x[i, 0]), int(pos[i]), 10000.0)
+        np.testing.assert_allclose(y[i, 0], ref, rtol=0, atol=1e-12)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 1, 32))
+    k = rng.standard_normal((1, 1, 32))
+    base = None
+    for m in (0, 5, 1000, 77777):
+        s = float((oracle.rope(q, [m + 9], 500.0) * oracle.rope(k, [m], 500.0)).sum())
+        base = s if base is None else base
+        assert abs(s - base) < 1e-9
+
+
+# ----------------------------------------------------------------------------- brute force
+
+def _as_bf_inputs(wl, rows_pass):
+    p = rows_pass
+    d = dict(indptr=p.indptr, positions=p.positions, slots=p.slots, kv_len=p.kv_len, fold=p.fold,
+             k=p.k.tolist(), v=p.v.tolist(), q=None if p.q is None else p.q.tolist())
+    return d
+
+
+def _mask_sets(wl):
+    """Decode LSB-first mask words into per-row slot sets (independent of the oracle)."""
+    if wl.mask_bits is None:
+        return None
+    st = wl.step
+    out = [None] * st.num_rows
+    for lane in range(st.num_lanes):
+        o0, o1 = int(wl.mask_word_offset[lane]), int(wl.mask_word_offset[lane + 1])
+        r0, r1 = int(st.indptr[lane]), int(st.indptr[lane + 1])
+        if o1 == o0:
+            continue
+        wpr = (o1 - o0) // (r1 - r0)
+        for r in range(r0, r1):
+            words = wl.mask_bits[o0 + (r - r0) * wpr: o0 + (r - r0 + 1) * wpr]
+            out[r] = {32 * wi + b for wi, wd in enumerate(words) for b in range(32) if (int(wd) >> b) & 1}
+    return out
+
+
+def _oracle_run(wl, fill=0):
+    pool = oracle.Pool(wl.num_pages, wl.P, wl.H_kv, wl.d, wl.page_indptr, wl.page_ids, fill_bits=fill)
+    committed = np.zeros(wl.num_lanes, np.int32)
+    if wl.prefix is not None:
+        p = wl.prefix
+        oracle.append(pool, committed, p.indptr, p.positions, p.slots, p.k, p.v, wl.theta)
+        committed, _ = oracle.fold(committed, p.indptr, p.fold)
+    res = oracle.step(pool, committed, wl.step, wl.H_q, wl.theta, wl.sm_scale, wl.mask_bits,
+                      wl.mask_word_offset, wl.channel, wl.readout_rows)
+    res["pool"] = pool
+    res["committed0"] = committed
+    return res
+
+
+def _bf_run(wl):
+    st = _as_bf_inputs(wl, wl.step)
+    st["mask"] = _mask_sets(wl)
+    st["channel"] = wl.channel
+    pre = _as_bf_inputs(wl, wl.prefix) if wl.prefix is not None else None
+    return bf.run(st, H_q=wl.H_q, H_kv=wl.H_kv, d=wl.d, theta=wl.theta, sm_scale=wl.sm_scale,
+                  cap=[int(c) for c in wl.capacity()], prefix=pre)
+
+
+def _compare_to_bruteforce(wl, res, ref):
+    O = np.array(ref["O"])
+    LSE = np.array(ref["LSE"])
+    assert np.max(np.abs(res["O"] - O)) <= 1e-12
+    fin = np.isfinite(LSE)
+    assert np.array_equal(fin, np.isfinite(res["LSE"]))
+    assert np.max(np.abs(res["LSE"][fin] - LSE[fin]), initial=0.0) <= 1e-12
+    assert list(res["committed"]) == list(ref["committed"])
+    # stored K/V: every slot the brute force holds matches the paged pool bit for bit
+    pool = res["pool"]
+    for lane, slots in enumerate(ref["store"]):
+        for s, (ks, vs) in slots.items():
+            pg, off = pool.locate(lane, s)
+            got_k = oracle.bf16_to_f64(pool.k[pg, :, off, :])
+            got_v = oracle.bf16_to_f64(pool.v[pg, :, off, :])
+            assert np.array_equal(got_k, np.array(ks)) and np.array_equal(got_v, np.array(vs))
+
+
+def _with_page_order(wl, order):
+    wl2 = W.make_config(1)
+    wl2.page_ids = np.asarray(order, dtype=np.int32)
+    return wl2
+
+
+def test_config1_all_page_orders_match_bruteforce_and_each_other():
+    wl = W.make_config(1)
+    ref = _bf_run(wl)
+    outs = []
+    for order in itertools.permutations(range(3)):
+        w2 = _with_page_order(wl, order)
+        res = _oracle_run(w2)
+        _compare_to_bruteforce(w2, res, ref)
+        outs.append(res)
+        # default readout: the lane's last row (row 36)
+        assert list(res["readout_rows"]) == [36]
+        assert np.array_equal(res["readout"][0], res["O"][36].reshape(-1))
+    for r in outs[1:]:
+        assert np.array_equal(r["O"], outs[0]["O"]) and np.array_equal(r["LSE"], outs[0]["LSE"])
+
+
+@pytest.mark.parametrize("seed,P,G,d", [(0, 1, 2, 16), (1, 2, 1, 16), (2, 4, 4, 8), (3, 16, 2, 16),
+                                         (4, 8, 8, 8), (5, 16, 1, 32)])
+def test_random_passes_match_bruteforce(seed, P, G, d):
+    wl = W.make_random(seed, H_kv=2, G=G, d=d, P=P, num_lanes=5, max_rows=20, max_ctx=40)
+    res = _oracle_run(wl)
+    ref = _bf_run(wl)
+    _compare_to_bruteforce(wl, res, ref)
+
+
+# ----------------------------------------------------------------------------- invariants
+
+def _split_config1(split):
+    """Config 1 as a prefix pass of `split` rows (folded all) followed by the rest."""
+    wl = W.make_config(1)
+    st = wl.step
+    pre = W.Pass(indptr=np.array([0, split], np.int32), positions=st.positions[:split], slots=st.slots[:split],
+                 kv_len=np.array([split], np.int32), fold=np.array([W.FOLD_ALL], np.int32),
+                 k=st.k[:split], v=st.v[:split], q=st.q[:split])
+    post = W.Pass(indptr=np.array([0, 37 - split], np.int32), positions=st.positions[split:], slots=st.slots[split:],
+                  kv_len=np.array([37], np.int32), fold=np.array([W.FOLD_ALL], np.int32),
+                  k=st.k[split:], v=st.v[split:], q=st.q[split:])
+    return wl, pre, post
+
+
+def test_whole_prompt_equals_prefix_then_continuation():
+    wl = W.make_config(1)
+    whole = _oracle_run(wl)
+    for split in range(1, 37):
+        _, pre, post = _split_config1(split)
+        pool = oracle.Pool(wl.num_pages, wl.P, wl.H_kv, wl.d, wl.page_indptr, wl.page_ids)
+        c = np.zeros(1, np.int32)
+        r1 = oracle.step(pool, c, pre, wl.H_q, wl.theta, wl.sm_scale)
+        r2 = oracle.step(pool, r1["committed"], post, wl.H_q, wl.theta, wl.sm_scale)
+        assert np.array_equal(np.concatenate([r1["O"], r2["O"]]), whole["O"])
+        assert np.array_equal(np.concatenate([r1["LSE"], r2["LSE"]]), whole["LSE"])
+        assert np.array_equal(pool.k, whole["pool"].k) and np.array_equal(pool.v, whole["pool"].v)
+        assert int(r2["committed"][0]) == 37
+
+
+def test_all_causal_bitmap_equals_folding():
+    wl = W.make_config(1)
+    base = _oracle_run(wl)
+    j = np.arange(64)
+    rows = []
+    for r in range(37):
+        allowed = (j <= wl.step.slots[r])
+        rows.append([int(sum(1 << b for b in range(32) if allowed[32 * w + b])) for w in range(2)])
+    wl.mask_bits = np.array(rows, dtype=np.uint32).reshape(-1)
+    wl.mask_word_offset = np.array([0, 74], dtype=np.int64)
+    masked = _oracle_run(wl)
+    assert np.array_equal(masked["O"], base["O"]) and np.array_equal(masked["LSE"], base["LSE"])
+
+
+def test_single_slot_row_returns_its_value_exactly():
+    wl = W.make_config(1)
+    res = _oracle_run(wl)
+    # row 0 of a fresh lane sees only slot 0: softmax weight 1
+    pg, off = res["pool"].locate(0, 0)
+    V0 = oracle.bf16_to_f64(res["pool"].v[pg, :, off, :])
+    G = wl.H_q // wl.H_kv
+    for h in range(wl.H_q):
+        assert np.array_equal(res["O"][0, h], V0[h // G])
+
+
+def test_zero_query_gives_mean_of_allowed_values():
+    wl = W.make_config(1)
+    wl.step.q[:] = 0
+    res = _oracle_run(wl)
+    K, V = res["pool"].lane_kv(0, 37)
+    G = wl.H_q // wl.H_kv
+    for r in (0, 5, 36):
+        for h in range(wl.H_q):
+            np.testing.assert_allclose(res["O"][r, h], V[: r + 1, h // G].mean(axis=0), rtol=0, atol=1e-14)
+            assert abs(res["LSE"][r, h] - math.log(r + 1)) < 1e-14
+
+
+def test_empty_allowed_set_gives_zero_and_minus_inf():
+    wl = W.make_config(1)
+    wl.mask_bits = np.zeros(37 * 2, dtype=np.uint32)
+    wl.mask_word_offset = np.array([0, 74], dtype=np.int64)
+    res = _oracle_run(wl)
+    assert np.all(res["O"] == 0) and np.all(np.isneginf(res["LSE"]))
+
+
+def test_page_permutation_with_decoys_is_bit_invariant():
+    wl = W.make_random(11, H_kv=2, G=2, d=16, P=4, num_lanes=5, max_rows=20, max_ctx=40, extra_pages=6)
+    a = _oracle_run(wl, fill=0x7FC0)
+    rng = np.random.default_rng(5)
+    wl.page_ids = rng.permutation(wl.num_pages)[: len(wl.page_ids)].astype(np.int32)
+    b = _oracle_run(wl, fill=0x7FC0)
+    assert np.array_equal(a["O"], b["O"]) and np.array_equal(a["LSE"], b["LSE"])
+    assert np.all(np.isfinite(a["O"]))
+
+
+# ----------------------------------------------------------------------------- fold, readout, errors
+
+def test_fold_closed_form_and_channel_clamp():
+    indptr = np.array([0, 3, 3, 11, 19, 27, 28])
+    spec = np.array([W.FOLD_ALL, W.FOLD_ALL, 5, W.FOLD_CHANNEL, W.FOLD_CHANNEL, 0])
+    chan = np.array([0, 0, 0, 4, 12, 0])
+    c0 = np.array([10, 20, 30, 40, 50, 60])
+    c1, st = oracle.fold(c0, indptr, spec, chan)
+    assert list(c1) == [13, 20, 35, 44, 58, 60]
+    assert st == oracle.ST_FOLD_CLAMP
+    c2, st2 = oracle.fold(c0, indptr, spec, np.array([0, 0, 0, 4, 8, 0]))
+    assert list(c2) == [13, 20, 35, 44, 58, 60] and st2 == 0
+    c3, st3 = oracle.fold(c0, indptr, np.array([9, -7, 0, 0, 0, 0]), None)
+    assert list(c3) == [13, 20, 30, 40, 50, 60] and st3 == oracle.ST_FOLD_CLAMP
+
+
+def test_default_readout_is_last_row_of_each_lane():
+    g = _load("lanes_indptr.json")
+    assert list(oracle.readout_rows(np.array(g["indptr"]))) == g["default_readout_rows"]
+    assert list(oracle.readout_rows(np.array([0, 0, 4, 4, 5]))) == [3, 4]
+    O = np.arange(12.0).reshape(6, 2)
+    out, st = oracle.readout(O, 6, [5, 0, 9])
+    assert st == oracle.ST_READOUT_RANGE and out.tolist() == [[10, 11], [0, 1], [0, 0]]
+
+
+def test_suppressed_writes_and_status():
+    wl = W.make_config(1)
+    pool = oracle.Pool(wl.num_pages, wl.P, wl.H_kv, wl.d, wl.page_indptr, wl.page_ids, fill_bits=0x1234)
+    st = wl.step
+    slots = st.slots.copy()
+    slots[3] = 48          # capacity is 3 pages x 16 = 48
+    slots[4] = -1
+    s = oracle.append(pool, np.array([2]), st.indptr, st.positions, slots, st.k, st.v, wl.theta)
+    assert s == oracle.ST_SLOT_RANGE | oracle.ST_FROZEN
+    for bad_slot in (0, 1):  # frozen
+        pg, off = pool.locate(0, bad_slot)
+        assert np.all(pool.k[pg, :, off, :] == 0x1234)
+    pg, off = pool.locate(0, 2)
+    assert not np.all(pool.v[pg, :, off, :] == 0x1234)
+
+
+def test_kv_len_beyond_capacity_is_clamped_and_flagged():
+    wl = W.make_config(1)
+    wl.step.kv_len[:] = 60
+    res = _oracle_run(wl)
+    assert res["status"] & oracle.ST_KVLEN
+    wl2 = W.make_config(1)
+    base = _oracle_run(wl2)
+    assert np.array_equal(res["O"], base["O"])

@@ -1,0 +1,414 @@
+"""Seeded synthetic workloads shaped like the Pie ForwardPass attention step.
+
+Every array here is an *input*: row offsets, slots, positions, page tables,
+mask bitmaps, device-channel counts and bf16 bit patterns of Q/K/V. The
+method's arithmetic (RoPE, attention, fold, readout) lives elsewhere.
+
+Workload shapes follow the five configurations of the hot path:
+  1  one lane, 37-token prompt, GQA 4/2, d=64, 3 shuffled pages of 16
+  2  decode wave: 64 lanes x 1 row, kv_len ~ U{512..8192}, 32/8 heads, d=128, P=16
+  3  mixed wave: 8 prefill lanes (1024-4096 rows on 0-2048 cached slots)
+     plus 120 decode lanes (kv_len 256-16384), P=32
+  4  guidance pairs (cond prefix 2048, uncond prefix 512) plus 32 speculative
+     verify lanes of 8 draft rows whose fold count comes from a device channel
+  5  16 lanes x 512-row chunks over kv_len 32768 with non-contiguous positions,
+     sliding-window+sink masks on half the lanes, TOVA-style random drops on the rest
+
+Random streams are child seeds of one SeedSequence, drawn in a fixed order
+(lengths, permutation, prefix K/V, Q, K, V, mask, channel), so a workload is a
+pure function of (config, seed, scale).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+# Fold sentinels of the C ABI (a literal count is any value >= 0).
+FOLD_ALL = -1
+FOLD_CHANNEL = -2
+
+CONFIG_NAMES = {
+    1: "single_lane_gqa_37",
+    2: "decode_wave_64",
+    3: "mixed_prefill_decode_128",
+    4: "guidance_spec_verify_48",
+    5: "long_context_masks_16",
+}
+
+_STREAMS = ("lengths", "perm", "prefix_kv", "q", "k", "v", "mask", "channel")
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 samples to bf16 (nearest-even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def _normal_bf16(rng: np.random.Generator, shape, chunk_rows: int = 1 << 14) -> np.ndarray:
+    """N(0,1) float32 draws rounded to bf16, generated in row chunks to bound memory."""
+    shape = tuple(int(s) for s in shape)
+    out = np.empty(shape, dtype=np.uint16)
+    if out.size == 0:
+        return out
+    rows = shape[0]
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        out[r0:r1] = bf16_bits_from_f32(rng.standard_normal((r1 - r0,) + shape[1:], dtype=np.float32))
+    return out
+
+
+@dataclass
+class Pass:
+    """One ForwardPass worth of rows (concatenated by lane, offsets in indptr)."""
+
+    indptr: np.ndarray      # int32 [L+1]
+    positions: np.ndarray   # int32 [N]
+    slots: np.ndarray       # int32 [N]
+    kv_len: np.ndarray      # int32 [L]
+    fold: np.ndarray        # int32 [L]: >=0 literal, FOLD_ALL, FOLD_CHANNEL
+    k: np.ndarray           # uint16 bf16 bits [N][H_kv][d]
+    v: np.ndarray           # uint16 bf16 bits [N][H_kv][d]
+    q: Optional[np.ndarray] = None  # uint16 bf16 bits [N][H_q][d]
+
+    @property
+    def num_lanes(self) -> int:
+        return int(self.indptr.shape[0] - 1)
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.indptr[-1])
+
+
+@dataclass
+class Workload:
+    name: str
+    H_q: int
+    H_kv: int
+    d: int
+    P: int
+    theta: float
+    sm_scale: float
+    num_pages: int
+    page_indptr: np.ndarray          # int32 [L+1]
+    page_ids: np.ndarray             # int32 [page_indptr[-1]]
+    prefix: Optional[Pass]           # appended and folded (all) before the step
+    step: Pass
+    mask_bits: Optional[np.ndarray] = None         # uint32 words
+    mask_word_offset: Optional[np.ndarray] = None  # int64 [L+1]
+    channel: Optional[np.ndarray] = None           # int32 [L]
+    readout_rows: Optional[np.ndarray] = None      # int32 list of global rows; None = default
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_lanes(self) -> int:
+        return self.step.num_lanes
+
+    def capacity(self) -> np.ndarray:
+        return (np.diff(self.page_indptr).astype(np.int64) * self.P).astype(np.int64)
+
+
+def _rngs(seed: int):
+    ss = np.random.SeedSequence(int(seed))
+    kids = ss.spawn(len(_STREAMS))
+    return {name: np.random.default_rng(kid) for name, kid in zip(_STREAMS, kids)}
+
+
+def _assemble(
+    name: str,
+    rngs,
+    *,
+    H_q: int,
+    H_kv: int,
+    d: int,
+    P: int,
+    lanes: List[dict],
+    theta: float = 10000.0,
+    shuffle_lanes: bool = True,
+    extra_pages: int = 0,
+    mask_fn=None,
+    readout_fn=None,
+    channel_fn=None,
+) -> Workload:
+    """Lay out lanes into a paged pool.
+
+    Each lane dict holds: c (cached prefix length), n (rows this pass), kv_len,
+    fold, pos_of_slot (int64 array over all slots the lane uses) and optional
+    'slots' (default c..c+n-1), 'pages' (default ceil(kv_len/P)).
+    """
+    L = len(lanes)
+    order = rngs["perm"].permutation(L) if shuffle_lanes and L > 1 else np.arange(L)
+    lanes = [lanes[i] for i in order]
+
+    pages = np.array([int(ln.get("pages", -(-max(ln["kv_len"], 1) // P))) for ln in lanes], dtype=np.int64)
+    page_indptr = np.zeros(L + 1, dtype=np.int64)
+    page_indptr[1:] = np.cumsum(pages)
+    num_pages = int(page_indptr[-1]) + int(extra_pages)
+    perm = rngs["perm"].permutation(num_pages).astype(np.int32)
+    page_ids = perm[: int(page_indptr[-1])].copy()
+
+    # Prefix pass: slots 0..c-1 of each lane at their positions, folded all.
+    pre_counts = np.array([ln["c"] for ln in lanes], dtype=np.int64)
+    pre_indptr = np.zeros(L + 1, dtype=np.int64)
+    pre_indptr[1:] = np.cumsum(pre_counts)
+    Np = int(pre_indptr[-1])
+    pre_slots = np.concatenate([np.arange(ln["c"], dtype=np.int64) for ln in lanes]) if Np else np.zeros(0, np.int64)
+    pre_pos = np.concatenate([ln["pos_of_slot"][: ln["c"]] for ln in lanes]) if Np else np.zeros(0, np.int64)
+    pre_k = _normal_bf16(rngs["prefix_kv"], (Np, H_kv, d))
+    pre_v = _normal_bf16(rngs["prefix_kv"], (Np, H_kv, d))
+    prefix = None
+    if Np:
+        prefix = Pass(
+            indptr=pre_indptr.astype(np.int32),
+            positions=pre_pos.astype(np.int32),
+            slots=pre_slots.astype(np.int32),
+            kv_len=pre_counts.astype(np.int32),
+            fold=np.full(L, FOLD_ALL, dtype=np.int32),
+            k=pre_k,
+            v=pre_v,
+        )
+
+    counts = np.array([ln["n"] for ln in lanes], dtype=np.int64)
+    indptr = np.zeros(L + 1, dtype=np.int64)
+    indptr[1:] = np.cumsum(counts)
+    N = int(indptr[-1])
+    slot_list, pos_list = [], []
+    for ln in lanes:
+        s = np.asarray(ln.get("slots", np.arange(ln["c"], ln["c"] + ln["n"])), dtype=np.int64)
+        slot_list.append(s)
+        pos_list.append(ln["pos_of_slot"][s] if len(s) else np.zeros(0, np.int64))
+    slots = np.concatenate(slot_list) if N else np.zeros(0, np.int64)
+    positions = np.concatenate(pos_list) if N else np.zeros(0, np.int64)
+    q = _normal_bf16(rngs["q"], (N, H_q, d))
+    k = _normal_bf16(rngs["k"], (N, H_kv, d))
+    v = _normal_bf16(rngs["v"], (N, H_kv, d))
+    step = Pass(
+        indptr=indptr.astype(np.int32),
+        positions=positions.astype(np.int32),
+        slots=slots.astype(np.int32),
+        kv_len=np.array([ln["kv_len"] for ln in lanes], dtype=np.int32),
+        fold=np.array([ln["fold"] for ln in lanes], dtype=np.int32),
+        k=k,
+        v=v,
+        q=q,
+    )
+
+    wl = Workload(
+        name=name,
+        H_q=H_q,
+        H_kv=H_kv,
+        d=d,
+        P=P,
+        theta=float(theta),
+        sm_scale=float(1.0 / np.sqrt(d)),
+        num_pages=num_pages,
+        page_indptr=page_indptr.astype(np.int32),
+        page_ids=page_ids,
+        prefix=prefix,
+        step=step,
+        meta={"lanes": [{k_: v_ for k_, v_ in ln.items() if k_ != "pos_of_slot"} for ln in lanes]},
+    )
+    if mask_fn is not None:
+        bits, offs = mask_fn(rngs["mask"], lanes, step)
+        wl.mask_bits, wl.mask_word_offset = bits, offs
+    if channel_fn is not None:
+        wl.channel = channel_fn(rngs["channel"], lanes)
+    if readout_fn is not None:
+        wl.readout_rows = readout_fn(lanes, step)
+    return wl
+
+
+def _ident_pos(n: int) -> np.ndarray:
+    return np.arange(n, dtype=np.int64)
+
+
+def _pack_lsb_first(allowed: np.ndarray) -> np.ndarray:
+    """bool [rows, 32*w] -> uint32 [rows, w]; bit b of word w is slot 32*w + b."""
+    rows, width = allowed.shape
+    w = width // 32
+    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+    return (allowed.reshape(rows, w, 32).astype(np.uint64) * weights).sum(axis=2).astype(np.uint32)
+
+
+def _bitmap_rows(lanes, step, rng):
+    """Per-row slot bitmaps for lanes that carry a mask (uint32 words, LSB first).
+
+    Each masked lane stores ceil(kv_len/32) words per row, rows in order; its
+    span is [offs[l], offs[l+1]). Lanes without a mask get an empty span and
+    keep the causal rule.
+    """
+    L = len(lanes)
+    offs = np.zeros(L + 1, dtype=np.int64)
+    chunks = []
+    for li, ln in enumerate(lanes):
+        n = ln["n"]
+        if ln.get("mask") is None or n == 0:
+            offs[li + 1] = offs[li]
+            continue
+        kvl = int(ln["kv_len"])
+        wpr = -(-kvl // 32)
+        r0 = int(step.indptr[li])
+        slot = step.slots[r0:r0 + n].astype(np.int64)[:, None]
+        allowed = np.zeros((n, wpr * 32), dtype=bool)
+        allowed[:, :kvl] = _mask_rule(ln["mask"], slot, np.arange(kvl, dtype=np.int64)[None, :], rng)
+        chunks.append(_pack_lsb_first(allowed).reshape(-1))
+        offs[li + 1] = offs[li] + n * wpr
+    bits = np.concatenate(chunks) if chunks else np.zeros(0, dtype=np.uint32)
+    return bits, offs
+
+
+def _mask_rule(m, slot, j, rng):
+    """Slot predicate for one lane: slot is [n,1] (row slots), j is [1,kv_len]."""
+    kind = m["kind"]
+    if kind == "window":      # sliding window of `window` slots ending at the row, plus sink slots
+        return (j < m["sinks"]) | ((j > slot - m["window"]) & (j <= slot))
+    if kind == "tova":        # causal, minus a random `drop` fraction; the row's own slot is kept
+        u = rng.random((slot.shape[0], j.shape[1]))
+        return (j <= slot) & ((j == slot) | (u >= m["drop"]))
+    if kind == "causal":
+        return np.broadcast_to(j <= slot, (slot.shape[0], j.shape[1]))
+    if kind == "random":      # not causal at all: any slot below kv_len may be chosen
+        return rng.random((slot.shape[0], j.shape[1])) < m["density"]
+    if kind == "empty":
+        return np.zeros((slot.shape[0], j.shape[1]), dtype=bool)
+    raise ValueError(kind)
+
+
+def _make_mask(rng, lanes, step):
+    return _bitmap_rows(lanes, step, rng)
+
+
+# --------------------------------------------------------------------------- configs
+
+
+def _config1(rngs, scale):
+    lanes = [dict(c=0, n=37, kv_len=37, fold=FOLD_ALL, pos_of_slot=_ident_pos(37))]
+    return _assemble(CONFIG_NAMES[1], rngs, H_q=4, H_kv=2, d=64, P=16, lanes=lanes)
+
+
+def _config2(rngs, scale):
+    L, lo, hi = (64, 512, 8192) if scale == "full" else (6, 33, 700)
+    kvs = rngs["lengths"].integers(lo, hi + 1, size=L)
+    lanes = [dict(c=int(kv) - 1, n=1, kv_len=int(kv), fold=FOLD_ALL, pos_of_slot=_ident_pos(int(kv))) for kv in kvs]
+    return _assemble(CONFIG_NAMES[2], rngs, H_q=32, H_kv=8, d=128, P=16, lanes=lanes)
+
+
+def _config3(rngs, scale):
+    if scale == "full":
+        Lp, n_rng, c_rng, Ld, kv_rng = 8, (1024, 4096), (0, 2048), 120, (256, 16384)
+    else:
+        Lp, n_rng, c_rng, Ld, kv_rng = 2, (40, 150), (0, 90), 5, (20, 500)
+    g = rngs["lengths"]
+    ns = g.integers(n_rng[0], n_rng[1] + 1, size=Lp)
+    cs = g.integers(c_rng[0], c_rng[1] + 1, size=Lp)
+    kvs = g.integers(kv_rng[0], kv_rng[1] + 1, size=Ld)
+    lanes = [dict(c=int(c), n=int(n), kv_len=int(c + n), fold=FOLD_ALL, pos_of_slot=_ident_pos(int(c + n))) for n, c in zip(ns, cs)]
+    lanes += [dict(c=int(kv) - 1, n=1, kv_len=int(kv), fold=FOLD_ALL, pos_of_slot=_ident_pos(int(kv))) for kv in kvs]
+    return _assemble(CONFIG_NAMES[3], rngs, H_q=32, H_kv=8, d=128, P=32, lanes=lanes)
+
+
+def _config4(rngs, scale):
+    if scale == "full":
+        pairs, c_cond, c_unc, Lv, c_hi = 8, 2048, 512, 32, 4088
+    else:
+        pairs, c_cond, c_unc, Lv, c_hi = 2, 200, 60, 4, 300
+    g = rngs["lengths"]
+    lanes = []
+    for _ in range(pairs):
+        lanes.append(dict(c=c_cond, n=1, kv_len=c_cond + 1, fold=FOLD_ALL, pos_of_slot=_ident_pos(c_cond + 1), role="cond"))
+        lanes.append(dict(c=c_unc, n=1, kv_len=c_unc + 1, fold=FOLD_ALL, pos_of_slot=_ident_pos(c_unc + 1), role="uncond"))
+    for c in g.integers(0, c_hi + 1, size=Lv):
+        c = int(c)
+        lanes.append(dict(c=c, n=8, kv_len=c + 8, fold=FOLD_CHANNEL, pos_of_slot=_ident_pos(c + 8), role="verify"))
+
+    def channel_fn(rng, lanes_):
+        return np.array([int(rng.integers(0, 9)) if ln["role"] == "verify" else 0 for ln in lanes_], dtype=np.int32)
+
+    def readout_fn(lanes_, step):
+        rows = []
+        for li, ln in enumerate(lanes_):
+            r0, r1 = int(step.indptr[li]), int(step.indptr[li + 1])
+            if ln["role"] == "verify":
+                rows.extend(range(r0, r1))
+            elif r1 > r0:
+                rows.append(r1 - 1)
+        return np.array(rows, dtype=np.int32)
+
+    return _assemble(CONFIG_NAMES[4], rngs, H_q=32, H_kv=8, d=128, P=16, lanes=lanes,
+                     channel_fn=channel_fn, readout_fn=readout_fn)
+
+
+def _config5(rngs, scale):
+    if scale == "full":
+        L, n, kvl, window, H_q = 16, 512, 32768, 1024, 64
+    else:
+        L, n, kvl, window, H_q = 4, 64, 1024, 128, 64
+    g = rngs["lengths"]
+    kinds = np.array(["window"] * (L // 2) + ["tova"] * (L - L // 2))
+    kinds = kinds[g.permutation(L)]
+    lanes = []
+    for kind in kinds:
+        gaps = g.integers(1, 5, size=kvl).astype(np.int64)
+        gaps[0] = 0
+        pos = np.cumsum(gaps)
+        mask = dict(kind="window", window=window, sinks=4) if kind == "window" else dict(kind="tova", drop=0.3)
+        lanes.append(dict(c=kvl - n, n=n, kv_len=kvl, fold=FOLD_ALL, pos_of_slot=pos, mask=mask))
+    return _assemble(CONFIG_NAMES[5], rngs, H_q=H_q, H_kv=8, d=128, P=16, lanes=lanes, mask_fn=_make_mask)
+
+
+_BUILDERS = {1: _config1, 2: _config2, 3: _config3, 4: _config4, 5: _config5}
+
+
+def make_config(k: int, seed: int = 0, scale: str = "full") -> Workload:
+    """Build configuration k (1..5). scale='full' gives the benchmark sizes,
+    scale='small' a reduced copy (same structure, a few tiles per lane and a
+    ragged tail) that the CPU oracle finishes in seconds."""
+    if scale not in ("full", "small"):
+        raise ValueError(scale)
+    wl = _BUILDERS[int(k)](_rngs(seed), scale)
+    wl.meta.update(config=int(k), seed=int(seed), scale=scale)
+    return wl
+
+
+def make_random(seed: int, *, H_kv: int = 2, G: int = 2, d: int = 64, P: int = 16,
+                num_lanes: int = 6, max_rows: int = 80, max_ctx: int = 300,
+                masked: bool = True, fold_modes: bool = True, extra_pages: int = 3) -> Workload:
+    """A random small pass mixing prefill, decode, verify and empty lanes, causal
+    and bitmap lanes, and every fold mode (literal, all, channel, out-of-range)."""
+    rngs = _rngs(seed)
+    g = rngs["lengths"]
+    lanes = []
+    for i in range(num_lanes):
+        kind = g.integers(0, 4)
+        if kind == 0:      # decode
+            n = 1
+        elif kind == 1:    # verify-like window
+            n = int(g.integers(2, 9))
+        elif kind == 2:    # prefill chunk
+            n = int(g.integers(9, max_rows + 1))
+        else:              # empty lane (reads nothing this pass)
+            n = 0
+        c = int(g.integers(0, max_ctx + 1))
+        kv = c + n
+        extra = int(g.integers(0, 2 * P))  # spare capacity beyond kv_len
+        ln = dict(c=c, n=n, kv_len=kv, pages=-(-max(kv + extra, 1) // P), pos_of_slot=np.cumsum(g.integers(1, 3, size=kv + extra + 1)) - 1)
+        if fold_modes:
+            fm = int(g.integers(0, 4))
+            ln["fold"] = [FOLD_ALL, FOLD_CHANNEL, int(g.integers(0, n + 1)), 0][fm]
+        else:
+            ln["fold"] = FOLD_ALL
+        if masked and n > 0 and g.random() < 0.5:
+            mk = ["window", "tova", "causal", "random"][int(g.integers(0, 4))]
+            ln["mask"] = dict(kind=mk, window=int(g.integers(1, 70)), sinks=int(g.integers(0, 5)), drop=0.3, density=0.4)
+        lanes.append(ln)
+
+    def channel_fn(rng, lanes_):
+        # includes out-of-range counts to exercise clamping
+        return np.array([int(rng.integers(-2, 12)) for _ in lanes_], dtype=np.int32)
+
+    return _assemble(f"random_{seed}", rngs, H_q=H_kv * G, H_kv=H_kv, d=d, P=P, lanes=lanes,
+                     extra_pages=extra_pages, mask_fn=_make_mask if masked else None,
+                     channel_fn=channel_fn)
