@@ -1,0 +1,198 @@
+/*
+ * fp.h - C ABI of the ForwardPass attention step on a paged KV pool (MI355X / gfx950).
+ *
+ * One pass carries several lanes (independent sequences) whose rows are
+ * concatenated and addressed by a row-offset array `indptr`, all run in one
+ * launch per stage (Pie docs, "The forward pass", section Lanes). Its
+ * StateGeometry gives, per row, a RoPE position and the working-set slot the
+ * row writes, and per lane, how many slots attention reads (kv_len) and how
+ * many newly written slots to freeze afterwards (fold) (section State
+ * geometry, field table). A lane may carry a per-row slot bitmap instead of
+ * the causal rule (section Attention masks); the caller picks readout rows
+ * (section Readouts). KV state is paged (Pie reviews, section 2.1/2.2,
+ * Eqs. (1) and (2)); the pages of a lane's working set are listed in slot order.
+ *
+ * A step is four calls, enqueued in this order on one stream:
+ *   fp_append_kv -> fp_attend -> fp_fold -> fp_readout.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless the name ends in `_host`.
+ *  - bf16 values are passed as 16-bit storage (bit patterns).
+ *  - The caller owns every buffer; the library allocates no memory, keeps no
+ *    state between calls and never synchronizes. Buffers must stay valid until
+ *    the work enqueued on `stream` has completed. `stream` may be NULL (the
+ *    default stream).
+ *  - Errors the host can see are returned synchronously, before anything is
+ *    enqueued (FP_ERR_*). Errors that depend on device data never stop the
+ *    stream: the kernel ORs a bit into *status (an int32 the caller zeroes)
+ *    and suppresses or clamps the offending access (FP_ST_*).
+ *  - Calls that overlap on one stream run in order (like passes on a Pie
+ *    Pipeline); two streams writing the same pool pages race.
+ */
+#ifndef FP_H_
+#define FP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;   /* same opaque type as HIP's */
+
+/* ---- return codes (host-detected, nothing enqueued) ---- */
+#define FP_OK               0
+#define FP_ERR_NULL        (-1)   /* a required pointer is NULL                              */
+#define FP_ERR_SHAPE       (-2)   /* inconsistent sizes (e.g. H_q % H_kv != 0, num_lanes < 1) */
+#define FP_ERR_UNSUPPORTED (-3)   /* head_dim not 64/128, page_size not 8/16/32, ...          */
+#define FP_ERR_WORKSPACE   (-4)   /* workspace smaller than fp_attend_workspace_bytes()       */
+#define FP_ERR_HIP         (-5)   /* a HIP launch failed                                      */
+
+/* ---- device status bits (ORed into *status) ---- */
+#define FP_ST_SLOT_RANGE     1    /* row slot outside [0, capacity): its write suppressed     */
+#define FP_ST_FROZEN         2    /* row slot below committed_len: its write suppressed      */
+#define FP_ST_KVLEN          4    /* kv_len outside [0, capacity]: clamped                    */
+#define FP_ST_FOLD_CLAMP     8    /* fold count outside [0, rows of lane]: clamped            */
+#define FP_ST_READOUT_RANGE 16    /* readout row outside [0, num_rows): zero row written      */
+#define FP_ST_MASK_SHORT    32    /* mask row has fewer than kv_len bits: missing bits are 0  */
+#define FP_ST_PAGE_RANGE    64    /* page id outside [0, num_pages): write suppressed, read clamped */
+#define FP_ST_PLAN_MISMATCH 128   /* device offset arrays disagree with their host copies:
+                                     fp_attend did no attention work (outputs untouched)      */
+
+/* ---- fold sentinels (StateGeometry.fold; a value >= 0 is a literal count) ---- */
+#define FP_FOLD_ALL      (-1)     /* freeze every row written this pass                       */
+#define FP_FOLD_CHANNEL  (-2)     /* freeze channel[lane] rows, a count written on the device */
+
+/*
+ * StateGeometry of one pass (Pie docs, "The forward pass", State geometry).
+ * Rows of lane l are [indptr[l], indptr[l+1]).
+ */
+typedef struct fp_geometry {
+    int32_t num_lanes;           /* L >= 1                                                    */
+    int32_t num_rows;            /* N = indptr[L]                                             */
+    const int32_t *indptr;       /* [L+1] row offsets, non-decreasing, indptr[0] = 0          */
+    const int32_t *indptr_host;  /* [L+1] host copy of indptr: used to size launches only     */
+    const int32_t *positions;    /* [N] RoPE position id of each row                          */
+    const int32_t *slots;        /* [N] working-set slot each row writes                      */
+    const int32_t *kv_len;       /* [L] slots each lane reads this pass                       */
+    const int32_t *fold;         /* [L] literal count >= 0, FP_FOLD_ALL or FP_FOLD_CHANNEL    */
+} fp_geometry;
+
+/*
+ * One attention layer of the paged KV pool.
+ *
+ * Page layout (bf16, page p at element offset p * 2*H*P*d):
+ *     K block  [H][P][d]   K[h][o][:] is slot o of the page, rotated by RoPE
+ *     V block  [H][d][P]   V stored transposed: V[h][:][o] is slot o
+ * Slot s of lane l lives in page page_ids[page_indptr[l] + s / P] at offset
+ * s % P. Lane l's capacity is (page_indptr[l+1] - page_indptr[l]) * P slots.
+ * Pages may be shared read-only between lanes; a page written this pass must
+ * belong to exactly one lane.
+ */
+typedef struct fp_kv_pool {
+    void *kv;                        /* bf16 pages, num_pages * 2*H*P*d elements             */
+    int32_t num_pages;
+    int32_t page_size;               /* P in {8, 16, 32}                                      */
+    int32_t num_kv_heads;            /* H                                                     */
+    int32_t head_dim;                /* d in {64, 128}                                        */
+    const int32_t *page_indptr;      /* [L+1] offsets into page_ids                           */
+    const int32_t *page_indptr_host; /* [L+1] host copy: used to size launches only           */
+    const int32_t *page_ids;         /* [page_indptr[L]] physical page of each working-set page */
+    int32_t *committed_len;          /* [L] frozen slots per lane; fp_fold adds to it         */
+} fp_kv_pool;
+
+/*
+ * Per-row slot bitmaps (Pie docs, "The forward pass", Attention masks).
+ * Lane l's words are bits[word_offset[l] .. word_offset[l+1]); an empty span
+ * means the lane keeps the causal rule. A non-empty span holds, for each of
+ * the lane's rows in order, the same number of uint32 words (span / rows);
+ * bit b of word w (LSB first) says the row attends slot 32*w + b. The bitmap
+ * replaces the causal rule for its lane; bits at or beyond kv_len are ignored.
+ */
+typedef struct fp_mask {
+    const uint32_t *bits;
+    const int64_t *word_offset;       /* [L+1]                                                */
+    const int64_t *word_offset_host;  /* [L+1] host copy: used to size launches only          */
+} fp_mask;
+
+/* Optional tuning; pass NULL for defaults. Results do not depend on it beyond fp rounding. */
+typedef struct fp_tuning {
+    int32_t decode_split_slots;       /* KV slots per decode work item, multiple of 32 (0 = default) */
+    int32_t reserved[7];              /* must be zero                                          */
+} fp_tuning;
+
+/*
+ * fp_append_kv - write each row's K (RoPE-rotated at positions[r]) and V into
+ * slot slots[r] of its lane's working set (State geometry: positions, slots;
+ * folding appends rows causally).
+ *   k, v : bf16 [N][H][d], un-rotated K and V of the pass's rows.
+ *   RoPE : pairs (2i, 2i+1) rotated by positions[r] * rope_theta^(-2i/d),
+ *          computed in fp64 and rounded once to bf16.
+ * A write whose slot is outside the lane's capacity (FP_ST_SLOT_RANGE) or below
+ * committed_len (FP_ST_FROZEN) is suppressed. Two rows of one pass writing the
+ * same slot of one lane is undefined.
+ */
+int fp_append_kv(const fp_kv_pool *pool, const fp_geometry *geom, const void *k, const void *v,
+                 float rope_theta, int32_t *status, hipStream_t stream);
+
+/* Workspace bytes fp_attend needs for this geometry (host-only, reads *_host arrays). */
+int64_t fp_attend_workspace_bytes(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *mask,
+                                  int32_t num_q_heads, const fp_tuning *tuning);
+
+/*
+ * fp_attend - softmax attention of every row over its lane's first kv_len
+ * slots (State geometry: kv_len; Attention masks).
+ *   q   : bf16 [N][H_q][d], un-rotated; rotated at positions[r] like K.
+ *   rule: without a bitmap, row r reads slots j <= slots[r] (j < kv_len);
+ *         with one, the slots whose bits are set (j < kv_len).
+ *   GQA : query head q reads KV head q / (H_q / H_kv).
+ *   out : fp32 [N][H_q][d]; lse: fp32 [N][H_q] natural-log sum-exp (nullable).
+ *         A row with no readable slot gets out = 0 and lse = -inf.
+ *   sm_scale multiplies q.k (use 1/sqrt(d) for the usual scaling).
+ *   mask may be NULL (every lane causal).
+ * Slots at or beyond kv_len are never read, whatever they hold.
+ */
+int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, int32_t num_q_heads,
+              float rope_theta, float sm_scale, const fp_mask *mask, float *out, float *lse,
+              void *workspace, size_t workspace_bytes, const fp_tuning *tuning,
+              int32_t *status, hipStream_t stream);
+
+/*
+ * fp_fold - after the pass, freeze k_l newly written slots of every lane:
+ * committed_len[l] += k_l, where k_l = fold[l] (literal), the lane's row count
+ * (FP_FOLD_ALL) or channel[l] (FP_FOLD_CHANNEL, a count another kernel wrote on
+ * the device, read without a host round trip). Counts are clamped to
+ * [0, rows of lane] (FP_ST_FOLD_CLAMP). channel may be NULL if no lane uses it
+ * (a lane that does then folds 0 and sets FP_ST_FOLD_CLAMP).
+ * (State geometry: fold; speculative-decoding paragraph.)
+ */
+int fp_fold(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *channel,
+            int32_t *status, hipStream_t stream);
+
+/*
+ * fp_readout - gather readout rows of `out` (Readouts section).
+ *   rows == NULL : the last row of every lane with at least one row, in lane
+ *                  order; num_readout must equal the number of such lanes.
+ *   rows != NULL : rows[0..num_readout) are global row indices, copied in the
+ *                  given order; an index outside [0, N) gives a zero row and
+ *                  FP_ST_READOUT_RANGE.
+ *   dst : fp32 [num_readout][row_elems], row_elems = H_q * d.
+ */
+int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, const int32_t *rows,
+               int32_t num_readout, float *dst, int32_t *status, hipStream_t stream);
+
+/* ---- host-only accounting (Pie reviews, Eq. (1) and Eq. (2)) ---- */
+uint64_t fp_kv_bytes(int32_t L, int32_t H_kv, int32_t d, uint64_t T, int32_t b); /* 2*L*H_kv*d*T*b   */
+uint64_t fp_pages_for(uint64_t T, int32_t P);                                   /* ceil(T/P)        */
+uint64_t fp_page_waste(uint64_t T, int32_t P);                                  /* P*ceil(T/P) - T  */
+uint64_t fp_page_bytes(int32_t P, int32_t H_kv, int32_t d);                     /* 2*H_kv*P*d*2     */
+
+/* Library version string (static storage). */
+const char *fp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP_H_ */

@@ -51,6 +51,7 @@ ST_KVLEN = 4           # kv_len outside [0, capacity]: clamped
 ST_FOLD_CLAMP = 8      # fold count outside [0, rows]: clamped
 ST_READOUT_RANGE = 16  # readout row outside [0, num_rows): zero row returned
 ST_MASK_SHORT = 32     # mask row holds fewer than kv_len bits: missing bits read as 0
+ST_PAGE_RANGE = 64     # page id outside [0, num_pages): write suppressed, read clamped
 
 FOLD_ALL = -1
 FOLD_CHANNEL = -2
@@ -153,11 +154,21 @@ class Pool:
     def capacity(self, lane: int) -> int:
         return int(self.page_indptr[lane + 1] - self.page_indptr[lane]) * self.P
 
-    def locate(self, lane: int, slot):
-        """Physical (page, offset) of a lane's working-set slot(s)."""
+    def locate(self, lane: int, slot, clamp: bool = True):
+        """Physical (page, offset) of a lane's working-set slot(s).
+
+        A page id outside [0, num_pages) is a caller error: reads use the
+        nearest valid page (clamp=True); writers check page_ok() first.
+        """
         slot = np.asarray(slot, dtype=np.int64)
         page = self.page_ids[self.page_indptr[lane] + slot // self.P]
+        if clamp:
+            page = np.clip(page, 0, self.num_pages - 1)
         return page, slot % self.P
+
+    def page_ok(self, lane: int, slot):
+        page = self.page_ids[self.page_indptr[lane] + np.asarray(slot, dtype=np.int64) // self.P]
+        return (page >= 0) & (page < self.num_pages)
 
     def lane_kv(self, lane: int, n: int):
         """K and V of the lane's first n slots, fp64, [n][H][d]."""
@@ -171,11 +182,15 @@ def _lane_rows(indptr, lane):
     return int(indptr[lane]), int(indptr[lane + 1])
 
 
-def append(pool: Pool, committed, indptr, positions, slots, k_bits, v_bits, theta) -> int:
-    """Write every row's rotated K and its V into the row's slot. Returns status bits."""
+def append(pool: Pool, committed, indptr, positions, slots, k_bits, v_bits, theta, lanes=None) -> int:
+    """Write every row's rotated K and its V into the row's slot. Returns status bits.
+
+    lanes: optional subset of lanes to process (the others are left untouched);
+    used to check large passes on a sample of lanes.
+    """
     status = 0
     committed = np.asarray(committed)
-    for lane in range(len(indptr) - 1):
+    for lane in (range(len(indptr) - 1) if lanes is None else lanes):
         r0, r1 = _lane_rows(indptr, lane)
         if r1 == r0:
             continue
@@ -192,6 +207,10 @@ def append(pool: Pool, committed, indptr, positions, slots, k_bits, v_bits, thet
         if not ok.any():
             continue
         rows, s = rows[ok], s[ok]
+        pok = pool.page_ok(lane, s)
+        if not pok.all():
+            status |= ST_PAGE_RANGE
+            rows, s = rows[pok], s[pok]
         if len(np.unique(s)) != len(s):
             raise ValueError("duplicate slot writes in one pass are undefined")
         kr = rope(bf16_to_f64(k_bits[rows]), np.asarray(positions)[rows], theta)

@@ -1,0 +1,101 @@
+"""ctypes view of libfp.so (the C ABI in include/fp.h). No torch here."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp.so")
+
+c_i32 = ctypes.c_int32
+c_i64 = ctypes.c_int64
+c_u64 = ctypes.c_uint64
+c_ptr = ctypes.c_void_p
+
+FP_OK = 0
+FP_ERR_NULL = -1
+FP_ERR_SHAPE = -2
+FP_ERR_UNSUPPORTED = -3
+FP_ERR_WORKSPACE = -4
+FP_ERR_HIP = -5
+ERR_NAMES = {FP_ERR_NULL: "FP_ERR_NULL", FP_ERR_SHAPE: "FP_ERR_SHAPE", FP_ERR_UNSUPPORTED: "FP_ERR_UNSUPPORTED",
+             FP_ERR_WORKSPACE: "FP_ERR_WORKSPACE", FP_ERR_HIP: "FP_ERR_HIP"}
+
+FP_ST_SLOT_RANGE = 1
+FP_ST_FROZEN = 2
+FP_ST_KVLEN = 4
+FP_ST_FOLD_CLAMP = 8
+FP_ST_READOUT_RANGE = 16
+FP_ST_MASK_SHORT = 32
+FP_ST_PAGE_RANGE = 64
+FP_ST_PLAN_MISMATCH = 128
+
+FP_FOLD_ALL = -1
+FP_FOLD_CHANNEL = -2
+
+EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_fold", "fp_readout",
+           "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version")
+
+
+class FpGeometry(ctypes.Structure):
+    _fields_ = [("num_lanes", c_i32), ("num_rows", c_i32), ("indptr", c_ptr), ("indptr_host", c_ptr),
+                ("positions", c_ptr), ("slots", c_ptr), ("kv_len", c_ptr), ("fold", c_ptr)]
+
+
+class FpKvPool(ctypes.Structure):
+    _fields_ = [("kv", c_ptr), ("num_pages", c_i32), ("page_size", c_i32), ("num_kv_heads", c_i32),
+                ("head_dim", c_i32), ("page_indptr", c_ptr), ("page_indptr_host", c_ptr), ("page_ids", c_ptr),
+                ("committed_len", c_ptr)]
+
+
+class FpMask(ctypes.Structure):
+    _fields_ = [("bits", c_ptr), ("word_offset", c_ptr), ("word_offset_host", c_ptr)]
+
+
+class FpTuning(ctypes.Structure):
+    _fields_ = [("decode_split_slots", c_i32), ("reserved", c_i32 * 7)]
+
+
+class FpError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} returned {code} ({ERR_NAMES.get(code, 'unknown')})")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfp.so; raises if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m ragged_paged_kv_fp_amd.build` "
+                          "(or __graft_entry__.build()); the step has no CPU fallback")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.fp_append_kv.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, ctypes.c_float, c_ptr, c_ptr]
+    lib.fp_append_kv.restype = c_i32
+    lib.fp_attend_workspace_bytes.argtypes = [P(FpKvPool), P(FpGeometry), P(FpMask), c_i32, P(FpTuning)]
+    lib.fp_attend_workspace_bytes.restype = c_i64
+    lib.fp_attend.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_i32, ctypes.c_float, ctypes.c_float, P(FpMask),
+                              c_ptr, c_ptr, c_ptr, ctypes.c_size_t, P(FpTuning), c_ptr, c_ptr]
+    lib.fp_attend.restype = c_i32
+    lib.fp_fold.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, c_ptr]
+    lib.fp_fold.restype = c_i32
+    lib.fp_readout.argtypes = [P(FpGeometry), c_ptr, c_i32, c_ptr, c_i32, c_ptr, c_ptr, c_ptr]
+    lib.fp_readout.restype = c_i32
+    lib.fp_kv_bytes.argtypes = [c_i32, c_i32, c_i32, c_u64, c_i32]
+    lib.fp_kv_bytes.restype = c_u64
+    lib.fp_pages_for.argtypes = [c_u64, c_i32]
+    lib.fp_pages_for.restype = c_u64
+    lib.fp_page_waste.argtypes = [c_u64, c_i32]
+    lib.fp_page_waste.restype = c_u64
+    lib.fp_page_bytes.argtypes = [c_i32, c_i32, c_i32]
+    lib.fp_page_bytes.restype = c_u64
+    lib.fp_version.argtypes = []
+    lib.fp_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib

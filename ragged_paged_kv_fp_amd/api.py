@@ -1,0 +1,192 @@
+"""Thin Python binding of the C ABI: argument marshalling only.
+
+Each function takes torch tensors that live on the GPU (plus numpy host copies
+of the offset arrays the library plans launches from), passes their addresses
+to libfp.so and raises FpError on a negative return code. Every step of the
+computation runs in the library's HIP kernels; nothing here computes.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import FpError, FpGeometry, FpKvPool, FpMask, FpTuning
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _hptr(a: Optional[np.ndarray]) -> Optional[int]:
+    return None if a is None else a.ctypes.data
+
+
+def _dev_check(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+@dataclass
+class Pool:
+    """One attention layer of the paged pool (page layout documented in include/fp.h)."""
+
+    kv: torch.Tensor              # uint16/bfloat16 [num_pages][2*H*P*d] (any shape, contiguous)
+    num_pages: int
+    page_size: int
+    num_kv_heads: int
+    head_dim: int
+    page_indptr: torch.Tensor     # int32 [L+1] device
+    page_indptr_host: np.ndarray  # int32 [L+1]
+    page_ids: torch.Tensor        # int32 device
+    committed_len: torch.Tensor   # int32 [L] device
+
+    def struct(self) -> FpKvPool:
+        self.page_indptr_host = np.ascontiguousarray(self.page_indptr_host, dtype=np.int32)
+        return FpKvPool(_ptr(self.kv), self.num_pages, self.page_size, self.num_kv_heads, self.head_dim,
+                        _ptr(self.page_indptr), _hptr(self.page_indptr_host), _ptr(self.page_ids),
+                        _ptr(self.committed_len))
+
+
+@dataclass
+class Geometry:
+    """StateGeometry of one pass: rows of lane l are [indptr[l], indptr[l+1])."""
+
+    indptr: torch.Tensor          # int32 [L+1] device
+    indptr_host: np.ndarray       # int32 [L+1]
+    positions: torch.Tensor       # int32 [N]
+    slots: torch.Tensor           # int32 [N]
+    kv_len: torch.Tensor          # int32 [L]
+    fold: torch.Tensor            # int32 [L]
+
+    @property
+    def num_lanes(self) -> int:
+        return int(self.indptr_host.shape[0] - 1)
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.indptr_host[-1])
+
+    def struct(self) -> FpGeometry:
+        self.indptr_host = np.ascontiguousarray(self.indptr_host, dtype=np.int32)
+        return FpGeometry(self.num_lanes, self.num_rows, _ptr(self.indptr), _hptr(self.indptr_host),
+                          _ptr(self.positions), _ptr(self.slots), _ptr(self.kv_len), _ptr(self.fold))
+
+
+@dataclass
+class Mask:
+    bits: torch.Tensor                # int32/uint32 words, device
+    word_offset: torch.Tensor         # int64 [L+1] device
+    word_offset_host: np.ndarray      # int64 [L+1]
+
+    def struct(self) -> FpMask:
+        self.word_offset_host = np.ascontiguousarray(self.word_offset_host, dtype=np.int64)
+        return FpMask(_ptr(self.bits), _ptr(self.word_offset), _hptr(self.word_offset_host))
+
+
+def _tuning(split: Optional[int]):
+    if split is None:
+        return None
+    t = FpTuning()
+    t.decode_split_slots = int(split)
+    return ctypes.byref(t)
+
+
+def _check(fn: str, rc: int) -> int:
+    if rc < 0:
+        raise FpError(fn, rc)
+    return rc
+
+
+def append_kv(pool: Pool, geom: Geometry, k: torch.Tensor, v: torch.Tensor, rope_theta: float,
+              status: torch.Tensor, stream=None) -> None:
+    """fp_append_kv: RoPE K at positions, write K/V into each row's slot."""
+    lib = _lib.load()
+    ps, gs = pool.struct(), geom.struct()
+    _check("fp_append_kv", lib.fp_append_kv(ctypes.byref(ps), ctypes.byref(gs), _ptr(k), _ptr(v),
+                                            float(rope_theta), _ptr(status), _stream(stream)))
+
+
+def attend_workspace_bytes(pool: Pool, geom: Geometry, num_q_heads: int, mask: Optional[Mask] = None,
+                           split: Optional[int] = None) -> int:
+    lib = _lib.load()
+    ps, gs = pool.struct(), geom.struct()
+    ms = mask.struct() if mask is not None else None
+    return _check("fp_attend_workspace_bytes",
+                  lib.fp_attend_workspace_bytes(ctypes.byref(ps), ctypes.byref(gs),
+                                                ctypes.byref(ms) if ms is not None else None,
+                                                int(num_q_heads), _tuning(split)))
+
+
+def attend(pool: Pool, geom: Geometry, q: torch.Tensor, num_q_heads: int, rope_theta: float, sm_scale: float,
+           out: torch.Tensor, workspace: torch.Tensor, status: torch.Tensor, lse: Optional[torch.Tensor] = None,
+           mask: Optional[Mask] = None, split: Optional[int] = None, stream=None) -> None:
+    """fp_attend: attention of every row over its lane's kv_len slots (causal or bitmap)."""
+    lib = _lib.load()
+    ps, gs = pool.struct(), geom.struct()
+    ms = mask.struct() if mask is not None else None
+    _check("fp_attend", lib.fp_attend(ctypes.byref(ps), ctypes.byref(gs), _ptr(q), int(num_q_heads),
+                                      float(rope_theta), float(sm_scale),
+                                      ctypes.byref(ms) if ms is not None else None,
+                                      _ptr(out), _ptr(lse), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _tuning(split),
+                                      _ptr(status), _stream(stream)))
+
+
+def fold(pool: Pool, geom: Geometry, status: torch.Tensor, channel: Optional[torch.Tensor] = None,
+         stream=None) -> None:
+    """fp_fold: committed_len += none | all | literal | channel count, clamped."""
+    lib = _lib.load()
+    ps, gs = pool.struct(), geom.struct()
+    _check("fp_fold", lib.fp_fold(ctypes.byref(ps), ctypes.byref(gs), _ptr(channel), _ptr(status),
+                                  _stream(stream)))
+
+
+def readout(geom: Geometry, out: torch.Tensor, dst: torch.Tensor, status: torch.Tensor,
+            rows: Optional[torch.Tensor] = None, stream=None) -> None:
+    """fp_readout: gather the chosen rows of out (default: last row of each lane)."""
+    lib = _lib.load()
+    gs = geom.struct()
+    row_elems = int(out.numel() // max(1, geom.num_rows)) if geom.num_rows else int(dst.shape[-1])
+    num = int(dst.shape[0])
+    _check("fp_readout", lib.fp_readout(ctypes.byref(gs), _ptr(out), row_elems, _ptr(rows), num, _ptr(dst),
+                                        _ptr(status), _stream(stream)))
+
+
+def kv_bytes(L: int, H_kv: int, d: int, T: int, b: int) -> int:
+    return int(_lib.load().fp_kv_bytes(L, H_kv, d, T, b))
+
+
+def pages_for(T: int, P: int) -> int:
+    return int(_lib.load().fp_pages_for(T, P))
+
+
+def page_waste(T: int, P: int) -> int:
+    return int(_lib.load().fp_page_waste(T, P))
+
+
+def page_bytes(P: int, H_kv: int, d: int) -> int:
+    return int(_lib.load().fp_page_bytes(P, H_kv, d))
+
+
+def version() -> str:
+    return _lib.load().fp_version().decode()

@@ -1,0 +1,81 @@
+// fp_device.h - device helpers shared by the kernels of the ForwardPass attention step.
+// gfx950 (CDNA4) only: 64-lane waves, bf16 MFMA 32x32x16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fpk {
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_inff();
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Nearest-even bf16 of a double in one rounding: truncate to float (toward
+// zero), set the last float bit if anything was dropped (round-to-odd), then
+// round that float to bf16 nearest-even. Float keeps enough extra bits for
+// the two steps to equal one correct rounding.
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+    float f = __double2float_rz(x);
+    uint32_t u = __float_as_uint(f);
+    if ((double)f != x) u |= 1u;
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u;  // NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Rotation angle of RoPE pair i (dims 2i, 2i+1) at position pos:
+// pos * theta^(-2i/d), evaluated in fp64.
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, int d, double theta, double *c, double *s) {
+    const double w = pow(theta, -2.0 * (double)i / (double)d);
+    const double ang = (double)pos * w;
+    sincos(ang, s, c);
+}
+
+// Largest lane l with indptr[l] <= row (rows of lane l are [indptr[l], indptr[l+1])).
+__device__ __forceinline__ int find_lane(const int32_t *indptr, int num_lanes, int64_t row) {
+    int lo = 0, hi = num_lanes;  // answer in [lo, hi)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)indptr[mid] <= row) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ int clamp_kv(int kv, int cap) { return kv < 0 ? 0 : (kv > cap ? cap : kv); }
+
+// Row of the 32-row K operand that holds tile slot pi(m). Chosen so that, after
+// S^T = K * Q^T, lane half h holds the scores of tile slots 8h..8h+7 in
+// accumulator registers 0..7 and 16+8h..16+8h+7 in registers 8..15: exactly
+// the B-operand layout the P*V product needs, so P never moves between lanes.
+__device__ __forceinline__ int kslot_of_row(int m) {
+    return 16 * ((m >> 3) >> 1) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
+}
+
+__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+}  // namespace fpk

@@ -1,0 +1,714 @@
+// fp_kernels.h - HIP kernels of the ForwardPass attention step (gfx950).
+//
+// Pool page layout (bf16): K block [H][P][D] then V block [H][D][P] (V transposed),
+// so that both MFMA operands of S^T = K*Q^T and O^T = V^T*P^T load as 16-byte
+// vectors straight from the page, with no LDS transpose.
+#pragma once
+
+#include "fp_device.h"
+#include "../../include/fp.h"
+
+namespace fpk {
+
+// Per-lane plan record written by plan_kernel.
+struct LaneInfo {
+    int dec_off;   // first decode work item of the lane, -1 if the lane is not a decode lane
+    int nsplit;    // decode KV splits of the lane (items per KV head)
+    int sum_off;   // first mask-summary word of the lane, -1 if none
+    int sum_wpb;   // summary words per 32-row block (per bitmap kind)
+};
+
+// ============================================================================ append
+
+__device__ __forceinline__ void rotate_pair_f64(double x0, double x1, double c, double s, double *y0, double *y1) {
+#pragma clang fp contract(off)
+    *y0 = x0 * c - x1 * s;
+    *y1 = x0 * s + x1 * c;
+}
+
+struct AppendArgs {
+    uint16_t *pool;
+    int64_t page_elems;
+    int num_pages, P, H, D;
+    const int32_t *page_indptr, *page_ids, *committed;
+    const int32_t *indptr;
+    int L;
+    int64_t N;
+    const int32_t *positions, *slots;
+    const uint16_t *k, *v;
+    double theta;
+    int32_t *status;
+};
+
+// One thread per (row, RoPE pair); loops over KV heads, which share the angle.
+__global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+    const int pairs = a.D >> 1;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = t / pairs;
+    const int i = (int)(t - row * pairs);
+    if (row >= a.N) return;
+    const int lane = find_lane(a.indptr, a.L, row);
+    const int slot = a.slots[row];
+    const int p0 = a.page_indptr[lane];
+    const int cap = (a.page_indptr[lane + 1] - p0) * a.P;
+    if (slot < 0 || slot >= cap) {
+        if (i == 0) atomicOr(a.status, FP_ST_SLOT_RANGE);
+        return;
+    }
+    if (slot < a.committed[lane]) {
+        if (i == 0) atomicOr(a.status, FP_ST_FROZEN);
+        return;
+    }
+    const int64_t page = a.page_ids[p0 + slot / a.P];
+    if (page < 0 || page >= a.num_pages) {
+        if (i == 0) atomicOr(a.status, FP_ST_PAGE_RANGE);
+        return;
+    }
+    const int off = slot % a.P;
+    double c, s;
+    rope_cos_sin(a.positions[row], i, a.D, a.theta, &c, &s);
+    uint16_t *kb = a.pool + page * a.page_elems;          // K block [H][P][D]
+    uint16_t *vb = kb + (int64_t)a.H * a.P * a.D;        // V block [H][D][P]
+    const uint32_t *kin = reinterpret_cast<const uint32_t *>(a.k + row * a.H * a.D) + i;
+    const uint32_t *vin = reinterpret_cast<const uint32_t *>(a.v + row * a.H * a.D) + i;
+    for (int h = 0; h < a.H; ++h) {
+        const uint32_t kw = kin[h * pairs];
+        double y0, y1;
+        rotate_pair_f64((double)bf16_lo(kw), (double)bf16_hi(kw), c, s, &y0, &y1);
+        reinterpret_cast<uint32_t *>(kb + ((int64_t)h * a.P + off) * a.D)[i] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+        const uint32_t vw = vin[h * pairs];
+        uint16_t *vh = vb + (int64_t)h * a.D * a.P;
+        vh[(2 * i) * a.P + off] = (uint16_t)(vw & 0xFFFFu);
+        vh[(2 * i + 1) * a.P + off] = (uint16_t)(vw >> 16);
+    }
+}
+
+// ============================================================================ fold
+
+__global__ void __launch_bounds__(256) fold_kernel(const int32_t *indptr, const int32_t *fold, const int32_t *channel,
+                                                    int32_t *committed, int L, int32_t *status) {
+    const int l = blockIdx.x * blockDim.x + threadIdx.x;
+    if (l >= L) return;
+    const int n = indptr[l + 1] - indptr[l];
+    const int f = fold[l];
+    int k;
+    bool clamped = false;
+    if (f == FP_FOLD_ALL) {
+        k = n;
+    } else if (f == FP_FOLD_CHANNEL) {
+        if (channel) k = channel[l];
+        else { k = 0; clamped = true; }
+    } else if (f >= 0) {
+        k = f;
+    } else {
+        k = 0;
+        clamped = true;
+    }
+    if (k < 0) { k = 0; clamped = true; }
+    if (k > n) { k = n; clamped = true; }
+    committed[l] += k;
+    if (clamped) atomicOr(status, FP_ST_FOLD_CLAMP);
+}
+
+// ============================================================================ readout
+
+// Block b copies one readout row: rows[b] if a list is given, else the last row
+// of lane b (its destination index counts the non-empty lanes before it).
+__global__ void __launch_bounds__(256) readout_kernel(const int32_t *indptr, int L, int64_t N, const float *out,
+                                                       int row_elems, const int32_t *rows, int num_readout, float *dst,
+                                                       int32_t *status) {
+    __shared__ int s_cnt[256 / kWave];
+    const int b = blockIdx.x;
+    int64_t src, di;
+    if (rows) {
+        di = b;
+        src = rows[b];
+        if (src < 0 || src >= N) {
+            src = -1;
+            if (threadIdx.x == 0) atomicOr(status, FP_ST_READOUT_RANGE);
+        }
+    } else {
+        const int n = indptr[b + 1] - indptr[b];
+        if (n <= 0) return;
+        int cnt = 0;
+        for (int j = threadIdx.x; j < b; j += blockDim.x) cnt += (indptr[j + 1] > indptr[j]) ? 1 : 0;
+        for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
+        if (lane_id() == 0) s_cnt[threadIdx.x / kWave] = cnt;
+        __syncthreads();
+        int tot = 0;
+        for (int w = 0; w < (int)(blockDim.x / kWave); ++w) tot += s_cnt[w];
+        di = tot;
+        if (di >= num_readout) return;  // device offsets disagree with the host count
+        src = indptr[b + 1] - 1;
+        if (src >= N) {
+            src = -1;
+            if (threadIdx.x == 0) atomicOr(status, FP_ST_READOUT_RANGE);
+        }
+    }
+    float *d = dst + di * (int64_t)row_elems;
+    if (src < 0) {
+        for (int e = threadIdx.x; e < row_elems; e += blockDim.x) d[e] = 0.0f;
+        return;
+    }
+    const float *s = out + src * (int64_t)row_elems;
+    if ((row_elems & 3) == 0) {
+        const float4 *s4 = reinterpret_cast<const float4 *>(s);
+        float4 *d4 = reinterpret_cast<float4 *>(d);
+        for (int e = threadIdx.x; e < (row_elems >> 2); e += blockDim.x) d4[e] = s4[e];
+    } else {
+        for (int e = threadIdx.x; e < row_elems; e += blockDim.x) d[e] = s[e];
+    }
+}
+
+// ============================================================================ Q rotation
+
+struct RopeQArgs {
+    const uint16_t *q;
+    uint16_t *qrot;
+    const int32_t *positions;
+    int64_t N;
+    int Hq, D;
+    double theta;
+    double qscale;  // sm_scale * log2(e): scores come out in base-2 units
+};
+
+// One thread per (row, RoPE pair); rotated, prescaled Q in bf16, same layout as q.
+__global__ void __launch_bounds__(256) rope_q_kernel(RopeQArgs a) {
+    const int pairs = a.D >> 1;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = t / pairs;
+    const int i = (int)(t - row * pairs);
+    if (row >= a.N) return;
+    double c, s;
+    rope_cos_sin(a.positions[row], i, a.D, a.theta, &c, &s);
+    c *= a.qscale;
+    s *= a.qscale;
+    const uint32_t *qin = reinterpret_cast<const uint32_t *>(a.q + row * a.Hq * a.D) + i;
+    uint32_t *qo = reinterpret_cast<uint32_t *>(a.qrot + row * a.Hq * a.D) + i;
+    for (int h = 0; h < a.Hq; ++h) {
+        const uint32_t w = qin[h * pairs];
+        double y0, y1;
+        rotate_pair_f64((double)bf16_lo(w), (double)bf16_hi(w), c, s, &y0, &y1);
+        qo[h * pairs] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+    }
+}
+
+// ============================================================================ plan
+
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxLanes = 4096;
+constexpr int kDecodeCols = 32;  // query row-heads one decode wave holds (MFMA N)
+constexpr int kRowBlock = 32;    // rows per prefill work item
+
+struct PlanArgs {
+    const int32_t *indptr, *page_indptr, *kv_len;
+    const int64_t *mask_off;  // nullable
+    int L, H, G, P, split;
+    int64_t n_dec_host, n_pre_host, sum_host, N_host;
+    int ncols_host;
+    int merge_host;     // the host allotted split-merge buffers
+    LaneInfo *lane_info;
+    int4 *dec_items;   // {lane, kv head, first slot, end slot}
+    int4 *pre_items;   // {lane, kv head, first local row, rows}
+    int32_t *status;
+};
+
+struct LaneCounts {
+    int dec, pre, sum, nsplit, nrb, wpb, ncols;
+};
+
+__device__ __forceinline__ LaneCounts lane_counts(const PlanArgs &a, int l, int32_t *st) {
+    LaneCounts r = {0, 0, 0, 0, 0, 0, 0};
+    const int n = a.indptr[l + 1] - a.indptr[l];
+    const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
+    const int kv = a.kv_len[l];
+    if (kv < 0 || kv > cap) *st |= FP_ST_KVLEN;
+    if (n <= 0) return r;
+    const bool masked = a.mask_off && a.mask_off[l + 1] > a.mask_off[l];
+    if (masked) {
+        const int64_t wpr = (a.mask_off[l + 1] - a.mask_off[l]) / n;
+        if (32 * wpr < (int64_t)clamp_kv(kv, cap)) *st |= FP_ST_MASK_SHORT;
+    }
+    if (n * a.G <= kDecodeCols) {
+        r.nsplit = cap > 0 ? (cap + a.split - 1) / a.split : 1;
+        r.dec = a.H * r.nsplit;
+        r.ncols = n * a.G;
+    } else {
+        r.nrb = (n + kRowBlock - 1) / kRowBlock;
+        r.pre = a.H * r.nrb;
+        if (masked) {
+            const int tiles = (cap + 31) / 32;
+            r.wpb = (tiles + 31) / 32;
+            r.sum = r.nrb * 2 * r.wpb;
+        }
+    }
+    return r;
+}
+
+__device__ __forceinline__ int upper_lane(const int *offs, int L, int idx) {
+    int lo = 0, hi = L;  // largest l in [0, L) with offs[l] <= idx
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offs[mid] <= idx) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// Single workgroup: per-lane classification (decode if all rows x GQA heads fit
+// one MFMA tile, prefill otherwise), prefix offsets, and the work-item lists.
+__global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
+    __shared__ int s_dec[kMaxLanes + 1];
+    __shared__ int s_pre[kMaxLanes + 1];
+    __shared__ int s_scan[3][kPlanThreads];
+    __shared__ int s_bad;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_bad = 0;
+    const int per = (a.L + kPlanThreads - 1) / kPlanThreads;
+    const int l0 = tid * per, l1 = min(a.L, l0 + per);
+    int32_t st = 0;
+    int td = 0, tp = 0, ts = 0, tc = 0;
+    for (int l = l0; l < l1; ++l) {
+        const LaneCounts c = lane_counts(a, l, &st);
+        td += c.dec; tp += c.pre; ts += c.sum;
+        tc = max(tc, c.ncols);
+        if (c.nsplit > 1 && !a.merge_host) tc = kDecodeCols + 1;  // forces the mismatch path
+    }
+    if (st) atomicOr(a.status, st);
+    __syncthreads();
+    if (tc > a.ncols_host) atomicOr(&s_bad, 1);
+    s_scan[0][tid] = td; s_scan[1][tid] = tp; s_scan[2][tid] = ts;
+    __syncthreads();
+    for (int o = 1; o < kPlanThreads; o <<= 1) {
+        int v0 = 0, v1 = 0, v2 = 0;
+        if (tid >= o) { v0 = s_scan[0][tid - o]; v1 = s_scan[1][tid - o]; v2 = s_scan[2][tid - o]; }
+        __syncthreads();
+        s_scan[0][tid] += v0; s_scan[1][tid] += v1; s_scan[2][tid] += v2;
+        __syncthreads();
+    }
+    int od = s_scan[0][tid] - td, op = s_scan[1][tid] - tp, os = s_scan[2][tid] - ts;
+    int32_t dummy = 0;
+    for (int l = l0; l < l1; ++l) {
+        const LaneCounts c = lane_counts(a, l, &dummy);
+        s_dec[l] = od;
+        s_pre[l] = op;
+        LaneInfo li;
+        li.dec_off = c.dec ? od : -1;
+        li.nsplit = c.nsplit;
+        li.sum_off = c.sum ? os : -1;
+        li.sum_wpb = c.wpb;
+        a.lane_info[l] = li;
+        od += c.dec; op += c.pre; os += c.sum;
+    }
+    if (tid == kPlanThreads - 1) {
+        s_dec[a.L] = s_scan[0][tid];
+        s_pre[a.L] = s_scan[1][tid];
+        // Launch grids and workspace were sized from the host copies; device
+        // offsets that disagree would index past them, so no work is emitted.
+        if (s_scan[0][tid] != a.n_dec_host || s_scan[1][tid] != a.n_pre_host || s_scan[2][tid] != a.sum_host ||
+            (int64_t)a.indptr[a.L] != a.N_host)
+            atomicOr(&s_bad, 1);
+    }
+    __syncthreads();
+    const bool bad = s_bad != 0;
+    if (bad) {
+        for (int l = tid; l < a.L; l += kPlanThreads) a.lane_info[l] = LaneInfo{-1, 0, -1, 0};
+        if (tid == 0) atomicOr(a.status, FP_ST_PLAN_MISMATCH);
+    }
+    const int tot_d = bad ? 0 : s_dec[a.L], tot_p = bad ? 0 : s_pre[a.L];
+    for (int64_t idx = tid; idx < a.n_dec_host; idx += kPlanThreads) {
+        int4 it = make_int4(-1, 0, 0, 0);
+        if (idx < tot_d) {
+            const int l = upper_lane(s_dec, a.L, (int)idx);
+            const int local = (int)idx - s_dec[l];
+            const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
+            const int nsplit = cap > 0 ? (cap + a.split - 1) / a.split : 1;
+            const int g = local / nsplit, sp = local - g * nsplit;
+            it = make_int4(l, g, sp * a.split, min((sp + 1) * a.split, cap));
+        }
+        a.dec_items[idx] = it;
+    }
+    for (int64_t idx = tid; idx < a.n_pre_host; idx += kPlanThreads) {
+        int4 it = make_int4(-1, 0, 0, 0);
+        if (idx < tot_p) {
+            const int l = upper_lane(s_pre, a.L, (int)idx);
+            const int local = (int)idx - s_pre[l];
+            const int n = a.indptr[l + 1] - a.indptr[l];
+            // KV head fastest: consecutive items go to different XCDs, and the
+            // row blocks of one (lane, KV head) land on the same XCD and L2.
+            const int rb = local / a.H, g = local - rb * a.H;
+            it = make_int4(l, g, rb * kRowBlock, min(kRowBlock, n - rb * kRowBlock));
+        }
+        a.pre_items[idx] = it;
+    }
+}
+
+// ============================================================================ mask summary
+
+struct SummaryArgs {
+    const int4 *pre_items;
+    const LaneInfo *lane_info;
+    const int32_t *indptr, *page_indptr, *kv_len;
+    const uint32_t *bits;
+    const int64_t *mask_off;
+    int P;
+    uint32_t *summary;
+};
+
+// For each 32-row block of a masked prefill lane: which 32-slot KV tiles hold
+// any set bit (word run "any"), and which are fully set below kv_len ("all").
+__global__ void __launch_bounds__(256) summary_kernel(SummaryArgs a) {
+    const int4 it = a.pre_items[blockIdx.x];
+    if (it.x < 0 || it.y != 0) return;
+    const int l = it.x;
+    const LaneInfo li = a.lane_info[l];
+    if (li.sum_off < 0) return;
+    const int nl = a.indptr[l + 1] - a.indptr[l];
+    const int64_t wpr = (a.mask_off[l + 1] - a.mask_off[l]) / nl;
+    const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
+    const int eff = clamp_kv(a.kv_len[l], cap);
+    const int rstart = it.z, nr = it.w;
+    const int64_t base = (int64_t)li.sum_off + (int64_t)(rstart / kRowBlock) * 2 * li.sum_wpb;
+    const uint32_t *rb = a.bits + a.mask_off[l] + (int64_t)rstart * wpr;
+    const int lane = lane_id();
+    const int ntiles = li.sum_wpb * 32;
+    for (int t0 = (int)(threadIdx.x & ~(kWave - 1)); t0 < ntiles; t0 += blockDim.x) {
+        const int t = t0 + lane;
+        const bool inr = (t < wpr) && (32 * t < eff);
+        uint32_t any = 0, all = ~0u;
+        if (inr) {
+            for (int r = 0; r < nr; ++r) {
+                const uint32_t w = rb[(int64_t)r * wpr + t];
+                any |= w;
+                all &= w;
+            }
+        }
+        const uint32_t valid = !inr ? 0u : ((32 * t + 32 <= eff) ? ~0u : ((1u << (eff - 32 * t)) - 1u));
+        const bool anyb = inr && (any & valid);
+        const bool allb = inr && ((all | ~valid) == ~0u);
+        const uint64_t ba = __ballot(anyb), bl = __ballot(allb);
+        if (lane == 0) {
+            const int wi = t0 >> 5;
+            if (wi < li.sum_wpb) { a.summary[base + wi] = (uint32_t)ba; a.summary[base + li.sum_wpb + wi] = (uint32_t)bl; }
+            if (wi + 1 < li.sum_wpb) { a.summary[base + wi + 1] = (uint32_t)(ba >> 32); a.summary[base + li.sum_wpb + wi + 1] = (uint32_t)(bl >> 32); }
+        }
+    }
+}
+
+// ============================================================================ attention
+
+struct AttnArgs {
+    const uint16_t *pool;
+    int64_t page_elems;
+    int num_pages, P, H, G, Hq;
+    const int32_t *page_indptr, *page_ids;
+    const int32_t *indptr, *slots, *kv_len;
+    const uint16_t *qrot;             // [N][Hq][D] rotated, prescaled bf16
+    const uint32_t *mask_bits;        // nullable
+    const int64_t *mask_off;          // nullable
+    float *out, *lse;                 // lse nullable
+    const int4 *dec_items, *pre_items;
+    const LaneInfo *lane_info;
+    float *part_o;                    // [items][ncols_max][D]
+    float *part_ml;                   // [items][2][32]
+    int ncols_max;
+    const uint32_t *summary;
+};
+
+// Per-wave view of one (lane, KV head): where its slots live and how far rows may read.
+struct KvView {
+    const uint16_t *kbase;   // pool
+    const int32_t *pids;     // page_ids + page_indptr[lane]
+    int64_t page_elems;
+    int64_t vblock;          // element offset of the V block in a page
+    int P, g, H, eff, last_page;
+};
+
+// Physical page of working-set page j; an id outside the pool reads the nearest valid page.
+__device__ __forceinline__ int64_t page_of(const KvView &kv, int j) {
+    const int p = kv.pids[j];
+    return (int64_t)min(max(p, 0), kv.last_page);
+}
+
+template <int D>
+struct WaveState {
+    uint4 qf[D / 16];
+    f32x16 o[D / 32];
+    float m, l;
+};
+
+// One 32-slot KV tile for the wave's 32 query columns.
+//   S^T[slot][col] = K[slot] . Q[col]   (8 or 4 MFMAs, d split over the lane halves)
+//   online softmax per column (a column lives in lanes n and n+32)
+//   O^T[d][col] += V^T[d][slot] * P^T[slot][col]
+template <int D>
+__device__ __forceinline__ void attn_tile(const KvView &kv, int j0, int lim, uint32_t mword, bool masked,
+                                          WaveState<D> &w) {
+    constexpr int KS = D / 16, DB = D / 32;
+    const int ln = lane_id(), h = ln >> 5, n = ln & 31;
+    uint4 kf[KS];
+    const int ks = j0 + kslot_of_row(n);
+    if (ks < kv.eff) {
+        const int64_t page = page_of(kv, ks / kv.P);
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            kv.kbase + page * kv.page_elems + ((int64_t)kv.g * kv.P + (ks % kv.P)) * D + h * (D / 2));
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kf[s] = src[s];
+    } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kf[s] = make_uint4(0, 0, 0, 0);
+    }
+    uint4 vf[DB][2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+        const int vs = j0 + 16 * t2 + 8 * h;
+        if (vs < kv.eff) {
+            const int64_t page = page_of(kv, vs / kv.P);
+            const uint16_t *vb = kv.kbase + page * kv.page_elems + kv.vblock + (int64_t)kv.g * D * kv.P + (vs % kv.P);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) vf[db][t2] = *reinterpret_cast<const uint4 *>(vb + (int64_t)(32 * db + n) * kv.P);
+            const int nv = kv.eff - vs;
+            if (nv < 8) {  // tail of the lane: slots at or past kv_len must not reach P*V (0*NaN)
+                uint32_t mk[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) mk[q] = (2 * q + 1 < nv) ? 0xFFFFFFFFu : ((2 * q < nv) ? 0x0000FFFFu : 0u);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    vf[db][t2].x &= mk[0]; vf[db][t2].y &= mk[1]; vf[db][t2].z &= mk[2]; vf[db][t2].w &= mk[3];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) vf[db][t2] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    f32x16 sacc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) sacc = mfma32(kf[s], w.qf[s], sacc);
+
+    float sv[16];
+    float mt = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int so = 16 * (i >> 3) + 8 * h + (i & 7);
+        bool ok = (j0 + so) < lim;
+        if (masked) ok = ok && ((mword >> so) & 1u);
+        sv[i] = ok ? sacc[i] : kNegInf;
+        mt = fmaxf(mt, sv[i]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(w.m, mt);
+    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(w.m - m_use);
+    float ps = 0.0f;
+    uint32_t pk[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[2 * q] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(sv[2 * q + 1] - m_use);
+        ps += p0 + p1;
+        pk[q] = pack_bf16x2(p0, p1);
+    }
+    w.l = w.l * alpha + ps;
+    w.m = m_new;
+    const uint4 pb0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    const uint4 pb1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        w.o[db] *= alpha;
+        w.o[db] = mfma32(vf[db][0], pb0, w.o[db]);
+        w.o[db] = mfma32(vf[db][1], pb1, w.o[db]);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(const uint16_t *qrot, int64_t row, int head, int Hq, bool valid, WaveState<D> &w) {
+    constexpr int KS = D / 16;
+    const int h = lane_id() >> 5;
+    if (valid) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(qrot + (row * Hq + head) * D + h * (D / 2));
+#pragma unroll
+        for (int s = 0; s < KS; ++s) w.qf[s] = src[s];
+    } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) w.qf[s] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) w.o[db] = f32x16{};
+    w.m = kNegInf;
+    w.l = 0.0f;
+}
+
+// Normalized output for the wave's valid columns: O = acc / l, LSE = (m + log2 l) ln 2.
+template <int D>
+__device__ __forceinline__ void store_final(const WaveState<D> &w, float l_tot, float *out_row, float *lse_ptr, bool valid) {
+    const int h = lane_id() >> 5;
+    if (!valid) return;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            float4 v = make_float4(w.o[db][4 * i4] * inv, w.o[db][4 * i4 + 1] * inv, w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv);
+            *reinterpret_cast<float4 *>(out_row + 32 * db + 8 * i4 + 4 * h) = v;
+        }
+    }
+    if (lse_ptr && h == 0) *lse_ptr = l_tot > 0.0f ? (w.m + __log2f(l_tot)) * 0.69314718055994531f : kNegInf;
+}
+
+__device__ __forceinline__ KvView make_view(const AttnArgs &a, int lane, int g, int *cap_out) {
+    KvView kv;
+    const int p0 = a.page_indptr[lane];
+    const int cap = (a.page_indptr[lane + 1] - p0) * a.P;
+    kv.kbase = a.pool;
+    kv.pids = a.page_ids + p0;
+    kv.page_elems = a.page_elems;
+    kv.P = a.P;
+    kv.g = g;
+    kv.H = a.H;
+    kv.eff = clamp_kv(a.kv_len[lane], cap);
+    kv.last_page = a.num_pages - 1;
+    *cap_out = cap;
+    return kv;
+}
+
+// Decode: one wave per (lane, KV head, KV split); all rows x GQA heads of the
+// lane (<= 32) share every loaded K/V tile as the MFMA N dimension.
+template <int D>
+__global__ void __launch_bounds__(64) decode_kernel(AttnArgs a) {
+    const int item = blockIdx.x;
+    const int4 it = a.dec_items[item];
+    if (it.x < 0) return;
+    const int lane = it.x, g = it.y, s0 = it.z, s1 = it.w;
+    const LaneInfo li = a.lane_info[lane];
+    const int r0 = a.indptr[lane];
+    const int nrows = a.indptr[lane + 1] - r0;
+    const int ncols = nrows * a.G;
+    const int ln = lane_id(), n = ln & 31, h = ln >> 5;
+    const bool colv = n < ncols;
+    const int64_t row = r0 + (colv ? n / a.G : 0);
+    const int head = g * a.G + (colv ? n % a.G : 0);
+    int cap;
+    KvView kv = make_view(a, lane, g, &cap);
+    kv.vblock = (int64_t)a.H * a.P * D;
+    WaveState<D> w;
+    load_q<D>(a.qrot, row, head, a.Hq, colv, w);
+    const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
+    const uint32_t *mrow = nullptr;
+    int64_t wpr = 0;
+    if (masked) {
+        wpr = (a.mask_off[lane + 1] - a.mask_off[lane]) / nrows;
+        mrow = a.mask_bits + a.mask_off[lane] + (colv ? (n / a.G) : 0) * wpr;
+    }
+    const int lim = !colv ? 0 : (masked ? kv.eff : min(a.slots[row] + 1, kv.eff));
+    const int lmax = wave_max_i(lim);
+    const int jend = min(s1, lmax);
+    for (int j0 = s0; j0 < jend; j0 += 32) {
+        uint32_t mw = 0;
+        if (masked) {
+            const int64_t wi = j0 >> 5;
+            mw = (colv && wi < wpr) ? mrow[wi] : 0u;
+            if (__ballot(mw != 0u) == 0) continue;
+        }
+        attn_tile<D>(kv, j0, lim, mw, masked, w);
+    }
+    const float l_tot = w.l + __shfl_xor(w.l, 32);
+    if (li.nsplit <= 1) {
+        store_final<D>(w, l_tot, a.out + (row * a.Hq + head) * D, a.lse ? a.lse + row * a.Hq + head : nullptr, colv);
+        return;
+    }
+    if (colv) {
+        float *po = a.part_o + ((int64_t)item * a.ncols_max + n) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                *reinterpret_cast<float4 *>(po + 32 * db + 8 * i4 + 4 * h) =
+                    make_float4(w.o[db][4 * i4], w.o[db][4 * i4 + 1], w.o[db][4 * i4 + 2], w.o[db][4 * i4 + 3]);
+        if (h == 0) {
+            a.part_ml[(int64_t)item * 64 + n] = w.m;
+            a.part_ml[(int64_t)item * 64 + 32 + n] = l_tot;
+        }
+    }
+}
+
+// Prefill: one workgroup per (lane, KV head, 32-row block); wave w handles
+// query head g*G + w for the block's rows (32 MFMA columns).
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW) prefill_kernel(AttnArgs a) {
+    const int4 it = a.pre_items[blockIdx.x];
+    if (it.x < 0) return;
+    const int lane = it.x, g = it.y, rstart = it.z, nr = it.w;
+    const int wv = threadIdx.x / kWave;
+    const int ln = lane_id(), n = ln & 31;
+    const bool colv = n < nr;
+    const int r0 = a.indptr[lane];
+    const int nrows = a.indptr[lane + 1] - r0;
+    const int64_t row = r0 + rstart + (colv ? n : 0);
+    const int head = g * a.G + wv;
+    int cap;
+    KvView kv = make_view(a, lane, g, &cap);
+    kv.vblock = (int64_t)a.H * a.P * D;
+    WaveState<D> w;
+    load_q<D>(a.qrot, row, head, a.Hq, colv, w);
+    const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
+    const uint32_t *mrow = nullptr;
+    int64_t wpr = 0;
+    if (masked) {
+        wpr = (a.mask_off[lane + 1] - a.mask_off[lane]) / nrows;
+        mrow = a.mask_bits + a.mask_off[lane] + (int64_t)(rstart + (colv ? n : 0)) * wpr;
+    }
+    const int lim = !colv ? 0 : (masked ? kv.eff : min(a.slots[row] + 1, kv.eff));
+    const int lmax = wave_max_i(lim);
+    if (!masked) {
+        for (int j0 = 0; j0 < lmax; j0 += 32) attn_tile<D>(kv, j0, lim, 0u, false, w);
+    } else {
+        const LaneInfo li = a.lane_info[lane];
+        const uint32_t *any = a.summary + li.sum_off + (int64_t)(rstart / kRowBlock) * 2 * li.sum_wpb;
+        const int ntile = (lmax + 31) >> 5;
+        for (int wi = 0; wi * 32 < ntile; ++wi) {
+            uint32_t bw = any[wi];
+            const int rem = ntile - wi * 32;
+            if (rem < 32) bw &= (1u << rem) - 1u;
+            while (bw) {
+                const int b = __builtin_ctz(bw);
+                bw &= bw - 1u;
+                const int t = 32 * wi + b;
+                const uint32_t mw = (colv && t < wpr) ? mrow[t] : 0u;
+                attn_tile<D>(kv, 32 * t, lim, mw, true, w);
+            }
+        }
+    }
+    const float l_tot = w.l + __shfl_xor(w.l, 32);
+    store_final<D>(w, l_tot, a.out + (row * a.Hq + head) * D, a.lse ? a.lse + row * a.Hq + head : nullptr, colv);
+}
+
+// Combine the KV splits of a decode lane by their running max and sum (base 2).
+template <int D>
+__global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
+    const int lane = blockIdx.x, g = blockIdx.y;
+    const LaneInfo li = a.lane_info[lane];
+    if (li.dec_off < 0 || li.nsplit <= 1) return;
+    const int r0 = a.indptr[lane];
+    const int ncols = (a.indptr[lane + 1] - r0) * a.G;
+    const int64_t first = (int64_t)li.dec_off + (int64_t)g * li.nsplit;
+    for (int e = threadIdx.x; e < ncols * D; e += blockDim.x) {
+        const int n = e / D, dd = e - n * D;
+        float M = kNegInf;
+        for (int s = 0; s < li.nsplit; ++s) M = fmaxf(M, a.part_ml[(first + s) * 64 + n]);
+        float den = 0.0f, num = 0.0f;
+        if (M != kNegInf) {
+            for (int s = 0; s < li.nsplit; ++s) {
+                const float ms = a.part_ml[(first + s) * 64 + n];
+                const float wgt = __builtin_amdgcn_exp2f(ms - M);
+                den += wgt * a.part_ml[(first + s) * 64 + 32 + n];
+                num += wgt * a.part_o[((first + s) * a.ncols_max + n) * D + dd];
+            }
+        }
+        const int64_t row = r0 + n / a.G;
+        const int head = g * a.G + n % a.G;
+        a.out[(row * a.Hq + head) * D + dd] = den > 0.0f ? num / den : 0.0f;
+        if (dd == 0 && a.lse) a.lse[row * a.Hq + head] = den > 0.0f ? (M + __log2f(den)) * 0.69314718055994531f : kNegInf;
+    }
+}
+
+}  // namespace fpk

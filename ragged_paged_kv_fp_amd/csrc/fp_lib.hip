@@ -1,0 +1,344 @@
+// fp_lib.hip - host side of the C ABI declared in include/fp.h.
+//
+// Host work is limited to argument checks, shape-only planning from the
+// *_host copies of the offset arrays (how many work items to launch, how big
+// the workspace is) and kernel launches on the caller's stream. All per-lane
+// decisions that depend on device data (kv_len, slots, committed_len, channel
+// counts, mask bits) are taken by the kernels.
+#include "fp_kernels.h"
+
+#include <stdint.h>
+#include <string.h>
+
+namespace {
+
+using namespace fpk;
+
+constexpr int kDefaultSplit = 512;
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_pool(const fp_kv_pool *p) {
+    if (!p || !p->kv || !p->page_indptr || !p->page_indptr_host || !p->page_ids || !p->committed_len) return FP_ERR_NULL;
+    if (p->num_pages < 1 || p->num_kv_heads < 1) return FP_ERR_SHAPE;
+    if (p->page_size != 8 && p->page_size != 16 && p->page_size != 32) return FP_ERR_UNSUPPORTED;
+    if (p->head_dim != 64 && p->head_dim != 128) return FP_ERR_UNSUPPORTED;
+    return FP_OK;
+}
+
+int check_geom(const fp_geometry *g, const fp_kv_pool *p) {
+    if (!g || !g->indptr || !g->indptr_host || !g->kv_len || !g->fold) return FP_ERR_NULL;
+    if (g->num_lanes < 1 || g->num_rows < 0) return FP_ERR_SHAPE;
+    if (g->num_rows > 0 && (!g->positions || !g->slots)) return FP_ERR_NULL;
+    const int32_t *ip = g->indptr_host;
+    if (ip[0] != 0 || ip[g->num_lanes] != g->num_rows) return FP_ERR_SHAPE;
+    for (int l = 0; l < g->num_lanes; ++l)
+        if (ip[l + 1] < ip[l]) return FP_ERR_SHAPE;
+    if (p) {
+        const int32_t *pp = p->page_indptr_host;
+        if (pp[0] != 0) return FP_ERR_SHAPE;
+        for (int l = 0; l < g->num_lanes; ++l) {
+            if (pp[l + 1] < pp[l]) return FP_ERR_SHAPE;
+            if ((int64_t)(pp[l + 1] - pp[l]) * p->page_size > (int64_t)INT32_MAX / 2) return FP_ERR_UNSUPPORTED;
+        }
+    }
+    return FP_OK;
+}
+
+int check_mask(const fp_mask *m, const fp_geometry *g) {
+    if (!m) return FP_OK;
+    if (!m->bits || !m->word_offset || !m->word_offset_host) return FP_ERR_NULL;
+    const int64_t *wo = m->word_offset_host;
+    for (int l = 0; l < g->num_lanes; ++l) {
+        const int64_t span = wo[l + 1] - wo[l];
+        const int n = g->indptr_host[l + 1] - g->indptr_host[l];
+        if (span < 0) return FP_ERR_SHAPE;
+        if (span > 0 && (n == 0 || span % n != 0)) return FP_ERR_SHAPE;
+    }
+    return FP_OK;
+}
+
+struct Plan {
+    int L = 0, H = 0, G = 0, Hq = 0, D = 0, P = 0, split = 0, ncols_max = 1;
+    int64_t N = 0, n_dec = 0, n_pre = 0, sum_words = 0;
+    bool merge = false, summaries = false;
+    size_t off_lane = 0, off_dec = 0, off_pre = 0, off_qrot = 0, off_po = 0, off_pml = 0, off_sum = 0, total = 0;
+};
+
+// Shape-only plan: mirrors lane_counts() of plan_kernel from the host copies.
+int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *mask, int32_t Hq,
+              const fp_tuning *tun, Plan *pl) {
+    int rc = check_pool(pool);
+    if (rc) return rc;
+    if ((rc = check_geom(geom, pool))) return rc;
+    if ((rc = check_mask(mask, geom))) return rc;
+    if (Hq < 1 || Hq % pool->num_kv_heads) return FP_ERR_SHAPE;
+    const int G = Hq / pool->num_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return FP_ERR_UNSUPPORTED;
+    if (geom->num_lanes > kMaxLanes) return FP_ERR_UNSUPPORTED;
+    int split = kDefaultSplit;
+    if (tun) {
+        for (int i = 0; i < 7; ++i)
+            if (tun->reserved[i]) return FP_ERR_SHAPE;
+        if (tun->decode_split_slots) {
+            if (tun->decode_split_slots < 32 || tun->decode_split_slots % 32) return FP_ERR_SHAPE;
+            split = tun->decode_split_slots;
+        }
+    }
+    Plan p;
+    p.L = geom->num_lanes;
+    p.H = pool->num_kv_heads;
+    p.G = G;
+    p.Hq = Hq;
+    p.D = pool->head_dim;
+    p.P = pool->page_size;
+    p.split = split;
+    p.N = geom->num_rows;
+    for (int l = 0; l < p.L; ++l) {
+        const int n = geom->indptr_host[l + 1] - geom->indptr_host[l];
+        const int cap = (pool->page_indptr_host[l + 1] - pool->page_indptr_host[l]) * p.P;
+        if (n <= 0) continue;
+        const bool masked = mask && mask->word_offset_host[l + 1] > mask->word_offset_host[l];
+        if (n * G <= kDecodeCols) {
+            const int nsplit = cap > 0 ? (cap + split - 1) / split : 1;
+            p.n_dec += (int64_t)p.H * nsplit;
+            if (nsplit > 1) p.merge = true;
+            if (n * G > p.ncols_max) p.ncols_max = n * G;
+        } else {
+            const int nrb = (n + kRowBlock - 1) / kRowBlock;
+            p.n_pre += (int64_t)p.H * nrb;
+            if (masked) {
+                const int tiles = (cap + 31) / 32;
+                p.sum_words += (int64_t)nrb * 2 * ((tiles + 31) / 32);
+                p.summaries = true;
+            }
+        }
+    }
+    if (p.n_dec > INT32_MAX / 2 || p.n_pre > INT32_MAX / 2 || p.sum_words > INT32_MAX / 2) return FP_ERR_UNSUPPORTED;
+    size_t off = 0;
+    p.off_lane = off; off = align256(off + sizeof(LaneInfo) * (size_t)p.L);
+    p.off_dec = off;  off = align256(off + sizeof(int4) * (size_t)p.n_dec);
+    p.off_pre = off;  off = align256(off + sizeof(int4) * (size_t)p.n_pre);
+    p.off_qrot = off; off = align256(off + sizeof(uint16_t) * (size_t)p.N * Hq * p.D);
+    p.off_po = off;   off = align256(off + (p.merge ? sizeof(float) * (size_t)p.n_dec * p.ncols_max * p.D : 0));
+    p.off_pml = off;  off = align256(off + (p.merge ? sizeof(float) * (size_t)p.n_dec * 64 : 0));
+    p.off_sum = off;  off = align256(off + sizeof(uint32_t) * (size_t)p.sum_words);
+    p.total = off;
+    *pl = p;
+    return FP_OK;
+}
+
+inline int launch_ok() { return hipGetLastError() == hipSuccess ? FP_OK : FP_ERR_HIP; }
+
+template <int D, int NW>
+void launch_prefill(const AttnArgs &a, int64_t n, hipStream_t s) {
+    hipLaunchKernelGGL((prefill_kernel<D, NW>), dim3((unsigned)n), dim3(64 * NW), 0, s, a);
+}
+
+template <int D>
+void launch_prefill_g(const AttnArgs &a, int G, int64_t n, hipStream_t s) {
+    switch (G) {
+        case 1: launch_prefill<D, 1>(a, n, s); break;
+        case 2: launch_prefill<D, 2>(a, n, s); break;
+        case 4: launch_prefill<D, 4>(a, n, s); break;
+        default: launch_prefill<D, 8>(a, n, s); break;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp_append_kv(const fp_kv_pool *pool, const fp_geometry *geom, const void *k, const void *v, float rope_theta,
+                 int32_t *status, hipStream_t stream) {
+    int rc = check_pool(pool);
+    if (rc) return rc;
+    if ((rc = check_geom(geom, pool))) return rc;
+    if (!status) return FP_ERR_NULL;
+    if (geom->num_rows == 0) return FP_OK;
+    if (!k || !v) return FP_ERR_NULL;
+    AppendArgs a;
+    a.pool = static_cast<uint16_t *>(pool->kv);
+    a.num_pages = pool->num_pages;
+    a.P = pool->page_size;
+    a.H = pool->num_kv_heads;
+    a.D = pool->head_dim;
+    a.page_elems = 2LL * a.H * a.P * a.D;
+    a.page_indptr = pool->page_indptr;
+    a.page_ids = pool->page_ids;
+    a.committed = pool->committed_len;
+    a.indptr = geom->indptr;
+    a.L = geom->num_lanes;
+    a.N = geom->num_rows;
+    a.positions = geom->positions;
+    a.slots = geom->slots;
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.theta = (double)rope_theta;
+    a.status = status;
+    const int64_t threads = a.N * (a.D / 2);
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+    return launch_ok();
+}
+
+int64_t fp_attend_workspace_bytes(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *mask,
+                                  int32_t num_q_heads, const fp_tuning *tuning) {
+    Plan p;
+    const int rc = make_plan(pool, geom, mask, num_q_heads, tuning, &p);
+    if (rc) return rc;
+    return (int64_t)p.total;
+}
+
+int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, int32_t num_q_heads, float rope_theta,
+              float sm_scale, const fp_mask *mask, float *out, float *lse, void *workspace, size_t workspace_bytes,
+              const fp_tuning *tuning, int32_t *status, hipStream_t stream) {
+    Plan p;
+    int rc = make_plan(pool, geom, mask, num_q_heads, tuning, &p);
+    if (rc) return rc;
+    if (!status) return FP_ERR_NULL;
+    if (p.N == 0) return FP_OK;
+    if (!q || !out) return FP_ERR_NULL;
+    if (!workspace) return FP_ERR_NULL;
+    if (workspace_bytes < p.total) return FP_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    LaneInfo *lane_info = reinterpret_cast<LaneInfo *>(ws + p.off_lane);
+    int4 *dec_items = reinterpret_cast<int4 *>(ws + p.off_dec);
+    int4 *pre_items = reinterpret_cast<int4 *>(ws + p.off_pre);
+    uint16_t *qrot = reinterpret_cast<uint16_t *>(ws + p.off_qrot);
+
+    PlanArgs pa;
+    pa.indptr = geom->indptr;
+    pa.page_indptr = pool->page_indptr;
+    pa.kv_len = geom->kv_len;
+    pa.mask_off = mask ? mask->word_offset : nullptr;
+    pa.L = p.L; pa.H = p.H; pa.G = p.G; pa.P = p.P; pa.split = p.split;
+    pa.n_dec_host = p.n_dec;
+    pa.n_pre_host = p.n_pre;
+    pa.sum_host = p.sum_words;
+    pa.N_host = p.N;
+    pa.ncols_host = p.ncols_max;
+    pa.merge_host = p.merge ? 1 : 0;
+    pa.lane_info = lane_info;
+    pa.dec_items = dec_items;
+    pa.pre_items = pre_items;
+    pa.status = status;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, pa);
+    if ((rc = launch_ok())) return rc;
+
+    RopeQArgs ra;
+    ra.q = static_cast<const uint16_t *>(q);
+    ra.qrot = qrot;
+    ra.positions = geom->positions;
+    ra.N = p.N;
+    ra.Hq = p.Hq;
+    ra.D = p.D;
+    ra.theta = (double)rope_theta;
+    ra.qscale = (double)sm_scale * 1.4426950408889634;  // log2(e)
+    const int64_t qthreads = p.N * (p.D / 2);
+    hipLaunchKernelGGL(rope_q_kernel, dim3((unsigned)((qthreads + 255) / 256)), dim3(256), 0, stream, ra);
+    if ((rc = launch_ok())) return rc;
+
+    AttnArgs a;
+    a.pool = static_cast<const uint16_t *>(pool->kv);
+    a.num_pages = pool->num_pages;
+    a.P = p.P; a.H = p.H; a.G = p.G; a.Hq = p.Hq;
+    a.page_elems = 2LL * p.H * p.P * p.D;
+    a.page_indptr = pool->page_indptr;
+    a.page_ids = pool->page_ids;
+    a.indptr = geom->indptr;
+    a.slots = geom->slots;
+    a.kv_len = geom->kv_len;
+    a.qrot = qrot;
+    a.mask_bits = mask ? mask->bits : nullptr;
+    a.mask_off = mask ? mask->word_offset : nullptr;
+    a.out = out;
+    a.lse = lse;
+    a.dec_items = dec_items;
+    a.pre_items = pre_items;
+    a.lane_info = lane_info;
+    a.part_o = p.merge ? reinterpret_cast<float *>(ws + p.off_po) : nullptr;
+    a.part_ml = p.merge ? reinterpret_cast<float *>(ws + p.off_pml) : nullptr;
+    a.ncols_max = p.ncols_max;
+    a.summary = reinterpret_cast<const uint32_t *>(ws + p.off_sum);
+
+    if (p.summaries) {
+        SummaryArgs sa;
+        sa.pre_items = pre_items;
+        sa.lane_info = lane_info;
+        sa.indptr = geom->indptr;
+        sa.page_indptr = pool->page_indptr;
+        sa.kv_len = geom->kv_len;
+        sa.bits = mask->bits;
+        sa.mask_off = mask->word_offset;
+        sa.P = p.P;
+        sa.summary = reinterpret_cast<uint32_t *>(ws + p.off_sum);
+        hipLaunchKernelGGL(summary_kernel, dim3((unsigned)p.n_pre), dim3(256), 0, stream, sa);
+        if ((rc = launch_ok())) return rc;
+    }
+    if (p.n_pre) {
+        if (p.D == 128) launch_prefill_g<128>(a, p.G, p.n_pre, stream);
+        else launch_prefill_g<64>(a, p.G, p.n_pre, stream);
+        if ((rc = launch_ok())) return rc;
+    }
+    if (p.n_dec) {
+        if (p.D == 128) hipLaunchKernelGGL(decode_kernel<128>, dim3((unsigned)p.n_dec), dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL(decode_kernel<64>, dim3((unsigned)p.n_dec), dim3(64), 0, stream, a);
+        if ((rc = launch_ok())) return rc;
+    }
+    if (p.merge) {
+        if (p.D == 128) hipLaunchKernelGGL(merge_kernel<128>, dim3(p.L, p.H), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL(merge_kernel<64>, dim3(p.L, p.H), dim3(256), 0, stream, a);
+        if ((rc = launch_ok())) return rc;
+    }
+    return FP_OK;
+}
+
+int fp_fold(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *channel, int32_t *status,
+            hipStream_t stream) {
+    if (!pool || !pool->committed_len) return FP_ERR_NULL;
+    if (!geom || !geom->indptr || !geom->fold || !geom->indptr_host) return FP_ERR_NULL;
+    if (!status) return FP_ERR_NULL;
+    if (geom->num_lanes < 1) return FP_ERR_SHAPE;
+    const int L = geom->num_lanes;
+    hipLaunchKernelGGL(fold_kernel, dim3((L + 255) / 256), dim3(256), 0, stream, geom->indptr, geom->fold, channel,
+                       pool->committed_len, L, status);
+    return launch_ok();
+}
+
+int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, const int32_t *rows, int32_t num_readout,
+               float *dst, int32_t *status, hipStream_t stream) {
+    if (!geom || !geom->indptr || !geom->indptr_host) return FP_ERR_NULL;
+    if (geom->num_lanes < 1 || row_elems < 1 || num_readout < 0) return FP_ERR_SHAPE;
+    if (!status) return FP_ERR_NULL;
+    const int L = geom->num_lanes;
+    const int32_t *ip = geom->indptr_host;
+    if (ip[0] != 0 || ip[L] != geom->num_rows) return FP_ERR_SHAPE;
+    if (!rows) {
+        int nonempty = 0;
+        for (int l = 0; l < L; ++l) {
+            if (ip[l + 1] < ip[l]) return FP_ERR_SHAPE;
+            nonempty += ip[l + 1] > ip[l];
+        }
+        if (nonempty != num_readout) return FP_ERR_SHAPE;
+    }
+    if (num_readout == 0) return FP_OK;
+    if (!out || !dst) return FP_ERR_NULL;
+    const unsigned grid = rows ? (unsigned)num_readout : (unsigned)L;
+    hipLaunchKernelGGL(readout_kernel, dim3(grid), dim3(256), 0, stream, geom->indptr, L, (int64_t)geom->num_rows, out,
+                       row_elems, rows, num_readout, dst, status);
+    return launch_ok();
+}
+
+uint64_t fp_kv_bytes(int32_t L, int32_t H_kv, int32_t d, uint64_t T, int32_t b) {
+    return 2ull * (uint64_t)L * (uint64_t)H_kv * (uint64_t)d * T * (uint64_t)b;
+}
+
+uint64_t fp_pages_for(uint64_t T, int32_t P) { return P > 0 ? (T + (uint64_t)P - 1) / (uint64_t)P : 0; }
+
+uint64_t fp_page_waste(uint64_t T, int32_t P) { return P > 0 ? fp_pages_for(T, P) * (uint64_t)P - T : 0; }
+
+uint64_t fp_page_bytes(int32_t P, int32_t H_kv, int32_t d) { return 2ull * (uint64_t)H_kv * (uint64_t)P * (uint64_t)d * 2ull; }
+
+const char *fp_version(void) { return "ragged_paged_kv_fp_amd 0.1 (gfx950)"; }
+
+}  // extern "C"

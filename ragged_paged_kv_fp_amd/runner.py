@@ -1,0 +1,122 @@
+"""Device buffers for one pass and the four ABI calls in order.
+
+Uploads a host-side description of a pass (offset arrays, slots, positions,
+bf16 bit patterns, page table, masks, channel) into caller-owned torch
+tensors and issues append -> attend -> fold -> readout on one stream.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import api
+
+
+def _dev(a: np.ndarray, device, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(device)
+
+
+def _bits16(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+
+def _geometry(p, device) -> api.Geometry:
+    return api.Geometry(indptr=_dev(p.indptr.astype(np.int32), device), indptr_host=p.indptr.astype(np.int32).copy(),
+                        positions=_dev(p.positions.astype(np.int32), device),
+                        slots=_dev(p.slots.astype(np.int32), device),
+                        kv_len=_dev(p.kv_len.astype(np.int32), device), fold=_dev(p.fold.astype(np.int32), device))
+
+
+class DeviceStep:
+    """Owns the device tensors of one workload (a prefix pass plus the step)."""
+
+    def __init__(self, wl, device="cuda", fill_bits: int = 0, split: Optional[int] = None, with_lse: bool = True):
+        self.wl = wl
+        self.device = torch.device(device)
+        self.split = split
+        dev = self.device
+        page_elems = 2 * wl.H_kv * wl.P * wl.d
+        fill = int(np.array([fill_bits], dtype=np.uint16).view(np.int16)[0])
+        self.pool_t = torch.full((wl.num_pages, page_elems), fill, dtype=torch.int16, device=dev)
+        L = wl.num_lanes
+        self.pool = api.Pool(kv=self.pool_t, num_pages=wl.num_pages, page_size=wl.P, num_kv_heads=wl.H_kv,
+                             head_dim=wl.d, page_indptr=_dev(wl.page_indptr.astype(np.int32), dev),
+                             page_indptr_host=wl.page_indptr.astype(np.int32).copy(),
+                             page_ids=_dev(wl.page_ids.astype(np.int32), dev),
+                             committed_len=torch.zeros(L, dtype=torch.int32, device=dev))
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.prefix_geom = _geometry(wl.prefix, dev) if wl.prefix is not None else None
+        if wl.prefix is not None:
+            self.prefix_k = _bits16(wl.prefix.k, dev)
+            self.prefix_v = _bits16(wl.prefix.v, dev)
+        st = wl.step
+        self.geom = _geometry(st, dev)
+        self.k = _bits16(st.k, dev)
+        self.v = _bits16(st.v, dev)
+        self.q = _bits16(st.q, dev)
+        N = st.num_rows
+        self.out = torch.zeros((N, wl.H_q, wl.d), dtype=torch.float32, device=dev)
+        self.lse = torch.zeros((N, wl.H_q), dtype=torch.float32, device=dev) if with_lse else None
+        self.mask = None
+        if wl.mask_bits is not None:
+            self.mask = api.Mask(bits=_dev(wl.mask_bits.view(np.int32), dev),
+                                 word_offset=_dev(wl.mask_word_offset.astype(np.int64), dev),
+                                 word_offset_host=wl.mask_word_offset.astype(np.int64).copy())
+        self.channel = _dev(wl.channel.astype(np.int32), dev) if wl.channel is not None else None
+        self.readout_rows = _dev(wl.readout_rows.astype(np.int32), dev) if wl.readout_rows is not None else None
+        if wl.readout_rows is not None:
+            nro = len(wl.readout_rows)
+        else:
+            nro = int((np.diff(st.indptr) > 0).sum())
+        self.dst = torch.zeros((nro, wl.H_q * wl.d), dtype=torch.float32, device=dev)
+        ws = api.attend_workspace_bytes(self.pool, self.geom, wl.H_q, self.mask, split)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.committed0 = None
+
+    # ------------------------------------------------------------------ passes
+    def run_prefix(self) -> None:
+        """Append the cached prefix of every lane and fold it (untimed set-up)."""
+        wl = self.wl
+        if self.prefix_geom is not None:
+            api.append_kv(self.pool, self.prefix_geom, self.prefix_k, self.prefix_v, wl.theta, self.status)
+            api.fold(self.pool, self.prefix_geom, self.status)
+        self.committed0 = self.pool.committed_len.clone()
+
+    def reset(self) -> None:
+        """Restore committed_len to its post-prefix value so the step can be replayed."""
+        self.pool.committed_len.copy_(self.committed0)
+
+    def append(self, stream=None):
+        api.append_kv(self.pool, self.geom, self.k, self.v, self.wl.theta, self.status, stream)
+
+    def attend(self, stream=None, split=None):
+        wl = self.wl
+        api.attend(self.pool, self.geom, self.q, wl.H_q, wl.theta, wl.sm_scale, self.out, self.workspace,
+                   self.status, self.lse, self.mask, self.split if split is None else split, stream)
+
+    def fold(self, stream=None):
+        api.fold(self.pool, self.geom, self.status, self.channel, stream)
+
+    def readout(self, stream=None):
+        api.readout(self.geom, self.out, self.dst, self.status, self.readout_rows, stream)
+
+    def step(self, stream=None) -> None:
+        self.append(stream)
+        self.attend(stream)
+        self.fold(stream)
+        self.readout(stream)
+
+    # ------------------------------------------------------------------ views
+    def pool_logical(self):
+        """Pool as (K [pages][H][P][d], V [pages][H][P][d]) uint16 numpy arrays (V un-transposed)."""
+        wl = self.wl
+        raw = self.pool_t.cpu().numpy().view(np.uint16).reshape(wl.num_pages, 2, wl.H_kv, -1)
+        K = raw[:, 0].reshape(wl.num_pages, wl.H_kv, wl.P, wl.d)
+        V = raw[:, 1].reshape(wl.num_pages, wl.H_kv, wl.d, wl.P).transpose(0, 1, 3, 2)
+        return K, V

@@ -1,0 +1,159 @@
+"""CPU-side checks of the C ABI library: it loads, exports every function
+include/fp.h declares, its host-only accounting matches Eqs. (1)/(2) and the
+oracle, and bad arguments are rejected with the documented codes before
+anything is enqueued (no GPU call is made by these tests)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from ragged_paged_kv_fp_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from ragged_paged_kv_fp_amd import build
+
+        build.build()
+    return _lib.load()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    from ragged_paged_kv_fp_amd import _lib
+
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert b"gfx950" in lib.fp_version()
+
+
+def test_header_constants_match_binding_and_oracle():
+    from ragged_paged_kv_fp_amd import _lib
+
+    src = open(HEADER).read()
+    consts = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(FP_\w+)\s+\(?(-?\d+)\)?", src)}
+    for name, val in consts.items():
+        assert getattr(_lib, name) == val, name
+    assert consts["FP_ST_SLOT_RANGE"] == oracle.ST_SLOT_RANGE
+    assert consts["FP_ST_FROZEN"] == oracle.ST_FROZEN
+    assert consts["FP_ST_KVLEN"] == oracle.ST_KVLEN
+    assert consts["FP_ST_FOLD_CLAMP"] == oracle.ST_FOLD_CLAMP
+    assert consts["FP_ST_READOUT_RANGE"] == oracle.ST_READOUT_RANGE
+    assert consts["FP_ST_MASK_SHORT"] == oracle.ST_MASK_SHORT
+    assert consts["FP_ST_PAGE_RANGE"] == oracle.ST_PAGE_RANGE
+    assert consts["FP_FOLD_ALL"] == oracle.FOLD_ALL and consts["FP_FOLD_CHANNEL"] == oracle.FOLD_CHANNEL
+
+
+def test_accounting_matches_eq1_eq2(lib):
+    assert lib.fp_kv_bytes(32, 8, 128, 1, 2) == 131072
+    assert lib.fp_kv_bytes(32, 8, 128, 8192, 2) == 1 << 30
+    for P in (8, 16, 32):
+        assert lib.fp_page_bytes(P, 8, 128) == oracle.kv_bytes(1, 8, 128, P, 2)
+        for T in range(0, 65537):
+            assert lib.fp_pages_for(T, P) == oracle.pages_for(T, P)
+            assert lib.fp_page_waste(T, P) == oracle.page_waste(T, P)
+    assert lib.fp_pages_for(37, 16) == 3 and lib.fp_page_waste(37, 16) == 11
+
+
+# ------------------------------------------------------------------ host validation
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _structs(L=2, rows=(3, 1), pages=(1, 2), P=16, H=2, d=64):
+    from ragged_paged_kv_fp_amd import _lib
+
+    keep = []
+    ip = np.array([0] + list(np.cumsum(rows)), np.int32)
+    pp = np.array([0] + list(np.cumsum(pages)), np.int32)
+    keep += [ip, pp]
+    g = _lib.FpGeometry(L, int(ip[-1]), FAKE, ip.ctypes.data, FAKE, FAKE, FAKE, FAKE)
+    p = _lib.FpKvPool(FAKE, int(pp[-1]), P, H, d, FAKE, pp.ctypes.data, FAKE, FAKE)
+    return g, p, keep
+
+
+def _ws(lib, p, g, hq=4, m=None, t=None):
+    return lib.fp_attend_workspace_bytes(ctypes.byref(p), ctypes.byref(g), m, hq, t)
+
+
+def test_workspace_query_is_host_only_and_sized(lib):
+    g, p, keep = _structs()
+    n = _ws(lib, p, g)
+    assert n > 0
+    # two decode lanes (3*2 and 1*2 row-heads <= 32): items = H * ceil(cap/512) each; q copy = N*Hq*d*2
+    assert n >= 4 * 4 * 64 * 2
+
+
+@pytest.mark.parametrize("mut,code", [
+    ("page_size=12", -3), ("head_dim=96", -3), ("num_kv_heads=0", -2), ("num_pages=0", -2),
+    ("hq=5", -2), ("hq=6", -3), ("hq=32", -3), ("num_lanes=0", -2), ("num_rows=7", -2), ("kv=0", -1),
+])
+def test_bad_arguments_rejected(lib, mut, code):
+    g, p, keep = _structs()
+    hq = 4
+    k, v = mut.split("=")
+    v = int(v)
+    if k == "hq":
+        hq = v
+    elif hasattr(p, k) and k not in ("num_rows", "num_lanes"):
+        setattr(p, k, v)
+    else:
+        setattr(g, k, v)
+    assert _ws(lib, p, g, hq=hq) == code
+
+
+def test_workspace_too_small_and_null_pointers(lib):
+    g, p, keep = _structs()
+    st = ctypes.c_int32(0)
+    rc = lib.fp_attend(ctypes.byref(p), ctypes.byref(g), FAKE, 4, 10000.0, 0.125, None, FAKE, None, FAKE, 16, None,
+                       ctypes.addressof(st), None)
+    assert rc == -4
+    rc = lib.fp_attend(ctypes.byref(p), ctypes.byref(g), None, 4, 10000.0, 0.125, None, FAKE, None, FAKE, 1 << 30,
+                       None, ctypes.addressof(st), None)
+    assert rc == -1
+    assert lib.fp_append_kv(None, ctypes.byref(g), FAKE, FAKE, 1e4, ctypes.addressof(st), None) == -1
+    assert lib.fp_append_kv(ctypes.byref(p), ctypes.byref(g), None, FAKE, 1e4, ctypes.addressof(st), None) == -1
+    assert lib.fp_append_kv(ctypes.byref(p), ctypes.byref(g), FAKE, FAKE, 1e4, None, None) == -1
+    assert lib.fp_fold(ctypes.byref(p), ctypes.byref(g), None, None, None) == -1
+
+
+def test_mask_and_tuning_validation(lib):
+    from ragged_paged_kv_fp_amd import _lib
+
+    g, p, keep = _structs(rows=(3, 1))
+    wo = np.array([0, 7, 7], np.int64)  # 7 words over 3 rows: not a whole number per row
+    m = _lib.FpMask(FAKE, FAKE, wo.ctypes.data)
+    assert _ws(lib, p, g, m=ctypes.byref(m)) == -2
+    wo2 = np.array([0, 6, 8], np.int64)
+    m2 = _lib.FpMask(FAKE, FAKE, wo2.ctypes.data)
+    assert _ws(lib, p, g, m=ctypes.byref(m2)) > 0
+    t = _lib.FpTuning()
+    t.decode_split_slots = 48
+    assert _ws(lib, p, g, t=ctypes.byref(t)) == -2
+    t.decode_split_slots = 64
+    assert _ws(lib, p, g, t=ctypes.byref(t)) > 0
+    t.reserved[2] = 1
+    assert _ws(lib, p, g, t=ctypes.byref(t)) == -2
+
+
+def test_readout_default_count_checked(lib):
+    g, p, keep = _structs(L=3, rows=(3, 0, 2), pages=(1, 1, 1))
+    st = ctypes.c_int32(0)
+    assert lib.fp_readout(ctypes.byref(g), FAKE, 8, None, 3, FAKE, ctypes.addressof(st), None) == -2
+    assert lib.fp_readout(ctypes.byref(g), FAKE, 8, None, 2, FAKE, None, None) == -1

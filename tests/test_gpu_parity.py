@@ -1,0 +1,270 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small copies of the five workload configurations and random geometries run
+whole on both sides; the full-size configurations run whole on the GPU and
+are checked on sampled lanes and rows. Invariants: page-pool permutation,
+NaN-poisoned pool, prefix/suffix split, all-causal bitmap vs folding,
+determinism, decode split size. Error paths set status bits and suppress writes.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import parity_util as pu
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ragged_paged_kv_fp_amd import _lib
+
+    _lib.load()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_config_small(cfg, seed):
+    wl = W.make_config(cfg, seed=seed, scale="small" if cfg > 1 else "full")
+    _say(f"config {cfg} seed {seed}: lanes={wl.num_lanes} rows={wl.step.num_rows}")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)
+    r = pu.compare_step(ds, ref)
+    _say(r)
+
+
+@pytest.mark.parametrize("seed,H_kv,G,d,P", [
+    (0, 2, 2, 64, 16), (1, 1, 4, 128, 8), (2, 2, 8, 64, 32), (3, 4, 1, 128, 16),
+    (4, 2, 4, 128, 32), (5, 1, 2, 64, 8), (6, 3, 4, 128, 16), (7, 2, 8, 128, 8),
+])
+def test_random_geometry(seed, H_kv, G, d, P):
+    wl = W.make_random(seed, H_kv=H_kv, G=G, d=d, P=P, num_lanes=7, max_rows=90, max_ctx=400)
+    _say(f"random seed {seed}: H_kv={H_kv} G={G} d={d} P={P} rows={wl.step.num_rows}")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)
+    _say(pu.compare_step(ds, ref))
+
+
+def test_page_permutation_bit_identical_with_nan_decoys():
+    wl = W.make_random(21, H_kv=2, G=4, d=128, P=16, num_lanes=6, max_rows=70, max_ctx=300, extra_pages=9)
+    a = pu.gpu_run(wl, fill=NAN_BF16)
+    rng = np.random.default_rng(3)
+    wl.page_ids = rng.permutation(wl.num_pages)[: len(wl.page_ids)].astype(np.int32)
+    b = pu.gpu_run(wl, fill=NAN_BF16)
+    assert np.array_equal(a.out.cpu().numpy(), b.out.cpu().numpy())
+    assert np.array_equal(a.lse.cpu().numpy(), b.lse.cpu().numpy())
+    ref = pu.oracle_run(wl, fill=NAN_BF16)
+    pu.compare_step(b, ref)
+
+
+def test_poisoned_pool_outputs_finite_and_equal():
+    wl = W.make_config(2, seed=4, scale="small")
+    a = pu.gpu_run(wl, fill=0)
+    b = pu.gpu_run(wl, fill=NAN_BF16)
+    oa, ob = a.out.cpu().numpy(), b.out.cpu().numpy()
+    assert np.all(np.isfinite(ob)) and np.array_equal(oa, ob)
+    wl3 = W.make_config(3, seed=4, scale="small")
+    a3, b3 = pu.gpu_run(wl3, fill=0), pu.gpu_run(wl3, fill=NAN_BF16)
+    assert np.array_equal(a3.out.cpu().numpy(), b3.out.cpu().numpy())
+
+
+def test_prefix_then_continuation_equals_whole_prompt():
+    import torch
+
+    from ragged_paged_kv_fp_amd import api, runner
+
+    wl = W.make_config(1)
+    whole = pu.gpu_run(wl)
+    K0, V0 = whole.pool_logical()
+    O0 = whole.out.cpu().numpy()
+    st = wl.step
+    for split in (1, 5, 16, 31, 32, 33, 36):
+        ds = runner.DeviceStep(wl)
+        ds.run_prefix()
+        pre = W.Pass(indptr=np.array([0, split], np.int32), positions=st.positions[:split], slots=st.slots[:split],
+                     kv_len=np.array([split], np.int32), fold=np.array([W.FOLD_ALL], np.int32),
+                     k=st.k[:split], v=st.v[:split], q=st.q[:split])
+        post = W.Pass(indptr=np.array([0, 37 - split], np.int32), positions=st.positions[split:],
+                      slots=st.slots[split:], kv_len=np.array([37], np.int32),
+                      fold=np.array([W.FOLD_ALL], np.int32), k=st.k[split:], v=st.v[split:], q=st.q[split:])
+        outs = []
+        for p in (pre, post):
+            g = runner._geometry(p, ds.device)
+            k, v, q = runner._bits16(p.k, ds.device), runner._bits16(p.v, ds.device), runner._bits16(p.q, ds.device)
+            out = torch.zeros((p.num_rows, wl.H_q, wl.d), dtype=torch.float32, device=ds.device)
+            ws = torch.empty(max(256, api.attend_workspace_bytes(ds.pool, g, wl.H_q)), dtype=torch.uint8,
+                             device=ds.device)
+            api.append_kv(ds.pool, g, k, v, wl.theta, ds.status)
+            api.attend(ds.pool, g, q, wl.H_q, wl.theta, wl.sm_scale, out, ws, ds.status)
+            api.fold(ds.pool, g, ds.status)
+            outs.append(out)
+        torch.cuda.synchronize()
+        K1, V1 = ds.pool_logical()
+        assert np.array_equal(K0, K1) and np.array_equal(V0, V1), f"pool bytes differ at split {split}"
+        O1 = torch.cat(outs).cpu().numpy()
+        assert np.abs(O1 - O0).max() <= pu.MAX_ABS
+        assert int(ds.pool.committed_len.cpu()[0]) == 37 and int(ds.status.cpu()[0]) == 0
+
+
+def test_all_causal_bitmap_equals_folding():
+    wl = W.make_config(3, seed=1, scale="small")
+    base = pu.gpu_run(wl)
+    st = wl.step
+    offs = [0]
+    words = []
+    for lane in range(wl.num_lanes):
+        n = int(st.indptr[lane + 1] - st.indptr[lane])
+        kvl = int(st.kv_len[lane])
+        wpr = -(-kvl // 32)
+        j = np.arange(wpr * 32)
+        for r in range(int(st.indptr[lane]), int(st.indptr[lane + 1])):
+            allowed = (j <= st.slots[r]) & (j < kvl)
+            words.append((allowed.reshape(wpr, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(1))
+        offs.append(offs[-1] + n * wpr)
+    wl.mask_bits = np.concatenate(words).astype(np.uint32)
+    wl.mask_word_offset = np.array(offs, np.int64)
+    masked = pu.gpu_run(wl)
+    assert np.array_equal(base.out.cpu().numpy(), masked.out.cpu().numpy())
+    assert np.array_equal(base.lse.cpu().numpy(), masked.lse.cpu().numpy())
+
+
+def test_run_to_run_deterministic():
+    wl = W.make_config(4, seed=2, scale="small")
+    a, b = pu.gpu_run(wl), pu.gpu_run(wl)
+    assert np.array_equal(a.out.cpu().numpy(), b.out.cpu().numpy())
+    assert np.array_equal(a.lse.cpu().numpy(), b.lse.cpu().numpy())
+
+
+@pytest.mark.parametrize("split", [32, 64, 256, 4096])
+def test_decode_split_size_invariance(split):
+    wl = W.make_config(2, seed=5, scale="small")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl, split=split)
+    pu.compare_step(ds, ref)
+
+
+def test_error_paths_set_status_and_suppress_writes():
+    wl = W.make_config(1)
+    st = wl.step
+    st.slots = st.slots.copy()
+    st.slots[3] = 48      # beyond 3 pages x 16
+    st.slots[4] = -5
+    st.kv_len = np.array([60], np.int32)   # beyond capacity: clamped
+    st.fold = np.array([50], np.int32)     # literal beyond rows: clamped
+    ref = pu.oracle_run(wl, fill=0x1234)
+    ds = pu.gpu_run(wl, fill=0x1234)
+    want = oracle.ST_SLOT_RANGE | oracle.ST_KVLEN | oracle.ST_FOLD_CLAMP
+    assert ref["status"] == want
+    pu.compare_step(ds, ref)
+
+
+def test_frozen_slot_writes_are_suppressed():
+    import torch
+
+    wl = W.make_config(4, seed=0, scale="small")
+    ds = pu.gpu_run(wl, fill=0x1234)
+    # replay the append with sign-flipped K/V without resetting committed_len:
+    # folded slots are frozen now and must keep their values, the rest take the new ones
+    K0, V0 = ds.pool_logical()
+    c = ds.pool.committed_len.cpu().numpy()
+    ds.status.zero_()
+    ds.k ^= torch.tensor(-0x8000, dtype=torch.int16, device=ds.k.device)
+    ds.v ^= torch.tensor(-0x8000, dtype=torch.int16, device=ds.v.device)
+    ds.append()
+    torch.cuda.synchronize()
+    assert int(ds.status.cpu()[0]) == oracle.ST_FROZEN
+    K1, V1 = ds.pool_logical()
+    st = wl.step
+    n_frozen = n_new = 0
+    for lane in range(wl.num_lanes):
+        for r in range(int(st.indptr[lane]), int(st.indptr[lane + 1])):
+            s_ = int(st.slots[r])
+            pg = int(wl.page_ids[wl.page_indptr[lane] + s_ // wl.P])
+            off = s_ % wl.P
+            if s_ < c[lane]:
+                n_frozen += 1
+                assert np.array_equal(V1[pg, :, off], V0[pg, :, off]) and np.array_equal(K1[pg, :, off], K0[pg, :, off])
+            else:
+                n_new += 1
+                assert np.array_equal(V1[pg, :, off], st.v[r] ^ 0x8000)
+    assert n_frozen > 0 and n_new > 0
+
+
+def test_channel_fold_out_of_range_clamped():
+    wl = W.make_config(4, seed=1, scale="small")
+    wl.channel = wl.channel.copy()
+    verify = [i for i, f in enumerate(wl.step.fold) if f == W.FOLD_CHANNEL]
+    wl.channel[verify[0]] = 99
+    wl.channel[verify[-1]] = -3
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)
+    assert ref["status"] == oracle.ST_FOLD_CLAMP
+    pu.compare_step(ds, ref)
+
+
+def test_empty_rows_and_mask_short():
+    wl = W.make_random(33, H_kv=2, G=4, d=128, P=16, num_lanes=6, max_rows=60, max_ctx=200)
+    # an all-zero bitmap lane: every row empty -> O = 0, LSE = -inf
+    for lane in range(wl.num_lanes):
+        o0, o1 = int(wl.mask_word_offset[lane]), int(wl.mask_word_offset[lane + 1])
+        if o1 > o0:
+            wl.mask_bits = wl.mask_bits.copy()
+            wl.mask_bits[o0:o1] = 0
+            break
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)
+    pu.compare_step(ds, ref)
+
+
+# ------------------------------------------------------------------ full-size configurations, sampled
+
+def _sample(wl, n_lanes, rows_per_lane, seed):
+    rng = np.random.default_rng(seed)
+    st = wl.step
+    nonempty = [l for l in range(wl.num_lanes) if st.indptr[l + 1] > st.indptr[l]]
+    lanes = sorted(rng.choice(nonempty, size=min(n_lanes, len(nonempty)), replace=False).tolist())
+    rows = []
+    for l in lanes:
+        r0, r1 = int(st.indptr[l]), int(st.indptr[l + 1])
+        pick = {r0, r1 - 1} | set(rng.integers(r0, r1, size=min(rows_per_lane, r1 - r0)).tolist())
+        rows.extend(sorted(pick))
+    return lanes, np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("cfg,n_lanes,rows_per_lane", [(2, 8, 1), (3, 6, 6), (4, 10, 8), (5, 3, 5)])
+def test_full_size_sampled(cfg, n_lanes, rows_per_lane):
+    wl = W.make_config(cfg, seed=0, scale="full")
+    _say(f"full config {cfg}: lanes={wl.num_lanes} rows={wl.step.num_rows} pages={wl.num_pages}")
+    ds = pu.gpu_run(wl)
+    lanes, rows = _sample(wl, n_lanes, rows_per_lane, seed=cfg)
+    # prefill lanes of config 3 are the expensive, MFMA-bound part: make sure some are sampled
+    if cfg == 3:
+        pre = [l for l in range(wl.num_lanes) if wl.step.indptr[l + 1] - wl.step.indptr[l] > 1][:2]
+        extra = []
+        for l in pre:
+            r0, r1 = int(wl.step.indptr[l]), int(wl.step.indptr[l + 1])
+            extra += [r0, (r0 + r1) // 2, r1 - 1]
+        lanes = sorted(set(lanes) | set(pre))
+        rows = np.array(sorted(set(rows.tolist()) | set(extra)), dtype=np.int64)
+    ref = pu.oracle_run(wl, lanes=lanes, rows=rows)
+    pu.compare_pool(ds, ref, lanes=lanes)
+    err, rel = pu.compare_outputs(ds, ref)
+    assert ds.pool.committed_len.cpu().numpy().tolist() == ref["committed"].tolist()
+    assert int(ds.status.cpu()[0]) == 0 and ref["status"] == 0
+    rl = ref["readout_rows"]
+    out = ds.out.cpu().numpy().reshape(ds.out.shape[0], -1)
+    assert np.array_equal(ds.dst.cpu().numpy(), out[rl])
+    # properties that hold at any size: finite outputs; single-head rows are convex combinations of V
+    assert np.all(np.isfinite(ds.out.cpu().numpy()))
+    _say(dict(max_abs=err, rel_l2=rel, lanes=len(lanes), rows=len(rows)))
