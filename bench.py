@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the ForwardPass attention step on one MI355X.
+
+A step is one whole pass through the four ABI calls (append -> attend ->
+fold -> readout) over one batch of synthetic input that is already resident
+in HBM, plus the reset of committed_len that makes the step replayable.
+
+Default workload: the decode wave (64 lanes x 1 row, kv_len ~ U{512..8192},
+H_q=32, H_kv=8, d=128, bf16, pages of 16 in a permuted pool). `value` is the
+decode KV read rate of the whole step: algorithmic KV bytes (each lane's
+kv_len slots x 2 x H_kv x d x 2 B, read once for all GQA heads) per second.
+`roofline` prices the attention kernels alone, timed with HIP events recorded
+on the launch stream around them inside every timed step. `cpu_baseline` is
+the fp64 oracle timed on the host on a bounded sample of the same workload.
+
+Other workloads: --config 1..5 (3: mixed prefill+decode; 4: guidance +
+speculative verify; 5: long-context masked prefill, reported in TFLOP/s).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s + decode KV-read GB/s (1 GPU), % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+
+WORKLOAD_TEXT = {
+    1: "one lane, 37-row prompt, H_q=4 H_kv=2 d=64, 3 shuffled pages of 16",
+    2: "decode wave: 64 lanes x 1 row, kv_len U{512..8192}, H_q=32 H_kv=8 d=128, P=16, permuted pool",
+    3: "mixed wave: 8 prefill lanes (1024-4096 rows on 0-2048 cached) + 120 decode lanes (kv 256-16384), "
+       "H_q=32 H_kv=8 d=128, P=32",
+    4: "guidance pairs (prefix 2048/512) + 32 verify lanes x 8 draft rows, channel fold, H_q=32 H_kv=8 d=128, P=16",
+    5: "16 lanes x 512-row chunks over kv_len 32768, window-1024+4-sink / TOVA-30% bitmaps, "
+       "H_q=64 H_kv=8 d=128, P=16",
+}
+
+
+# --------------------------------------------------------------------------- algorithmic work
+
+def attended_pairs(wl) -> np.ndarray:
+    """|A(r)| per row: slots each row attends (causal rule or bitmap), from the inputs."""
+    st = wl.step
+    cap = wl.capacity()
+    out = np.zeros(st.num_rows, dtype=np.int64)
+    for lane in range(wl.num_lanes):
+        r0, r1 = int(st.indptr[lane]), int(st.indptr[lane + 1])
+        if r1 == r0:
+            continue
+        eff = min(max(int(st.kv_len[lane]), 0), int(cap[lane]))
+        masked = wl.mask_bits is not None and wl.mask_word_offset[lane + 1] > wl.mask_word_offset[lane]
+        if not masked:
+            out[r0:r1] = np.clip(np.minimum(st.slots[r0:r1].astype(np.int64) + 1, eff), 0, None)
+            continue
+        o0, o1 = int(wl.mask_word_offset[lane]), int(wl.mask_word_offset[lane + 1])
+        wpr = (o1 - o0) // (r1 - r0)
+        words = wl.mask_bits[o0:o1].reshape(r1 - r0, wpr)
+        nfull = eff // 32
+        cnt = np.unpackbits(words[:, :nfull].view(np.uint8), axis=1).sum(axis=1).astype(np.int64)
+        if eff % 32 and nfull < wpr:
+            tail = words[:, nfull] & np.uint32((1 << (eff % 32)) - 1)
+            cnt += np.unpackbits(tail.view(np.uint8).reshape(-1, 4), axis=1).sum(axis=1)
+        out[r0:r1] = cnt
+    return out
+
+
+def work(wl):
+    """Algorithmic bytes of decode-class lanes and flops of all attention."""
+    st = wl.step
+    G = wl.H_q // wl.H_kv
+    n = np.diff(st.indptr).astype(np.int64)
+    eff = np.minimum(np.maximum(st.kv_len.astype(np.int64), 0), wl.capacity())
+    decode = (n > 0) & (n * G <= 32)
+    kv_bytes = int((eff[decode] * 2 * wl.H_kv * wl.d * 2).sum())
+    pairs = attended_pairs(wl)
+    lane_of = np.repeat(np.arange(wl.num_lanes), n)
+    flops_all = 4.0 * wl.d * wl.H_q * float(pairs.sum())
+    flops_prefill = 4.0 * wl.d * wl.H_q * float(pairs[~decode[lane_of]].sum()) if len(pairs) else 0.0
+    return dict(kv_bytes_decode=kv_bytes, kv_bytes_all=int((eff * 2 * wl.H_kv * wl.d * 2).sum()),
+                flops=flops_all, flops_prefill=flops_prefill, pairs=int(pairs.sum()))
+
+
+# --------------------------------------------------------------------------- HIP events
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch has loaded (same soname)."""
+
+    def __init__(self):
+        import ctypes
+
+        self.ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        rc = self.lib.hipEventCreate(self.ct.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        self.lib.hipEventSynchronize(self.ct.c_void_p(b))
+        t = self.ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self.ct.byref(t), self.ct.c_void_p(a), self.ct.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(t.value)
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(self.ct.c_void_p(ev))
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(wl, cfg: int, unit: str, budget_s: float = 20.0):
+    """Time the fp64 oracle on a bounded sample of the same step, one host thread."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    st = wl.step
+    n = np.diff(st.indptr).astype(np.int64)
+    order = [l for l in range(wl.num_lanes) if n[l] > 0]
+    G = wl.H_q // wl.H_kv
+    # bounded sample: whole lanes for decode-class work, sampled rows of prefill lanes
+    if cfg in (1, 2, 4):
+        lanes, rows = order, None
+    else:
+        rng = np.random.default_rng(7)
+        lanes = sorted(rng.choice(order, size=min(4, len(order)), replace=False).tolist())
+        rows = []
+        for l in lanes:
+            r0, r1 = int(st.indptr[l]), int(st.indptr[l + 1])
+            rows += sorted(set(rng.integers(r0, r1, size=min(8, r1 - r0)).tolist()))
+        rows = np.array(rows, dtype=np.int64)
+    pool = oracle.Pool(wl.num_pages, wl.P, wl.H_kv, wl.d, wl.page_indptr, wl.page_ids)
+    c = np.zeros(wl.num_lanes, np.int32)
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        if wl.prefix is not None:  # untimed set-up, like the GPU prefix pass
+            p = wl.prefix
+            oracle.append(pool, c, p.indptr, p.positions, p.slots, p.k, p.v, wl.theta, lanes=lanes)
+            c, _ = oracle.fold(c, p.indptr, p.fold)
+        t0 = time.perf_counter()
+        oracle.append(pool, c, st.indptr, st.positions, st.slots, st.k, st.v, wl.theta, lanes=lanes)
+        sample_rows = rows if rows is not None else np.concatenate(
+            [np.arange(st.indptr[l], st.indptr[l + 1]) for l in lanes]).astype(np.int64)
+        O, LSE, _ = oracle.attend(pool, st.indptr, st.positions, st.slots, st.kv_len, st.q, wl.H_q, wl.theta,
+                                  wl.sm_scale, wl.mask_bits, wl.mask_word_offset, rows=sample_rows)
+        oracle.fold(c, st.indptr, st.fold, wl.channel)
+        if rows is None:
+            rl = oracle.readout_rows(st.indptr, wl.readout_rows)
+            oracle.readout(np.zeros((st.num_rows, 1)), st.num_rows, rl)
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    eff = np.minimum(np.maximum(st.kv_len.astype(np.int64), 0), wl.capacity())
+    if unit == "GB/s":
+        work_units = float(sum(eff[l] * 2 * wl.H_kv * wl.d * 2 for l in lanes if n[l] * G <= 32))
+        val = work_units / dt / 1e9
+        what = f"{len(lanes)} lanes ({len(sample_rows)} rows), decode KV bytes {work_units:.3e}"
+    else:
+        pairs = attended_pairs(wl)[sample_rows]
+        work_units = 4.0 * wl.d * wl.H_q * float(pairs.sum())
+        val = work_units / dt / 1e12
+        what = f"{len(sample_rows)} sampled rows of {len(lanes)} lanes, {work_units:.3e} algorithmic flop"
+    return {"value": val, "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{what}; append+attend+fold+readout in {dt:.2f} s (fp64 numpy, one thread)"}
+
+
+# --------------------------------------------------------------------------- main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--split", type=int, default=None, help="decode KV slots per work item")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as W
+    from ragged_paged_kv_fp_amd import _lib, runner
+
+    _lib.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    cfg = args.config
+    wl = W.make_config(cfg, seed=args.seed, scale="full")
+    w = work(wl)
+    ds = runner.DeviceStep(wl, device="cuda", split=args.split)
+    ds.run_prefix()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = HipEvents()
+    K, Wm = args.steps, args.warmup
+    pairs_ev = [(ev.create(), ev.create()) for _ in range(K)]
+
+    for _ in range(Wm):
+        ds.reset()
+        ds.step()
+    torch.cuda.synchronize()
+    ds.status.zero_()
+
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(K):
+        ds.reset()
+        ds.step(events=pairs_ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    h1 = time.perf_counter()
+    total_ms = t_begin.elapsed_time(t_end)
+    attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs_ev]
+    status = int(ds.status.cpu()[0])
+    if status != 0:
+        print(f"warning: device status {status}", file=sys.stderr)
+
+    ms_step = total_ms / K
+    attn_avg = float(np.mean(attn_ms))
+    if cfg == 5:
+        unit, work_units, scale = "TFLOP/s", w["flops"], 1e12
+        bound, peak, r_unit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        unit, work_units, scale = "GB/s", w["kv_bytes_all"] if cfg == 1 else w["kv_bytes_decode"], 1e9
+        bound, peak, r_unit = "hbm", HBM_PEAK_GBS, "GB/s"
+        if cfg == 3:
+            work_units = w["kv_bytes_decode"]
+    value = work_units / (ms_step * 1e-3) / scale
+    achieved = work_units / (attn_avg * 1e-3) / scale
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"config {cfg}: " + WORKLOAD_TEXT[cfg], "seed": args.seed,
+                   "lanes": wl.num_lanes, "rows": wl.step.num_rows, "kv_bytes_decode": w["kv_bytes_decode"],
+                   "attn_flops": w["flops"], "attended_pairs": w["pairs"], "host_wall_ms_per_step":
+                   round((h1 - h0) * 1e3 / K, 4)},
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": r_unit,
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "attention kernels (decode_kernel / prefill_kernel), HIP events per step",
+                     "kernel_avg_ms": round(attn_avg, 5)},
+    }
+    if cfg == 3:
+        line["config"]["prefill_tflops_step"] = round(w["flops_prefill"] / (ms_step * 1e-3) / 1e12, 3)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, cfg, unit)
+    print(json.dumps(line), flush=True)
+    for a, b in pairs_ev:
+        ev.destroy(a)
+        ev.destroy(b)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

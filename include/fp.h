@@ -39,7 +39,8 @@
 extern "C" {
 #endif
 
-typedef struct ihipStream_t *hipStream_t;   /* same opaque type as HIP's */
+typedef struct ihipStream_t *hipStream_t;   /* same opaque types as HIP's */
+typedef struct ihipEvent_t *hipEvent_t;
 
 /* ---- return codes (host-detected, nothing enqueued) ---- */
 #define FP_OK               0
@@ -116,10 +117,17 @@ typedef struct fp_mask {
     const int64_t *word_offset_host;  /* [L+1] host copy: used to size launches only          */
 } fp_mask;
 
-/* Optional tuning; pass NULL for defaults. Results do not depend on it beyond fp rounding. */
+/*
+ * Optional tuning and profiling hooks for fp_attend; pass NULL for defaults.
+ * Results do not depend on it beyond fp rounding order.
+ */
 typedef struct fp_tuning {
     int32_t decode_split_slots;       /* KV slots per decode work item, multiple of 32 (0 = default) */
     int32_t reserved[7];              /* must be zero                                          */
+    hipEvent_t attn_begin;            /* nullable: recorded on the stream right before the
+                                         attention kernels (prefill and decode)              */
+    hipEvent_t attn_end;              /* nullable: recorded right after them (before the merge of
+                                         decode splits)                                       */
 } fp_tuning;
 
 /*

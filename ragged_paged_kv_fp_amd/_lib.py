@@ -54,7 +54,7 @@ class FpMask(ctypes.Structure):
 
 
 class FpTuning(ctypes.Structure):
-    _fields_ = [("decode_split_slots", c_i32), ("reserved", c_i32 * 7)]
+    _fields_ = [("decode_split_slots", c_i32), ("reserved", c_i32 * 7), ("attn_begin", c_ptr), ("attn_end", c_ptr)]
 
 
 class FpError(RuntimeError):

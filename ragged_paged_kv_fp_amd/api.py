@@ -103,11 +103,13 @@ class Mask:
         return FpMask(_ptr(self.bits), _ptr(self.word_offset), _hptr(self.word_offset_host))
 
 
-def _tuning(split: Optional[int]):
-    if split is None:
+def _tuning(split: Optional[int], events=None):
+    if split is None and events is None:
         return None
     t = FpTuning()
-    t.decode_split_slots = int(split)
+    t.decode_split_slots = int(split or 0)
+    if events is not None:
+        t.attn_begin, t.attn_end = int(events[0]), int(events[1])
     return ctypes.byref(t)
 
 
@@ -139,8 +141,11 @@ def attend_workspace_bytes(pool: Pool, geom: Geometry, num_q_heads: int, mask: O
 
 def attend(pool: Pool, geom: Geometry, q: torch.Tensor, num_q_heads: int, rope_theta: float, sm_scale: float,
            out: torch.Tensor, workspace: torch.Tensor, status: torch.Tensor, lse: Optional[torch.Tensor] = None,
-           mask: Optional[Mask] = None, split: Optional[int] = None, stream=None) -> None:
-    """fp_attend: attention of every row over its lane's kv_len slots (causal or bitmap)."""
+           mask: Optional[Mask] = None, split: Optional[int] = None, stream=None, events=None) -> None:
+    """fp_attend: attention of every row over its lane's kv_len slots (causal or bitmap).
+
+    events: optional (begin, end) raw hipEvent_t handles recorded around the attention kernels.
+    """
     lib = _lib.load()
     ps, gs = pool.struct(), geom.struct()
     ms = mask.struct() if mask is not None else None
@@ -148,7 +153,7 @@ def attend(pool: Pool, geom: Geometry, q: torch.Tensor, num_q_heads: int, rope_t
                                       float(rope_theta), float(sm_scale),
                                       ctypes.byref(ms) if ms is not None else None,
                                       _ptr(out), _ptr(lse), _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(), _tuning(split),
+                                      workspace.numel() * workspace.element_size(), _tuning(split, events),
                                       _ptr(status), _stream(stream)))
 
 

@@ -275,6 +275,7 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
         hipLaunchKernelGGL(summary_kernel, dim3((unsigned)p.n_pre), dim3(256), 0, stream, sa);
         if ((rc = launch_ok())) return rc;
     }
+    if (tuning && tuning->attn_begin && hipEventRecord(tuning->attn_begin, stream) != hipSuccess) return FP_ERR_HIP;
     if (p.n_pre) {
         if (p.D == 128) launch_prefill_g<128>(a, p.G, p.n_pre, stream);
         else launch_prefill_g<64>(a, p.G, p.n_pre, stream);
@@ -285,6 +286,7 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
         else hipLaunchKernelGGL(decode_kernel<64>, dim3((unsigned)p.n_dec), dim3(64), 0, stream, a);
         if ((rc = launch_ok())) return rc;
     }
+    if (tuning && tuning->attn_end && hipEventRecord(tuning->attn_end, stream) != hipSuccess) return FP_ERR_HIP;
     if (p.merge) {
         if (p.D == 128) hipLaunchKernelGGL(merge_kernel<128>, dim3(p.L, p.H), dim3(256), 0, stream, a);
         else hipLaunchKernelGGL(merge_kernel<64>, dim3(p.L, p.H), dim3(256), 0, stream, a);

@@ -95,10 +95,10 @@ class DeviceStep:
     def append(self, stream=None):
         api.append_kv(self.pool, self.geom, self.k, self.v, self.wl.theta, self.status, stream)
 
-    def attend(self, stream=None, split=None):
+    def attend(self, stream=None, split=None, events=None):
         wl = self.wl
         api.attend(self.pool, self.geom, self.q, wl.H_q, wl.theta, wl.sm_scale, self.out, self.workspace,
-                   self.status, self.lse, self.mask, self.split if split is None else split, stream)
+                   self.status, self.lse, self.mask, self.split if split is None else split, stream, events)
 
     def fold(self, stream=None):
         api.fold(self.pool, self.geom, self.status, self.channel, stream)
@@ -106,9 +106,9 @@ class DeviceStep:
     def readout(self, stream=None):
         api.readout(self.geom, self.out, self.dst, self.status, self.readout_rows, stream)
 
-    def step(self, stream=None) -> None:
+    def step(self, stream=None, events=None) -> None:
         self.append(stream)
-        self.attend(stream)
+        self.attend(stream, events=events)
         self.fold(stream)
         self.readout(stream)
 

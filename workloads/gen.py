@@ -42,10 +42,17 @@ _STREAMS = ("lengths", "perm", "prefix_kv", "q", "k", "v", "mask", "channel")
 
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
-    """Round finite float32 samples to bf16 (nearest-even); returns uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    """Round finite float32 samples to bf16 (nearest-even); returns uint16 bit patterns.
+
+    Finite floats stay below 0x7F800000 in magnitude bits, so the 32-bit sum
+    below cannot carry out of the word.
+    """
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= 16
+    return u.astype(np.uint16)
 
 
 def _normal_bf16(rng: np.random.Generator, shape, chunk_rows: int = 1 << 14) -> np.ndarray:
