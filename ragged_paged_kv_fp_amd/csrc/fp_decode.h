@@ -1,0 +1,449 @@
+// fp_decode.h - split-KV decode attention (lanes whose rows x GQA heads fit one MFMA N block).
+//
+// One workgroup of four waves per (lane, KV head, KV split). The waves take
+// every fourth 32-slot tile of the split; each keeps the next tile's K/V in a
+// second register set while it computes the current one, with the page ids
+// fetched one tile further ahead. At the end the waves combine through LDS,
+// and a lane read in several splits is combined by merge_kernel.
+//
+// Two MFMA shapes:
+//   NC = 16 : v_mfma_f32_16x16x32_bf16, up to 16 query row-heads per lane
+//   NC = 32 : v_mfma_f32_32x32x16_bf16, up to 32 (e.g. 8 draft rows x 4 heads)
+#pragma once
+
+#include <type_traits>
+
+#include "fp_kernels.h"
+
+namespace fpk {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kLdsRow = 68;  // padded row of 64 floats: rows land on different LDS banks
+
+template <int D>
+struct KvFrags {
+    uint4 k[D / 16];
+    uint4 v[D / 16];
+};
+
+struct TilePages {
+    int64_t k, v0, v1;
+};
+
+// Keep bf16 elements [0, nv) of an 8-element fragment (slots at or past kv_len
+// must not reach P*V, since 0 * NaN is NaN).
+__device__ __forceinline__ uint4 keep_first(uint4 v, int nv) {
+    if (nv >= 8) return v;
+    uint32_t mk[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mk[q] = (2 * q + 1 < nv) ? 0xFFFFFFFFu : ((2 * q < nv) ? 0x0000FFFFu : 0u);
+    return make_uint4(v.x & mk[0], v.y & mk[1], v.z & mk[2], v.w & mk[3]);
+}
+
+// Physical pages of the 8-slot groups this lane loads for the tile at j0.
+template <int NC>
+__device__ __forceinline__ TilePages tile_pages(const KvView &kv, int j0) {
+    const int l = lane_id();
+    int kg, vg0, vg1;
+    if (NC == 16) {
+        const int m = l & 15;
+        kg = j0 + 8 * (m >> 2);
+        vg0 = j0 + 8 * (l >> 4);
+        vg1 = vg0;
+    } else {
+        const int n = l & 31;
+        kg = j0 + 16 * (n >> 4) + 8 * ((n >> 2) & 1);
+        vg0 = j0 + 8 * (l >> 5);
+        vg1 = vg0 + 16;
+    }
+    TilePages tp;
+    tp.k = kg < kv.eff ? page_of(kv, kg / kv.P) : 0;
+    tp.v0 = vg0 < kv.eff ? page_of(kv, vg0 / kv.P) : 0;
+    tp.v1 = (NC == 32 && vg1 < kv.eff) ? page_of(kv, vg1 / kv.P) : 0;
+    return tp;
+}
+
+// K rows of the S^T = K * Q^T operand and V^T rows of the O^T = V^T * P^T operand.
+//  NC=16: lane (q = l/16, m = l%16). K row m of M-block b is slot 8(m/4) + 4b + m%4,
+//         d in [q D/4, (q+1) D/4); V^T row d = 16 db + m, slots 8q .. 8q+7.
+//         Then S^T register i of M-block b is slot 8q + 4b + i: exactly the
+//         k index 8q + 4b + i the P^T operand needs.
+//  NC=32: lane (h = l/32, n = l%32). K row n is slot kslot_of_row(n),
+//         d in [h D/2, (h+1) D/2); V^T row d = 32 db + n, slots 16 t + 8h .. +7.
+template <int D, int NC>
+__device__ __forceinline__ void tile_load(const KvView &kv, int j0, const TilePages &tp, KvFrags<D> &f) {
+    const int l = lane_id();
+    const int64_t vbase = kv.vblock + (int64_t)kv.g * D * kv.P;
+    if (NC == 16) {
+        constexpr int KS = D / 32;
+        const int m = l & 15, q = l >> 4;
+        const int kg = j0 + 8 * (m >> 2);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int ks = kg + 4 * b + (m & 3);
+            if (ks < kv.eff) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(
+                    kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (ks % kv.P)) * D + q * (D / 4));
+#pragma unroll
+                for (int s = 0; s < KS; ++s) f.k[b * KS + s] = src[s];
+            } else {
+#pragma unroll
+                for (int s = 0; s < KS; ++s) f.k[b * KS + s] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        const int vg = j0 + 8 * q;
+        if (vg < kv.eff) {
+            const uint16_t *vb = kv.kbase + tp.v0 * kv.page_elems + vbase + (vg % kv.P);
+            const int nv = kv.eff - vg;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db)
+                f.v[db] = keep_first(*reinterpret_cast<const uint4 *>(vb + (int64_t)(16 * db + m) * kv.P), nv);
+        } else {
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) f.v[db] = make_uint4(0, 0, 0, 0);
+        }
+    } else {
+        const int n = l & 31, h = l >> 5;
+        const int ks = j0 + kslot_of_row(n);
+        if (ks < kv.eff) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (ks % kv.P)) * D + h * (D / 2));
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) f.k[s] = src[s];
+        } else {
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) f.k[s] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            const int vs = j0 + 16 * t2 + 8 * h;
+            if (vs < kv.eff) {
+                const uint16_t *vb = kv.kbase + (t2 ? tp.v1 : tp.v0) * kv.page_elems + vbase + (vs % kv.P);
+                const int nv = kv.eff - vs;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    f.v[2 * db + t2] = keep_first(*reinterpret_cast<const uint4 *>(vb + (int64_t)(32 * db + n) * kv.P), nv);
+            } else {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) f.v[2 * db + t2] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int D, int NC>
+struct DecState {
+    static constexpr int QF = (NC == 16) ? D / 32 : D / 16;   // Q^T fragments per lane
+    static constexpr int OB = (NC == 16) ? D / 16 : D / 32;   // O^T accumulator blocks
+    using Acc = typename std::conditional<NC == 16, f32x4, f32x16>::type;
+    uint4 qf[QF];
+    Acc o[OB];
+    float m, l;
+};
+
+__device__ __forceinline__ void softmax_update(float mt, float &m_run, float &m_use, float &alpha) {
+    const float m_new = fmaxf(m_run, mt);
+    m_use = (m_new == kNegInf) ? 0.0f : m_new;
+    alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+}
+
+template <int D>
+__device__ __forceinline__ void tile_compute(const KvFrags<D> &f, int j0, int lim, uint32_t mw, bool masked,
+                                             DecState<D, 16> &w) {
+    constexpr int KS = D / 32;
+    const int q = lane_id() >> 4;
+    f32x4 s0 = {}, s1 = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        s0 = mfma16(f.k[s], w.qf[s], s0);
+        s1 = mfma16(f.k[KS + s], w.qf[s], s1);
+    }
+    float sv[8];
+    float mt = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int so = 8 * q + j;
+        bool ok = (j0 + so) < lim;
+        if (masked) ok = ok && ((mw >> so) & 1u);
+        sv[j] = ok ? (j < 4 ? s0[j] : s1[j - 4]) : kNegInf;
+        mt = fmaxf(mt, sv[j]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    float m_use, alpha;
+    softmax_update(mt, w.m, m_use, alpha);
+    float ps = 0.0f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[2 * j] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(sv[2 * j + 1] - m_use);
+        ps += p0 + p1;
+        pk[j] = pack_bf16x2(p0, p1);
+    }
+    w.l = w.l * alpha + ps;
+    const uint4 pb = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        w.o[db] *= alpha;
+        w.o[db] = mfma16(f.v[db], pb, w.o[db]);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_compute(const KvFrags<D> &f, int j0, int lim, uint32_t mw, bool masked,
+                                             DecState<D, 32> &w) {
+    const int h = lane_id() >> 5;
+    f32x16 sacc = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) sacc = mfma32(f.k[s], w.qf[s], sacc);
+    float sv[16];
+    float mt = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int so = 16 * (i >> 3) + 8 * h + (i & 7);
+        bool ok = (j0 + so) < lim;
+        if (masked) ok = ok && ((mw >> so) & 1u);
+        sv[i] = ok ? sacc[i] : kNegInf;
+        mt = fmaxf(mt, sv[i]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    float m_use, alpha;
+    softmax_update(mt, w.m, m_use, alpha);
+    float ps = 0.0f;
+    uint32_t pk[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[2 * q] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(sv[2 * q + 1] - m_use);
+        ps += p0 + p1;
+        pk[q] = pack_bf16x2(p0, p1);
+    }
+    w.l = w.l * alpha + ps;
+    const uint4 pb0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    const uint4 pb1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        w.o[db] *= alpha;
+        w.o[db] = mfma32(f.v[2 * db], pb0, w.o[db]);
+        w.o[db] = mfma32(f.v[2 * db + 1], pb1, w.o[db]);
+    }
+}
+
+// Write this wave's accumulator values whose d falls in [64c, 64c+64), scaled, into LDS row `col`.
+template <int D, int NC>
+__device__ __forceinline__ void stage_o(const DecState<D, NC> &w, int c, float scale, float *row) {
+    const int l = lane_id();
+    if (NC == 16) {
+        const int q = l >> 4;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            if (db / 4 != c) continue;
+            const float4 v = make_float4(w.o[db][0] * scale, w.o[db][1] * scale, w.o[db][2] * scale, w.o[db][3] * scale);
+            *reinterpret_cast<float4 *>(row + 16 * (db - 4 * c) + 4 * q) = v;
+        }
+    } else {
+        const int h = l >> 5;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            if (db / 2 != c) continue;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const float4 v = make_float4(w.o[db][4 * i4] * scale, w.o[db][4 * i4 + 1] * scale,
+                                             w.o[db][4 * i4 + 2] * scale, w.o[db][4 * i4 + 3] * scale);
+                *reinterpret_cast<float4 *>(row + 32 * (db - 2 * c) + 8 * i4 + 4 * h) = v;
+            }
+        }
+    }
+}
+
+template <int D, int NC>
+__global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(AttnArgs a) {
+    __shared__ float s_ml[kDecWaves][2][32];
+    __shared__ float s_fin[2][32];
+    __shared__ float s_o[kDecWaves][NC][kLdsRow];
+
+    const int item = blockIdx.x;
+    const int4 it = a.dec_items[item];
+    if (it.x < 0) return;
+    const int lane = it.x, g = it.y, s0 = it.z, s1 = it.w;
+    const LaneInfo li = a.lane_info[lane];
+    const int r0 = a.indptr[lane];
+    const int nrows = a.indptr[lane + 1] - r0;
+    const int ncols = nrows * a.G;
+    const int wv = threadIdx.x / kWave, l = lane_id();
+    const int col = (NC == 16) ? (l & 15) : (l & 31);
+    const int part = (NC == 16) ? (l >> 4) : (l >> 5);
+    const bool colv = col < ncols;
+    const int64_t row = r0 + (colv ? col / a.G : 0);
+    const int head = g * a.G + (colv ? col % a.G : 0);
+    int cap;
+    KvView kv = make_view(a, lane, g, &cap);
+    kv.vblock = (int64_t)a.H * a.P * D;
+
+    DecState<D, NC> w;
+    {
+        constexpr int QF = DecState<D, NC>::QF;
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.qrot + (row * a.Hq + head) * D + part * (D / (NC == 16 ? 4 : 2)));
+#pragma unroll
+        for (int s = 0; s < QF; ++s) w.qf[s] = colv ? src[s] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < DecState<D, NC>::OB; ++b) w.o[b] = typename DecState<D, NC>::Acc{};
+        w.m = kNegInf;
+        w.l = 0.0f;
+    }
+    const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
+    const uint32_t *mrow = nullptr;
+    int64_t wpr = 0;
+    if (masked) {
+        wpr = (a.mask_off[lane + 1] - a.mask_off[lane]) / nrows;
+        mrow = a.mask_bits + a.mask_off[lane] + (colv ? (col / a.G) : 0) * wpr;
+    }
+    const int lim = !colv ? 0 : (masked ? kv.eff : min(a.slots[row] + 1, kv.eff));
+    const int jend = min(s1, wave_max_i(lim));
+    constexpr int kStep = 32 * kDecWaves;
+
+    // ---- stream this wave's tiles: cur in fa, nxt in fb, page ids one tile further ahead
+    int cur = s0 + 32 * wv;
+    if (cur < jend) {
+        KvFrags<D> fa, fb;
+        TilePages pa = tile_pages<NC>(kv, cur), pb = pa;
+        tile_load<D, NC>(kv, cur, pa, fa);
+        int nxt = cur + kStep;
+        if (nxt < jend) pb = tile_pages<NC>(kv, nxt);
+        for (;;) {
+            if (nxt < jend) tile_load<D, NC>(kv, nxt, pb, fb);
+            const int n2 = nxt + kStep;
+            if (n2 < jend) pa = tile_pages<NC>(kv, n2);
+            uint32_t mw = (masked && colv && (cur >> 5) < wpr) ? mrow[cur >> 5] : 0u;
+            tile_compute<D>(fa, cur, lim, mw, masked, w);
+            if (nxt >= jend) break;
+            if (n2 < jend) tile_load<D, NC>(kv, n2, pa, fa);
+            const int n3 = n2 + kStep;
+            if (n3 < jend) pb = tile_pages<NC>(kv, n3);
+            mw = (masked && colv && (nxt >> 5) < wpr) ? mrow[nxt >> 5] : 0u;
+            tile_compute<D>(fb, nxt, lim, mw, masked, w);
+            if (n2 >= jend) break;
+            cur = n2;
+            nxt = n3;
+        }
+    }
+
+    // ---- combine the four waves through LDS
+    float lsum = w.l;
+    if (NC == 16) lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (part == 0) {
+        s_ml[wv][0][col] = w.m;
+        s_ml[wv][1][col] = lsum;
+    }
+    __syncthreads();
+    float M = kNegInf;
+#pragma unroll
+    for (int v = 0; v < kDecWaves; ++v) M = fmaxf(M, s_ml[v][0][col]);
+    const float scale = (M == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(w.m - M);
+    if (wv == 0 && part == 0) {
+        float L = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kDecWaves; ++v)
+            L += (M == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(s_ml[v][0][col] - M) * s_ml[v][1][col];
+        s_fin[0][col] = M;
+        s_fin[1][col] = L;
+    }
+    const bool single = li.nsplit <= 1;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+        stage_o<D, NC>(w, c, scale, &s_o[wv][col][0]);
+        __syncthreads();
+        for (int e = threadIdx.x; e < NC * 64; e += kDecThreads) {
+            const int n = e >> 6, dl = e & 63;
+            if (n >= ncols) continue;
+            float acc = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kDecWaves; ++v) acc += s_o[v][n][dl];
+            const float Lt = s_fin[1][n];
+            if (single) {
+                const int64_t orow = r0 + n / a.G;
+                const int ohead = g * a.G + n % a.G;
+                a.out[(orow * a.Hq + ohead) * D + 64 * c + dl] = Lt > 0.0f ? acc / Lt : 0.0f;
+                if (c == 0 && dl == 0 && a.lse)
+                    a.lse[orow * a.Hq + ohead] = Lt > 0.0f ? (s_fin[0][n] + __log2f(Lt)) * 0.69314718055994531f : kNegInf;
+            } else {
+                a.part_o[((int64_t)item * a.ncols_max + n) * D + 64 * c + dl] = acc;
+                if (c == 0 && dl == 0) {
+                    a.part_ml[(int64_t)item * 64 + n] = s_fin[0][n];
+                    a.part_ml[(int64_t)item * 64 + 32 + n] = Lt;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Combine the KV splits of one (decode lane, KV head, query column): block of
+// D threads, one output element each. Split statistics go through LDS so the
+// partial-output loads of all splits are issued back to back.
+constexpr int kMergeChunk = 256;
+
+template <int D>
+__global__ void __launch_bounds__(D) merge_kernel(AttnArgs a) {
+    __shared__ float s_w[kMergeChunk];
+    __shared__ float s_red[D / kWave];
+    __shared__ float s_stat[2];
+    const int lane = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
+    const LaneInfo li = a.lane_info[lane];
+    if (li.dec_off < 0 || li.nsplit <= 1) return;
+    const int r0 = a.indptr[lane];
+    const int ncols = (a.indptr[lane + 1] - r0) * a.G;
+    if (n >= ncols) return;
+    const int tid = threadIdx.x, dd = tid;
+    const int64_t first = (int64_t)li.dec_off + (int64_t)g * li.nsplit;
+    const int ns = li.nsplit;
+    // global max over splits
+    float mloc = kNegInf;
+    for (int s = tid; s < ns; s += D) mloc = fmaxf(mloc, a.part_ml[(first + s) * 64 + n]);
+    mloc = wave_max(mloc);
+    if (lane_id() == 0) s_red[tid / kWave] = mloc;
+    __syncthreads();
+    if (tid == 0) {
+        float M = kNegInf;
+        for (int v = 0; v < D / kWave; ++v) M = fmaxf(M, s_red[v]);
+        s_stat[0] = M;
+    }
+    __syncthreads();
+    const float M = s_stat[0];
+    float num = 0.0f, den = 0.0f;
+    for (int c0 = 0; c0 < ns; c0 += kMergeChunk) {
+        const int cn = min(kMergeChunk, ns - c0);
+        for (int s = tid; s < cn; s += D)
+            s_w[s] = (M == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(a.part_ml[(first + c0 + s) * 64 + n] - M);
+        __syncthreads();
+        for (int s = 0; s < cn; ++s) den += s_w[s] * a.part_ml[(first + c0 + s) * 64 + 32 + n];
+        const float *po = a.part_o + ((first + c0) * a.ncols_max + n) * D + dd;
+        const int64_t stride = (int64_t)a.ncols_max * D;
+        int s = 0;
+        for (; s + 8 <= cn; s += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = po[(s + u) * stride];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) num += s_w[s + u] * v[u];
+        }
+        for (; s < cn; ++s) num += s_w[s] * po[s * stride];
+        __syncthreads();
+    }
+    const int64_t orow = r0 + n / a.G;
+    const int ohead = g * a.G + n % a.G;
+    a.out[(orow * a.Hq + ohead) * D + dd] = den > 0.0f ? num / den : 0.0f;
+    if (dd == 0 && a.lse) a.lse[orow * a.Hq + ohead] = den > 0.0f ? (M + __log2f(den)) * 0.69314718055994531f : kNegInf;
+}
+
+}  // namespace fpk

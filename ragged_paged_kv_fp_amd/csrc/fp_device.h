@@ -31,12 +31,16 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
     return u >> 16;
 }
 
-// Rotation angle of RoPE pair i (dims 2i, 2i+1) at position pos:
-// pos * theta^(-2i/d), evaluated in fp64.
-__device__ __forceinline__ void rope_cos_sin(int pos, int i, int d, double theta, double *c, double *s) {
-    const double w = pow(theta, -2.0 * (double)i / (double)d);
-    const double ang = (double)pos * w;
-    sincos(ang, s, c);
+constexpr int kMaxPairs = 64;  // head_dim / 2 for head_dim <= 128
+
+// Frequencies of the RoPE pairs, w_i = theta^(-2i/d), filled on the host in fp64.
+struct RopeFreqs {
+    double w[kMaxPairs];
+};
+
+// cos and sin of the rotation angle pos * w_i of RoPE pair i, in fp64.
+__device__ __forceinline__ void rope_cos_sin(int pos, double w, double *c, double *s) {
+    sincos((double)pos * w, s, c);
 }
 
 // Largest lane l with indptr[l] <= row (rows of lane l are [indptr[l], indptr[l+1])).

@@ -36,8 +36,8 @@ struct AppendArgs {
     int64_t N;
     const int32_t *positions, *slots;
     const uint16_t *k, *v;
-    double theta;
     int32_t *status;
+    RopeFreqs freqs;
 };
 
 // One thread per (row, RoPE pair); loops over KV heads, which share the angle.
@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     }
     const int off = slot % a.P;
     double c, s;
-    rope_cos_sin(a.positions[row], i, a.D, a.theta, &c, &s);
+    rope_cos_sin(a.positions[row], a.freqs.w[i], &c, &s);
     uint16_t *kb = a.pool + page * a.page_elems;          // K block [H][P][D]
     uint16_t *vb = kb + (int64_t)a.H * a.P * a.D;        // V block [H][D][P]
     const uint32_t *kin = reinterpret_cast<const uint32_t *>(a.k + row * a.H * a.D) + i;
@@ -168,24 +168,31 @@ struct RopeQArgs {
     const int32_t *positions;
     int64_t N;
     int Hq, D;
-    double theta;
     double qscale;  // sm_scale * log2(e): scores come out in base-2 units
+    RopeFreqs freqs;
 };
 
-// One thread per (row, RoPE pair); rotated, prescaled Q in bf16, same layout as q.
+constexpr int kRopeHeadChunk = 8;  // query heads one thread rotates (they share the angle)
+
+// One thread per (row, RoPE pair, chunk of query heads); rotated, prescaled Q
+// in bf16, same [N][Hq][D] layout as q.
 __global__ void __launch_bounds__(256) rope_q_kernel(RopeQArgs a) {
     const int pairs = a.D >> 1;
+    const int chunks = (a.Hq + kRopeHeadChunk - 1) / kRopeHeadChunk;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t row = t / pairs;
-    const int i = (int)(t - row * pairs);
+    const int i = (int)(t % pairs);
+    const int64_t rc = t / pairs;
+    const int ch = (int)(rc % chunks);
+    const int64_t row = rc / chunks;
     if (row >= a.N) return;
     double c, s;
-    rope_cos_sin(a.positions[row], i, a.D, a.theta, &c, &s);
+    rope_cos_sin(a.positions[row], a.freqs.w[i], &c, &s);
     c *= a.qscale;
     s *= a.qscale;
     const uint32_t *qin = reinterpret_cast<const uint32_t *>(a.q + row * a.Hq * a.D) + i;
     uint32_t *qo = reinterpret_cast<uint32_t *>(a.qrot + row * a.Hq * a.D) + i;
-    for (int h = 0; h < a.Hq; ++h) {
+    const int h1 = min(a.Hq, (ch + 1) * kRopeHeadChunk);
+    for (int h = ch * kRopeHeadChunk; h < h1; ++h) {
         const uint32_t w = qin[h * pairs];
         double y0, y1;
         rotate_pair_f64((double)bf16_lo(w), (double)bf16_hi(w), c, s, &y0, &y1);
@@ -408,8 +415,8 @@ struct AttnArgs {
     float *out, *lse;                 // lse nullable
     const int4 *dec_items, *pre_items;
     const LaneInfo *lane_info;
-    float *part_o;                    // [items][ncols_max][D]
-    float *part_ml;                   // [items][2][32]
+    float *part_o;                    // [items][ncols_max][D] unnormalized split outputs
+    float *part_ml;                   // [items][2][32] split max (base 2) and sum
     int ncols_max;
     const uint32_t *summary;
 };
@@ -571,66 +578,6 @@ __device__ __forceinline__ KvView make_view(const AttnArgs &a, int lane, int g, 
     return kv;
 }
 
-// Decode: one wave per (lane, KV head, KV split); all rows x GQA heads of the
-// lane (<= 32) share every loaded K/V tile as the MFMA N dimension.
-template <int D>
-__global__ void __launch_bounds__(64) decode_kernel(AttnArgs a) {
-    const int item = blockIdx.x;
-    const int4 it = a.dec_items[item];
-    if (it.x < 0) return;
-    const int lane = it.x, g = it.y, s0 = it.z, s1 = it.w;
-    const LaneInfo li = a.lane_info[lane];
-    const int r0 = a.indptr[lane];
-    const int nrows = a.indptr[lane + 1] - r0;
-    const int ncols = nrows * a.G;
-    const int ln = lane_id(), n = ln & 31, h = ln >> 5;
-    const bool colv = n < ncols;
-    const int64_t row = r0 + (colv ? n / a.G : 0);
-    const int head = g * a.G + (colv ? n % a.G : 0);
-    int cap;
-    KvView kv = make_view(a, lane, g, &cap);
-    kv.vblock = (int64_t)a.H * a.P * D;
-    WaveState<D> w;
-    load_q<D>(a.qrot, row, head, a.Hq, colv, w);
-    const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
-    const uint32_t *mrow = nullptr;
-    int64_t wpr = 0;
-    if (masked) {
-        wpr = (a.mask_off[lane + 1] - a.mask_off[lane]) / nrows;
-        mrow = a.mask_bits + a.mask_off[lane] + (colv ? (n / a.G) : 0) * wpr;
-    }
-    const int lim = !colv ? 0 : (masked ? kv.eff : min(a.slots[row] + 1, kv.eff));
-    const int lmax = wave_max_i(lim);
-    const int jend = min(s1, lmax);
-    for (int j0 = s0; j0 < jend; j0 += 32) {
-        uint32_t mw = 0;
-        if (masked) {
-            const int64_t wi = j0 >> 5;
-            mw = (colv && wi < wpr) ? mrow[wi] : 0u;
-            if (__ballot(mw != 0u) == 0) continue;
-        }
-        attn_tile<D>(kv, j0, lim, mw, masked, w);
-    }
-    const float l_tot = w.l + __shfl_xor(w.l, 32);
-    if (li.nsplit <= 1) {
-        store_final<D>(w, l_tot, a.out + (row * a.Hq + head) * D, a.lse ? a.lse + row * a.Hq + head : nullptr, colv);
-        return;
-    }
-    if (colv) {
-        float *po = a.part_o + ((int64_t)item * a.ncols_max + n) * D;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-                *reinterpret_cast<float4 *>(po + 32 * db + 8 * i4 + 4 * h) =
-                    make_float4(w.o[db][4 * i4], w.o[db][4 * i4 + 1], w.o[db][4 * i4 + 2], w.o[db][4 * i4 + 3]);
-        if (h == 0) {
-            a.part_ml[(int64_t)item * 64 + n] = w.m;
-            a.part_ml[(int64_t)item * 64 + 32 + n] = l_tot;
-        }
-    }
-}
-
 // Prefill: one workgroup per (lane, KV head, 32-row block); wave w handles
 // query head g*G + w for the block's rows (32 MFMA columns).
 template <int D, int NW>
@@ -682,33 +629,6 @@ __global__ void __launch_bounds__(64 * NW) prefill_kernel(AttnArgs a) {
     store_final<D>(w, l_tot, a.out + (row * a.Hq + head) * D, a.lse ? a.lse + row * a.Hq + head : nullptr, colv);
 }
 
-// Combine the KV splits of a decode lane by their running max and sum (base 2).
-template <int D>
-__global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
-    const int lane = blockIdx.x, g = blockIdx.y;
-    const LaneInfo li = a.lane_info[lane];
-    if (li.dec_off < 0 || li.nsplit <= 1) return;
-    const int r0 = a.indptr[lane];
-    const int ncols = (a.indptr[lane + 1] - r0) * a.G;
-    const int64_t first = (int64_t)li.dec_off + (int64_t)g * li.nsplit;
-    for (int e = threadIdx.x; e < ncols * D; e += blockDim.x) {
-        const int n = e / D, dd = e - n * D;
-        float M = kNegInf;
-        for (int s = 0; s < li.nsplit; ++s) M = fmaxf(M, a.part_ml[(first + s) * 64 + n]);
-        float den = 0.0f, num = 0.0f;
-        if (M != kNegInf) {
-            for (int s = 0; s < li.nsplit; ++s) {
-                const float ms = a.part_ml[(first + s) * 64 + n];
-                const float wgt = __builtin_amdgcn_exp2f(ms - M);
-                den += wgt * a.part_ml[(first + s) * 64 + 32 + n];
-                num += wgt * a.part_o[((first + s) * a.ncols_max + n) * D + dd];
-            }
-        }
-        const int64_t row = r0 + n / a.G;
-        const int head = g * a.G + n % a.G;
-        a.out[(row * a.Hq + head) * D + dd] = den > 0.0f ? num / den : 0.0f;
-        if (dd == 0 && a.lse) a.lse[row * a.Hq + head] = den > 0.0f ? (M + __log2f(den)) * 0.69314718055994531f : kNegInf;
-    }
-}
-
 }  // namespace fpk
+
+#include "fp_decode.h"

@@ -7,6 +7,7 @@
 // counts, mask bits) are taken by the kernels.
 #include "fp_kernels.h"
 
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -14,7 +15,7 @@ namespace {
 
 using namespace fpk;
 
-constexpr int kDefaultSplit = 512;
+constexpr int kDefaultSplit = 1024;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -62,7 +63,8 @@ struct Plan {
     int L = 0, H = 0, G = 0, Hq = 0, D = 0, P = 0, split = 0, ncols_max = 1;
     int64_t N = 0, n_dec = 0, n_pre = 0, sum_words = 0;
     bool merge = false, summaries = false;
-    size_t off_lane = 0, off_dec = 0, off_pre = 0, off_qrot = 0, off_po = 0, off_pml = 0, off_sum = 0, total = 0;
+    size_t off_lane = 0, off_dec = 0, off_pre = 0, off_qrot = 0, off_po = 0, off_pml = 0, off_sum = 0;
+    size_t total = 0;
 };
 
 // Shape-only plan: mirrors lane_counts() of plan_kernel from the host copies.
@@ -128,6 +130,13 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
     return FP_OK;
 }
 
+// w_i = theta^(-2i/d) in fp64, the RoPE frequency of pair (2i, 2i+1).
+RopeFreqs rope_freqs(float theta, int d) {
+    RopeFreqs f;
+    for (int i = 0; i < kMaxPairs; ++i) f.w[i] = i < d / 2 ? pow((double)theta, -2.0 * (double)i / (double)d) : 0.0;
+    return f;
+}
+
 inline int launch_ok() { return hipGetLastError() == hipSuccess ? FP_OK : FP_ERR_HIP; }
 
 template <int D, int NW>
@@ -174,8 +183,8 @@ int fp_append_kv(const fp_kv_pool *pool, const fp_geometry *geom, const void *k,
     a.slots = geom->slots;
     a.k = static_cast<const uint16_t *>(k);
     a.v = static_cast<const uint16_t *>(v);
-    a.theta = (double)rope_theta;
     a.status = status;
+    a.freqs = rope_freqs(rope_theta, a.D);
     const int64_t threads = a.N * (a.D / 2);
     hipLaunchKernelGGL(append_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
     return launch_ok();
@@ -232,9 +241,9 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
     ra.N = p.N;
     ra.Hq = p.Hq;
     ra.D = p.D;
-    ra.theta = (double)rope_theta;
     ra.qscale = (double)sm_scale * 1.4426950408889634;  // log2(e)
-    const int64_t qthreads = p.N * (p.D / 2);
+    ra.freqs = rope_freqs(rope_theta, p.D);
+    const int64_t qthreads = p.N * (p.D / 2) * ((p.Hq + kRopeHeadChunk - 1) / kRopeHeadChunk);
     hipLaunchKernelGGL(rope_q_kernel, dim3((unsigned)((qthreads + 255) / 256)), dim3(256), 0, stream, ra);
     if ((rc = launch_ok())) return rc;
 
@@ -282,14 +291,21 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
         if ((rc = launch_ok())) return rc;
     }
     if (p.n_dec) {
-        if (p.D == 128) hipLaunchKernelGGL(decode_kernel<128>, dim3((unsigned)p.n_dec), dim3(64), 0, stream, a);
-        else hipLaunchKernelGGL(decode_kernel<64>, dim3((unsigned)p.n_dec), dim3(64), 0, stream, a);
+        const dim3 grid((unsigned)p.n_dec), block(kDecThreads);
+        if (p.D == 128) {
+            if (p.ncols_max <= 16) hipLaunchKernelGGL((decode_kernel<128, 16>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((decode_kernel<128, 32>), grid, block, 0, stream, a);
+        } else {
+            if (p.ncols_max <= 16) hipLaunchKernelGGL((decode_kernel<64, 16>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((decode_kernel<64, 32>), grid, block, 0, stream, a);
+        }
         if ((rc = launch_ok())) return rc;
     }
     if (tuning && tuning->attn_end && hipEventRecord(tuning->attn_end, stream) != hipSuccess) return FP_ERR_HIP;
     if (p.merge) {
-        if (p.D == 128) hipLaunchKernelGGL(merge_kernel<128>, dim3(p.L, p.H), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL(merge_kernel<64>, dim3(p.L, p.H), dim3(256), 0, stream, a);
+        const dim3 grid(p.L, p.H, p.ncols_max);
+        if (p.D == 128) hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, a);
+        else hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, a);
         if ((rc = launch_ok())) return rc;
     }
     return FP_OK;
