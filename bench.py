@@ -198,6 +198,8 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--split", type=int, default=None, help="decode KV slots per work item")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="first run 5 plain device copies of MIB MiB (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -212,6 +214,15 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.calib_copy:
+        nbytes = args.calib_copy << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": nbytes}), file=sys.stderr, flush=True)
+        del src, dst
     cfg = args.config
     wl = W.make_config(cfg, seed=args.seed, scale="full")
     w = work(wl)

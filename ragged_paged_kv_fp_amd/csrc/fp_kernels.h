@@ -205,7 +205,10 @@ __global__ void __launch_bounds__(256) rope_q_kernel(RopeQArgs a) {
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxLanes = 4096;
 constexpr int kDecodeCols = 32;  // query row-heads one decode wave holds (MFMA N)
-constexpr int kRowBlock = 32;    // rows per prefill work item
+constexpr int kPreCols = 256;    // query row-heads per prefill workgroup (8 waves x 32 columns)
+
+// Rows of one prefill work item: all GQA heads of those rows fill the workgroup.
+__host__ __device__ __forceinline__ int prefill_rows(int G) { return kPreCols / G; }
 
 struct PlanArgs {
     const int32_t *indptr, *page_indptr, *kv_len;
@@ -241,7 +244,7 @@ __device__ __forceinline__ LaneCounts lane_counts(const PlanArgs &a, int l, int3
         r.dec = a.H * r.nsplit;
         r.ncols = n * a.G;
     } else {
-        r.nrb = (n + kRowBlock - 1) / kRowBlock;
+        r.nrb = (n + prefill_rows(a.G) - 1) / prefill_rows(a.G);
         r.pre = a.H * r.nrb;
         if (masked) {
             const int tiles = (cap + 31) / 32;
@@ -342,8 +345,11 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
             const int n = a.indptr[l + 1] - a.indptr[l];
             // KV head fastest: consecutive items go to different XCDs, and the
             // row blocks of one (lane, KV head) land on the same XCD and L2.
-            const int rb = local / a.H, g = local - rb * a.H;
-            it = make_int4(l, g, rb * kRowBlock, min(kRowBlock, n - rb * kRowBlock));
+            // Last row blocks first: under the causal rule they read the most slots.
+            const int RB = prefill_rows(a.G);
+            const int nrb = (n + RB - 1) / RB;
+            const int rb = nrb - 1 - local / a.H, g = local % a.H;
+            it = make_int4(l, g, rb * RB, min(RB, n - rb * RB));
         }
         a.pre_items[idx] = it;
     }
@@ -357,12 +363,13 @@ struct SummaryArgs {
     const int32_t *indptr, *page_indptr, *kv_len;
     const uint32_t *bits;
     const int64_t *mask_off;
-    int P;
+    int P, G;
     uint32_t *summary;
 };
 
-// For each 32-row block of a masked prefill lane: which 32-slot KV tiles hold
-// any set bit (word run "any"), and which are fully set below kv_len ("all").
+// For each row block of a masked prefill lane (the rows of one prefill work
+// item): which 32-slot KV tiles hold any set bit (word run "any"), and which
+// are fully set below kv_len ("all").
 __global__ void __launch_bounds__(256) summary_kernel(SummaryArgs a) {
     const int4 it = a.pre_items[blockIdx.x];
     if (it.x < 0 || it.y != 0) return;
@@ -374,7 +381,7 @@ __global__ void __launch_bounds__(256) summary_kernel(SummaryArgs a) {
     const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
     const int eff = clamp_kv(a.kv_len[l], cap);
     const int rstart = it.z, nr = it.w;
-    const int64_t base = (int64_t)li.sum_off + (int64_t)(rstart / kRowBlock) * 2 * li.sum_wpb;
+    const int64_t base = (int64_t)li.sum_off + (int64_t)(rstart / prefill_rows(a.G)) * 2 * li.sum_wpb;
     const uint32_t *rb = a.bits + a.mask_off[l] + (int64_t)rstart * wpr;
     const int lane = lane_id();
     const int ntiles = li.sum_wpb * 32;
@@ -383,7 +390,18 @@ __global__ void __launch_bounds__(256) summary_kernel(SummaryArgs a) {
         const bool inr = (t < wpr) && (32 * t < eff);
         uint32_t any = 0, all = ~0u;
         if (inr) {
-            for (int r = 0; r < nr; ++r) {
+            int r = 0;
+            for (; r + 8 <= nr; r += 8) {
+                uint32_t w8[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) w8[u] = rb[(int64_t)(r + u) * wpr + t];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    any |= w8[u];
+                    all &= w8[u];
+                }
+            }
+            for (; r < nr; ++r) {
                 const uint32_t w = rb[(int64_t)r * wpr + t];
                 any |= w;
                 all &= w;
@@ -436,132 +454,6 @@ __device__ __forceinline__ int64_t page_of(const KvView &kv, int j) {
     return (int64_t)min(max(p, 0), kv.last_page);
 }
 
-template <int D>
-struct WaveState {
-    uint4 qf[D / 16];
-    f32x16 o[D / 32];
-    float m, l;
-};
-
-// One 32-slot KV tile for the wave's 32 query columns.
-//   S^T[slot][col] = K[slot] . Q[col]   (8 or 4 MFMAs, d split over the lane halves)
-//   online softmax per column (a column lives in lanes n and n+32)
-//   O^T[d][col] += V^T[d][slot] * P^T[slot][col]
-template <int D>
-__device__ __forceinline__ void attn_tile(const KvView &kv, int j0, int lim, uint32_t mword, bool masked,
-                                          WaveState<D> &w) {
-    constexpr int KS = D / 16, DB = D / 32;
-    const int ln = lane_id(), h = ln >> 5, n = ln & 31;
-    uint4 kf[KS];
-    const int ks = j0 + kslot_of_row(n);
-    if (ks < kv.eff) {
-        const int64_t page = page_of(kv, ks / kv.P);
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            kv.kbase + page * kv.page_elems + ((int64_t)kv.g * kv.P + (ks % kv.P)) * D + h * (D / 2));
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kf[s] = src[s];
-    } else {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kf[s] = make_uint4(0, 0, 0, 0);
-    }
-    uint4 vf[DB][2];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-        const int vs = j0 + 16 * t2 + 8 * h;
-        if (vs < kv.eff) {
-            const int64_t page = page_of(kv, vs / kv.P);
-            const uint16_t *vb = kv.kbase + page * kv.page_elems + kv.vblock + (int64_t)kv.g * D * kv.P + (vs % kv.P);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) vf[db][t2] = *reinterpret_cast<const uint4 *>(vb + (int64_t)(32 * db + n) * kv.P);
-            const int nv = kv.eff - vs;
-            if (nv < 8) {  // tail of the lane: slots at or past kv_len must not reach P*V (0*NaN)
-                uint32_t mk[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) mk[q] = (2 * q + 1 < nv) ? 0xFFFFFFFFu : ((2 * q < nv) ? 0x0000FFFFu : 0u);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    vf[db][t2].x &= mk[0]; vf[db][t2].y &= mk[1]; vf[db][t2].z &= mk[2]; vf[db][t2].w &= mk[3];
-                }
-            }
-        } else {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) vf[db][t2] = make_uint4(0, 0, 0, 0);
-        }
-    }
-    f32x16 sacc = {};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) sacc = mfma32(kf[s], w.qf[s], sacc);
-
-    float sv[16];
-    float mt = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int so = 16 * (i >> 3) + 8 * h + (i & 7);
-        bool ok = (j0 + so) < lim;
-        if (masked) ok = ok && ((mword >> so) & 1u);
-        sv[i] = ok ? sacc[i] : kNegInf;
-        mt = fmaxf(mt, sv[i]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(w.m, mt);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(w.m - m_use);
-    float ps = 0.0f;
-    uint32_t pk[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const float p0 = __builtin_amdgcn_exp2f(sv[2 * q] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(sv[2 * q + 1] - m_use);
-        ps += p0 + p1;
-        pk[q] = pack_bf16x2(p0, p1);
-    }
-    w.l = w.l * alpha + ps;
-    w.m = m_new;
-    const uint4 pb0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    const uint4 pb1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        w.o[db] *= alpha;
-        w.o[db] = mfma32(vf[db][0], pb0, w.o[db]);
-        w.o[db] = mfma32(vf[db][1], pb1, w.o[db]);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void load_q(const uint16_t *qrot, int64_t row, int head, int Hq, bool valid, WaveState<D> &w) {
-    constexpr int KS = D / 16;
-    const int h = lane_id() >> 5;
-    if (valid) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(qrot + (row * Hq + head) * D + h * (D / 2));
-#pragma unroll
-        for (int s = 0; s < KS; ++s) w.qf[s] = src[s];
-    } else {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) w.qf[s] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) w.o[db] = f32x16{};
-    w.m = kNegInf;
-    w.l = 0.0f;
-}
-
-// Normalized output for the wave's valid columns: O = acc / l, LSE = (m + log2 l) ln 2.
-template <int D>
-__device__ __forceinline__ void store_final(const WaveState<D> &w, float l_tot, float *out_row, float *lse_ptr, bool valid) {
-    const int h = lane_id() >> 5;
-    if (!valid) return;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            float4 v = make_float4(w.o[db][4 * i4] * inv, w.o[db][4 * i4 + 1] * inv, w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv);
-            *reinterpret_cast<float4 *>(out_row + 32 * db + 8 * i4 + 4 * h) = v;
-        }
-    }
-    if (lse_ptr && h == 0) *lse_ptr = l_tot > 0.0f ? (w.m + __log2f(l_tot)) * 0.69314718055994531f : kNegInf;
-}
-
 __device__ __forceinline__ KvView make_view(const AttnArgs &a, int lane, int g, int *cap_out) {
     KvView kv;
     const int p0 = a.page_indptr[lane];
@@ -578,57 +470,7 @@ __device__ __forceinline__ KvView make_view(const AttnArgs &a, int lane, int g, 
     return kv;
 }
 
-// Prefill: one workgroup per (lane, KV head, 32-row block); wave w handles
-// query head g*G + w for the block's rows (32 MFMA columns).
-template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW) prefill_kernel(AttnArgs a) {
-    const int4 it = a.pre_items[blockIdx.x];
-    if (it.x < 0) return;
-    const int lane = it.x, g = it.y, rstart = it.z, nr = it.w;
-    const int wv = threadIdx.x / kWave;
-    const int ln = lane_id(), n = ln & 31;
-    const bool colv = n < nr;
-    const int r0 = a.indptr[lane];
-    const int nrows = a.indptr[lane + 1] - r0;
-    const int64_t row = r0 + rstart + (colv ? n : 0);
-    const int head = g * a.G + wv;
-    int cap;
-    KvView kv = make_view(a, lane, g, &cap);
-    kv.vblock = (int64_t)a.H * a.P * D;
-    WaveState<D> w;
-    load_q<D>(a.qrot, row, head, a.Hq, colv, w);
-    const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
-    const uint32_t *mrow = nullptr;
-    int64_t wpr = 0;
-    if (masked) {
-        wpr = (a.mask_off[lane + 1] - a.mask_off[lane]) / nrows;
-        mrow = a.mask_bits + a.mask_off[lane] + (int64_t)(rstart + (colv ? n : 0)) * wpr;
-    }
-    const int lim = !colv ? 0 : (masked ? kv.eff : min(a.slots[row] + 1, kv.eff));
-    const int lmax = wave_max_i(lim);
-    if (!masked) {
-        for (int j0 = 0; j0 < lmax; j0 += 32) attn_tile<D>(kv, j0, lim, 0u, false, w);
-    } else {
-        const LaneInfo li = a.lane_info[lane];
-        const uint32_t *any = a.summary + li.sum_off + (int64_t)(rstart / kRowBlock) * 2 * li.sum_wpb;
-        const int ntile = (lmax + 31) >> 5;
-        for (int wi = 0; wi * 32 < ntile; ++wi) {
-            uint32_t bw = any[wi];
-            const int rem = ntile - wi * 32;
-            if (rem < 32) bw &= (1u << rem) - 1u;
-            while (bw) {
-                const int b = __builtin_ctz(bw);
-                bw &= bw - 1u;
-                const int t = 32 * wi + b;
-                const uint32_t mw = (colv && t < wpr) ? mrow[t] : 0u;
-                attn_tile<D>(kv, 32 * t, lim, mw, true, w);
-            }
-        }
-    }
-    const float l_tot = w.l + __shfl_xor(w.l, 32);
-    store_final<D>(w, l_tot, a.out + (row * a.Hq + head) * D, a.lse ? a.lse + row * a.Hq + head : nullptr, colv);
-}
-
 }  // namespace fpk
 
 #include "fp_decode.h"
+#include "fp_prefill.h"

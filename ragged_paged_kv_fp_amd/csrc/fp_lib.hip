@@ -107,7 +107,7 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
             if (nsplit > 1) p.merge = true;
             if (n * G > p.ncols_max) p.ncols_max = n * G;
         } else {
-            const int nrb = (n + kRowBlock - 1) / kRowBlock;
+            const int nrb = (n + prefill_rows(G) - 1) / prefill_rows(G);
             p.n_pre += (int64_t)p.H * nrb;
             if (masked) {
                 const int tiles = (cap + 31) / 32;
@@ -139,9 +139,9 @@ RopeFreqs rope_freqs(float theta, int d) {
 
 inline int launch_ok() { return hipGetLastError() == hipSuccess ? FP_OK : FP_ERR_HIP; }
 
-template <int D, int NW>
+template <int D, int G>
 void launch_prefill(const AttnArgs &a, int64_t n, hipStream_t s) {
-    hipLaunchKernelGGL((prefill_kernel<D, NW>), dim3((unsigned)n), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)n), dim3(kPreThreads), 0, s, a);
 }
 
 template <int D>
@@ -280,6 +280,7 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
         sa.bits = mask->bits;
         sa.mask_off = mask->word_offset;
         sa.P = p.P;
+        sa.G = p.G;
         sa.summary = reinterpret_cast<uint32_t *>(ws + p.off_sum);
         hipLaunchKernelGGL(summary_kernel, dim3((unsigned)p.n_pre), dim3(256), 0, stream, sa);
         if ((rc = launch_ok())) return rc;
