@@ -40,14 +40,15 @@ struct TilePages {
 // Keep bf16 elements [0, nv) of an 8-element fragment (slots at or past kv_len
 // must not reach P*V, since 0 * NaN is NaN).
 __device__ __forceinline__ uint4 keep_first(uint4 v, int nv) {
-    if (nv >= 8) return v;
     uint32_t mk[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) mk[q] = (2 * q + 1 < nv) ? 0xFFFFFFFFu : ((2 * q < nv) ? 0x0000FFFFu : 0u);
     return make_uint4(v.x & mk[0], v.y & mk[1], v.z & mk[2], v.w & mk[3]);
 }
 
-// Physical pages of the 8-slot groups this lane loads for the tile at j0.
+// Physical pages of the 8-slot groups this lane loads for the tile at j0
+// (slot groups at or past kv_len read the lane's first page instead: every
+// load stays branch-free and in bounds).
 template <int NC>
 __device__ __forceinline__ TilePages tile_pages(const KvView &kv, int j0) {
     const int l = lane_id();
@@ -64,9 +65,9 @@ __device__ __forceinline__ TilePages tile_pages(const KvView &kv, int j0) {
         vg1 = vg0 + 16;
     }
     TilePages tp;
-    tp.k = kg < kv.eff ? page_of(kv, kg / kv.P) : 0;
-    tp.v0 = vg0 < kv.eff ? page_of(kv, vg0 / kv.P) : 0;
-    tp.v1 = (NC == 32 && vg1 < kv.eff) ? page_of(kv, vg1 / kv.P) : 0;
+    tp.k = page_of(kv, (kg < kv.eff ? kg : 0) / kv.P);
+    tp.v0 = page_of(kv, (vg0 < kv.eff ? vg0 : 0) / kv.P);
+    tp.v1 = NC == 32 ? page_of(kv, (vg1 < kv.eff ? vg1 : 0) / kv.P) : tp.v0;
     return tp;
 }
 
@@ -81,6 +82,7 @@ template <int D, int NC>
 __device__ __forceinline__ void tile_load(const KvView &kv, int j0, const TilePages &tp, KvFrags<D> &f) {
     const int l = lane_id();
     const int64_t vbase = kv.vblock + (int64_t)kv.g * D * kv.P;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
     if (NC == 16) {
         constexpr int KS = D / 32;
         const int m = l & 15, q = l >> 4;
@@ -88,52 +90,44 @@ __device__ __forceinline__ void tile_load(const KvView &kv, int j0, const TilePa
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int ks = kg + 4 * b + (m & 3);
-            if (ks < kv.eff) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(
-                    kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (ks % kv.P)) * D + q * (D / 4));
+            const bool ok = ks < kv.eff;
+            const int kc = ok ? ks : 0;
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (kc % kv.P)) * D + q * (D / 4));
 #pragma unroll
-                for (int s = 0; s < KS; ++s) f.k[b * KS + s] = src[s];
-            } else {
-#pragma unroll
-                for (int s = 0; s < KS; ++s) f.k[b * KS + s] = make_uint4(0, 0, 0, 0);
+            for (int s = 0; s < KS; ++s) {
+                const uint4 v = src[s];
+                f.k[b * KS + s] = ok ? v : zero;
             }
         }
         const int vg = j0 + 8 * q;
-        if (vg < kv.eff) {
-            const uint16_t *vb = kv.kbase + tp.v0 * kv.page_elems + vbase + (vg % kv.P);
-            const int nv = kv.eff - vg;
+        const int vc = vg < kv.eff ? vg : 0;
+        const uint16_t *vb = kv.kbase + tp.v0 * kv.page_elems + vbase + (vc % kv.P);
+        const int nv = vg < kv.eff ? kv.eff - vg : 0;
 #pragma unroll
-            for (int db = 0; db < D / 16; ++db)
-                f.v[db] = keep_first(*reinterpret_cast<const uint4 *>(vb + (int64_t)(16 * db + m) * kv.P), nv);
-        } else {
-#pragma unroll
-            for (int db = 0; db < D / 16; ++db) f.v[db] = make_uint4(0, 0, 0, 0);
-        }
+        for (int db = 0; db < D / 16; ++db)
+            f.v[db] = keep_first(*reinterpret_cast<const uint4 *>(vb + (int64_t)(16 * db + m) * kv.P), nv);
     } else {
         const int n = l & 31, h = l >> 5;
         const int ks = j0 + kslot_of_row(n);
-        if (ks < kv.eff) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(
-                kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (ks % kv.P)) * D + h * (D / 2));
+        const bool ok = ks < kv.eff;
+        const int kc = ok ? ks : 0;
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (kc % kv.P)) * D + h * (D / 2));
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) f.k[s] = src[s];
-        } else {
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) f.k[s] = make_uint4(0, 0, 0, 0);
+        for (int s = 0; s < D / 16; ++s) {
+            const uint4 v = src[s];
+            f.k[s] = ok ? v : zero;
         }
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
             const int vs = j0 + 16 * t2 + 8 * h;
-            if (vs < kv.eff) {
-                const uint16_t *vb = kv.kbase + (t2 ? tp.v1 : tp.v0) * kv.page_elems + vbase + (vs % kv.P);
-                const int nv = kv.eff - vs;
+            const int vc = vs < kv.eff ? vs : 0;
+            const uint16_t *vb = kv.kbase + (t2 ? tp.v1 : tp.v0) * kv.page_elems + vbase + (vc % kv.P);
+            const int nv = vs < kv.eff ? kv.eff - vs : 0;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-                    f.v[2 * db + t2] = keep_first(*reinterpret_cast<const uint4 *>(vb + (int64_t)(32 * db + n) * kv.P), nv);
-            } else {
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) f.v[2 * db + t2] = make_uint4(0, 0, 0, 0);
-            }
+            for (int db = 0; db < D / 32; ++db)
+                f.v[2 * db + t2] = keep_first(*reinterpret_cast<const uint4 *>(vb + (int64_t)(32 * db + n) * kv.P), nv);
         }
     }
 }
@@ -308,32 +302,37 @@ __global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(A
         mrow = a.mask_bits + a.mask_off[lane] + (colv ? (col / a.G) : 0) * wpr;
     }
     const int lim = !colv ? 0 : (masked ? kv.eff : min(a.slots[row] + 1, kv.eff));
-    const int jend = min(s1, wave_max_i(lim));
-    constexpr int kStep = 32 * kDecWaves;
+    const int jend = __builtin_amdgcn_readfirstlane(min(s1, wave_max_i(lim)));
 
-    // ---- stream this wave's tiles: cur in fa, nxt in fb, page ids one tile further ahead
-    int cur = s0 + 32 * wv;
-    if (cur < jend) {
+    // ---- stream this wave's tiles (every kDecWaves-th of the split). While
+    // tile c is computed, tile c+S is in flight and the page ids of c+2S are
+    // being read; a tile index past the wave's range maps to the wave's last
+    // real tile (a cache hit), so every load is unconditional and the
+    // compiler's memory waits only cover the data actually needed.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // Q has landed before the pipeline starts
+    constexpr int kStep = 32 * kDecWaves;
+    const int first = s0 + 32 * wv;
+    if (first < jend) {  // wave-uniform
+        const int last = first + kStep * ((jend - 1 - first) / kStep);
+        auto clampt = [&](int t) { return t <= last ? t : last; };
+        int cur = first;
         KvFrags<D> fa, fb;
-        TilePages pa = tile_pages<NC>(kv, cur), pb = pa;
-        tile_load<D, NC>(kv, cur, pa, fa);
-        int nxt = cur + kStep;
-        if (nxt < jend) pb = tile_pages<NC>(kv, nxt);
+        TilePages pa = tile_pages<NC>(kv, clampt(cur));
+        TilePages pb = tile_pages<NC>(kv, clampt(cur + kStep));
+        tile_load<D, NC>(kv, clampt(cur), pa, fa);
+        pa = tile_pages<NC>(kv, clampt(cur + 2 * kStep));
         for (;;) {
-            if (nxt < jend) tile_load<D, NC>(kv, nxt, pb, fb);
-            const int n2 = nxt + kStep;
-            if (n2 < jend) pa = tile_pages<NC>(kv, n2);
+            tile_load<D, NC>(kv, clampt(cur + kStep), pb, fb);
+            pb = tile_pages<NC>(kv, clampt(cur + 3 * kStep));
             uint32_t mw = (masked && colv && (cur >> 5) < wpr) ? mrow[cur >> 5] : 0u;
             tile_compute<D>(fa, cur, lim, mw, masked, w);
-            if (nxt >= jend) break;
-            if (n2 < jend) tile_load<D, NC>(kv, n2, pa, fa);
-            const int n3 = n2 + kStep;
-            if (n3 < jend) pb = tile_pages<NC>(kv, n3);
-            mw = (masked && colv && (nxt >> 5) < wpr) ? mrow[nxt >> 5] : 0u;
-            tile_compute<D>(fb, nxt, lim, mw, masked, w);
-            if (n2 >= jend) break;
-            cur = n2;
-            nxt = n3;
+            if (cur + kStep > last) break;
+            tile_load<D, NC>(kv, clampt(cur + 2 * kStep), pa, fa);
+            pa = tile_pages<NC>(kv, clampt(cur + 4 * kStep));
+            mw = (masked && colv && ((cur + kStep) >> 5) < wpr) ? mrow[(cur + kStep) >> 5] : 0u;
+            tile_compute<D>(fb, cur + kStep, lim, mw, masked, w);
+            if (cur + 2 * kStep > last) break;
+            cur += 2 * kStep;
         }
     }
 

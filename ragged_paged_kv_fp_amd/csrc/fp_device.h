@@ -8,6 +8,7 @@
 namespace fpk {
 
 constexpr int kWave = 64;
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt encoding: vmcnt(0), other counters unconstrained
 constexpr float kNegInf = -__builtin_inff();
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;

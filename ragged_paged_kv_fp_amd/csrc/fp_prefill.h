@@ -21,8 +21,7 @@ namespace fpk {
 constexpr int kPreWaves = 8;
 constexpr int kPreThreads = 64 * kPreWaves;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p stays below 2^8 between rescales
-constexpr int kPreSumWords = 1024;
-constexpr int kWaitVmcnt0 = 0x0F70;    // s_waitcnt encoding: vmcnt(0), other counters unconstrained     // summary words per kind staged in LDS: capacity <= 1M slots
+constexpr int kPreSumWords = 1024;     // summary words per kind staged in LDS: capacity <= 1M slots
 
 template <int D>
 struct PreLds {
