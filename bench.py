@@ -187,6 +187,90 @@ def cpu_baseline(wl, cfg: int, unit: str, budget_s: float = 20.0):
             "sample": f"{what}; append+attend+fold+readout in {dt:.2f} s (fp64 numpy, one thread)"}
 
 
+# --------------------------------------------------------------------------- measured traffic
+
+KERNEL_SOURCES = ("ragged_paged_kv_fp_amd/csrc/fp_lib.hip", "ragged_paged_kv_fp_amd/csrc/fp_kernels.h",
+                  "ragged_paged_kv_fp_amd/csrc/fp_decode.h", "ragged_paged_kv_fp_amd/csrc/fp_prefill.h",
+                  "ragged_paged_kv_fp_amd/csrc/fp_device.h", "include/fp.h")
+DOMINANT_KERNEL = {2: "decode_kernel", 3: "prefill_kernel", 4: "decode_kernel", 5: "prefill_kernel", 1: "prefill_kernel"}
+
+
+def source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(cfg: int) -> str:
+    return os.path.join(ROOT, "profiles", f"{DOMINANT_KERNEL[cfg]}_config{cfg}_hbm_traffic.txt")
+
+
+def pmc_summary(fetch_db: str, write_db: str, cfg: int, calib_bytes: int, out: str) -> dict:
+    """Per-launch HBM bytes of the dominant kernel from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs (KiB per dispatch), each scaled by what the same counter
+    reads for the plain device copy of calib_bytes run in the same process."""
+    import sqlite3
+
+    def per_kernel(db, counter):
+        c = sqlite3.connect(db)
+        rows = c.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                         (counter,)).fetchall()
+        return rows
+
+    kern = DOMINANT_KERNEL[cfg]
+    res = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        rows = per_kernel(db, counter)
+        copies = [v for n, v in rows if "copyBuffer" in n]
+        kvals = [v for n, v in rows if kern in n]
+        # the calibration copies are the largest copy dispatches of the run
+        copies = sorted(copies)[-5:]
+        calib_kib = float(np.median(copies))
+        scale = (calib_bytes / 1024.0) / calib_kib
+        res[counter] = dict(kernel_kib=float(np.mean(kvals)), launches=len(kvals), copy_kib=calib_kib, scale=scale)
+    traffic = sum(v["kernel_kib"] * v["scale"] * 1024.0 for v in res.values())
+    rec = {"kernel": kern, "config": cfg, "source_hash": source_hash(), "calib_copy_bytes": calib_bytes,
+           "counters": res, "traffic_bytes_per_launch": traffic,
+           "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d <dir> -o c -- python3 bench.py "
+                      f"--config {cfg} --no-cpu-baseline --steps 5 --warmup 1 --calib-copy {calib_bytes >> 20}"}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def trace_summary(db: str, command: str) -> str:
+    """Markdown table of per-kernel durations from a rocprofv3 --kernel-trace results db."""
+    import sqlite3
+
+    c = sqlite3.connect(db)
+    q = ("select name, count(*), avg(duration)/1000.0, min(duration)/1000.0, max(duration)/1000.0, "
+         "sum(duration)/1000.0 from kernels group by name order by sum(duration) desc")
+    lines = [f"Command: `{command}`", "",
+             "| kernel | calls | avg us | min us | max us | total us |", "|---|---|---|---|---|---|"]
+    for name, n, avg, mn, mx, tot in c.execute(q):
+        name = name.replace("|", "/")
+        lines.append(f"| `{name[:90]}` | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {tot:.1f} |")
+    return "\n".join(lines) + "\n"
+
+
+def measured_traffic(cfg: int):
+    """Committed counter-based traffic for this config, or None if absent or
+    taken on different kernel sources."""
+    path = traffic_file(cfg)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 # --------------------------------------------------------------------------- main
 
 def main(argv=None):
@@ -200,7 +284,19 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run 5 plain device copies of MIB MiB (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write the measured-traffic record for --config from two rocprofv3 --pmc result dbs")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("DB", "COMMAND"),
+                    help="print a markdown per-kernel summary of a rocprofv3 --kernel-trace results db")
     args = ap.parse_args(argv)
+    if args.trace_summary:
+        print(trace_summary(*args.trace_summary), end="")
+        return 0
+    if args.pmc_summary:
+        rec = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, (args.calib_copy or 1024) << 20,
+                          traffic_file(args.config))
+        print(json.dumps(rec))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         return 2
@@ -287,7 +383,7 @@ def main(argv=None):
                    "attn_flops": w["flops"], "attended_pairs": w["pairs"], "host_wall_ms_per_step":
                    round((h1 - h0) * 1e3 / K, 4)},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": r_unit,
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(cfg),
                      "kernel": "attention kernels (decode_kernel / prefill_kernel), HIP events per step",
                      "kernel_avg_ms": round(attn_avg, 5)},
     }
