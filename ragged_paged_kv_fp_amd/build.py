@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfp.so")
 SOURCES = [os.path.join(HERE, "csrc", "fp_lib.hip")]
-DEPS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("fp_kernels.h", "fp_device.h")] + [
+DEPS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("fp_kernels.h", "fp_device.h", "fp_decode.h", "fp_prefill.h")] + [
     os.path.join(ROOT, "include", "fp.h")]
 
 HIPCC_FLAGS = [

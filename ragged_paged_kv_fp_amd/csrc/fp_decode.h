@@ -65,9 +65,9 @@ __device__ __forceinline__ TilePages tile_pages(const KvView &kv, int j0) {
         vg1 = vg0 + 16;
     }
     TilePages tp;
-    tp.k = page_of(kv, (kg < kv.eff ? kg : 0) / kv.P);
-    tp.v0 = page_of(kv, (vg0 < kv.eff ? vg0 : 0) / kv.P);
-    tp.v1 = NC == 32 ? page_of(kv, (vg1 < kv.eff ? vg1 : 0) / kv.P) : tp.v0;
+    tp.k = page_of(kv, (kg < kv.eff ? kg : 0) >> kv.pshift);
+    tp.v0 = page_of(kv, (vg0 < kv.eff ? vg0 : 0) >> kv.pshift);
+    tp.v1 = NC == 32 ? page_of(kv, (vg1 < kv.eff ? vg1 : 0) >> kv.pshift) : tp.v0;
     return tp;
 }
 
@@ -93,7 +93,7 @@ __device__ __forceinline__ void tile_load(const KvView &kv, int j0, const TilePa
             const bool ok = ks < kv.eff;
             const int kc = ok ? ks : 0;
             const uint4 *src = reinterpret_cast<const uint4 *>(
-                kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (kc % kv.P)) * D + q * (D / 4));
+                kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (kc & kv.pmask)) * D + q * (D / 4));
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const uint4 v = src[s];
@@ -102,7 +102,7 @@ __device__ __forceinline__ void tile_load(const KvView &kv, int j0, const TilePa
         }
         const int vg = j0 + 8 * q;
         const int vc = vg < kv.eff ? vg : 0;
-        const uint16_t *vb = kv.kbase + tp.v0 * kv.page_elems + vbase + (vc % kv.P);
+        const uint16_t *vb = kv.kbase + tp.v0 * kv.page_elems + vbase + (vc & kv.pmask);
         const int nv = vg < kv.eff ? kv.eff - vg : 0;
 #pragma unroll
         for (int db = 0; db < D / 16; ++db)
@@ -113,7 +113,7 @@ __device__ __forceinline__ void tile_load(const KvView &kv, int j0, const TilePa
         const bool ok = ks < kv.eff;
         const int kc = ok ? ks : 0;
         const uint4 *src = reinterpret_cast<const uint4 *>(
-            kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (kc % kv.P)) * D + h * (D / 2));
+            kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (kc & kv.pmask)) * D + h * (D / 2));
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
             const uint4 v = src[s];
@@ -123,7 +123,7 @@ __device__ __forceinline__ void tile_load(const KvView &kv, int j0, const TilePa
         for (int t2 = 0; t2 < 2; ++t2) {
             const int vs = j0 + 16 * t2 + 8 * h;
             const int vc = vs < kv.eff ? vs : 0;
-            const uint16_t *vb = kv.kbase + (t2 ? tp.v1 : tp.v0) * kv.page_elems + vbase + (vc % kv.P);
+            const uint16_t *vb = kv.kbase + (t2 ? tp.v1 : tp.v0) * kv.page_elems + vbase + (vc & kv.pmask);
             const int nv = vs < kv.eff ? kv.eff - vs : 0;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)

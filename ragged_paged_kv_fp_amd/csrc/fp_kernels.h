@@ -445,7 +445,8 @@ struct KvView {
     const int32_t *pids;     // page_ids + page_indptr[lane]
     int64_t page_elems;
     int64_t vblock;          // element offset of the V block in a page
-    int P, g, H, eff, last_page;
+    int P, pshift, pmask;    // page size (a power of two), log2 and P - 1
+    int g, H, eff, last_page;
 };
 
 // Physical page of working-set page j; an id outside the pool reads the nearest valid page.
@@ -462,6 +463,8 @@ __device__ __forceinline__ KvView make_view(const AttnArgs &a, int lane, int g, 
     kv.pids = a.page_ids + p0;
     kv.page_elems = a.page_elems;
     kv.P = a.P;
+    kv.pshift = __builtin_ctz(a.P);
+    kv.pmask = a.P - 1;
     kv.g = g;
     kv.H = a.H;
     kv.eff = clamp_kv(a.kv_len[lane], cap);

@@ -30,11 +30,13 @@ struct PreLds {
     static constexpr int VROW = 32 * 2 + 16;      // padded V^T row (bytes)
     static constexpr int K_BYTES = 32 * KROW;
     static constexpr int V_BYTES = D * VROW;
-    static constexpr int STAGE = K_BYTES + V_BYTES;
+    static constexpr int MW_OFF = K_BYTES + V_BYTES;  // mask words of the block's rows (masked lanes)
+    static constexpr int STAGE = MW_OFF + 4 * 256;
 };
 
-// What this thread brings in for one tile: a 16-byte K chunk and V^T chunk for
-// the shared LDS stage and the mask word of its own query column.
+// What this thread brings in for one tile: a 16-byte K chunk and V^T chunk and
+// the mask word of its own query row, all for the shared LDS stage (the word
+// goes through LDS too, so no loaded value outlives its ring slot).
 template <int D>
 struct PreStage {
     uint4 k, v;
@@ -48,69 +50,90 @@ struct PrePages {
     int k, v;
 };
 
+// Per-thread constants of the tile copy. A tile is 32 slots and a page holds
+// P in {8, 16, 32} slots, so a tile starts on a page boundary and the chunk a
+// thread moves sits at the same offset inside the same page of every tile:
+// only the page id changes from tile to tile.
 template <int D>
-__device__ __forceinline__ void pre_pages(const KvView &kv, int t, PrePages &pp) {
+struct PreCopy {
+    const char *kp, *vp;  // chunk address inside physical page 0
+    uint32_t pbytes;      // bytes per physical page
+    int last_page;        // highest physical page id in the pool
+    int kpg, vpg;         // page of the chunk within the tile's pages
+    int tshift;           // log2(pages per tile)
+    int lastpg;           // last working-set page holding a slot below kv_len
+    int vslot;            // first tile slot of the V^T chunk
+    int k_lds, v_lds;     // LDS byte offsets of the chunk in a stage
+    int mw_lds;           // LDS byte offset of the row's mask word, or -1: another wave stores it
+};
+
+template <int D>
+__device__ __forceinline__ PreCopy<D> pre_copy(const KvView &kv, int rloc, bool mw_owner) {
     constexpr int KC = PreLds<D>::KC;
     const int tid = threadIdx.x;
-    t = t < 0 ? 0 : t;
-    const int j0 = 32 * t;
-    const int sk = j0 + (tid % (32 * KC)) / KC;
-    const int sv = j0 + 8 * (tid & 3);
-    pp.k = kv.pids[(sk < kv.eff ? sk : 0) / kv.P];
-    pp.v = kv.pids[(sv < kv.eff ? sv : 0) / kv.P];
+    PreCopy<D> c;
+    const int rk = (tid % (32 * KC)) / KC, ck = tid % KC;          // K: slot rk, 16-byte chunk ck
+    const int dv = (tid % (4 * D)) >> 2, cv = tid & 3;             // V^T: row dv, slots 8cv..8cv+7
+    const char *base = reinterpret_cast<const char *>(kv.kbase);
+    c.kp = base + 2 * (((int64_t)kv.g * kv.P + (rk & kv.pmask)) * D + 8 * ck);
+    c.vp = base + 2 * (kv.vblock + (int64_t)kv.g * D * kv.P + (int64_t)dv * kv.P + ((8 * cv) & kv.pmask));
+    c.pbytes = (uint32_t)(2 * kv.page_elems);
+    c.last_page = kv.last_page;
+    c.kpg = rk >> kv.pshift;
+    c.vpg = (8 * cv) >> kv.pshift;
+    c.tshift = 5 - kv.pshift;
+    c.lastpg = kv.eff > 0 ? (kv.eff - 1) >> kv.pshift : 0;
+    c.vslot = 8 * cv;
+    c.k_lds = rk * PreLds<D>::KROW + 16 * ck;
+    c.v_lds = PreLds<D>::K_BYTES + dv * PreLds<D>::VROW + 16 * cv;
+    c.mw_lds = mw_owner ? PreLds<D>::MW_OFF + 4 * rloc : -1;
+    return c;
 }
 
-// Every load here is unconditional (out-of-range slots read a valid address and
-// are zeroed afterwards; tiles past the sequence fetch tile 0 and are never
-// used), so the compiler can count outstanding loads exactly and wait for one
-// tile's data without draining the later prefetches.
 template <int D>
-__device__ __forceinline__ void pre_data(const KvView &kv, int t, const PrePages &pp, PreStage<D> &st,
-                                         const uint32_t *mrow, int64_t wpr) {
-    constexpr int KC = PreLds<D>::KC;
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void pre_pages(const KvView &kv, const PreCopy<D> &c, int t, PrePages &pp) {
+    const int base = (t < 0 ? 0 : t) << c.tshift;
+    pp.k = kv.pids[min(base + c.kpg, c.lastpg)];
+    pp.v = kv.pids[min(base + c.vpg, c.lastpg)];
+}
+
+// Every load here is unconditional and nothing is done to the loaded values
+// until they are stored to LDS a step later (tiles past the sequence fetch
+// tile 0 and are never used), so the compiler can count outstanding loads
+// exactly and wait for one tile's data without draining later prefetches.
+// K of slots at or past kv_len is never zeroed: those slots only occur in
+// tiles whose scores go through the per-slot select, which drops them.
+template <int D>
+__device__ __forceinline__ void pre_data(const PreCopy<D> &c, int t, const PrePages &pp, PreStage<D> &st,
+                                         const uint32_t *mrow, int wpr) {
     t = t < 0 ? 0 : t;
-    const int j0 = 32 * t;
     st.mw = mrow[t < wpr ? t : 0];  // mrow points at valid memory for every lane
-    {
-        const int s = j0 + (tid % (32 * KC)) / KC, c = tid % KC;
-        const bool ok = (tid < 32 * KC) && s < kv.eff;
-        const int sc = ok ? s : 0;
-        const int64_t page = (int64_t)min(max(pp.k, 0), kv.last_page);
-        const uint4 v = *reinterpret_cast<const uint4 *>(kv.kbase + page * kv.page_elems +
-                                                         ((int64_t)kv.g * kv.P + (sc % kv.P)) * D + 8 * c);
-        st.k = ok ? v : make_uint4(0, 0, 0, 0);
-    }
-    {
-        const int d = (tid % (4 * D)) >> 2, cc = tid & 3;
-        const int s8 = j0 + 8 * cc;
-        const bool ok = (tid < 4 * D) && s8 < kv.eff;
-        const int sc = ok ? s8 : 0;
-        const int64_t page = (int64_t)min(max(pp.v, 0), kv.last_page);
-        const uint16_t *src = kv.kbase + page * kv.page_elems + kv.vblock + (int64_t)kv.g * D * kv.P +
-                              (int64_t)d * kv.P + (sc % kv.P);
-        const uint4 v = *reinterpret_cast<const uint4 *>(src);
-        // slots at or past kv_len must not reach P*V (0 * NaN is NaN)
-        const int nv = ok ? kv.eff - s8 : 0;
-        uint32_t mk[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) mk[q] = (2 * q + 1 < nv) ? 0xFFFFFFFFu : ((2 * q < nv) ? 0x0000FFFFu : 0u);
-        st.v = make_uint4(v.x & mk[0], v.y & mk[1], v.z & mk[2], v.w & mk[3]);
-    }
+    const uint32_t pk = (uint32_t)min(max(pp.k, 0), c.last_page);
+    const uint32_t pv = (uint32_t)min(max(pp.v, 0), c.last_page);
+    st.k = *reinterpret_cast<const uint4 *>(c.kp + (uint64_t)pk * c.pbytes);
+    st.v = *reinterpret_cast<const uint4 *>(c.vp + (uint64_t)pv * c.pbytes);
 }
 
+// Stores tile t's chunks into an LDS stage. V^T entries of slots at or past
+// kv_len are zeroed here (p = 0 times a stale NaN would still be NaN); only
+// the tile that straddles kv_len pays for it.
 template <int D>
-__device__ __forceinline__ void pre_store(const PreStage<D> &st, char *stage) {
+__device__ __forceinline__ void pre_store(const PreCopy<D> &c, const PreStage<D> &st, char *stage, int t, int eff) {
     constexpr int KC = PreLds<D>::KC;
     const int tid = threadIdx.x;
-    if (tid < 32 * KC) {
-        const int s = tid / KC, c = tid % KC;
-        *reinterpret_cast<uint4 *>(stage + s * PreLds<D>::KROW + 16 * c) = st.k;
-    }
+    if (tid < 32 * KC) *reinterpret_cast<uint4 *>(stage + c.k_lds) = st.k;
     if (tid < D * 4) {
-        const int d = tid >> 2, cc = tid & 3;
-        *reinterpret_cast<uint4 *>(stage + PreLds<D>::K_BYTES + d * PreLds<D>::VROW + 16 * cc) = st.v;
+        uint4 v = st.v;
+        if (32 * t + 32 > eff) {  // workgroup-uniform
+            const int nv = eff - 32 * t - c.vslot;
+            v.x &= nv >= 2 ? 0xFFFFFFFFu : (nv >= 1 ? 0x0000FFFFu : 0u);
+            v.y &= nv >= 4 ? 0xFFFFFFFFu : (nv >= 3 ? 0x0000FFFFu : 0u);
+            v.z &= nv >= 6 ? 0xFFFFFFFFu : (nv >= 5 ? 0x0000FFFFu : 0u);
+            v.w &= nv >= 8 ? 0xFFFFFFFFu : (nv >= 7 ? 0x0000FFFFu : 0u);
+        }
+        *reinterpret_cast<uint4 *>(stage + c.v_lds) = v;
     }
+    if (c.mw_lds >= 0) *reinterpret_cast<uint32_t *>(stage + c.mw_lds) = st.mw;
 }
 
 template <int D>
@@ -136,10 +159,11 @@ __device__ __forceinline__ f32x16 pre_qk(const char *stage, const PreWave<D> &w)
 }
 
 // Softmax of one tile's scores (valid-slot bits per lane, or all valid) and
-// O^T += V^T * P^T from the staged tile.
+// O^T += V^T * P^T from the staged tile. The running max starts at -FLT_MAX,
+// not -inf, so p = exp2(s - m) needs no special case for a column that has
+// seen no valid slot yet (a masked score is -inf and gives p = 0).
 template <int D>
-__device__ __forceinline__ void pre_pv(const char *stage, const f32x16 &sacc, bool full, uint32_t vbits,
-                                       PreWave<D> &w) {
+__device__ __forceinline__ void pre_pv(const char *stage, f32x16 s, bool full, uint32_t vbits, PreWave<D> &w) {
     const int ln = lane_id(), h = ln >> 5, n = ln & 31;
     // V^T fragments do not depend on P: issue their reads before the softmax
     const char *vrow = stage + PreLds<D>::K_BYTES + n * PreLds<D>::VROW + 16 * h;
@@ -149,43 +173,40 @@ __device__ __forceinline__ void pre_pv(const char *stage, const f32x16 &sacc, bo
         vf[db][0] = *reinterpret_cast<const uint4 *>(vrow + 32 * db * PreLds<D>::VROW);
         vf[db][1] = *reinterpret_cast<const uint4 *>(vrow + 32 * db * PreLds<D>::VROW + 32);
     }
-    float sv[16];
-    float mt = kNegInf;
-    if (full) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sv[i] = sacc[i];
-            mt = fmaxf(mt, sv[i]);
-        }
-    } else {
+    if (!full) {
         const uint32_t vb = vbits >> (8 * h);  // register i holds tile slot 16(i/8) + 8h + i%8
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            sv[i] = ((vb >> (16 * (i >> 3) + (i & 7))) & 1u) ? sacc[i] : kNegInf;
-            mt = fmaxf(mt, sv[i]);
+            const int k = 16 * (i >> 3) + (i & 7);
+            const uint32_t keep = (uint32_t)((int32_t)(vb << (31 - k)) >> 31);  // all ones if allowed
+            s[i] = __uint_as_float((__float_as_uint(s[i]) & keep) | (0xFF800000u & ~keep));
         }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    float mt = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) mt = fmaxf(fmaxf(mt, s[i]), s[i + 1]);
+    {
+        // the two lane halves hold the two halves of the column's 32 slots
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const bool grow = mt > w.m + kRescaleSlack;
     if (__any(grow)) {
         const float m_new = grow ? mt : w.m;
-        const float alpha = (w.m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(w.m - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(w.m - m_new);
         w.l *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) w.o[db] *= alpha;
         w.m = m_new;
     }
-    const float m_use = (w.m == kNegInf) ? 0.0f : w.m;
-    float ps = 0.0f;
     uint32_t pk[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const float p0 = __builtin_amdgcn_exp2f(sv[2 * q] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(sv[2 * q + 1] - m_use);
-        ps += p0 + p1;
-        pk[q] = pack_bf16x2(p0, p1);
-    }
-    w.l += ps;
+    for (int q = 0; q < 8; ++q)
+        pk[q] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * q] - w.m), __builtin_amdgcn_exp2f(s[2 * q + 1] - w.m));
+    // the denominator sums the same bf16 weights the numerator uses
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[q]),
+                                                                     __builtin_bit_cast(bf16x2, 0x3F803F80u), w.l, false);
     const uint4 pb0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     const uint4 pb1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
 #pragma unroll
@@ -256,16 +277,16 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnArgs a) {
         for (int s = 0; s < D / 16; ++s) w.qf[s] = colv ? src[s] : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) w.o[db] = f32x16{};
-        w.m = kNegInf;
+        w.m = -__FLT_MAX__;
         w.l = 0.0f;
     }
     const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
     // Mask-word pointers are always valid so their loads need no branch: a
     // causal lane reads a harmless word of indptr and ignores it.
     const uint32_t *mrow = reinterpret_cast<const uint32_t *>(a.indptr);
-    int64_t wpr = 1;
+    int wpr = 1;
     if (masked) {
-        wpr = (a.mask_off[lane + 1] - a.mask_off[lane]) / nrows;
+        wpr = (int)((a.mask_off[lane + 1] - a.mask_off[lane]) / nrows);
         mrow = a.mask_bits + a.mask_off[lane] + (int64_t)(rstart + (colv ? rloc : 0)) * wpr;
     }
     const int lim = !colv ? 0 : (masked ? kv.eff : min(a.slots[row] + 1, kv.eff));
@@ -312,57 +333,60 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnArgs a) {
     int t2 = t1 >= 0 ? seq_next(seq, t1) : -1;
     int t3 = t2 >= 0 ? seq_next(seq, t2) : -1;
     int t4 = t3 >= 0 ? seq_next(seq, t3) : -1;
+    // one wave per row group (w % G == 0) stores the rows' mask words
+    const PreCopy<D> cp = pre_copy<D>(kv, rloc, masked && h == 0 && (wv % G) == 0);
+    const int eff = kv.eff;
     PreStage<D> ringA, ringB;
     PrePages pgA, pgB;
-    uint32_t mw0 = 0u, mw1 = 0u;
     if (t0 >= 0) {  // workgroup-uniform
-        pre_pages<D>(kv, t0, pgA);
-        pre_pages<D>(kv, t1, pgB);
-        pre_data<D>(kv, t0, pgA, ringA, mrow, wpr);
-        pre_data<D>(kv, t1, pgB, ringB, mrow, wpr);
-        pre_pages<D>(kv, t2, pgA);
-        pre_pages<D>(kv, t3, pgB);
-        pre_store<D>(ringA, s_tile[0]);
-        mw0 = ringA.mw;
-        pre_store<D>(ringB, s_tile[1]);
-        mw1 = ringB.mw;
-        pre_data<D>(kv, t2, pgA, ringA, mrow, wpr);
-        pre_data<D>(kv, t3, pgB, ringB, mrow, wpr);
-        pre_pages<D>(kv, t4, pgA);
+        pre_pages<D>(kv, cp, t0, pgA);
+        pre_pages<D>(kv, cp, t1, pgB);
+        pre_data<D>(cp, t0, pgA, ringA, mrow, wpr);
+        pre_data<D>(cp, t1, pgB, ringB, mrow, wpr);
+        pre_pages<D>(kv, cp, t2, pgA);
+        pre_pages<D>(kv, cp, t3, pgB);
+        pre_store<D>(cp, ringA, s_tile[0], t0, eff);
+        pre_store<D>(cp, ringB, s_tile[1], t1, eff);
+        pre_data<D>(cp, t2, pgA, ringA, mrow, wpr);
+        pre_data<D>(cp, t3, pgB, ringB, mrow, wpr);
+        pre_pages<D>(kv, cp, t4, pgA);
     }
     __syncthreads();
 
     auto active = [&](int t) { return t >= 0 && 32 * t < lmax_w; };
-    auto finish = [&](int t, const f32x16 &sacc, uint32_t mw, int stage) {
+    auto finish = [&](int t, const f32x16 &sacc, int stage) {
         const int j0 = 32 * t;
         const bool full = masked ? (((allw[t >> 5] >> (t & 31)) & 1u) && j0 + 32 <= kv.eff) : (j0 + 32 <= lmin_w);
-        pre_pv<D>(s_tile[stage], sacc, full, full ? 0u : tile_bits(j0, lim, masked, mw), w);
+        uint32_t bits = 0u;
+        if (!full) {
+            const uint32_t mw = masked ? *reinterpret_cast<const uint32_t *>(s_tile[stage] + PreLds<D>::MW_OFF + 4 * rloc) : 0u;
+            bits = tile_bits(j0, lim, masked, mw);
+        }
+        pre_pv<D>(s_tile[stage], sacc, full, bits, w);
     };
     f32x16 sA = {}, sB = {};
     if (active(t0)) sA = pre_qk<D>(s_tile[0], w);
     while (t0 >= 0) {
         const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
         if (active(t1)) sB = pre_qk<D>(s_tile[st1], w);
-        if (active(t0)) finish(t0, sA, mw0, st);
+        if (active(t0)) finish(t0, sA, st);
         // page ids first: the data loads below then wait only on page ids
         // read one step earlier, never on the newest loads
         const int t5 = t4 >= 0 ? seq_next(seq, t4) : -1;
-        pre_pages<D>(kv, t5, pgB);
-        pre_store<D>(ringA, s_tile[st2]);  // tile t2
-        const uint32_t mw2 = ringA.mw;
-        pre_data<D>(kv, t4, pgA, ringA, mrow, wpr);
+        pre_pages<D>(kv, cp, t5, pgB);
+        pre_store<D>(cp, ringA, s_tile[st2], t2, eff);
+        pre_data<D>(cp, t4, pgA, ringA, mrow, wpr);
         __syncthreads();
         st = st1;
         if (t1 < 0) break;
 
         const int su1 = st == 2 ? 0 : st + 1, su2 = su1 == 2 ? 0 : su1 + 1;
         if (active(t2)) sA = pre_qk<D>(s_tile[su1], w);
-        if (active(t1)) finish(t1, sB, mw1, st);
+        if (active(t1)) finish(t1, sB, st);
         const int t6 = t5 >= 0 ? seq_next(seq, t5) : -1;
-        pre_pages<D>(kv, t6, pgA);
-        pre_store<D>(ringB, s_tile[su2]);  // tile t3
-        const uint32_t mw3 = ringB.mw;
-        pre_data<D>(kv, t5, pgB, ringB, mrow, wpr);
+        pre_pages<D>(kv, cp, t6, pgA);
+        pre_store<D>(cp, ringB, s_tile[su2], t3, eff);
+        pre_data<D>(cp, t5, pgB, ringB, mrow, wpr);
         __syncthreads();
         st = su1;
         if (t2 < 0) break;
@@ -371,8 +395,6 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnArgs a) {
         t2 = t4;
         t3 = t5;
         t4 = t6;
-        mw0 = mw2;
-        mw1 = mw3;
     }
 
     if (!colv) return;
