@@ -37,49 +37,101 @@ struct AppendArgs {
     const int32_t *positions, *slots;
     const uint16_t *k, *v;
     int32_t *status;
+    int rows, chunks;  // rows per workgroup (<= kAppendRows), KV-head chunks per (row, pair)
     RopeFreqs freqs;
 };
 
-// One thread per (row, RoPE pair); loops over KV heads, which share the angle.
+constexpr int kAppendRows = 16;  // most consecutive rows one append workgroup writes
+
+// Rows per workgroup and head chunks per (row, RoPE pair) for the row-grouped
+// kernels: many rows share a workgroup when there are enough rows to fill the
+// chip, few rows get all their heads spread over the workgroup's threads.
+__host__ __forceinline__ void row_grouping(int64_t N, int pairs, int heads, int *rows, int *chunks) {
+    int r = 1;
+    while (r < kAppendRows && N / (2 * r) >= 1024) r *= 2;
+    int c = 256 / (r * pairs);
+    c = c < 1 ? 1 : (c > heads ? heads : c);
+    *rows = r;
+    *chunks = c;
+}
+
+// One workgroup per a.rows consecutive rows. The rows are validated once
+// (lane, slot, freeze, page); K is rotated by one thread per (row, RoPE pair,
+// head chunk) looping over the chunk's KV heads, which share the angle, each 4-byte pair store
+// coalescing with its neighbours in the K row; V goes through LDS one head at
+// a time so that consecutive threads store consecutive rows of one V^T row:
+// the rows of a prefill chunk sit in consecutive slots of a page, and their
+// 2-byte stores then merge into one contiguous segment per V^T row.
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+    __shared__ int64_t s_base[kAppendRows];  // element offset of the row's page, -1: row not written
+    __shared__ int s_off[kAppendRows];
+    __shared__ uint32_t s_vw[kAppendRows][kMaxPairs + 1];  // one head's V of the rows, padded rows
+    const int64_t r0 = (int64_t)blockIdx.x * a.rows;
+    const int nr = (int)(a.N - r0 < a.rows ? a.N - r0 : a.rows);
+    const int tid = threadIdx.x;
+    if (tid < kAppendRows) {
+        int64_t base = -1;
+        int off = 0;
+        if (tid < nr) {
+            const int64_t row = r0 + tid;
+            const int lane = find_lane(a.indptr, a.L, row);
+            const int slot = a.slots[row];
+            const int p0 = a.page_indptr[lane];
+            const int cap = (a.page_indptr[lane + 1] - p0) * a.P;
+            if (slot < 0 || slot >= cap) {
+                atomicOr(a.status, FP_ST_SLOT_RANGE);
+            } else if (slot < a.committed[lane]) {
+                atomicOr(a.status, FP_ST_FROZEN);
+            } else {
+                const int64_t page = a.page_ids[p0 + slot / a.P];
+                if (page < 0 || page >= a.num_pages) {
+                    atomicOr(a.status, FP_ST_PAGE_RANGE);
+                } else {
+                    base = page * a.page_elems;
+                    off = slot % a.P;
+                }
+            }
+        }
+        s_base[tid] = base;
+        s_off[tid] = off;
+    }
+    __syncthreads();
     const int pairs = a.D >> 1;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t row = t / pairs;
-    const int i = (int)(t - row * pairs);
-    if (row >= a.N) return;
-    const int lane = find_lane(a.indptr, a.L, row);
-    const int slot = a.slots[row];
-    const int p0 = a.page_indptr[lane];
-    const int cap = (a.page_indptr[lane + 1] - p0) * a.P;
-    if (slot < 0 || slot >= cap) {
-        if (i == 0) atomicOr(a.status, FP_ST_SLOT_RANGE);
-        return;
+    const int hpc = (a.H + a.chunks - 1) / a.chunks;
+    for (int idx = tid; idx < nr * a.chunks * pairs; idx += blockDim.x) {
+        const int rc = idx / pairs, i = idx - rc * pairs;
+        const int j = rc / a.chunks, h0 = (rc - j * a.chunks) * hpc, h1 = min(a.H, h0 + hpc);
+        const int64_t base = s_base[j];
+        if (base < 0) continue;
+        const int64_t row = r0 + j;
+        double c, s;
+        rope_cos_sin(a.positions[row], a.freqs.w[i], &c, &s);
+        uint32_t *kb = reinterpret_cast<uint32_t *>(a.pool + base + (int64_t)s_off[j] * a.D) + i;  // K block [H][P][D]
+        const uint32_t *kin = reinterpret_cast<const uint32_t *>(a.k + row * a.H * a.D) + i;
+#pragma unroll 4
+        for (int h = h0; h < h1; ++h) {
+            const uint32_t kw = kin[h * pairs];
+            double y0, y1;
+            rotate_pair_f64((double)bf16_lo(kw), (double)bf16_hi(kw), c, s, &y0, &y1);
+            kb[(int64_t)h * a.P * pairs] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+        }
     }
-    if (slot < a.committed[lane]) {
-        if (i == 0) atomicOr(a.status, FP_ST_FROZEN);
-        return;
-    }
-    const int64_t page = a.page_ids[p0 + slot / a.P];
-    if (page < 0 || page >= a.num_pages) {
-        if (i == 0) atomicOr(a.status, FP_ST_PAGE_RANGE);
-        return;
-    }
-    const int off = slot % a.P;
-    double c, s;
-    rope_cos_sin(a.positions[row], a.freqs.w[i], &c, &s);
-    uint16_t *kb = a.pool + page * a.page_elems;          // K block [H][P][D]
-    uint16_t *vb = kb + (int64_t)a.H * a.P * a.D;        // V block [H][D][P]
-    const uint32_t *kin = reinterpret_cast<const uint32_t *>(a.k + row * a.H * a.D) + i;
-    const uint32_t *vin = reinterpret_cast<const uint32_t *>(a.v + row * a.H * a.D) + i;
+    const int64_t vblock = (int64_t)a.H * a.P * a.D;  // V block [H][D][P] follows the K block
     for (int h = 0; h < a.H; ++h) {
-        const uint32_t kw = kin[h * pairs];
-        double y0, y1;
-        rotate_pair_f64((double)bf16_lo(kw), (double)bf16_hi(kw), c, s, &y0, &y1);
-        reinterpret_cast<uint32_t *>(kb + ((int64_t)h * a.P + off) * a.D)[i] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
-        const uint32_t vw = vin[h * pairs];
-        uint16_t *vh = vb + (int64_t)h * a.D * a.P;
-        vh[(2 * i) * a.P + off] = (uint16_t)(vw & 0xFFFFu);
-        vh[(2 * i + 1) * a.P + off] = (uint16_t)(vw >> 16);
+        for (int e = tid; e < nr * pairs; e += blockDim.x) {
+            const int j = e / pairs, i = e - j * pairs;
+            s_vw[j][i] = reinterpret_cast<const uint32_t *>(a.v + ((r0 + j) * a.H + h) * a.D)[i];
+        }
+        __syncthreads();
+        for (int e = tid; e < a.rows * a.D; e += blockDim.x) {
+            const int j = e % a.rows, d = e / a.rows;
+            const int64_t base = s_base[j];
+            if (j < nr && base >= 0) {
+                const uint32_t w = s_vw[j][d >> 1];
+                a.pool[base + vblock + ((int64_t)h * a.D + d) * a.P + s_off[j]] = (uint16_t)((d & 1) ? (w >> 16) : (w & 0xFFFFu));
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -169,34 +221,36 @@ struct RopeQArgs {
     int64_t N;
     int Hq, D;
     double qscale;  // sm_scale * log2(e): scores come out in base-2 units
+    int rows, chunks;  // rows per workgroup, query-head chunks per (row, pair)
     RopeFreqs freqs;
 };
 
-constexpr int kRopeHeadChunk = 8;  // query heads one thread rotates (they share the angle)
-
-// One thread per (row, RoPE pair, chunk of query heads); rotated, prescaled Q
-// in bf16, same [N][Hq][D] layout as q.
+// One workgroup per a.rows rows, one thread per (row, RoPE pair, head chunk)
+// looping over the chunk's query heads, which share the angle; the 4-byte pair
+// loads and stores of a wave cover whole Q rows. Output is the rotated,
+// prescaled Q in bf16, same [N][Hq][D] layout as q.
 __global__ void __launch_bounds__(256) rope_q_kernel(RopeQArgs a) {
+    const int64_t r0 = (int64_t)blockIdx.x * a.rows;
+    const int nr = (int)(a.N - r0 < a.rows ? a.N - r0 : a.rows);
     const int pairs = a.D >> 1;
-    const int chunks = (a.Hq + kRopeHeadChunk - 1) / kRopeHeadChunk;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int i = (int)(t % pairs);
-    const int64_t rc = t / pairs;
-    const int ch = (int)(rc % chunks);
-    const int64_t row = rc / chunks;
-    if (row >= a.N) return;
-    double c, s;
-    rope_cos_sin(a.positions[row], a.freqs.w[i], &c, &s);
-    c *= a.qscale;
-    s *= a.qscale;
-    const uint32_t *qin = reinterpret_cast<const uint32_t *>(a.q + row * a.Hq * a.D) + i;
-    uint32_t *qo = reinterpret_cast<uint32_t *>(a.qrot + row * a.Hq * a.D) + i;
-    const int h1 = min(a.Hq, (ch + 1) * kRopeHeadChunk);
-    for (int h = ch * kRopeHeadChunk; h < h1; ++h) {
-        const uint32_t w = qin[h * pairs];
-        double y0, y1;
-        rotate_pair_f64((double)bf16_lo(w), (double)bf16_hi(w), c, s, &y0, &y1);
-        qo[h * pairs] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+    const int hpc = (a.Hq + a.chunks - 1) / a.chunks;
+    for (int idx = threadIdx.x; idx < nr * a.chunks * pairs; idx += blockDim.x) {
+        const int rc = idx / pairs, i = idx - rc * pairs;
+        const int j = rc / a.chunks, h0 = (rc - j * a.chunks) * hpc, h1 = min(a.Hq, h0 + hpc);
+        const int64_t row = r0 + j;
+        double c, s;
+        rope_cos_sin(a.positions[row], a.freqs.w[i], &c, &s);
+        c *= a.qscale;
+        s *= a.qscale;
+        const uint32_t *qin = reinterpret_cast<const uint32_t *>(a.q + row * a.Hq * a.D) + i;
+        uint32_t *qo = reinterpret_cast<uint32_t *>(a.qrot + row * a.Hq * a.D) + i;
+#pragma unroll 8
+        for (int h = h0; h < h1; ++h) {
+            const uint32_t w = qin[h * pairs];
+            double y0, y1;
+            rotate_pair_f64((double)bf16_lo(w), (double)bf16_hi(w), c, s, &y0, &y1);
+            qo[h * pairs] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+        }
     }
 }
 

@@ -185,8 +185,8 @@ int fp_append_kv(const fp_kv_pool *pool, const fp_geometry *geom, const void *k,
     a.v = static_cast<const uint16_t *>(v);
     a.status = status;
     a.freqs = rope_freqs(rope_theta, a.D);
-    const int64_t threads = a.N * (a.D / 2);
-    hipLaunchKernelGGL(append_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+    row_grouping(a.N, a.D / 2, a.H, &a.rows, &a.chunks);
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)((a.N + a.rows - 1) / a.rows)), dim3(256), 0, stream, a);
     return launch_ok();
 }
 
@@ -243,8 +243,8 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
     ra.D = p.D;
     ra.qscale = (double)sm_scale * 1.4426950408889634;  // log2(e)
     ra.freqs = rope_freqs(rope_theta, p.D);
-    const int64_t qthreads = p.N * (p.D / 2) * ((p.Hq + kRopeHeadChunk - 1) / kRopeHeadChunk);
-    hipLaunchKernelGGL(rope_q_kernel, dim3((unsigned)((qthreads + 255) / 256)), dim3(256), 0, stream, ra);
+    row_grouping(p.N, p.D / 2, p.Hq, &ra.rows, &ra.chunks);
+    hipLaunchKernelGGL(rope_q_kernel, dim3((unsigned)((p.N + ra.rows - 1) / ra.rows)), dim3(256), 0, stream, ra);
     if ((rc = launch_ok())) return rc;
 
     AttnArgs a;

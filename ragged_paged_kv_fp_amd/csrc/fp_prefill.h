@@ -64,11 +64,13 @@ struct PreCopy {
     int lastpg;           // last working-set page holding a slot below kv_len
     int vslot;            // first tile slot of the V^T chunk
     int k_lds, v_lds;     // LDS byte offsets of the chunk in a stage
-    int mw_lds;           // LDS byte offset of the row's mask word, or -1: another wave stores it
+    int mw_lds;           // LDS byte offset of the row's mask word
+    int ts;               // the tile holding slot kv_len (its tail slots are not part of the sequence)
+    uint32_t vmk[4];      // V^T chunk mask for tile ts: the words of slots below kv_len
 };
 
 template <int D>
-__device__ __forceinline__ PreCopy<D> pre_copy(const KvView &kv, int rloc, bool mw_owner) {
+__device__ __forceinline__ PreCopy<D> pre_copy(const KvView &kv, int rloc) {
     constexpr int KC = PreLds<D>::KC;
     const int tid = threadIdx.x;
     PreCopy<D> c;
@@ -86,7 +88,11 @@ __device__ __forceinline__ PreCopy<D> pre_copy(const KvView &kv, int rloc, bool 
     c.vslot = 8 * cv;
     c.k_lds = rk * PreLds<D>::KROW + 16 * ck;
     c.v_lds = PreLds<D>::K_BYTES + dv * PreLds<D>::VROW + 16 * cv;
-    c.mw_lds = mw_owner ? PreLds<D>::MW_OFF + 4 * rloc : -1;
+    c.mw_lds = PreLds<D>::MW_OFF + 4 * rloc;
+    c.ts = kv.eff >> 5;
+    const int nv = (kv.eff & 31) - c.vslot;  // valid slots of the chunk in tile ts
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c.vmk[q] = nv >= 2 * q + 2 ? 0xFFFFFFFFu : (nv >= 2 * q + 1 ? 0x0000FFFFu : 0u);
     return c;
 }
 
@@ -115,25 +121,18 @@ __device__ __forceinline__ void pre_data(const PreCopy<D> &c, int t, const PrePa
 }
 
 // Stores tile t's chunks into an LDS stage. V^T entries of slots at or past
-// kv_len are zeroed here (p = 0 times a stale NaN would still be NaN); only
-// the tile that straddles kv_len pays for it.
+// kv_len are zeroed here (p = 0 times a stale NaN would still be NaN); only the
+// tile that straddles kv_len has such entries. Every thread stores: with fewer
+// chunks than threads (head_dim 64) two threads write the same bytes, and all
+// lanes of a row write the same mask word, so no store needs a branch.
 template <int D>
-__device__ __forceinline__ void pre_store(const PreCopy<D> &c, const PreStage<D> &st, char *stage, int t, int eff) {
-    constexpr int KC = PreLds<D>::KC;
-    const int tid = threadIdx.x;
-    if (tid < 32 * KC) *reinterpret_cast<uint4 *>(stage + c.k_lds) = st.k;
-    if (tid < D * 4) {
-        uint4 v = st.v;
-        if (32 * t + 32 > eff) {  // workgroup-uniform
-            const int nv = eff - 32 * t - c.vslot;
-            v.x &= nv >= 2 ? 0xFFFFFFFFu : (nv >= 1 ? 0x0000FFFFu : 0u);
-            v.y &= nv >= 4 ? 0xFFFFFFFFu : (nv >= 3 ? 0x0000FFFFu : 0u);
-            v.z &= nv >= 6 ? 0xFFFFFFFFu : (nv >= 5 ? 0x0000FFFFu : 0u);
-            v.w &= nv >= 8 ? 0xFFFFFFFFu : (nv >= 7 ? 0x0000FFFFu : 0u);
-        }
-        *reinterpret_cast<uint4 *>(stage + c.v_lds) = v;
-    }
-    if (c.mw_lds >= 0) *reinterpret_cast<uint32_t *>(stage + c.mw_lds) = st.mw;
+__device__ __forceinline__ void pre_store(const PreCopy<D> &c, const PreStage<D> &st, char *stage, int t) {
+    const uint32_t keep = (t < 0 ? 0 : t) == c.ts ? 0u : 0xFFFFFFFFu;  // workgroup-uniform
+    *reinterpret_cast<uint4 *>(stage + c.k_lds) = st.k;
+    *reinterpret_cast<uint4 *>(stage + c.v_lds) =
+        make_uint4(st.v.x & (c.vmk[0] | keep), st.v.y & (c.vmk[1] | keep), st.v.z & (c.vmk[2] | keep),
+                   st.v.w & (c.vmk[3] | keep));
+    *reinterpret_cast<uint32_t *>(stage + c.mw_lds) = st.mw;
 }
 
 template <int D>
@@ -158,21 +157,14 @@ __device__ __forceinline__ f32x16 pre_qk(const char *stage, const PreWave<D> &w)
     return acc;
 }
 
-// Softmax of one tile's scores (valid-slot bits per lane, or all valid) and
-// O^T += V^T * P^T from the staged tile. The running max starts at -FLT_MAX,
-// not -inf, so p = exp2(s - m) needs no special case for a column that has
-// seen no valid slot yet (a masked score is -inf and gives p = 0).
+// Softmax prologue of one tile: drop the slots a column may not see (unless
+// the whole tile is allowed), take the column max over both lane halves and
+// rescale O and l when it grew by more than 2^kRescaleSlack. The running max
+// starts at -FLT_MAX, not -inf, so p = exp2(s - m) needs no special case for a
+// column that has seen no valid slot yet (a dropped score is -inf, p = 0).
 template <int D>
-__device__ __forceinline__ void pre_pv(const char *stage, f32x16 s, bool full, uint32_t vbits, PreWave<D> &w) {
-    const int ln = lane_id(), h = ln >> 5, n = ln & 31;
-    // V^T fragments do not depend on P: issue their reads before the softmax
-    const char *vrow = stage + PreLds<D>::K_BYTES + n * PreLds<D>::VROW + 16 * h;
-    uint4 vf[D / 32][2];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        vf[db][0] = *reinterpret_cast<const uint4 *>(vrow + 32 * db * PreLds<D>::VROW);
-        vf[db][1] = *reinterpret_cast<const uint4 *>(vrow + 32 * db * PreLds<D>::VROW + 32);
-    }
+__device__ __forceinline__ void pre_prologue(f32x16 &s, bool full, uint32_t vbits, PreWave<D> &w) {
+    const int h = lane_id() >> 5;
     if (!full) {
         const uint32_t vb = vbits >> (8 * h);  // register i holds tile slot 16(i/8) + 8h + i%8
 #pragma unroll
@@ -199,20 +191,69 @@ __device__ __forceinline__ void pre_pv(const char *stage, f32x16 s, bool full, u
         for (int db = 0; db < D / 32; ++db) w.o[db] *= alpha;
         w.m = m_new;
     }
+}
+
+// Main block of one pipeline step, free of branches and cut into segments
+// the scheduler keeps in order (it reorders only inside one): after the K and
+// V^T fragment reads, each segment issues one MFMA of the next tile's QK^T
+// chain together with the exp2 / bf16 packing of two weights of the current
+// tile, so the VALU work runs while the dependent MFMA chain waits on itself;
+// the P*V MFMAs of the first weight half join the chain's later segments, and
+// the second half shares its segments with the tile copy (page ids, LDS store,
+// prefetch loads: copy(k) is called for k = 0, 1, 2). The denominator sums the
+// same bf16 weights the numerator uses.
+template <int D, class Copy>
+__device__ __forceinline__ void pre_main(const char *stc, const char *stn, const f32x16 &sc, f32x16 &sn,
+                                         PreWave<D> &w, Copy &&copy) {
+    constexpr int NQK = D / 16;          // QK^T MFMAs of the chain
+    constexpr int NDB = D / 32;          // 32-row blocks of O^T
+    constexpr int PPS = 8 / NQK;         // weight pairs packed per chain segment
+    static_assert(NQK >= 2 * NDB && 8 % NQK == 0, "segment plan");
+    const int ln = lane_id(), h = ln >> 5, n = ln & 31;
+    const char *krow = stn + kslot_of_row(n) * PreLds<D>::KROW + h * D;
+    const char *vrow = stc + PreLds<D>::K_BYTES + n * PreLds<D>::VROW + 16 * h;
+    uint4 kf[NQK], vf[NDB][2];
+#pragma unroll
+    for (int s = 0; s < NQK; ++s) kf[s] = *reinterpret_cast<const uint4 *>(krow + 16 * s);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        vf[db][0] = *reinterpret_cast<const uint4 *>(vrow + 32 * db * PreLds<D>::VROW);
+        vf[db][1] = *reinterpret_cast<const uint4 *>(vrow + 32 * db * PreLds<D>::VROW + 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t pk[8];
+    f32x16 acc = {};
+    uint4 pb0 = {};
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-        pk[q] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * q] - w.m), __builtin_amdgcn_exp2f(s[2 * q + 1] - w.m));
-    // the denominator sums the same bf16 weights the numerator uses
+    for (int s = 0; s < NQK; ++s) {
+        acc = mfma32(kf[s], w.qf[s], acc);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) w.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[q]),
-                                                                     __builtin_bit_cast(bf16x2, 0x3F803F80u), w.l, false);
-    const uint4 pb0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        for (int u = 0; u < PPS; ++u) {
+            const int q = s * PPS + u;
+            pk[q] = pack_bf16x2(__builtin_amdgcn_exp2f(sc[2 * q] - w.m), __builtin_amdgcn_exp2f(sc[2 * q + 1] - w.m));
+        }
+        if (s == NQK - NDB - 1) pb0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        if (s >= NQK - NDB) {
+            const int db = s - (NQK - NDB);
+            w.o[db] = mfma32(vf[db][0], pb0, w.o[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    sn = acc;
     const uint4 pb1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        w.o[db] = mfma32(vf[db][0], pb0, w.o[db]);
+    for (int db = 0; db < NDB; ++db) {
         w.o[db] = mfma32(vf[db][1], pb1, w.o[db]);
+#pragma unroll
+        for (int q = db * (8 / NDB); q < (db + 1) * (8 / NDB); ++q)
+            w.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[q]),
+                                                  __builtin_bit_cast(bf16x2, 0x3F803F80u), w.l, false);
+        if (db < 3) copy(db);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NDB < 3) {
+#pragma unroll
+        for (int k = NDB; k < 3; ++k) copy(k);
     }
 }
 
@@ -322,20 +363,20 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnArgs a) {
     const uint32_t *allw = s_sum[1];
 
     // Software pipeline over the tile sequence t0, t1, t2, ...: while the
-    // softmax and P*V of tile t0 run, the QK^T MFMAs of t1 are already issued
-    // (its K sits in the next LDS stage), t2 and t3 are in flight from HBM in
+    // softmax and P*V of tile t0 run, the QK^T MFMAs of t1 are issued (its K
+    // sits in the next LDS stage), t2 and t3 are in flight from HBM in
     // registers (ring), and the page ids of t4 are being read. Three LDS stages
     // rotate; the loop is unrolled twice so no register holding in-flight data
-    // is copied, and every global load in the loop is unconditional.
+    // is copied, and every global load in the loop is unconditional. Tiles
+    // past a wave's last row (the end of the causal diagonal) are computed like
+    // the others with every slot dropped, which keeps each step branch-free.
     int st = 0;
     int t0 = seq_next(seq, -1);
     int t1 = t0 >= 0 ? seq_next(seq, t0) : -1;
     int t2 = t1 >= 0 ? seq_next(seq, t1) : -1;
     int t3 = t2 >= 0 ? seq_next(seq, t2) : -1;
     int t4 = t3 >= 0 ? seq_next(seq, t3) : -1;
-    // one wave per row group (w % G == 0) stores the rows' mask words
-    const PreCopy<D> cp = pre_copy<D>(kv, rloc, masked && h == 0 && (wv % G) == 0);
-    const int eff = kv.eff;
+    const PreCopy<D> cp = pre_copy<D>(kv, rloc);
     PreStage<D> ringA, ringB;
     PrePages pgA, pgB;
     if (t0 >= 0) {  // workgroup-uniform
@@ -345,48 +386,48 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnArgs a) {
         pre_data<D>(cp, t1, pgB, ringB, mrow, wpr);
         pre_pages<D>(kv, cp, t2, pgA);
         pre_pages<D>(kv, cp, t3, pgB);
-        pre_store<D>(cp, ringA, s_tile[0], t0, eff);
-        pre_store<D>(cp, ringB, s_tile[1], t1, eff);
+        pre_store<D>(cp, ringA, s_tile[0], t0);
+        pre_store<D>(cp, ringB, s_tile[1], t1);
         pre_data<D>(cp, t2, pgA, ringA, mrow, wpr);
         pre_data<D>(cp, t3, pgB, ringB, mrow, wpr);
         pre_pages<D>(kv, cp, t4, pgA);
     }
     __syncthreads();
 
-    auto active = [&](int t) { return t >= 0 && 32 * t < lmax_w; };
-    auto finish = [&](int t, const f32x16 &sacc, int stage) {
+    auto prologue = [&](int t, f32x16 &sacc, int stage) {
         const int j0 = 32 * t;
         const bool full = masked ? (((allw[t >> 5] >> (t & 31)) & 1u) && j0 + 32 <= kv.eff) : (j0 + 32 <= lmin_w);
         uint32_t bits = 0u;
         if (!full) {
-            const uint32_t mw = masked ? *reinterpret_cast<const uint32_t *>(s_tile[stage] + PreLds<D>::MW_OFF + 4 * rloc) : 0u;
+            const uint32_t mw = *reinterpret_cast<const uint32_t *>(s_tile[stage] + PreLds<D>::MW_OFF + 4 * rloc);
             bits = tile_bits(j0, lim, masked, mw);
         }
-        pre_pv<D>(s_tile[stage], sacc, full, bits, w);
+        pre_prologue<D>(sacc, full, bits, w);
     };
-    f32x16 sA = {}, sB = {};
-    if (active(t0)) sA = pre_qk<D>(s_tile[0], w);
+    f32x16 sA = pre_qk<D>(s_tile[0], w), sB = {};
     while (t0 >= 0) {
         const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
-        if (active(t1)) sB = pre_qk<D>(s_tile[st1], w);
-        if (active(t0)) finish(t0, sA, st);
-        // page ids first: the data loads below then wait only on page ids
-        // read one step earlier, never on the newest loads
         const int t5 = t4 >= 0 ? seq_next(seq, t4) : -1;
-        pre_pages<D>(kv, cp, t5, pgB);
-        pre_store<D>(cp, ringA, s_tile[st2], t2, eff);
-        pre_data<D>(cp, t4, pgA, ringA, mrow, wpr);
+        prologue(t0, sA, st);
+        // page ids first: the data loads then wait only on page ids read one
+        // step earlier, never on the newest loads
+        pre_main<D>(s_tile[st], s_tile[st1], sA, sB, w, [&](int k) {
+            if (k == 0) pre_pages<D>(kv, cp, t5, pgB);
+            if (k == 1) pre_store<D>(cp, ringA, s_tile[st2], t2);
+            if (k == 2) pre_data<D>(cp, t4, pgA, ringA, mrow, wpr);
+        });
         __syncthreads();
         st = st1;
         if (t1 < 0) break;
 
         const int su1 = st == 2 ? 0 : st + 1, su2 = su1 == 2 ? 0 : su1 + 1;
-        if (active(t2)) sA = pre_qk<D>(s_tile[su1], w);
-        if (active(t1)) finish(t1, sB, st);
         const int t6 = t5 >= 0 ? seq_next(seq, t5) : -1;
-        pre_pages<D>(kv, cp, t6, pgA);
-        pre_store<D>(cp, ringB, s_tile[su2], t3, eff);
-        pre_data<D>(cp, t5, pgB, ringB, mrow, wpr);
+        prologue(t1, sB, st);
+        pre_main<D>(s_tile[st], s_tile[su1], sB, sA, w, [&](int k) {
+            if (k == 0) pre_pages<D>(kv, cp, t6, pgA);
+            if (k == 1) pre_store<D>(cp, ringB, s_tile[su2], t3);
+            if (k == 2) pre_data<D>(cp, t5, pgB, ringB, mrow, wpr);
+        });
         __syncthreads();
         st = su1;
         if (t2 < 0) break;
