@@ -14,8 +14,8 @@ namespace fpk {
 struct LaneInfo {
     int dec_off;   // first decode work item of the lane, -1 if the lane is not a decode lane
     int nsplit;    // decode KV splits of the lane (items per KV head)
-    int sum_off;   // first mask-summary word of the lane, -1 if none
-    int sum_wpb;   // summary words per 32-row block (per bitmap kind)
+    int sum_off;     // first word of the lane's tile lists, -1 if the lane has none
+    int sum_stride;  // words per row-block tile list: a count, then one entry per KV tile
 };
 
 // ============================================================================ append
@@ -278,7 +278,7 @@ struct PlanArgs {
 };
 
 struct LaneCounts {
-    int dec, pre, sum, nsplit, nrb, wpb, ncols;
+    int dec, pre, sum, nsplit, nrb, stride, ncols;
 };
 
 __device__ __forceinline__ LaneCounts lane_counts(const PlanArgs &a, int l, int32_t *st) {
@@ -301,9 +301,8 @@ __device__ __forceinline__ LaneCounts lane_counts(const PlanArgs &a, int l, int3
         r.nrb = (n + prefill_rows(a.G) - 1) / prefill_rows(a.G);
         r.pre = a.H * r.nrb;
         if (masked) {
-            const int tiles = (cap + 31) / 32;
-            r.wpb = (tiles + 31) / 32;
-            r.sum = r.nrb * 2 * r.wpb;
+            r.stride = (cap + 31) / 32 + 1;
+            r.sum = r.nrb * r.stride;
         }
     }
     return r;
@@ -359,7 +358,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
         li.dec_off = c.dec ? od : -1;
         li.nsplit = c.nsplit;
         li.sum_off = c.sum ? os : -1;
-        li.sum_wpb = c.wpb;
+        li.sum_stride = c.stride;
         a.lane_info[l] = li;
         od += c.dec; op += c.pre; os += c.sum;
     }
@@ -418,13 +417,19 @@ struct SummaryArgs {
     const uint32_t *bits;
     const int64_t *mask_off;
     int P, G;
-    uint32_t *summary;
+    int32_t *summary;
 };
 
-// For each row block of a masked prefill lane (the rows of one prefill work
-// item): which 32-slot KV tiles hold any set bit (word run "any"), and which
-// are fully set below kv_len ("all").
-__global__ void __launch_bounds__(256) summary_kernel(SummaryArgs a) {
+// Tile list of one row block of a masked prefill lane (the rows of one prefill
+// work item): the 32-slot KV tiles below kv_len in which some row of the block
+// has an allowed slot, in increasing order, each entry tagged in bit 31 when
+// every row of the block may read every slot of the tile. Record layout:
+// [count, entry 0, entry 1, ...]. The prefill kernel walks this list, so
+// tiles with no allowed slot are never loaded.
+constexpr int kSumThreads = 256;
+
+__global__ void __launch_bounds__(kSumThreads) summary_kernel(SummaryArgs a) {
+    __shared__ int s_wc[kSumThreads / kWave];
     const int4 it = a.pre_items[blockIdx.x];
     if (it.x < 0 || it.y != 0) return;
     const int l = it.x;
@@ -435,13 +440,15 @@ __global__ void __launch_bounds__(256) summary_kernel(SummaryArgs a) {
     const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
     const int eff = clamp_kv(a.kv_len[l], cap);
     const int rstart = it.z, nr = it.w;
-    const int64_t base = (int64_t)li.sum_off + (int64_t)(rstart / prefill_rows(a.G)) * 2 * li.sum_wpb;
+    int32_t *rec = a.summary + li.sum_off + (int64_t)(rstart / prefill_rows(a.G)) * li.sum_stride;
     const uint32_t *rb = a.bits + a.mask_off[l] + (int64_t)rstart * wpr;
-    const int lane = lane_id();
-    const int ntiles = li.sum_wpb * 32;
-    for (int t0 = (int)(threadIdx.x & ~(kWave - 1)); t0 < ntiles; t0 += blockDim.x) {
-        const int t = t0 + lane;
-        const bool inr = (t < wpr) && (32 * t < eff);
+    // tiles holding slots below kv_len whose mask word exists (a short row reads 0 beyond its words)
+    const int ntiles = (int)min((int64_t)((eff + 31) >> 5), wpr);
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    int running = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += kSumThreads) {
+        const int t = t0 + (int)threadIdx.x;
+        const bool inr = t < ntiles;
         uint32_t any = 0, all = ~0u;
         if (inr) {
             int r = 0;
@@ -464,13 +471,20 @@ __global__ void __launch_bounds__(256) summary_kernel(SummaryArgs a) {
         const uint32_t valid = !inr ? 0u : ((32 * t + 32 <= eff) ? ~0u : ((1u << (eff - 32 * t)) - 1u));
         const bool anyb = inr && (any & valid);
         const bool allb = inr && ((all | ~valid) == ~0u);
-        const uint64_t ba = __ballot(anyb), bl = __ballot(allb);
-        if (lane == 0) {
-            const int wi = t0 >> 5;
-            if (wi < li.sum_wpb) { a.summary[base + wi] = (uint32_t)ba; a.summary[base + li.sum_wpb + wi] = (uint32_t)bl; }
-            if (wi + 1 < li.sum_wpb) { a.summary[base + wi + 1] = (uint32_t)(ba >> 32); a.summary[base + li.sum_wpb + wi + 1] = (uint32_t)(bl >> 32); }
+        const uint64_t ba = __ballot(anyb);
+        if (lane == 0) s_wc[wv] = __popcll(ba);
+        __syncthreads();
+        int before = running, total = 0;
+#pragma unroll
+        for (int v = 0; v < kSumThreads / kWave; ++v) {
+            before += v < wv ? s_wc[v] : 0;
+            total += s_wc[v];
         }
+        if (anyb) rec[1 + before + __popcll(ba & ((1ull << lane) - 1ull))] = t | (allb ? (int)0x80000000u : 0);
+        running += total;
+        __syncthreads();
     }
+    if (threadIdx.x == 0) rec[0] = running;
 }
 
 // ============================================================================ attention
@@ -490,7 +504,7 @@ struct AttnArgs {
     float *part_o;                    // [items][ncols_max][D] unnormalized split outputs
     float *part_ml;                   // [items][2][32] split max (base 2) and sum
     int ncols_max;
-    const uint32_t *summary;
+    const int32_t *summary;           // row-block tile lists of masked prefill lanes
 };
 
 // Per-wave view of one (lane, KV head): where its slots live and how far rows may read.

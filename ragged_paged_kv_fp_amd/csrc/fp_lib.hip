@@ -110,8 +110,7 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
             const int nrb = (n + prefill_rows(G) - 1) / prefill_rows(G);
             p.n_pre += (int64_t)p.H * nrb;
             if (masked) {
-                const int tiles = (cap + 31) / 32;
-                p.sum_words += (int64_t)nrb * 2 * ((tiles + 31) / 32);
+                p.sum_words += (int64_t)nrb * ((cap + 31) / 32 + 1);
                 p.summaries = true;
             }
         }
@@ -268,7 +267,7 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
     a.part_o = p.merge ? reinterpret_cast<float *>(ws + p.off_po) : nullptr;
     a.part_ml = p.merge ? reinterpret_cast<float *>(ws + p.off_pml) : nullptr;
     a.ncols_max = p.ncols_max;
-    a.summary = reinterpret_cast<const uint32_t *>(ws + p.off_sum);
+    a.summary = reinterpret_cast<const int32_t *>(ws + p.off_sum);
 
     if (p.summaries) {
         SummaryArgs sa;
@@ -281,8 +280,8 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
         sa.mask_off = mask->word_offset;
         sa.P = p.P;
         sa.G = p.G;
-        sa.summary = reinterpret_cast<uint32_t *>(ws + p.off_sum);
-        hipLaunchKernelGGL(summary_kernel, dim3((unsigned)p.n_pre), dim3(256), 0, stream, sa);
+        sa.summary = reinterpret_cast<int32_t *>(ws + p.off_sum);
+        hipLaunchKernelGGL(summary_kernel, dim3((unsigned)p.n_pre), dim3(kSumThreads), 0, stream, sa);
         if ((rc = launch_ok())) return rc;
     }
     if (tuning && tuning->attn_begin && hipEventRecord(tuning->attn_begin, stream) != hipSuccess) return FP_ERR_HIP;

@@ -3,7 +3,7 @@
 // One workgroup of eight waves per (lane, KV head, block of 256/G rows): wave w
 // owns query head g*G + w%G for 32 rows of the block, so every K/V tile the
 // workgroup stages in LDS feeds all G query heads of the KV head (GQA sharing).
-// Tiles of 32 slots are read from HBM once per workgroup into a three-stage
+// Tiles of 32 slots are read from HBM once per workgroup into a four-stage
 // LDS ring laid out so the MFMA fragment reads are free of bank conflicts:
 //   K   [32 slots][D]   rows padded by 16 bytes
 //   V^T [D][32 slots]   rows padded by 16 bytes
@@ -12,7 +12,16 @@
 // Scores use S^T = K * Q^T and O^T += V^T * P^T on v_mfma_f32_32x32x16_bf16
 // (the same register mapping as the 32-column decode path), with the online
 // softmax rescaling O only when a column's running max grows by more than 2^8.
+//
+// The tile loop is unrolled by the ring depth, so every LDS stage address is a
+// constant, and it is specialised for the two kinds of lane: causal lanes walk
+// tiles 0..T-1 and mask only the tiles that cross a row's causal limit; masked
+// lanes walk the row block's tile list (written by summary_kernel: the tiles
+// with any allowed slot, tagged when all slots are allowed) and carry each
+// row's mask word through LDS with the tile.
 #pragma once
+
+#include <type_traits>
 
 #include "fp_kernels.h"
 
@@ -20,8 +29,8 @@ namespace fpk {
 
 constexpr int kPreWaves = 8;
 constexpr int kPreThreads = 64 * kPreWaves;
+constexpr int kPreStages = 4;          // LDS ring depth (the loop is unrolled by the same count)
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p stays below 2^8 between rescales
-constexpr int kPreSumWords = 1024;     // summary words per kind staged in LDS: capacity <= 1M slots
 
 template <int D>
 struct PreLds {
@@ -34,16 +43,15 @@ struct PreLds {
     static constexpr int STAGE = MW_OFF + 4 * 256;
 };
 
-// What this thread brings in for one tile: a 16-byte K chunk and V^T chunk and
-// the mask word of its own query row, all for the shared LDS stage (the word
-// goes through LDS too, so no loaded value outlives its ring slot).
-template <int D>
+// What this thread brings in for one tile: a 16-byte K chunk and V^T chunk and,
+// on masked lanes, the mask word of its own query row, all for the shared LDS
+// stage (the word goes through LDS too, so no loaded value outlives its ring slot).
 struct PreStage {
     uint4 k, v;
     uint32_t mw;
 };
 
-// Physical pages of the K and V^T chunks this thread moves for tile t (loaded
+// Physical pages of the K and V^T chunks this thread moves for one tile (loaded
 // one pipeline step before the data, so waiting for them never waits for the
 // data loads still in flight behind them).
 struct PrePages {
@@ -62,7 +70,6 @@ struct PreCopy {
     int kpg, vpg;         // page of the chunk within the tile's pages
     int tshift;           // log2(pages per tile)
     int lastpg;           // last working-set page holding a slot below kv_len
-    int vslot;            // first tile slot of the V^T chunk
     int k_lds, v_lds;     // LDS byte offsets of the chunk in a stage
     int mw_lds;           // LDS byte offset of the row's mask word
     int ts;               // the tile holding slot kv_len (its tail slots are not part of the sequence)
@@ -85,12 +92,11 @@ __device__ __forceinline__ PreCopy<D> pre_copy(const KvView &kv, int rloc) {
     c.vpg = (8 * cv) >> kv.pshift;
     c.tshift = 5 - kv.pshift;
     c.lastpg = kv.eff > 0 ? (kv.eff - 1) >> kv.pshift : 0;
-    c.vslot = 8 * cv;
     c.k_lds = rk * PreLds<D>::KROW + 16 * ck;
     c.v_lds = PreLds<D>::K_BYTES + dv * PreLds<D>::VROW + 16 * cv;
     c.mw_lds = PreLds<D>::MW_OFF + 4 * rloc;
     c.ts = kv.eff >> 5;
-    const int nv = (kv.eff & 31) - c.vslot;  // valid slots of the chunk in tile ts
+    const int nv = (kv.eff & 31) - 8 * cv;  // valid slots of the V^T chunk in tile ts
 #pragma unroll
     for (int q = 0; q < 4; ++q) c.vmk[q] = nv >= 2 * q + 2 ? 0xFFFFFFFFu : (nv >= 2 * q + 1 ? 0x0000FFFFu : 0u);
     return c;
@@ -98,22 +104,20 @@ __device__ __forceinline__ PreCopy<D> pre_copy(const KvView &kv, int rloc) {
 
 template <int D>
 __device__ __forceinline__ void pre_pages(const KvView &kv, const PreCopy<D> &c, int t, PrePages &pp) {
-    const int base = (t < 0 ? 0 : t) << c.tshift;
+    const int base = t << c.tshift;
     pp.k = kv.pids[min(base + c.kpg, c.lastpg)];
     pp.v = kv.pids[min(base + c.vpg, c.lastpg)];
 }
 
 // Every load here is unconditional and nothing is done to the loaded values
-// until they are stored to LDS a step later (tiles past the sequence fetch
-// tile 0 and are never used), so the compiler can count outstanding loads
-// exactly and wait for one tile's data without draining later prefetches.
-// K of slots at or past kv_len is never zeroed: those slots only occur in
-// tiles whose scores go through the per-slot select, which drops them.
-template <int D>
-__device__ __forceinline__ void pre_data(const PreCopy<D> &c, int t, const PrePages &pp, PreStage<D> &st,
+// until they are stored to LDS two steps later, so the compiler can count
+// outstanding loads exactly and wait for one tile's data without draining
+// later prefetches. K of slots at or past kv_len is never zeroed: those slots
+// only occur in tiles whose scores go through the per-slot select, which drops them.
+template <int D, bool MASKED>
+__device__ __forceinline__ void pre_data(const PreCopy<D> &c, int t, const PrePages &pp, PreStage &st,
                                          const uint32_t *mrow, int wpr) {
-    t = t < 0 ? 0 : t;
-    st.mw = mrow[t < wpr ? t : 0];  // mrow points at valid memory for every lane
+    if constexpr (MASKED) st.mw = mrow[t < wpr ? t : 0];
     const uint32_t pk = (uint32_t)min(max(pp.k, 0), c.last_page);
     const uint32_t pv = (uint32_t)min(max(pp.v, 0), c.last_page);
     st.k = *reinterpret_cast<const uint4 *>(c.kp + (uint64_t)pk * c.pbytes);
@@ -121,18 +125,17 @@ __device__ __forceinline__ void pre_data(const PreCopy<D> &c, int t, const PrePa
 }
 
 // Stores tile t's chunks into an LDS stage. V^T entries of slots at or past
-// kv_len are zeroed here (p = 0 times a stale NaN would still be NaN); only the
-// tile that straddles kv_len has such entries. Every thread stores: with fewer
-// chunks than threads (head_dim 64) two threads write the same bytes, and all
-// lanes of a row write the same mask word, so no store needs a branch.
-template <int D>
-__device__ __forceinline__ void pre_store(const PreCopy<D> &c, const PreStage<D> &st, char *stage, int t) {
-    const uint32_t keep = (t < 0 ? 0 : t) == c.ts ? 0u : 0xFFFFFFFFu;  // workgroup-uniform
+// kv_len are zeroed (p = 0 times a stale NaN would still be NaN); only tile ts
+// has such entries. Every thread stores: with fewer chunks than threads (head
+// dim 64) two threads write the same bytes, and all lanes of a row write the
+// same mask word, so no store needs a lane condition.
+template <int D, bool MASKED>
+__device__ __forceinline__ void pre_store(const PreCopy<D> &c, const PreStage &st, char *stage, int t) {
     *reinterpret_cast<uint4 *>(stage + c.k_lds) = st.k;
-    *reinterpret_cast<uint4 *>(stage + c.v_lds) =
-        make_uint4(st.v.x & (c.vmk[0] | keep), st.v.y & (c.vmk[1] | keep), st.v.z & (c.vmk[2] | keep),
-                   st.v.w & (c.vmk[3] | keep));
-    *reinterpret_cast<uint32_t *>(stage + c.mw_lds) = st.mw;
+    uint4 v = st.v;
+    if (t == c.ts) v = make_uint4(v.x & c.vmk[0], v.y & c.vmk[1], v.z & c.vmk[2], v.w & c.vmk[3]);  // uniform
+    *reinterpret_cast<uint4 *>(stage + c.v_lds) = v;
+    if constexpr (MASKED) *reinterpret_cast<uint32_t *>(stage + c.mw_lds) = st.mw;
 }
 
 template <int D>
@@ -199,9 +202,9 @@ __device__ __forceinline__ void pre_prologue(f32x16 &s, bool full, uint32_t vbit
 // chain together with the exp2 / bf16 packing of two weights of the current
 // tile, so the VALU work runs while the dependent MFMA chain waits on itself;
 // the P*V MFMAs of the first weight half join the chain's later segments, and
-// the second half shares its segments with the tile copy (page ids, LDS store,
-// prefetch loads: copy(k) is called for k = 0, 1, 2). The denominator sums the
-// same bf16 weights the numerator uses.
+// the second half shares its segments with the tile copy (list entry and page
+// ids, LDS store, prefetch loads: copy(k) is called for k = 0, 1, 2). The
+// denominator sums the same bf16 weights the numerator uses.
 template <int D, class Copy>
 __device__ __forceinline__ void pre_main(const char *stc, const char *stn, const f32x16 &sc, f32x16 &sn,
                                          PreWave<D> &w, Copy &&copy) {
@@ -264,39 +267,20 @@ __device__ __forceinline__ uint32_t tile_bits(int j0, int lim, bool masked, uint
     return masked ? (mw & lm) : lm;
 }
 
-// Tiles a workgroup visits: 0..T-1 under the causal rule, or the tiles whose
-// summary bit is set for a masked lane (all threads walk the same sequence).
-struct TileSeq {
-    const uint32_t *any;  // summary words staged in LDS; nullptr: dense
-    int T, wi;
-    uint32_t bits;
-};
-
-__device__ __forceinline__ int seq_next(TileSeq &q, int cur) {
-    if (!q.any) return (cur + 1 < q.T) ? cur + 1 : -1;
-    for (;;) {
-        if (q.bits) {
-            const int b = __builtin_ctz(q.bits);
-            q.bits &= q.bits - 1u;
-            const int t = 32 * q.wi + b;
-            return t < q.T ? t : -1;
-        }
-        ++q.wi;
-        if (32 * q.wi >= q.T) return -1;
-        q.bits = __builtin_amdgcn_readfirstlane(q.any[q.wi]);
-    }
+// Keeps an index in a vector register, so a load through it is a vector
+// memory load (ordered with the tile loads) rather than a scalar one.
+__device__ __forceinline__ int in_vgpr(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
-// Prefill: one workgroup of eight waves per (lane, KV head, block of 256/G
-// rows); wave w owns query head g*G + w%G for the 32 rows at 32*(w/G).
-template <int D, int G>
-__global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) char s_tile[3][PreLds<D>::STAGE];
-    __shared__ int s_lmax[kPreWaves];
-    __shared__ uint32_t s_sum[2][kPreSumWords];  // the row block's summary words: any, all
+template <int K>
+using StepK = std::integral_constant<int, K>;
 
-    const int4 it = a.pre_items[blockIdx.x];
-    if (it.x < 0) return;
+// Prefill body for one work item; MASKED selects the masked-lane walk.
+template <int D, int G, bool MASKED>
+__device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char (*s_tile)[PreLds<D>::STAGE],
+                                             int *s_lmax) {
     const int lane = it.x, g = it.y, rstart = it.z, nr = it.w;
     const int wv = threadIdx.x / kWave;
     const int ln = lane_id(), n = ln & 31, h = ln >> 5;
@@ -321,121 +305,132 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnArgs a) {
         w.m = -__FLT_MAX__;
         w.l = 0.0f;
     }
-    const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
-    // Mask-word pointers are always valid so their loads need no branch: a
-    // causal lane reads a harmless word of indptr and ignores it.
+    // Mask-word pointers are always valid so their loads need no branch.
     const uint32_t *mrow = reinterpret_cast<const uint32_t *>(a.indptr);
     int wpr = 1;
-    if (masked) {
+    const int32_t *lst = nullptr;  // masked lanes: [count, entries...] of this row block
+    int T;                         // tiles this workgroup visits
+    if constexpr (MASKED) {
         wpr = (int)((a.mask_off[lane + 1] - a.mask_off[lane]) / nrows);
         mrow = a.mask_bits + a.mask_off[lane] + (int64_t)(rstart + (colv ? rloc : 0)) * wpr;
+        const LaneInfo li = a.lane_info[lane];
+        lst = a.summary + li.sum_off + (int64_t)(rstart / prefill_rows(G)) * li.sum_stride;
+        T = li.sum_off >= 0 ? __builtin_amdgcn_readfirstlane(lst[0]) : 0;
     }
-    const int lim = !colv ? 0 : (masked ? kv.eff : min(a.slots[row] + 1, kv.eff));
-    const int lmax_w = __builtin_amdgcn_readfirstlane(wave_max_i(lim));
+    const int lim = !colv ? 0 : (MASKED ? kv.eff : min(a.slots[row] + 1, kv.eff));
     const int lmin_w = __builtin_amdgcn_readfirstlane(-wave_max_i(colv ? -lim : -0x7FFFFFFF));  // valid columns
     // Let the Q loads land before the pipeline starts: otherwise the first use
     // of Q inside the loop carries a wait for every load in flight.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    if (ln == 0) s_lmax[wv] = lmax_w;
-    __syncthreads();
-    int lwg = 0;
+    if constexpr (!MASKED) {
+        const int lmax_w = __builtin_amdgcn_readfirstlane(wave_max_i(lim));
+        if (ln == 0) s_lmax[wv] = lmax_w;
+        __syncthreads();
+        int lwg = 0;
 #pragma unroll
-    for (int v = 0; v < kPreWaves; ++v) lwg = max(lwg, s_lmax[v]);
-    lwg = __builtin_amdgcn_readfirstlane(lwg);
-
-    TileSeq seq;
-    seq.T = (lwg + 31) >> 5;
-    seq.any = nullptr;
-    seq.wi = 0;
-    seq.bits = 0;
-    if (masked) {  // workgroup-uniform
-        const LaneInfo li = a.lane_info[lane];
-        const uint32_t *gs = a.summary + li.sum_off + (int64_t)(rstart / prefill_rows(G)) * 2 * li.sum_wpb;
-        const int nw = min(li.sum_wpb, kPreSumWords);
-        for (int i = threadIdx.x; i < nw; i += kPreThreads) {
-            s_sum[0][i] = gs[i];
-            s_sum[1][i] = gs[li.sum_wpb + i];
-        }
-        __syncthreads();
-        seq.any = s_sum[0];
-        seq.bits = seq.T > 0 ? __builtin_amdgcn_readfirstlane(seq.any[0]) : 0u;
+        for (int v = 0; v < kPreWaves; ++v) lwg = max(lwg, s_lmax[v]);
+        T = (__builtin_amdgcn_readfirstlane(lwg) + 31) >> 5;
     }
-    const uint32_t *allw = s_sum[1];
 
-    // Software pipeline over the tile sequence t0, t1, t2, ...: while the
-    // softmax and P*V of tile t0 run, the QK^T MFMAs of t1 are issued (its K
-    // sits in the next LDS stage), t2 and t3 are in flight from HBM in
-    // registers (ring), and the page ids of t4 are being read. Three LDS stages
-    // rotate; the loop is unrolled twice so no register holding in-flight data
-    // is copied, and every global load in the loop is unconditional. Tiles
-    // past a wave's last row (the end of the causal diagonal) are computed like
-    // the others with every slot dropped, which keeps each step branch-free.
-    int st = 0;
-    int t0 = seq_next(seq, -1);
-    int t1 = t0 >= 0 ? seq_next(seq, t0) : -1;
-    int t2 = t1 >= 0 ? seq_next(seq, t1) : -1;
-    int t3 = t2 >= 0 ? seq_next(seq, t2) : -1;
-    int t4 = t3 >= 0 ? seq_next(seq, t3) : -1;
-    const PreCopy<D> cp = pre_copy<D>(kv, rloc);
-    PreStage<D> ringA, ringB;
-    PrePages pgA, pgB;
-    if (t0 >= 0) {  // workgroup-uniform
-        pre_pages<D>(kv, cp, t0, pgA);
-        pre_pages<D>(kv, cp, t1, pgB);
-        pre_data<D>(cp, t0, pgA, ringA, mrow, wpr);
-        pre_data<D>(cp, t1, pgB, ringB, mrow, wpr);
-        pre_pages<D>(kv, cp, t2, pgA);
-        pre_pages<D>(kv, cp, t3, pgB);
-        pre_store<D>(cp, ringA, s_tile[0], t0);
-        pre_store<D>(cp, ringB, s_tile[1], t1);
-        pre_data<D>(cp, t2, pgA, ringA, mrow, wpr);
-        pre_data<D>(cp, t3, pgB, ringB, mrow, wpr);
-        pre_pages<D>(kv, cp, t4, pgA);
-    }
-    __syncthreads();
-
-    auto prologue = [&](int t, f32x16 &sacc, int stage) {
-        const int j0 = 32 * t;
-        const bool full = masked ? (((allw[t >> 5] >> (t & 31)) & 1u) && j0 + 32 <= kv.eff) : (j0 + 32 <= lmin_w);
-        uint32_t bits = 0u;
-        if (!full) {
-            const uint32_t mw = *reinterpret_cast<const uint32_t *>(s_tile[stage] + PreLds<D>::MW_OFF + 4 * rloc);
-            bits = tile_bits(j0, lim, masked, mw);
+    if (T > 0) {  // workgroup-uniform
+        // Software pipeline over the tile sequence; at step i: the softmax and
+        // P*V of tile i run while the QK^T MFMAs of tile i+1 are issued (its K
+        // sits in the next LDS stage), tile i+2 moves from registers to LDS,
+        // tiles i+3 and i+4 are in flight from HBM, and the page ids of tile
+        // i+5 are read. Tile j lives in LDS stage j % 4. Steps past the end of
+        // the sequence repeat its last tile, so every load is unconditional;
+        // tiles past a wave's last row (the end of the causal diagonal) are
+        // computed like the others with every slot dropped.
+        const PreCopy<D> cp = pre_copy<D>(kv, rloc);
+        // masked lanes: list entries of steps i..i+5, and the load of step i+6
+        int q0 = 0, q1 = 0, q2 = 0, q3 = 0, q4 = 0, q5 = 0, lv = 0;
+        auto entry = [&](int i) { return lst[1 + min(i, T - 1)]; };
+        auto tile_at = [&](int i, int qe) {  // tile of step i
+            if constexpr (MASKED) return qe & 0x7FFFFFFF;
+            else return min(i, T - 1);
+        };
+        if constexpr (MASKED) {
+            q0 = __builtin_amdgcn_readfirstlane(entry(0));
+            q1 = __builtin_amdgcn_readfirstlane(entry(1));
+            q2 = __builtin_amdgcn_readfirstlane(entry(2));
+            q3 = __builtin_amdgcn_readfirstlane(entry(3));
+            q4 = __builtin_amdgcn_readfirstlane(entry(4));
+            q5 = __builtin_amdgcn_readfirstlane(entry(5));
+            lv = lst[in_vgpr(1 + min(6, T - 1))];
         }
-        pre_prologue<D>(sacc, full, bits, w);
-    };
-    f32x16 sA = pre_qk<D>(s_tile[0], w), sB = {};
-    while (t0 >= 0) {
-        const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
-        const int t5 = t4 >= 0 ? seq_next(seq, t4) : -1;
-        prologue(t0, sA, st);
-        // page ids first: the data loads then wait only on page ids read one
-        // step earlier, never on the newest loads
-        pre_main<D>(s_tile[st], s_tile[st1], sA, sB, w, [&](int k) {
-            if (k == 0) pre_pages<D>(kv, cp, t5, pgB);
-            if (k == 1) pre_store<D>(cp, ringA, s_tile[st2], t2);
-            if (k == 2) pre_data<D>(cp, t4, pgA, ringA, mrow, wpr);
-        });
+        PreStage ringA, ringB;
+        PrePages pgA, pgB;
+        pre_pages<D>(kv, cp, tile_at(0, q0), pgA);
+        pre_pages<D>(kv, cp, tile_at(1, q1), pgB);
+        pre_data<D, MASKED>(cp, tile_at(0, q0), pgA, ringA, mrow, wpr);
+        pre_data<D, MASKED>(cp, tile_at(1, q1), pgB, ringB, mrow, wpr);
+        pre_pages<D>(kv, cp, tile_at(2, q2), pgA);
+        pre_pages<D>(kv, cp, tile_at(3, q3), pgB);
+        pre_store<D, MASKED>(cp, ringA, s_tile[0], tile_at(0, q0));
+        pre_store<D, MASKED>(cp, ringB, s_tile[1], tile_at(1, q1));
+        pre_data<D, MASKED>(cp, tile_at(2, q2), pgA, ringA, mrow, wpr);
+        pre_data<D, MASKED>(cp, tile_at(3, q3), pgB, ringB, mrow, wpr);
+        pre_pages<D>(kv, cp, tile_at(4, q4), pgA);
         __syncthreads();
-        st = st1;
-        if (t1 < 0) break;
 
-        const int su1 = st == 2 ? 0 : st + 1, su2 = su1 == 2 ? 0 : su1 + 1;
-        const int t6 = t5 >= 0 ? seq_next(seq, t5) : -1;
-        prologue(t1, sB, st);
-        pre_main<D>(s_tile[st], s_tile[su1], sB, sA, w, [&](int k) {
-            if (k == 0) pre_pages<D>(kv, cp, t6, pgA);
-            if (k == 1) pre_store<D>(cp, ringB, s_tile[su2], t3);
-            if (k == 2) pre_data<D>(cp, t5, pgB, ringB, mrow, wpr);
-        });
-        __syncthreads();
-        st = su1;
-        if (t2 < 0) break;
-        t0 = t2;
-        t1 = t3;
-        t2 = t4;
-        t3 = t5;
-        t4 = t6;
+        f32x16 sA = pre_qk<D>(s_tile[0], w), sB = {};
+        auto step = [&](auto kc, int i) {
+            constexpr int K = decltype(kc)::value;
+            char *stc = s_tile[K];
+            char *stn = s_tile[(K + 1) % kPreStages];
+            char *sts = s_tile[(K + 2) % kPreStages];
+            f32x16 &sc = (K & 1) ? sB : sA;
+            f32x16 &sn = (K & 1) ? sA : sB;
+            PreStage &ring = (K & 1) ? ringB : ringA;
+            PrePages &pgc = (K & 1) ? pgB : pgA;  // page ids of tile i+4 (read one step ago)
+            PrePages &pgn = (K & 1) ? pgA : pgB;  // receives the page ids of tile i+5
+            int q6 = 0;
+            if constexpr (MASKED) q6 = __builtin_amdgcn_readfirstlane(lv);
+            const int tc = tile_at(i, q0), t2 = tile_at(i + 2, q2), t4 = tile_at(i + 4, q4),
+                      t5 = tile_at(i + 5, q5);
+            {
+                const int j0 = 32 * tc;
+                bool full;
+                uint32_t bits = 0u;
+                if constexpr (MASKED) {
+                    full = q0 < 0 && j0 + 32 <= kv.eff;  // bit 31: every slot allowed for every row
+                    if (!full) bits = tile_bits(j0, lim, true, *reinterpret_cast<const uint32_t *>(stc + cp.mw_lds));
+                } else {
+                    full = j0 + 32 <= lmin_w;
+                    if (!full) bits = tile_bits(j0, lim, false, 0u);
+                }
+                pre_prologue<D>(sc, full, bits, w);
+            }
+            pre_main<D>(stc, stn, sc, sn, w, [&](int k) {
+                if (k == 0) {
+                    // list entry and page ids first: the data loads then wait
+                    // only on loads issued one step earlier, never the newest
+                    if constexpr (MASKED) lv = lst[in_vgpr(1 + min(i + 7, T - 1))];
+                    pre_pages<D>(kv, cp, t5, pgn);
+                }
+                if (k == 1) pre_store<D, MASKED>(cp, ring, sts, t2);
+                if (k == 2) pre_data<D, MASKED>(cp, t4, pgc, ring, mrow, wpr);
+            });
+            __syncthreads();
+            if constexpr (MASKED) {
+                q0 = q1;
+                q1 = q2;
+                q2 = q3;
+                q3 = q4;
+                q4 = q5;
+                q5 = q6;
+            }
+        };
+        for (int i = 0;; i += kPreStages) {
+            step(StepK<0>{}, i);
+            if (i + 1 >= T) break;
+            step(StepK<1>{}, i + 1);
+            if (i + 2 >= T) break;
+            step(StepK<2>{}, i + 2);
+            if (i + 3 >= T) break;
+            step(StepK<3>{}, i + 3);
+            if (i + 4 >= T) break;
+        }
     }
 
     if (!colv) return;
@@ -451,6 +446,19 @@ __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnArgs a) {
                             w.o[db][4 * i4 + 3] * inv);
     if (a.lse && h == 0)
         a.lse[row * a.Hq + head] = l_tot > 0.0f ? (w.m + __log2f(l_tot)) * 0.69314718055994531f : kNegInf;
+}
+
+// Prefill: one workgroup of eight waves per (lane, KV head, block of 256/G
+// rows); wave w owns query head g*G + w%G for the 32 rows at 32*(w/G).
+template <int D, int G>
+__global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) char s_tile[kPreStages][PreLds<D>::STAGE];
+    __shared__ int s_lmax[kPreWaves];
+    const int4 it = a.pre_items[blockIdx.x];
+    if (it.x < 0) return;
+    const bool masked = a.mask_off && a.mask_off[it.x + 1] > a.mask_off[it.x];  // workgroup-uniform
+    if (masked) prefill_item<D, G, true>(a, it, s_tile, s_lmax);
+    else prefill_item<D, G, false>(a, it, s_tile, s_lmax);
 }
 
 }  // namespace fpk
