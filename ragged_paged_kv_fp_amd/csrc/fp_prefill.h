@@ -31,6 +31,8 @@ constexpr int kPreWaves = 8;
 constexpr int kPreThreads = 64 * kPreWaves;
 constexpr int kPreStages = 4;          // LDS ring depth (the loop is unrolled by the same count)
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p stays below 2^8 between rescales
+constexpr float kNoSlot = -0x1p100f;   // a tile max below this: the column may read no slot of the tile
+constexpr uint32_t kBiasOut = 0xFE80FE80u;  // two bf16 -2^126: the bias of a slot a row may not read
 
 template <int D>
 struct PreLds {
@@ -41,6 +43,9 @@ struct PreLds {
     static constexpr int V_BYTES = D * VROW;
     static constexpr int MW_OFF = K_BYTES + V_BYTES;  // mask words of the block's rows (masked lanes)
     static constexpr int STAGE = MW_OFF + 4 * 256;
+    static constexpr int LUT_OFF = kPreStages * STAGE;  // [256][4] uint32: bf16 keep masks of a mask byte
+    static constexpr int AOP_OFF = LUT_OFF + 256 * 16;   // [2][64] uint4: A operands of the bias MFMAs
+    static constexpr int TOTAL = AOP_OFF + 2 * 64 * 16;
 };
 
 // What this thread brings in for one tile: a 16-byte K chunk and V^T chunk and,
@@ -73,7 +78,7 @@ struct PreCopy {
     int k_lds, v_lds;     // LDS byte offsets of the chunk in a stage
     int mw_lds;           // LDS byte offset of the row's mask word
     int ts;               // the tile holding slot kv_len (its tail slots are not part of the sequence)
-    uint32_t vmk[4];      // V^T chunk mask for tile ts: the words of slots below kv_len
+    int vnv;              // slots of this thread's V^T chunk below kv_len in tile ts
 };
 
 template <int D>
@@ -96,9 +101,7 @@ __device__ __forceinline__ PreCopy<D> pre_copy(const KvView &kv, int rloc) {
     c.v_lds = PreLds<D>::K_BYTES + dv * PreLds<D>::VROW + 16 * cv;
     c.mw_lds = PreLds<D>::MW_OFF + 4 * rloc;
     c.ts = kv.eff >> 5;
-    const int nv = (kv.eff & 31) - 8 * cv;  // valid slots of the V^T chunk in tile ts
-#pragma unroll
-    for (int q = 0; q < 4; ++q) c.vmk[q] = nv >= 2 * q + 2 ? 0xFFFFFFFFu : (nv >= 2 * q + 1 ? 0x0000FFFFu : 0u);
+    c.vnv = (kv.eff & 31) - 8 * cv;
     return c;
 }
 
@@ -133,7 +136,12 @@ template <int D, bool MASKED>
 __device__ __forceinline__ void pre_store(const PreCopy<D> &c, const PreStage &st, char *stage, int t) {
     *reinterpret_cast<uint4 *>(stage + c.k_lds) = st.k;
     uint4 v = st.v;
-    if (t == c.ts) v = make_uint4(v.x & c.vmk[0], v.y & c.vmk[1], v.z & c.vmk[2], v.w & c.vmk[3]);  // uniform
+    if (t == c.ts) {  // workgroup-uniform: keep the chunk's slots below kv_len
+        uint32_t mk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mk[q] = c.vnv >= 2 * q + 2 ? 0xFFFFFFFFu : (c.vnv >= 2 * q + 1 ? 0x0000FFFFu : 0u);
+        v = make_uint4(v.x & mk[0], v.y & mk[1], v.z & mk[2], v.w & mk[3]);
+    }
     *reinterpret_cast<uint4 *>(stage + c.v_lds) = v;
     if constexpr (MASKED) *reinterpret_cast<uint32_t *>(stage + c.mw_lds) = st.mw;
 }
@@ -142,33 +150,119 @@ template <int D>
 struct PreWave {
     uint4 qf[D / 16];
     f32x16 o[D / 32];
-    float m, l;
+    float m, l;  // running max (log2 units, always a bf16 value) and denominator
+    bool seen;   // the column has had an allowed slot
 };
 
-// S^T = K * Q^T for the staged tile: the eight K fragments of a lane sit at
-// constant offsets from one address, read first, then one accumulator chain.
+__device__ __forceinline__ float bf16_round(float x) { return __uint_as_float(pack_bf16x2(x, x) << 16); }
+
+// -m of the column as two bf16 halves (exact: m is kept bf16-representable).
 template <int D>
-__device__ __forceinline__ f32x16 pre_qk(const char *stage, const PreWave<D> &w) {
+__device__ __forceinline__ uint32_t neg_m2(const PreWave<D> &w) {
+    const uint32_t hb = __float_as_uint(-w.m) >> 16;
+    return hb | (hb << 16);
+}
+
+// The score shift and the mask enter the QK^T accumulation as extra MFMAs,
+// so the softmax needs neither a subtraction nor a per-slot select:
+//  * RowBias (causal lanes): one rank-1 MFMA, A[m][k] = (k == 0), B[0][n] = -m_n,
+//    adds -m to every slot of the column.
+//  * MaskBias (masked lanes): two MFMAs over the 32 tile slots whose A operand
+//    is the slot permutation of the score rows (row m holds slot
+//    kslot_of_row(m), so A[m][k] = (kslot_of_row(m) == k)) and whose B operand
+//    holds -m for a slot the row may read and -2^126 for one it may not. The
+//    B operand is built from the row's mask bytes through a 256-entry table
+//    of bf16 keep masks in LDS.
+// A score the row may not read then sits near -2^126 and its weight is 0; the
+// column max of a tile therefore covers allowed slots only. Slots at or past
+// kv_len can hold stale K (even NaN), so the one tile that crosses kv_len
+// still drops them with a select.
+struct RowBias {
+    uint32_t a0, negm2;
+    __device__ __forceinline__ void fetch() {}
+    __device__ __forceinline__ void load(int) {}
+    __device__ __forceinline__ void build() {}
+    __device__ __forceinline__ f32x16 apply(f32x16 acc, int k) const {
+        return k == 0 ? mfma32(make_uint4(a0, 0u, 0u, 0u), make_uint4(negm2, 0u, 0u, 0u), acc) : acc;
+    }
+};
+
+// The two MFMAs of MaskBias run one after the other through one operand set
+// (load(k), build(), apply(acc, k)), which keeps eight registers free.
+struct MaskBias {
+    const char *lds;  // LDS base holding the keep-mask table and the A operands
+    const uint32_t *mw;  // the row's mask word for the tile (LDS)
+    uint32_t lm;      // slots below the row's limit, or all ones when the tile is fully allowed
+    bool full;        // every row may read every slot of the tile
+    uint32_t bits;    // slots of the tile the lane's row may read
+    uint32_t negm2;
+    int lut_off, aop_off;
+    uint4 a, b;
+    // issued together with the tile's fragment reads, consumed by load(0)
+    __device__ __forceinline__ void fetch() { bits = *mw; }
+    __device__ __forceinline__ void load(int k) {
+        const int ln = lane_id(), kg = ln >> 5;
+        if (k == 0) bits = full ? 0xFFFFFFFFu : (bits & lm);
+        // B lane (n, kg) of MFMA k holds slots 16k + 8kg .. 16k + 8kg + 7
+        b = *reinterpret_cast<const uint4 *>(lds + lut_off + 16 * ((bits >> (16 * k + 8 * kg)) & 0xFFu));
+        a = *reinterpret_cast<const uint4 *>(lds + aop_off + 1024 * k + 16 * ln);
+    }
+    __device__ __forceinline__ void build() { b = make_uint4(bfi(b.x), bfi(b.y), bfi(b.z), bfi(b.w)); }
+    __device__ __forceinline__ uint32_t bfi(uint32_t keep) const { return (keep & negm2) | (~keep & kBiasOut); }
+    __device__ __forceinline__ f32x16 apply(f32x16 acc, int) const { return mfma32(a, b, acc); }
+};
+
+// Fills the keep-mask table (entry e: word q keeps bf16 half 0 if bit 2q of e
+// is set and half 1 if bit 2q+1 is) and the A operands of MaskBias.
+template <int D>
+__device__ __forceinline__ void fill_bias_tables(char *lds) {
+    for (int wi = threadIdx.x; wi < 256 * 4; wi += kPreThreads) {
+        const int e = wi >> 2, q = wi & 3;
+        const uint32_t v = (((e >> (2 * q)) & 1) ? 0x0000FFFFu : 0u) | (((e >> (2 * q + 1)) & 1) ? 0xFFFF0000u : 0u);
+        reinterpret_cast<uint32_t *>(lds + PreLds<D>::LUT_OFF)[wi] = v;
+    }
+    for (int t = threadIdx.x; t < 2 * 64; t += kPreThreads) {
+        const int which = t >> 6, ln = t & 63, m = ln & 31, kg = ln >> 5;
+        const int j = kslot_of_row(m) - 16 * which - 8 * kg;  // position of the 1 in this lane's 8 k's
+        uint32_t r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = (j == 2 * q ? 0x00003F80u : 0u) | (j == 2 * q + 1 ? 0x3F800000u : 0u);
+        reinterpret_cast<uint4 *>(lds + PreLds<D>::AOP_OFF)[t] = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+}
+
+// S^T = K * Q^T (+ bias) for the staged tile: the K fragments of a lane sit at
+// constant offsets from one address, read first, then one accumulator chain.
+template <int D, class Bias>
+__device__ __forceinline__ f32x16 pre_qk(const char *stage, const PreWave<D> &w, Bias &bias) {
     const int ln = lane_id(), h = ln >> 5, n = ln & 31;
     const char *krow = stage + kslot_of_row(n) * PreLds<D>::KROW + h * D;
     uint4 kf[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) kf[s] = *reinterpret_cast<const uint4 *>(krow + 16 * s);
+    bias.fetch();
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) acc = mfma32(kf[s], w.qf[s], acc);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        bias.load(k);
+        bias.build();
+        acc = bias.apply(acc, k);
+    }
     return acc;
 }
 
-// Softmax prologue of one tile: drop the slots a column may not see (unless
-// the whole tile is allowed), take the column max over both lane halves and
-// rescale O and l when it grew by more than 2^kRescaleSlack. The running max
-// starts at -FLT_MAX, not -inf, so p = exp2(s - m) needs no special case for a
-// column that has seen no valid slot yet (a dropped score is -inf, p = 0).
+// Softmax prologue of one tile. The scores arrive as s - m (the shift was
+// added by the bias MFMA). With sel, slots outside vbits are first set to
+// -inf. Then the column max over both lane halves; the running max moves
+// (rounded to bf16, so -m stays exact in the next bias) the first time the
+// column sees an allowed slot and whenever the max grows by more than
+// 2^kRescaleSlack, rescaling O and l and re-shifting the scores.
 template <int D>
-__device__ __forceinline__ void pre_prologue(f32x16 &s, bool full, uint32_t vbits, PreWave<D> &w) {
+__device__ __forceinline__ void pre_prologue(f32x16 &s, bool sel, uint32_t vbits, PreWave<D> &w) {
     const int h = lane_id() >> 5;
-    if (!full) {
+    if (sel) {
         const uint32_t vb = vbits >> (8 * h);  // register i holds tile slot 16(i/8) + 8h + i%8
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -185,33 +279,39 @@ __device__ __forceinline__ void pre_prologue(f32x16 &s, bool full, uint32_t vbit
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
         mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    const bool grow = mt > w.m + kRescaleSlack;
+    const bool valid = mt > kNoSlot;
+    const bool grow = valid && (!w.seen || mt > kRescaleSlack);
     if (__any(grow)) {
-        const float m_new = grow ? mt : w.m;
-        const float alpha = __builtin_amdgcn_exp2f(w.m - m_new);
+        const float m_new = grow ? bf16_round(w.m + mt) : w.m;
+        const float delta = m_new - w.m;
+        const float alpha = w.seen ? __builtin_amdgcn_exp2f(-delta) : 1.0f;
         w.l *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) w.o[db] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] -= delta;
         w.m = m_new;
+        w.seen = w.seen || valid;
     }
 }
 
 // Main block of one pipeline step, free of branches and cut into segments
 // the scheduler keeps in order (it reorders only inside one): after the K and
-// V^T fragment reads, each segment issues one MFMA of the next tile's QK^T
+// first V^T fragment reads, each segment issues one MFMA of the next tile's QK^T
 // chain together with the exp2 / bf16 packing of two weights of the current
 // tile, so the VALU work runs while the dependent MFMA chain waits on itself;
-// the P*V MFMAs of the first weight half join the chain's later segments, and
-// the second half shares its segments with the tile copy (list entry and page
-// ids, LDS store, prefetch loads: copy(k) is called for k = 0, 1, 2). The
-// denominator sums the same bf16 weights the numerator uses.
-template <int D, class Copy>
+// the P*V MFMAs of the first weight half join the chain's later segments, the
+// bias MFMAs close the chain, and the second half of P*V shares its segments
+// with the tile copy (list entry and page ids, LDS store, prefetch loads:
+// copy(k) is called for k = 0, 1, 2). The denominator sums the same bf16
+// weights the numerator uses.
+template <int D, class Bias, class Copy>
 __device__ __forceinline__ void pre_main(const char *stc, const char *stn, const f32x16 &sc, f32x16 &sn,
-                                         PreWave<D> &w, Copy &&copy) {
+                                         PreWave<D> &w, Bias &bias, Copy &&copy) {
     constexpr int NQK = D / 16;          // QK^T MFMAs of the chain
     constexpr int NDB = D / 32;          // 32-row blocks of O^T
     constexpr int PPS = 8 / NQK;         // weight pairs packed per chain segment
-    static_assert(NQK >= 2 * NDB && 8 % NQK == 0, "segment plan");
+    static_assert(NQK >= 2 * NDB && 8 % NQK == 0 && NDB >= 2, "segment plan");
     const int ln = lane_id(), h = ln >> 5, n = ln & 31;
     const char *krow = stn + kslot_of_row(n) * PreLds<D>::KROW + h * D;
     const char *vrow = stc + PreLds<D>::K_BYTES + n * PreLds<D>::VROW + 16 * h;
@@ -219,10 +319,8 @@ __device__ __forceinline__ void pre_main(const char *stc, const char *stn, const
 #pragma unroll
     for (int s = 0; s < NQK; ++s) kf[s] = *reinterpret_cast<const uint4 *>(krow + 16 * s);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        vf[db][0] = *reinterpret_cast<const uint4 *>(vrow + 32 * db * PreLds<D>::VROW);
-        vf[db][1] = *reinterpret_cast<const uint4 *>(vrow + 32 * db * PreLds<D>::VROW + 32);
-    }
+    for (int db = 0; db < NDB; ++db) vf[db][0] = *reinterpret_cast<const uint4 *>(vrow + 32 * db * PreLds<D>::VROW);
+    bias.fetch();
     __builtin_amdgcn_sched_barrier(0);
     uint32_t pk[8];
     f32x16 acc = {};
@@ -233,20 +331,37 @@ __device__ __forceinline__ void pre_main(const char *stc, const char *stn, const
 #pragma unroll
         for (int u = 0; u < PPS; ++u) {
             const int q = s * PPS + u;
-            pk[q] = pack_bf16x2(__builtin_amdgcn_exp2f(sc[2 * q] - w.m), __builtin_amdgcn_exp2f(sc[2 * q + 1] - w.m));
+            pk[q] = pack_bf16x2(__builtin_amdgcn_exp2f(sc[2 * q]), __builtin_amdgcn_exp2f(sc[2 * q + 1]));
         }
         if (s == NQK - NDB - 1) pb0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         if (s >= NQK - NDB) {
             const int db = s - (NQK - NDB);
             w.o[db] = mfma32(vf[db][0], pb0, w.o[db]);
         }
+        if (s == NQK / 2) {
+            // the second V^T half takes the registers of the K fragments the
+            // chain has consumed by now
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                vf[db][1] = *reinterpret_cast<const uint4 *>(vrow + 32 * db * PreLds<D>::VROW + 32);
+        }
+        if (s == NQK - 1) bias.load(0);  // the K fragments are all consumed now
         __builtin_amdgcn_sched_barrier(0);
     }
-    sn = acc;
     const uint4 pb1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         w.o[db] = mfma32(vf[db][1], pb1, w.o[db]);
+        // bias MFMA 0 after the first P*V of the tail, MFMA 1 at its end
+        if (db == 0) {
+            bias.build();
+            acc = bias.apply(acc, 0);
+            bias.load(1);
+        }
+        if (db == NDB - 1) {
+            bias.build();
+            acc = bias.apply(acc, 1);
+        }
 #pragma unroll
         for (int q = db * (8 / NDB); q < (db + 1) * (8 / NDB); ++q)
             w.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[q]),
@@ -258,6 +373,7 @@ __device__ __forceinline__ void pre_main(const char *stc, const char *stn, const
 #pragma unroll
         for (int k = NDB; k < 3; ++k) copy(k);
     }
+    sn = acc;
 }
 
 // Allowed slots of tile j0 for this lane's column as a 32-bit mask.
@@ -279,8 +395,7 @@ using StepK = std::integral_constant<int, K>;
 
 // Prefill body for one work item; MASKED selects the masked-lane walk.
 template <int D, int G, bool MASKED>
-__device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char (*s_tile)[PreLds<D>::STAGE],
-                                             int *s_lmax) {
+__device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char *lds, int *s_lmax) {
     const int lane = it.x, g = it.y, rstart = it.z, nr = it.w;
     const int wv = threadIdx.x / kWave;
     const int ln = lane_id(), n = ln & 31, h = ln >> 5;
@@ -294,6 +409,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char (*
     int cap;
     KvView kv = make_view(a, lane, g, &cap);
     kv.vblock = (int64_t)a.H * a.P * D;
+    auto stage = [&](int k) { return lds + k * PreLds<D>::STAGE; };
 
     PreWave<D> w;
     {
@@ -302,8 +418,9 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char (*
         for (int s = 0; s < D / 16; ++s) w.qf[s] = colv ? src[s] : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) w.o[db] = f32x16{};
-        w.m = -__FLT_MAX__;
+        w.m = 0.0f;
         w.l = 0.0f;
+        w.seen = false;
     }
     // Mask-word pointers are always valid so their loads need no branch.
     const uint32_t *mrow = reinterpret_cast<const uint32_t *>(a.indptr);
@@ -316,6 +433,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char (*
         const LaneInfo li = a.lane_info[lane];
         lst = a.summary + li.sum_off + (int64_t)(rstart / prefill_rows(G)) * li.sum_stride;
         T = li.sum_off >= 0 ? __builtin_amdgcn_readfirstlane(lst[0]) : 0;
+        fill_bias_tables<D>(lds);
     }
     const int lim = !colv ? 0 : (MASKED ? kv.eff : min(a.slots[row] + 1, kv.eff));
     const int lmin_w = __builtin_amdgcn_readfirstlane(-wave_max_i(colv ? -lim : -0x7FFFFFFF));  // valid columns
@@ -366,19 +484,56 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char (*
         pre_data<D, MASKED>(cp, tile_at(1, q1), pgB, ringB, mrow, wpr);
         pre_pages<D>(kv, cp, tile_at(2, q2), pgA);
         pre_pages<D>(kv, cp, tile_at(3, q3), pgB);
-        pre_store<D, MASKED>(cp, ringA, s_tile[0], tile_at(0, q0));
-        pre_store<D, MASKED>(cp, ringB, s_tile[1], tile_at(1, q1));
+        pre_store<D, MASKED>(cp, ringA, stage(0), tile_at(0, q0));
+        pre_store<D, MASKED>(cp, ringB, stage(1), tile_at(1, q1));
         pre_data<D, MASKED>(cp, tile_at(2, q2), pgA, ringA, mrow, wpr);
         pre_data<D, MASKED>(cp, tile_at(3, q3), pgB, ringB, mrow, wpr);
         pre_pages<D>(kv, cp, tile_at(4, q4), pgA);
         __syncthreads();
 
-        f32x16 sA = pre_qk<D>(s_tile[0], w), sB = {};
+        // Bias operands of the tile of step i (staged in stage st): its
+        // allowed slots per row, and -m as it stands now.
+        auto make_bias = [&](int i, int qe, const char *st) {
+            if constexpr (MASKED) {
+                MaskBias b;
+                b.lds = lds;
+                b.lut_off = PreLds<D>::LUT_OFF;
+                b.aop_off = PreLds<D>::AOP_OFF;
+                const int j0 = 32 * tile_at(i, qe);
+                b.full = qe < 0 && j0 + 32 <= kv.eff;  // bit 31: every slot allowed for every row
+                b.lm = tile_bits(j0, lim, false, 0u);
+                b.mw = reinterpret_cast<const uint32_t *>(st + cp.mw_lds);
+                b.negm2 = neg_m2(w);
+                return b;
+            } else {
+                RowBias b;
+                b.a0 = h == 0 ? 0x00003F80u : 0u;
+                b.negm2 = neg_m2(w);
+                return b;
+            }
+        };
+        // Softmax prologue of the tile of step i: slots are dropped by a select
+        // only where the bias cannot do it (stale K past kv_len) or, on causal
+        // lanes, where the tile crosses a row's causal limit.
+        auto prologue = [&](int i, int qe, f32x16 &s) {
+            const int t = tile_at(i, qe);
+            int j0 = 32 * t;
+            bool sel;
+            if constexpr (MASKED) sel = t == cp.ts;
+            else sel = j0 + 32 > lmin_w;
+            // the selected tile's start stays opaque, so the compiler computes
+            // its drop masks where they are used instead of keeping them live
+            // across the loop
+            asm volatile("" : "+s"(j0));
+            pre_prologue<D>(s, sel, sel ? tile_bits(j0, lim, false, 0u) : 0u, w);
+        };
+        auto b0 = make_bias(0, q0, stage(0));
+        f32x16 sA = pre_qk<D>(stage(0), w, b0), sB = {};
         auto step = [&](auto kc, int i) {
             constexpr int K = decltype(kc)::value;
-            char *stc = s_tile[K];
-            char *stn = s_tile[(K + 1) % kPreStages];
-            char *sts = s_tile[(K + 2) % kPreStages];
+            char *stc = stage(K);
+            char *stn = stage((K + 1) % kPreStages);
+            char *sts = stage((K + 2) % kPreStages);
             f32x16 &sc = (K & 1) ? sB : sA;
             f32x16 &sn = (K & 1) ? sA : sB;
             PreStage &ring = (K & 1) ? ringB : ringA;
@@ -386,22 +541,10 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char (*
             PrePages &pgn = (K & 1) ? pgA : pgB;  // receives the page ids of tile i+5
             int q6 = 0;
             if constexpr (MASKED) q6 = __builtin_amdgcn_readfirstlane(lv);
-            const int tc = tile_at(i, q0), t2 = tile_at(i + 2, q2), t4 = tile_at(i + 4, q4),
-                      t5 = tile_at(i + 5, q5);
-            {
-                const int j0 = 32 * tc;
-                bool full;
-                uint32_t bits = 0u;
-                if constexpr (MASKED) {
-                    full = q0 < 0 && j0 + 32 <= kv.eff;  // bit 31: every slot allowed for every row
-                    if (!full) bits = tile_bits(j0, lim, true, *reinterpret_cast<const uint32_t *>(stc + cp.mw_lds));
-                } else {
-                    full = j0 + 32 <= lmin_w;
-                    if (!full) bits = tile_bits(j0, lim, false, 0u);
-                }
-                pre_prologue<D>(sc, full, bits, w);
-            }
-            pre_main<D>(stc, stn, sc, sn, w, [&](int k) {
+            const int t2 = tile_at(i + 2, q2), t4 = tile_at(i + 4, q4), t5 = tile_at(i + 5, q5);
+            prologue(i, q0, sc);
+            auto bias = make_bias(i + 1, q1, stn);
+            pre_main<D>(stc, stn, sc, sn, w, bias, [&](int k) {
                 if (k == 0) {
                     // list entry and page ids first: the data loads then wait
                     // only on loads issued one step earlier, never the newest
@@ -452,13 +595,13 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char (*
 // rows); wave w owns query head g*G + w%G for the 32 rows at 32*(w/G).
 template <int D, int G>
 __global__ void __launch_bounds__(kPreThreads) prefill_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) char s_tile[kPreStages][PreLds<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char s_lds[PreLds<D>::TOTAL];
     __shared__ int s_lmax[kPreWaves];
     const int4 it = a.pre_items[blockIdx.x];
     if (it.x < 0) return;
     const bool masked = a.mask_off && a.mask_off[it.x + 1] > a.mask_off[it.x];  // workgroup-uniform
-    if (masked) prefill_item<D, G, true>(a, it, s_tile, s_lmax);
-    else prefill_item<D, G, false>(a, it, s_tile, s_lmax);
+    if (masked) prefill_item<D, G, true>(a, it, s_lds, s_lmax);
+    else prefill_item<D, G, false>(a, it, s_lds, s_lmax);
 }
 
 }  // namespace fpk
