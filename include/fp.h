@@ -122,7 +122,9 @@ typedef struct fp_mask {
  * Results do not depend on it beyond fp rounding order.
  */
 typedef struct fp_tuning {
-    int32_t decode_split_slots;       /* KV slots per decode work item, multiple of 32 (0 = default) */
+    int32_t decode_split_slots;       /* KV slots per decode work item, multiple of 32; 0: the
+                                         largest of 4096/2048/1024/512 that gives each resident
+                                         decode workgroup of the device about two items      */
     int32_t reserved[7];              /* must be zero                                          */
     hipEvent_t attn_begin;            /* nullable: recorded on the stream right before the
                                          attention kernels (prefill and decode)              */

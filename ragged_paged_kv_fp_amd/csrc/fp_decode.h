@@ -27,14 +27,20 @@ constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kLdsRow = 68;  // padded row of 64 floats: rows land on different LDS banks
 
+// A tile's K/V as loaded from the pool. The K rows are read as whole
+// contiguous 1 KB runs of the pages (every load instruction covers complete
+// cache lines, so the loads can be non-temporal) and staged through a small
+// per-wave LDS buffer into the MFMA fragment layout; the V^T fragments are
+// already contiguous runs and are loaded directly.
 template <int D>
 struct KvFrags {
-    uint4 k[D / 16];
+    uint4 k[D / 16];  // raw K: run u holds tile rows u*(512/D) .. of this lane's 16-byte column
     uint4 v[D / 16];
 };
 
 struct TilePages {
-    int64_t k, v0, v1;
+    int kp;          // lane l: physical page of the tile's (l & 3)-th page (raw K runs)
+    int64_t v0, v1;  // physical pages of this lane's V^T fragments
 };
 
 // Keep bf16 elements [0, nv) of an 8-element fragment (slots at or past kv_len
@@ -46,79 +52,61 @@ __device__ __forceinline__ uint4 keep_first(uint4 v, int nv) {
     return make_uint4(v.x & mk[0], v.y & mk[1], v.z & mk[2], v.w & mk[3]);
 }
 
-// Physical pages of the 8-slot groups this lane loads for the tile at j0
+// Physical pages for the tile at j0: the tile's pages for the raw K runs (one
+// per lane, indexed by lane & 3) and the pages of this lane's V^T slot groups
 // (slot groups at or past kv_len read the lane's first page instead: every
 // load stays branch-free and in bounds).
 template <int NC>
 __device__ __forceinline__ TilePages tile_pages(const KvView &kv, int j0) {
     const int l = lane_id();
-    int kg, vg0, vg1;
+    int vg0, vg1;
     if (NC == 16) {
-        const int m = l & 15;
-        kg = j0 + 8 * (m >> 2);
         vg0 = j0 + 8 * (l >> 4);
         vg1 = vg0;
     } else {
-        const int n = l & 31;
-        kg = j0 + 16 * (n >> 4) + 8 * ((n >> 2) & 1);
         vg0 = j0 + 8 * (l >> 5);
         vg1 = vg0 + 16;
     }
     TilePages tp;
-    tp.k = page_of(kv, (kg < kv.eff ? kg : 0) >> kv.pshift);
+    const int lastpg = kv.eff > 0 ? (kv.eff - 1) >> kv.pshift : 0;
+    tp.kp = (int)page_of(kv, min((j0 >> kv.pshift) + (l & 3), lastpg));
     tp.v0 = page_of(kv, (vg0 < kv.eff ? vg0 : 0) >> kv.pshift);
     tp.v1 = NC == 32 ? page_of(kv, (vg1 < kv.eff ? vg1 : 0) >> kv.pshift) : tp.v0;
     return tp;
 }
 
-// K rows of the S^T = K * Q^T operand and V^T rows of the O^T = V^T * P^T operand.
-//  NC=16: lane (q = l/16, m = l%16). K row m of M-block b is slot 8(m/4) + 4b + m%4,
-//         d in [q D/4, (q+1) D/4); V^T row d = 16 db + m, slots 8q .. 8q+7.
-//         Then S^T register i of M-block b is slot 8q + 4b + i: exactly the
-//         k index 8q + 4b + i the P^T operand needs.
-//  NC=32: lane (h = l/32, n = l%32). K row n is slot kslot_of_row(n),
-//         d in [h D/2, (h+1) D/2); V^T row d = 32 db + n, slots 16 t + 8h .. +7.
+// Raw K runs and V^T fragments of the tile at j0 (all loads non-temporal: the
+// decode pass reads every KV byte once).
+//  K: run u covers tile rows u*(512/D) .. u*(512/D) + 512/D - 1, lane l takes
+//     row u*(512/D) + l/(D/8), 16-byte column l % (D/8); a run never crosses a
+//     page (P >= 8 >= 512/D rows), so its page is one wave-uniform value.
+//  V^T rows of the O^T = V^T * P^T operand:
+//  NC=16: lane (q = l/16, m = l%16): V^T row d = 16 db + m, slots 8q .. 8q+7.
+//  NC=32: lane (h = l/32, n = l%32): V^T row d = 32 db + n, slots 16 t + 8h .. +7.
 template <int D, int NC>
 __device__ __forceinline__ void tile_load(const KvView &kv, int j0, const TilePages &tp, KvFrags<D> &f) {
+    constexpr int RPR = 512 / D;  // tile rows per run
+    constexpr int LPR = D / 8;    // lanes per row
     const int l = lane_id();
+    const int64_t kcol = (int64_t)kv.g * kv.P * D + 8 * (l % LPR);
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+        const int r = u * RPR + l / LPR;
+        const int64_t page = __builtin_amdgcn_readlane(tp.kp, (u * RPR) >> kv.pshift);
+        f.k[u] = load_nt(kv.kbase + page * kv.page_elems + kcol + (int64_t)(r & kv.pmask) * D);
+    }
     const int64_t vbase = kv.vblock + (int64_t)kv.g * D * kv.P;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
     if (NC == 16) {
-        constexpr int KS = D / 32;
         const int m = l & 15, q = l >> 4;
-        const int kg = j0 + 8 * (m >> 2);
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int ks = kg + 4 * b + (m & 3);
-            const bool ok = ks < kv.eff;
-            const int kc = ok ? ks : 0;
-            const uint4 *src = reinterpret_cast<const uint4 *>(
-                kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (kc & kv.pmask)) * D + q * (D / 4));
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const uint4 v = src[s];
-                f.k[b * KS + s] = ok ? v : zero;
-            }
-        }
         const int vg = j0 + 8 * q;
         const int vc = vg < kv.eff ? vg : 0;
         const uint16_t *vb = kv.kbase + tp.v0 * kv.page_elems + vbase + (vc & kv.pmask);
         const int nv = vg < kv.eff ? kv.eff - vg : 0;
 #pragma unroll
         for (int db = 0; db < D / 16; ++db)
-            f.v[db] = keep_first(*reinterpret_cast<const uint4 *>(vb + (int64_t)(16 * db + m) * kv.P), nv);
+            f.v[db] = keep_first(load_nt(vb + (int64_t)(16 * db + m) * kv.P), nv);
     } else {
         const int n = l & 31, h = l >> 5;
-        const int ks = j0 + kslot_of_row(n);
-        const bool ok = ks < kv.eff;
-        const int kc = ok ? ks : 0;
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            kv.kbase + tp.k * kv.page_elems + ((int64_t)kv.g * kv.P + (kc & kv.pmask)) * D + h * (D / 2));
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const uint4 v = src[s];
-            f.k[s] = ok ? v : zero;
-        }
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
             const int vs = j0 + 16 * t2 + 8 * h;
@@ -127,8 +115,45 @@ __device__ __forceinline__ void tile_load(const KvView &kv, int j0, const TilePa
             const int nv = vs < kv.eff ? kv.eff - vs : 0;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
-                f.v[2 * db + t2] = keep_first(*reinterpret_cast<const uint4 *>(vb + (int64_t)(32 * db + n) * kv.P), nv);
+                f.v[2 * db + t2] = keep_first(load_nt(vb + (int64_t)(32 * db + n) * kv.P), nv);
         }
+    }
+}
+
+// Per-wave K staging buffer: 32 tile rows of D bf16, rows padded by 16 bytes.
+template <int D>
+struct DecLds {
+    static constexpr int KROW = 2 * D + 16;
+    static constexpr int BYTES = 32 * KROW;
+};
+
+// Writes the raw K runs to the wave's buffer and reads back the K operand
+// fragments of S^T = K * Q^T (rows as the MFMA shape expects them):
+//  NC=16: lane (q, m): K row 8(m/4) + 4b + m%4 of M-block b, d in [q D/4, (q+1) D/4).
+//  NC=32: lane (h, n): K row kslot_of_row(n), d in [h D/2, (h+1) D/2).
+// Slots at or past kv_len keep whatever the pool holds: their scores are
+// dropped by the softmax select.
+template <int D, int NC>
+__device__ __forceinline__ void stage_k(const KvFrags<D> &f, char *buf, uint4 (&kf)[D / 16]) {
+    constexpr int RPR = 512 / D, LPR = D / 8, KROW = DecLds<D>::KROW;
+    const int l = lane_id();
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u)
+        *reinterpret_cast<uint4 *>(buf + (u * RPR + l / LPR) * KROW + 16 * (l % LPR)) = f.k[u];
+    if (NC == 16) {
+        constexpr int KS = D / 32;
+        const int m = l & 15, q = l >> 4;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const char *row = buf + (8 * (m >> 2) + 4 * b + (m & 3)) * KROW + q * (D / 2);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) kf[b * KS + s] = *reinterpret_cast<const uint4 *>(row + 16 * s);
+        }
+    } else {
+        const int n = l & 31, h = l >> 5;
+        const char *row = buf + kslot_of_row(n) * KROW + h * D;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) kf[s] = *reinterpret_cast<const uint4 *>(row + 16 * s);
     }
 }
 
@@ -150,15 +175,17 @@ __device__ __forceinline__ void softmax_update(float mt, float &m_run, float &m_
 }
 
 template <int D>
-__device__ __forceinline__ void tile_compute(const KvFrags<D> &f, int j0, int lim, uint32_t mw, bool masked,
-                                             DecState<D, 16> &w) {
+__device__ __forceinline__ void tile_compute(const KvFrags<D> &f, char *kbuf, int j0, int lim, uint32_t mw,
+                                             bool masked, DecState<D, 16> &w) {
     constexpr int KS = D / 32;
     const int q = lane_id() >> 4;
+    uint4 kf[D / 16];
+    stage_k<D, 16>(f, kbuf, kf);
     f32x4 s0 = {}, s1 = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        s0 = mfma16(f.k[s], w.qf[s], s0);
-        s1 = mfma16(f.k[KS + s], w.qf[s], s1);
+        s0 = mfma16(kf[s], w.qf[s], s0);
+        s1 = mfma16(kf[KS + s], w.qf[s], s1);
     }
     float sv[8];
     float mt = kNegInf;
@@ -193,12 +220,14 @@ __device__ __forceinline__ void tile_compute(const KvFrags<D> &f, int j0, int li
 }
 
 template <int D>
-__device__ __forceinline__ void tile_compute(const KvFrags<D> &f, int j0, int lim, uint32_t mw, bool masked,
-                                             DecState<D, 32> &w) {
+__device__ __forceinline__ void tile_compute(const KvFrags<D> &f, char *kbuf, int j0, int lim, uint32_t mw,
+                                             bool masked, DecState<D, 32> &w) {
     const int h = lane_id() >> 5;
+    uint4 kf[D / 16];
+    stage_k<D, 32>(f, kbuf, kf);
     f32x16 sacc = {};
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) sacc = mfma32(f.k[s], w.qf[s], sacc);
+    for (int s = 0; s < D / 16; ++s) sacc = mfma32(kf[s], w.qf[s], sacc);
     float sv[16];
     float mt = kNegInf;
 #pragma unroll
@@ -264,6 +293,7 @@ __global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(A
     __shared__ float s_ml[kDecWaves][2][32];
     __shared__ float s_fin[2][32];
     __shared__ float s_o[kDecWaves][NC][kLdsRow];
+    __shared__ __attribute__((aligned(16))) char s_k[kDecWaves][DecLds<D>::BYTES];
 
     const int item = blockIdx.x;
     const int4 it = a.dec_items[item];
@@ -325,12 +355,12 @@ __global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(A
             tile_load<D, NC>(kv, clampt(cur + kStep), pb, fb);
             pb = tile_pages<NC>(kv, clampt(cur + 3 * kStep));
             uint32_t mw = (masked && colv && (cur >> 5) < wpr) ? mrow[cur >> 5] : 0u;
-            tile_compute<D>(fa, cur, lim, mw, masked, w);
+            tile_compute<D>(fa, s_k[wv], cur, lim, mw, masked, w);
             if (cur + kStep > last) break;
             tile_load<D, NC>(kv, clampt(cur + 2 * kStep), pa, fa);
             pa = tile_pages<NC>(kv, clampt(cur + 4 * kStep));
             mw = (masked && colv && ((cur + kStep) >> 5) < wpr) ? mrow[(cur + kStep) >> 5] : 0u;
-            tile_compute<D>(fb, cur + kStep, lim, mw, masked, w);
+            tile_compute<D>(fb, s_k[wv], cur + kStep, lim, mw, masked, w);
             if (cur + 2 * kStep > last) break;
             cur += 2 * kStep;
         }

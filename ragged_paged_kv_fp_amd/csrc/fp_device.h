@@ -16,6 +16,16 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// 16-byte load marked non-temporal: data read once per pass (the decode KV
+// stream) bypasses the cache reuse policy, which lets HBM reads run closer to
+// peak.
+__device__ __forceinline__ uint4 load_nt(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

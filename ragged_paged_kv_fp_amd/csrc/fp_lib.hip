@@ -15,7 +15,26 @@ namespace {
 
 using namespace fpk;
 
-constexpr int kDefaultSplit = 1024;
+// Decode split sizes the default plan chooses from, largest first: the largest
+// that still gives every resident decode workgroup slot on the device about
+// two work items. Longer splits pay the per-item start (page ids, then the
+// first KV loads: two dependent memory round trips) and the split merge
+// fewer times; too few items leave compute units idle at the end.
+constexpr int kSplitChoices[] = {4096, 2048, 1024, 512};
+constexpr double kItemsPerSlot = 1.7;
+
+// Compute units of the current device, queried once per device.
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -78,13 +97,26 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
     const int G = Hq / pool->num_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8) return FP_ERR_UNSUPPORTED;
     if (geom->num_lanes > kMaxLanes) return FP_ERR_UNSUPPORTED;
-    int split = kDefaultSplit;
+    int split = 0;
     if (tun) {
         for (int i = 0; i < 7; ++i)
             if (tun->reserved[i]) return FP_ERR_SHAPE;
         if (tun->decode_split_slots) {
             if (tun->decode_split_slots < 32 || tun->decode_split_slots % 32) return FP_ERR_SHAPE;
             split = tun->decode_split_slots;
+        }
+    }
+    if (split == 0) {
+        const double slots = 2.0 * device_cus();  // decode workgroups resident at once (about two per CU)
+        for (const int cand : kSplitChoices) {
+            split = cand;
+            int64_t items = 0;
+            for (int l = 0; l < geom->num_lanes; ++l) {
+                const int n = geom->indptr_host[l + 1] - geom->indptr_host[l];
+                const int cap = (pool->page_indptr_host[l + 1] - pool->page_indptr_host[l]) * pool->page_size;
+                if (n > 0 && n * G <= kDecodeCols) items += (int64_t)pool->num_kv_heads * (cap > 0 ? (cap + cand - 1) / cand : 1);
+            }
+            if ((double)items >= kItemsPerSlot * slots) break;
         }
     }
     Plan p;
