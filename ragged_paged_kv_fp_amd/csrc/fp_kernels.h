@@ -10,7 +10,7 @@
 
 namespace fpk {
 
-// Per-lane plan record written by plan_kernel.
+// Per-lane plan record written by the plan (prep_kernel, block 0).
 struct LaneInfo {
     int dec_off;   // first decode work item of the lane, -1 if the lane is not a decode lane
     int nsplit;    // decode KV splits of the lane (items per KV head)
@@ -41,15 +41,16 @@ struct AppendArgs {
     RopeFreqs freqs;
 };
 
-constexpr int kAppendRows = 16;  // most consecutive rows one append workgroup writes
+constexpr int kAppendRows = 16;      // most consecutive rows one append workgroup writes
+constexpr int kAppendVWords = 8320;  // LDS words staging V: 8 heads of 16 rows at head dim 128
 
 // Rows per workgroup and head chunks per (row, RoPE pair) for the row-grouped
 // kernels: many rows share a workgroup when there are enough rows to fill the
 // chip, few rows get all their heads spread over the workgroup's threads.
-__host__ __forceinline__ void row_grouping(int64_t N, int pairs, int heads, int *rows, int *chunks) {
+__host__ __forceinline__ void row_grouping(int64_t N, int pairs, int heads, int *rows, int *chunks, int threads = 256) {
     int r = 1;
     while (r < kAppendRows && N / (2 * r) >= 1024) r *= 2;
-    int c = 256 / (r * pairs);
+    int c = threads / (r * pairs);
     c = c < 1 ? 1 : (c > heads ? heads : c);
     *rows = r;
     *chunks = c;
@@ -59,13 +60,13 @@ __host__ __forceinline__ void row_grouping(int64_t N, int pairs, int heads, int 
 // (lane, slot, freeze, page); K is rotated by one thread per (row, RoPE pair,
 // head chunk) looping over the chunk's KV heads, which share the angle, each 4-byte pair store
 // coalescing with its neighbours in the K row; V goes through LDS one head at
-// a time so that consecutive threads store consecutive rows of one V^T row:
+// a group of heads at a time so that consecutive threads store consecutive rows of one V^T row:
 // the rows of a prefill chunk sit in consecutive slots of a page, and their
 // 2-byte stores then merge into one contiguous segment per V^T row.
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     __shared__ int64_t s_base[kAppendRows];  // element offset of the row's page, -1: row not written
     __shared__ int s_off[kAppendRows];
-    __shared__ uint32_t s_vw[kAppendRows][kMaxPairs + 1];  // one head's V of the rows, padded rows
+    __shared__ uint32_t s_vw[kAppendVWords];  // V of the rows for a group of heads, padded head rows
     const int64_t r0 = (int64_t)blockIdx.x * a.rows;
     const int nr = (int)(a.N - r0 < a.rows ? a.N - r0 : a.rows);
     const int tid = threadIdx.x;
@@ -117,18 +118,26 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
         }
     }
     const int64_t vblock = (int64_t)a.H * a.P * a.D;  // V block [H][D][P] follows the K block
-    for (int h = 0; h < a.H; ++h) {
-        for (int e = tid; e < nr * pairs; e += blockDim.x) {
-            const int j = e / pairs, i = e - j * pairs;
-            s_vw[j][i] = reinterpret_cast<const uint32_t *>(a.v + ((r0 + j) * a.H + h) * a.D)[i];
+    // V goes through LDS a group of heads at a time (all heads of a decode
+    // row in one round); stores then run with the row index fastest.
+    const int hg = max(1, min(a.H, kAppendVWords / (a.rows * (pairs + 1))));
+    for (int h0 = 0; h0 < a.H; h0 += hg) {
+        const int hn = min(hg, a.H - h0);
+        for (int e = tid; e < nr * hn * pairs; e += blockDim.x) {
+            const int j = e / (hn * pairs), rem = e - j * hn * pairs;
+            const int hh = rem / pairs, i = rem - hh * pairs;
+            s_vw[(j * hn + hh) * (pairs + 1) + i] =
+                reinterpret_cast<const uint32_t *>(a.v + ((r0 + j) * a.H + h0 + hh) * a.D)[i];
         }
         __syncthreads();
-        for (int e = tid; e < a.rows * a.D; e += blockDim.x) {
-            const int j = e % a.rows, d = e / a.rows;
+        for (int e = tid; e < hn * a.D * a.rows; e += blockDim.x) {
+            const int j = e % a.rows, dh = e / a.rows;
+            const int hh = dh / a.D, d = dh - hh * a.D;
             const int64_t base = s_base[j];
             if (j < nr && base >= 0) {
-                const uint32_t w = s_vw[j][d >> 1];
-                a.pool[base + vblock + ((int64_t)h * a.D + d) * a.P + s_off[j]] = (uint16_t)((d & 1) ? (w >> 16) : (w & 0xFFFFu));
+                const uint32_t w = s_vw[(j * hn + hh) * (pairs + 1) + (d >> 1)];
+                a.pool[base + vblock + ((int64_t)(h0 + hh) * a.D + d) * a.P + s_off[j]] =
+                    (uint16_t)((d & 1) ? (w >> 16) : (w & 0xFFFFu));
             }
         }
         __syncthreads();
@@ -229,8 +238,8 @@ struct RopeQArgs {
 // looping over the chunk's query heads, which share the angle; the 4-byte pair
 // loads and stores of a wave cover whole Q rows. Output is the rotated,
 // prescaled Q in bf16, same [N][Hq][D] layout as q.
-__global__ void __launch_bounds__(256) rope_q_kernel(RopeQArgs a) {
-    const int64_t r0 = (int64_t)blockIdx.x * a.rows;
+__device__ __forceinline__ void rope_q_body(const RopeQArgs &a, int block) {
+    const int64_t r0 = (int64_t)block * a.rows;
     const int nr = (int)(a.N - r0 < a.rows ? a.N - r0 : a.rows);
     const int pairs = a.D >> 1;
     const int hpc = (a.Hq + a.chunks - 1) / a.chunks;
@@ -319,7 +328,7 @@ __device__ __forceinline__ int upper_lane(const int *offs, int L, int idx) {
 
 // Single workgroup: per-lane classification (decode if all rows x GQA heads fit
 // one MFMA tile, prefill otherwise), prefix offsets, and the work-item lists.
-__global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
+__device__ __forceinline__ void plan_body(const PlanArgs &a) {
     __shared__ int s_dec[kMaxLanes + 1];
     __shared__ int s_pre[kMaxLanes + 1];
     __shared__ int s_scan[3][kPlanThreads];
@@ -406,6 +415,13 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
         }
         a.pre_items[idx] = it;
     }
+}
+
+// Plan and Q rotation in one launch (they read only the inputs): block 0
+// builds the plan, blocks 1.. rotate the rows of Q.
+__global__ void __launch_bounds__(kPlanThreads) prep_kernel(PlanArgs pa, RopeQArgs ra) {
+    if (blockIdx.x == 0) plan_body(pa);
+    else rope_q_body(ra, (int)blockIdx.x - 1);
 }
 
 // ============================================================================ mask summary

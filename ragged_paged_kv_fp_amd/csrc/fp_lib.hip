@@ -86,7 +86,7 @@ struct Plan {
     size_t total = 0;
 };
 
-// Shape-only plan: mirrors lane_counts() of plan_kernel from the host copies.
+// Shape-only plan: mirrors lane_counts() of the device plan from the host copies.
 int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *mask, int32_t Hq,
               const fp_tuning *tun, Plan *pl) {
     int rc = check_pool(pool);
@@ -262,8 +262,6 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
     pa.dec_items = dec_items;
     pa.pre_items = pre_items;
     pa.status = status;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, pa);
-    if ((rc = launch_ok())) return rc;
 
     RopeQArgs ra;
     ra.q = static_cast<const uint16_t *>(q);
@@ -274,8 +272,9 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
     ra.D = p.D;
     ra.qscale = (double)sm_scale * 1.4426950408889634;  // log2(e)
     ra.freqs = rope_freqs(rope_theta, p.D);
-    row_grouping(p.N, p.D / 2, p.Hq, &ra.rows, &ra.chunks);
-    hipLaunchKernelGGL(rope_q_kernel, dim3((unsigned)((p.N + ra.rows - 1) / ra.rows)), dim3(256), 0, stream, ra);
+    row_grouping(p.N, p.D / 2, p.Hq, &ra.rows, &ra.chunks, kPlanThreads);
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(1 + (p.N + ra.rows - 1) / ra.rows)), dim3(kPlanThreads), 0, stream,
+                       pa, ra);
     if ((rc = launch_ok())) return rc;
 
     AttnArgs a;
