@@ -178,6 +178,7 @@ __device__ __forceinline__ uint32_t neg_m2(const PreWave<D> &w) {
 // kv_len can hold stale K (even NaN), so the one tile that crosses kv_len
 // still drops them with a select.
 struct RowBias {
+    static constexpr int kDone = 0;  // tail segment after which the scores are complete
     uint32_t a0, negm2;
     __device__ __forceinline__ void fetch() {}
     __device__ __forceinline__ void load(int) {}
@@ -190,6 +191,7 @@ struct RowBias {
 // The two MFMAs of MaskBias run one after the other through one operand set
 // (load(k), build(), apply(acc, k)), which keeps eight registers free.
 struct MaskBias {
+    static constexpr int kDone = 1;  // tail segment after which the scores are complete
     const char *lds;  // LDS base holding the keep-mask table and the A operands
     const uint32_t *mw;  // the row's mask word for the tile (LDS)
     uint32_t lm;      // slots below the row's limit, or all ones when the tile is fully allowed
@@ -253,14 +255,15 @@ __device__ __forceinline__ f32x16 pre_qk(const char *stage, const PreWave<D> &w,
     return acc;
 }
 
-// Softmax prologue of one tile. The scores arrive as s - m (the shift was
-// added by the bias MFMA). With sel, slots outside vbits are first set to
-// -inf. Then the column max over both lane halves; the running max moves
-// (rounded to bf16, so -m stays exact in the next bias) the first time the
-// column sees an allowed slot and whenever the max grows by more than
-// 2^kRescaleSlack, rescaling O and l and re-shifting the scores.
-template <int D>
-__device__ __forceinline__ void pre_prologue(f32x16 &s, bool sel, uint32_t vbits, PreWave<D> &w) {
+// Softmax prologue of one tile, in two parts. pre_max: the scores arrive as
+// s - m (the shift was added by the bias MFMA); with sel, slots outside vbits
+// are first set to -inf; returns the column max over both lane halves.
+// pre_rescale: the running max moves (rounded to bf16, so -m stays exact in
+// the next bias) the first time the column sees an allowed slot and whenever
+// the max grows by more than 2^kRescaleSlack, rescaling O and l and
+// re-shifting the scores. It must follow every P*V and denominator update of
+// the previous tile.
+__device__ __forceinline__ float pre_max(f32x16 &s, bool sel, uint32_t vbits) {
     const int h = lane_id() >> 5;
     if (sel) {
         const uint32_t vb = vbits >> (8 * h);  // register i holds tile slot 16(i/8) + 8h + i%8
@@ -271,14 +274,17 @@ __device__ __forceinline__ void pre_prologue(f32x16 &s, bool sel, uint32_t vbits
             s[i] = __uint_as_float((__float_as_uint(s[i]) & keep) | (0xFF800000u & ~keep));
         }
     }
-    float mt = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int i = 2; i < 16; i += 2) mt = fmaxf(fmaxf(mt, s[i]), s[i + 1]);
-    {
-        // the two lane halves hold the two halves of the column's 32 slots
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
+    // a tree of three-input maxima keeps the dependent chain short
+    auto mx3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
+    float mt = fmaxf(mx3(mx3(s[0], s[1], s[2]), mx3(s[3], s[4], s[5]), mx3(s[6], s[7], s[8])),
+                     mx3(mx3(s[9], s[10], s[11]), mx3(s[12], s[13], s[14]), s[15]));
+    // the two lane halves hold the two halves of the column's 32 slots
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+template <int D>
+__device__ __forceinline__ void pre_rescale(f32x16 &s, float mt, PreWave<D> &w) {
     const bool valid = mt > kNoSlot;
     const bool grow = valid && (!w.seen || mt > kRescaleSlack);
     if (__any(grow)) {
@@ -305,9 +311,9 @@ __device__ __forceinline__ void pre_prologue(f32x16 &s, bool sel, uint32_t vbits
 // with the tile copy (list entry and page ids, LDS store, prefetch loads:
 // copy(k) is called for k = 0, 1, 2). The denominator sums the same bf16
 // weights the numerator uses.
-template <int D, class Bias, class Copy>
+template <int D, class Bias, class Copy, class Next>
 __device__ __forceinline__ void pre_main(const char *stc, const char *stn, const f32x16 &sc, f32x16 &sn,
-                                         PreWave<D> &w, Bias &bias, Copy &&copy) {
+                                         PreWave<D> &w, Bias &bias, Copy &&copy, Next &&next) {
     constexpr int NQK = D / 16;          // QK^T MFMAs of the chain
     constexpr int NDB = D / 32;          // 32-row blocks of O^T
     constexpr int PPS = 8 / NQK;         // weight pairs packed per chain segment
@@ -352,15 +358,23 @@ __device__ __forceinline__ void pre_main(const char *stc, const char *stn, const
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         w.o[db] = mfma32(vf[db][1], pb1, w.o[db]);
-        // bias MFMA 0 after the first P*V of the tail, MFMA 1 at its end
+        // the bias MFMAs close the chain with the first P*V of the tail (both
+        // kinds of lane add -m last, so an all-allowed bitmap reproduces the
+        // causal path bit for bit); then the next tile's scores are complete
+        // and its max is taken here, the dependent VALU chain overlapping the
+        // P*V MFMAs still in flight
         if (db == 0) {
             bias.build();
             acc = bias.apply(acc, 0);
             bias.load(1);
         }
-        if (db == NDB - 1) {
+        if (db == 1 && Bias::kDone >= 1) {
             bias.build();
             acc = bias.apply(acc, 1);
+        }
+        if (db == (Bias::kDone + 1 < NDB - 1 ? Bias::kDone + 1 : NDB - 1)) {
+            sn = acc;
+            next(0);
         }
 #pragma unroll
         for (int q = db * (8 / NDB); q < (db + 1) * (8 / NDB); ++q)
@@ -373,7 +387,7 @@ __device__ __forceinline__ void pre_main(const char *stc, const char *stn, const
 #pragma unroll
         for (int k = NDB; k < 3; ++k) copy(k);
     }
-    sn = acc;
+    next(1);
 }
 
 // Allowed slots of tile j0 for this lane's column as a 32-bit mask.
@@ -515,7 +529,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char *l
         // Softmax prologue of the tile of step i: slots are dropped by a select
         // only where the bias cannot do it (stale K past kv_len) or, on causal
         // lanes, where the tile crosses a row's causal limit.
-        auto prologue = [&](int i, int qe, f32x16 &s) {
+        auto tile_max = [&](int i, int qe, f32x16 &s) {
             const int t = tile_at(i, qe);
             int j0 = 32 * t;
             bool sel;
@@ -525,10 +539,11 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char *l
             // its drop masks where they are used instead of keeping them live
             // across the loop
             asm volatile("" : "+s"(j0));
-            pre_prologue<D>(s, sel, sel ? tile_bits(j0, lim, false, 0u) : 0u, w);
+            return pre_max(s, sel, sel ? tile_bits(j0, lim, false, 0u) : 0u);
         };
         auto b0 = make_bias(0, q0, stage(0));
         f32x16 sA = pre_qk<D>(stage(0), w, b0), sB = {};
+        pre_rescale<D>(sA, tile_max(0, q0, sA), w);
         auto step = [&](auto kc, int i) {
             constexpr int K = decltype(kc)::value;
             char *stc = stage(K);
@@ -542,8 +557,8 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char *l
             int q6 = 0;
             if constexpr (MASKED) q6 = __builtin_amdgcn_readfirstlane(lv);
             const int t2 = tile_at(i + 2, q2), t4 = tile_at(i + 4, q4), t5 = tile_at(i + 5, q5);
-            prologue(i, q0, sc);
             auto bias = make_bias(i + 1, q1, stn);
+            float mt_next = 0.0f;
             pre_main<D>(stc, stn, sc, sn, w, bias, [&](int k) {
                 if (k == 0) {
                     // list entry and page ids first: the data loads then wait
@@ -553,6 +568,11 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char *l
                 }
                 if (k == 1) pre_store<D, MASKED>(cp, ring, sts, t2);
                 if (k == 2) pre_data<D, MASKED>(cp, t4, pgc, ring, mrow, wpr);
+            }, [&](int part) {
+                if (i + 1 < T) {  // workgroup-uniform
+                    if (part == 0) mt_next = tile_max(i + 1, q1, sn);
+                    else pre_rescale<D>(sn, mt_next, w);
+                }
             });
             __syncthreads();
             if constexpr (MASKED) {
