@@ -87,7 +87,46 @@ def work(wl):
     flops_all = 4.0 * wl.d * wl.H_q * float(pairs.sum())
     flops_prefill = 4.0 * wl.d * wl.H_q * float(pairs[~decode[lane_of]].sum()) if len(pairs) else 0.0
     return dict(kv_bytes_decode=kv_bytes, kv_bytes_all=int((eff * 2 * wl.H_kv * wl.d * 2).sum()),
-                flops=flops_all, flops_prefill=flops_prefill, pairs=int(pairs.sum()))
+                flops=flops_all, flops_prefill=flops_prefill, pairs=int(pairs.sum()),
+                flops_prefill_executed=executed_prefill_flops(wl))
+
+
+def executed_prefill_flops(wl) -> float:
+    """MFMA flops the prefill kernel issues: each work item (one KV head, a block
+    of 256/G rows, all G query heads) runs QK^T and P*V over every 32-slot tile
+    it visits (causal lanes: up to the block's furthest row limit; masked lanes:
+    the tiles where some row of the block has an allowed slot), for every row
+    of the block, padded rows included."""
+    st = wl.step
+    G = wl.H_q // wl.H_kv
+    RB = 256 // G
+    cap = wl.capacity()
+    tot_tiles_rows = 0
+    for lane in range(wl.num_lanes):
+        r0, r1 = int(st.indptr[lane]), int(st.indptr[lane + 1])
+        n = r1 - r0
+        if n == 0 or n * G <= 32:
+            continue
+        eff = min(max(int(st.kv_len[lane]), 0), int(cap[lane]))
+        masked = wl.mask_bits is not None and wl.mask_word_offset[lane + 1] > wl.mask_word_offset[lane]
+        if masked:
+            o0, o1 = int(wl.mask_word_offset[lane]), int(wl.mask_word_offset[lane + 1])
+            wpr = (o1 - o0) // n
+            words = wl.mask_bits[o0:o1].reshape(n, wpr)
+            ntiles = min((eff + 31) // 32, wpr)
+            valid = np.full(ntiles, 0xFFFFFFFF, dtype=np.uint64)
+            if ntiles and eff % 32 and ntiles == (eff + 31) // 32:
+                valid[-1] = (1 << (eff % 32)) - 1
+        for b0 in range(0, n, RB):
+            b1 = min(n, b0 + RB)
+            if masked:
+                anyw = np.bitwise_or.reduce(words[b0:b1, :ntiles].astype(np.uint64), axis=0) & valid
+                t = int(np.count_nonzero(anyw))
+            else:
+                lim = np.minimum(st.slots[r0 + b0:r0 + b1].astype(np.int64) + 1, eff)
+                t = (int(lim.max()) + 31) // 32 if b1 > b0 else 0
+            tot_tiles_rows += t * RB
+    return 4.0 * wl.d * 32 * G * wl.H_kv * float(tot_tiles_rows)
 
 
 # --------------------------------------------------------------------------- HIP events
@@ -282,6 +321,7 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--split", type=int, default=None, help="decode KV slots per work item")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="config 2 only: skip the config 5 prefill measurement")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run 5 plain device copies of MIB MiB (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -320,41 +360,8 @@ def main(argv=None):
         print(json.dumps({"calib_copy_bytes": nbytes}), file=sys.stderr, flush=True)
         del src, dst
     cfg = args.config
-    wl = W.make_config(cfg, seed=args.seed, scale="full")
-    w = work(wl)
-    ds = runner.DeviceStep(wl, device="cuda", split=args.split)
-    ds.run_prefix()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = HipEvents()
+    wl, w, ms_step, attn_avg, host_ms = measure(W, runner, cfg, args.seed, args.split, args.steps, args.warmup)
     K, Wm = args.steps, args.warmup
-    pairs_ev = [(ev.create(), ev.create()) for _ in range(K)]
-
-    for _ in range(Wm):
-        ds.reset()
-        ds.step()
-    torch.cuda.synchronize()
-    ds.status.zero_()
-
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    h0 = time.perf_counter()
-    t_begin.record(stream)
-    for i in range(K):
-        ds.reset()
-        ds.step(events=pairs_ev[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    h1 = time.perf_counter()
-    total_ms = t_begin.elapsed_time(t_end)
-    attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs_ev]
-    status = int(ds.status.cpu()[0])
-    if status != 0:
-        print(f"warning: device status {status}", file=sys.stderr)
-
-    ms_step = total_ms / K
-    attn_avg = float(np.mean(attn_ms))
     if cfg == 5:
         unit, work_units, scale = "TFLOP/s", w["flops"], 1e12
         bound, peak, r_unit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
@@ -381,7 +388,7 @@ def main(argv=None):
         "config": {"workload": f"config {cfg}: " + WORKLOAD_TEXT[cfg], "seed": args.seed,
                    "lanes": wl.num_lanes, "rows": wl.step.num_rows, "kv_bytes_decode": w["kv_bytes_decode"],
                    "attn_flops": w["flops"], "attended_pairs": w["pairs"], "host_wall_ms_per_step":
-                   round((h1 - h0) * 1e3 / K, 4)},
+                   round(host_ms, 4)},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": r_unit,
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(cfg),
                      "kernel": "attention kernels (decode_kernel / prefill_kernel), HIP events per step",
@@ -389,13 +396,67 @@ def main(argv=None):
     }
     if cfg == 3:
         line["config"]["prefill_tflops_step"] = round(w["flops_prefill"] / (ms_step * 1e-3) / 1e12, 3)
+    if cfg == 5:
+        line["roofline"]["executed_frac"] = round(w["flops_prefill_executed"] / (attn_avg * 1e-3) / 1e12 / peak, 4)
+    if cfg == 2 and not args.no_prefill:
+        # the prefill half of the metric, on the long-context masked prefill wave
+        wl5, w5, ms5, attn5, _ = measure(W, runner, 5, args.seed, None, 5, 1)
+        alg = w5["flops"] / (attn5 * 1e-3) / 1e12
+        exe = w5["flops_prefill_executed"] / (attn5 * 1e-3) / 1e12
+        line["prefill"] = {"workload": "config 5: " + WORKLOAD_TEXT[5], "bound": "mfma", "unit": "TFLOP/s",
+                           "peak": BF16_PEAK_TFLOPS, "attn_ms": round(attn5, 4), "ms_per_step": round(ms5, 4),
+                           "achieved": round(alg, 2), "frac": round(alg / BF16_PEAK_TFLOPS, 4),
+                           "achieved_executed": round(exe, 2), "frac_executed": round(exe / BF16_PEAK_TFLOPS, 4),
+                           "algorithmic_flops": w5["flops"], "executed_flops": w5["flops_prefill_executed"],
+                           "traffic": measured_traffic(5), "steps": 5, "warmup": 1}
+        del wl5
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, cfg, unit)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def measure(W, runner, cfg, seed, split, K, Wm):
+    """Time K steps (after Wm warm-ups) of one configuration with inputs resident
+    in HBM: returns (workload, work, ms per step, attention-kernel ms per step
+    from HIP events on the launch stream, host wall ms per step)."""
+    import torch
+
+    wl = W.make_config(cfg, seed=seed, scale="full")
+    w = work(wl)
+    ds = runner.DeviceStep(wl, device="cuda", split=split)
+    ds.run_prefix()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = HipEvents()
+    pairs_ev = [(ev.create(), ev.create()) for _ in range(K)]
+    for _ in range(Wm):
+        ds.reset()
+        ds.step()
+    torch.cuda.synchronize()
+    ds.status.zero_()
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(K):
+        ds.reset()
+        ds.step(events=pairs_ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    h1 = time.perf_counter()
+    total_ms = t_begin.elapsed_time(t_end)
+    attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs_ev]
+    status = int(ds.status.cpu()[0])
+    if status != 0:
+        print(f"warning: device status {status} (config {cfg})", file=sys.stderr)
     for a, b in pairs_ev:
         ev.destroy(a)
         ev.destroy(b)
-    return 0
+    del ds
+    torch.cuda.empty_cache()
+    return wl, w, total_ms / K, float(np.mean(attn_ms)), (h1 - h0) * 1e3 / K
 
 
 if __name__ == "__main__":
