@@ -388,6 +388,7 @@ __global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(A
         s_fin[1][col] = L;
     }
     const bool single = li.nsplit <= 1;
+    const int64_t pidx = (int64_t)li.dec_off + (int64_t)g * li.nsplit + s0 / a.split;  // (lane, KV head, split)
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) {
         stage_o<D, NC>(w, c, scale, &s_o[wv][col][0]);
@@ -406,10 +407,10 @@ __global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(A
                 if (c == 0 && dl == 0 && a.lse)
                     a.lse[orow * a.Hq + ohead] = Lt > 0.0f ? (s_fin[0][n] + __log2f(Lt)) * 0.69314718055994531f : kNegInf;
             } else {
-                a.part_o[((int64_t)item * a.ncols_max + n) * D + 64 * c + dl] = acc;
+                a.part_o[(pidx * a.ncols_max + n) * D + 64 * c + dl] = acc;
                 if (c == 0 && dl == 0) {
-                    a.part_ml[(int64_t)item * 64 + n] = s_fin[0][n];
-                    a.part_ml[(int64_t)item * 64 + 32 + n] = Lt;
+                    a.part_ml[pidx * 64 + n] = s_fin[0][n];
+                    a.part_ml[pidx * 64 + 32 + n] = Lt;
                 }
             }
         }

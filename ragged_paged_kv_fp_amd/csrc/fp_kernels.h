@@ -331,49 +331,52 @@ __device__ __forceinline__ int upper_lane(const int *offs, int L, int idx) {
 __device__ __forceinline__ void plan_body(const PlanArgs &a) {
     __shared__ int s_dec[kMaxLanes + 1];
     __shared__ int s_pre[kMaxLanes + 1];
-    __shared__ int s_scan[3][kPlanThreads];
+    __shared__ int s_nd[kMaxLanes + 1];  // decode lanes before lane l
+    __shared__ int s_scan[4][kPlanThreads];
     __shared__ int s_bad;
     const int tid = threadIdx.x;
     if (tid == 0) s_bad = 0;
     const int per = (a.L + kPlanThreads - 1) / kPlanThreads;
     const int l0 = tid * per, l1 = min(a.L, l0 + per);
     int32_t st = 0;
-    int td = 0, tp = 0, ts = 0, tc = 0;
+    int td = 0, tp = 0, ts = 0, tc = 0, tn = 0;
     for (int l = l0; l < l1; ++l) {
         const LaneCounts c = lane_counts(a, l, &st);
-        td += c.dec; tp += c.pre; ts += c.sum;
+        td += c.dec; tp += c.pre; ts += c.sum; tn += c.dec ? 1 : 0;
         tc = max(tc, c.ncols);
         if (c.nsplit > 1 && !a.merge_host) tc = kDecodeCols + 1;  // forces the mismatch path
     }
     if (st) atomicOr(a.status, st);
     __syncthreads();
     if (tc > a.ncols_host) atomicOr(&s_bad, 1);
-    s_scan[0][tid] = td; s_scan[1][tid] = tp; s_scan[2][tid] = ts;
+    s_scan[0][tid] = td; s_scan[1][tid] = tp; s_scan[2][tid] = ts; s_scan[3][tid] = tn;
     __syncthreads();
     for (int o = 1; o < kPlanThreads; o <<= 1) {
-        int v0 = 0, v1 = 0, v2 = 0;
-        if (tid >= o) { v0 = s_scan[0][tid - o]; v1 = s_scan[1][tid - o]; v2 = s_scan[2][tid - o]; }
+        int v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+        if (tid >= o) { v0 = s_scan[0][tid - o]; v1 = s_scan[1][tid - o]; v2 = s_scan[2][tid - o]; v3 = s_scan[3][tid - o]; }
         __syncthreads();
-        s_scan[0][tid] += v0; s_scan[1][tid] += v1; s_scan[2][tid] += v2;
+        s_scan[0][tid] += v0; s_scan[1][tid] += v1; s_scan[2][tid] += v2; s_scan[3][tid] += v3;
         __syncthreads();
     }
-    int od = s_scan[0][tid] - td, op = s_scan[1][tid] - tp, os = s_scan[2][tid] - ts;
+    int od = s_scan[0][tid] - td, op = s_scan[1][tid] - tp, os = s_scan[2][tid] - ts, on = s_scan[3][tid] - tn;
     int32_t dummy = 0;
     for (int l = l0; l < l1; ++l) {
         const LaneCounts c = lane_counts(a, l, &dummy);
         s_dec[l] = od;
         s_pre[l] = op;
+        s_nd[l] = on;
         LaneInfo li;
         li.dec_off = c.dec ? od : -1;
         li.nsplit = c.nsplit;
         li.sum_off = c.sum ? os : -1;
         li.sum_stride = c.stride;
         a.lane_info[l] = li;
-        od += c.dec; op += c.pre; os += c.sum;
+        od += c.dec; op += c.pre; os += c.sum; on += c.dec ? 1 : 0;
     }
     if (tid == kPlanThreads - 1) {
         s_dec[a.L] = s_scan[0][tid];
         s_pre[a.L] = s_scan[1][tid];
+        s_nd[a.L] = s_scan[3][tid];
         // Launch grids and workspace were sized from the host copies; device
         // offsets that disagree would index past them, so no work is emitted.
         if (s_scan[0][tid] != a.n_dec_host || s_scan[1][tid] != a.n_pre_host || s_scan[2][tid] != a.sum_host ||
@@ -387,14 +390,35 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
         if (tid == 0) atomicOr(a.status, FP_ST_PLAN_MISMATCH);
     }
     const int tot_d = bad ? 0 : s_dec[a.L], tot_p = bad ? 0 : s_pre[a.L];
+    // Decode items in launch order: first every split but each (lane, KV
+    // head)'s last, then the last splits (the partial ones). Workgroups are
+    // dispatched in this order, so the short items fill the end of the grid.
+    // Split outputs are stored by (lane, KV head, split), not by launch order.
+    const int tot_last = a.H * s_nd[a.L];
+    const int tot_full = tot_d - tot_last;
     for (int64_t idx = tid; idx < a.n_dec_host; idx += kPlanThreads) {
         int4 it = make_int4(-1, 0, 0, 0);
         if (idx < tot_d) {
-            const int l = upper_lane(s_dec, a.L, (int)idx);
-            const int local = (int)idx - s_dec[l];
+            int l, g, sp;
+            if (idx < tot_full) {
+                // largest lane whose first non-last split is at or before idx
+                int lo = 0, hi = a.L;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_dec[mid] - a.H * s_nd[mid] <= idx) lo = mid; else hi = mid;
+                }
+                l = lo;
+                const int local = (int)idx - (s_dec[l] - a.H * s_nd[l]);
+                const LaneInfo li = a.lane_info[l];
+                g = local / (li.nsplit - 1);
+                sp = local - g * (li.nsplit - 1);
+            } else {
+                const int j = (int)idx - tot_full;
+                l = upper_lane(s_nd, a.L, j / a.H);
+                g = j % a.H;
+                sp = a.lane_info[l].nsplit - 1;
+            }
             const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
-            const int nsplit = cap > 0 ? (cap + a.split - 1) / a.split : 1;
-            const int g = local / nsplit, sp = local - g * nsplit;
             it = make_int4(l, g, sp * a.split, min((sp + 1) * a.split, cap));
         }
         a.dec_items[idx] = it;
@@ -520,6 +544,7 @@ struct AttnArgs {
     float *part_o;                    // [items][ncols_max][D] unnormalized split outputs
     float *part_ml;                   // [items][2][32] split max (base 2) and sum
     int ncols_max;
+    int split;                        // decode KV slots per work item
     const int32_t *summary;           // row-block tile lists of masked prefill lanes
 };
 

@@ -298,6 +298,7 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
     a.part_o = p.merge ? reinterpret_cast<float *>(ws + p.off_po) : nullptr;
     a.part_ml = p.merge ? reinterpret_cast<float *>(ws + p.off_pml) : nullptr;
     a.ncols_max = p.ncols_max;
+    a.split = p.split;
     a.summary = reinterpret_cast<const int32_t *>(ws + p.off_sum);
 
     if (p.summaries) {
