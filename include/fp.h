@@ -14,6 +14,8 @@
  *
  * A step is four calls, enqueued in this order on one stream:
  *   fp_append_kv -> fp_attend -> fp_fold -> fp_readout.
+ * A repeating decode loop may enqueue fp_advance after fp_fold to write the
+ * next pass's geometry on the device.
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless the name ends in `_host`.
@@ -191,6 +193,31 @@ int fp_fold(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *chan
  */
 int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, const int32_t *rows,
                int32_t num_readout, float *dst, int32_t *status, hipStream_t stream);
+
+/*
+ * fp_advance - the StateGeometry of the next pass of a repeating decode loop,
+ * written on the device from committed_len, so a loop that keeps its decode
+ * pass in flight (Pipelines and frames: run_ahead) never waits on the host for
+ * the lengths a fold produced (State geometry: folding appends rows causally
+ * after the frozen prefix; speculative decoding rewinds to the accepted prefix
+ * this way). For lane l with n_l = indptr[l+1] - indptr[l] rows (the shape of
+ * the next pass, fixed by the caller) and c_l = committed_len[l]:
+ *   slots[indptr[l] + i]     = c_l + i                               i < n_l
+ *   positions[indptr[l] + i] = c_l + i + (pos_offset ? pos_offset[l] : 0)
+ *   kv_len[l]                = c_l + n_l
+ *   geom      : the next pass's geometry; indptr / indptr_host / num_lanes /
+ *               num_rows are read, positions / slots / kv_len are the device
+ *               arrays written (geom->positions etc. are ignored: the writable
+ *               outputs are the arguments below), fold is untouched.
+ *   pos_offset: nullable int32 [L] device, position of slot 0 of each lane.
+ *   positions, slots : int32 [N] device outputs; kv_len : int32 [L] device output.
+ * Enqueue after fp_fold of the previous pass on the same stream. Nothing is
+ * validated on the device here: a slot past the lane's pages is caught by
+ * fp_append_kv (FP_ST_SLOT_RANGE) and kv_len by fp_attend (FP_ST_KVLEN).
+ * Returns FP_ERR_NULL / FP_ERR_SHAPE for bad arguments, FP_ERR_HIP on a launch error.
+ */
+int fp_advance(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *pos_offset, int32_t *positions,
+               int32_t *slots, int32_t *kv_len, hipStream_t stream);
 
 /* ---- host-only accounting (Pie reviews, Eq. (1) and Eq. (2)) ---- */
 uint64_t fp_kv_bytes(int32_t L, int32_t H_kv, int32_t d, uint64_t T, int32_t b); /* 2*L*H_kv*d*T*b   */

@@ -317,6 +317,27 @@ def fold(committed, indptr, fold_spec, channel=None):
     return out.astype(np.int32), status
 
 
+def advance(committed, indptr, pos_offset=None):
+    """Geometry of the next pass of a repeating decode loop ("Pipelines and
+    frames": run_ahead; "State geometry": folding appends rows causally after
+    the frozen prefix): lane l's rows take slots c_l, c_l+1, ..., their
+    positions add the lane's offset (0 if none), and the lane reads c_l + n_l slots.
+    Returns (positions, slots, kv_len) as int32 arrays."""
+    ip = np.asarray(indptr, dtype=np.int64)
+    L = len(ip) - 1
+    positions = np.zeros(int(ip[-1]), dtype=np.int64)
+    slots = np.zeros(int(ip[-1]), dtype=np.int64)
+    kv_len = np.zeros(L, dtype=np.int64)
+    for lane in range(L):
+        c = int(committed[lane])
+        off = 0 if pos_offset is None else int(pos_offset[lane])
+        for i, r in enumerate(range(int(ip[lane]), int(ip[lane + 1]))):
+            slots[r] = c + i
+            positions[r] = c + i + off
+        kv_len[lane] = c + int(ip[lane + 1] - ip[lane])
+    return positions.astype(np.int32), slots.astype(np.int32), kv_len.astype(np.int32)
+
+
 def readout_rows(indptr, rows=None):
     """Readout list: given rows in the given order, or the last row of each non-empty lane."""
     if rows is not None:

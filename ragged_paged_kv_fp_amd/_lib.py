@@ -34,7 +34,7 @@ FP_ST_PLAN_MISMATCH = 128
 FP_FOLD_ALL = -1
 FP_FOLD_CHANNEL = -2
 
-EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_fold", "fp_readout",
+EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_fold", "fp_readout", "fp_advance",
            "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version")
 
 
@@ -87,6 +87,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp_fold.restype = c_i32
     lib.fp_readout.argtypes = [P(FpGeometry), c_ptr, c_i32, c_ptr, c_i32, c_ptr, c_ptr, c_ptr]
     lib.fp_readout.restype = c_i32
+    lib.fp_advance.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
+    lib.fp_advance.restype = c_i32
     lib.fp_kv_bytes.argtypes = [c_i32, c_i32, c_i32, c_u64, c_i32]
     lib.fp_kv_bytes.restype = c_u64
     lib.fp_pages_for.argtypes = [c_u64, c_i32]

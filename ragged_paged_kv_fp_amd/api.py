@@ -177,6 +177,15 @@ def readout(geom: Geometry, out: torch.Tensor, dst: torch.Tensor, status: torch.
                                         _ptr(status), _stream(stream)))
 
 
+def advance(pool: Pool, geom: Geometry, pos_offset: Optional[torch.Tensor] = None, stream=None) -> None:
+    """fp_advance: write geom's positions / slots / kv_len on the device from the
+    pool's committed lengths (rows appended after the frozen prefix)."""
+    lib = _lib.load()
+    ps, gs = pool.struct(), geom.struct()
+    _check("fp_advance", lib.fp_advance(ctypes.byref(ps), ctypes.byref(gs), _ptr(pos_offset), _ptr(geom.positions),
+                                        _ptr(geom.slots), _ptr(geom.kv_len), _stream(stream)))
+
+
 def kv_bytes(L: int, H_kv: int, d: int, T: int, b: int) -> int:
     return int(_lib.load().fp_kv_bytes(L, H_kv, d, T, b))
 

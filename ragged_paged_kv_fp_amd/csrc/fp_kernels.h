@@ -171,6 +171,23 @@ __global__ void __launch_bounds__(256) fold_kernel(const int32_t *indptr, const 
     if (clamped) atomicOr(status, FP_ST_FOLD_CLAMP);
 }
 
+// ============================================================================ advance
+
+// Geometry of the next pass from the committed lengths: thread t < L writes
+// kv_len of lane t, thread t < N writes row t's slot and position.
+__global__ void __launch_bounds__(256) advance_kernel(const int32_t *indptr, const int32_t *committed,
+                                                       const int32_t *pos_offset, int L, int N,
+                                                       int32_t *positions, int32_t *slots, int32_t *kv_len) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < L) kv_len[t] = committed[t] + (indptr[t + 1] - indptr[t]);
+    if (t < N) {
+        const int lane = find_lane(indptr, L, t);
+        const int slot = committed[lane] + (t - indptr[lane]);
+        slots[t] = slot;
+        positions[t] = slot + (pos_offset ? pos_offset[lane] : 0);
+    }
+}
+
 // ============================================================================ readout
 
 // Block b copies one readout row: rows[b] if a list is given, else the last row

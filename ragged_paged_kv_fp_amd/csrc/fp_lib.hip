@@ -379,6 +379,22 @@ int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, con
     return launch_ok();
 }
 
+int fp_advance(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *pos_offset, int32_t *positions,
+               int32_t *slots, int32_t *kv_len, hipStream_t stream) {
+    if (!pool || !pool->committed_len) return FP_ERR_NULL;
+    if (!geom || !geom->indptr || !geom->indptr_host || !kv_len) return FP_ERR_NULL;
+    if (geom->num_lanes < 1 || geom->num_rows < 0) return FP_ERR_SHAPE;
+    const int32_t *ip = geom->indptr_host;
+    if (ip[0] != 0 || ip[geom->num_lanes] != geom->num_rows) return FP_ERR_SHAPE;
+    for (int l = 0; l < geom->num_lanes; ++l)
+        if (ip[l + 1] < ip[l]) return FP_ERR_SHAPE;
+    if (geom->num_rows > 0 && (!positions || !slots)) return FP_ERR_NULL;
+    const int n = geom->num_lanes > geom->num_rows ? geom->num_lanes : geom->num_rows;
+    hipLaunchKernelGGL(advance_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, geom->indptr,
+                       pool->committed_len, pos_offset, geom->num_lanes, geom->num_rows, positions, slots, kv_len);
+    return launch_ok();
+}
+
 uint64_t fp_kv_bytes(int32_t L, int32_t H_kv, int32_t d, uint64_t T, int32_t b) {
     return 2ull * (uint64_t)L * (uint64_t)H_kv * (uint64_t)d * T * (uint64_t)b;
 }

@@ -120,3 +120,78 @@ class DeviceStep:
         K = raw[:, 0].reshape(wl.num_pages, wl.H_kv, wl.P, wl.d)
         V = raw[:, 1].reshape(wl.num_pages, wl.H_kv, wl.d, wl.P).transpose(0, 1, 3, 2)
         return K, V
+
+
+class RunAheadLoop:
+    """Device buffers of a repeating decode loop (pass shape fixed, geometry from
+    committed_len): per pass advance -> append -> attend -> fold(channel) ->
+    readout, all on one stream with no host round trip between passes.
+
+    Inputs of pass t are uploaded up front (k[t], v[t], q[t], accept[t]); the
+    pass itself reads the static buffers k, v, q, channel, so a caller may
+    capture one pass in a HIP graph and feed it by copying into them.
+    """
+
+    def __init__(self, ra, device="cuda", split: Optional[int] = None):
+        self.ra = ra
+        self.device = dev = torch.device(device)
+        self.split = split
+        L, N = ra.num_lanes, int(ra.indptr[-1])
+        self.pool_t = torch.zeros((ra.num_pages, 2 * ra.H_kv * ra.P * ra.d), dtype=torch.int16, device=dev)
+        self.pool = api.Pool(kv=self.pool_t, num_pages=ra.num_pages, page_size=ra.P, num_kv_heads=ra.H_kv,
+                             head_dim=ra.d, page_indptr=_dev(ra.page_indptr.astype(np.int32), dev),
+                             page_indptr_host=ra.page_indptr.astype(np.int32).copy(),
+                             page_ids=_dev(ra.page_ids.astype(np.int32), dev),
+                             committed_len=torch.zeros(L, dtype=torch.int32, device=dev))
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.geom = api.Geometry(indptr=_dev(ra.indptr.astype(np.int32), dev),
+                                 indptr_host=ra.indptr.astype(np.int32).copy(),
+                                 positions=torch.zeros(N, dtype=torch.int32, device=dev),
+                                 slots=torch.zeros(N, dtype=torch.int32, device=dev),
+                                 kv_len=torch.zeros(L, dtype=torch.int32, device=dev),
+                                 fold=torch.full((L,), -2, dtype=torch.int32, device=dev))
+        self.pos_offset = _dev(ra.pos_offset.astype(np.int32), dev)
+        self.ks = [_bits16(x, dev) for x in ra.k]
+        self.vs = [_bits16(x, dev) for x in ra.v]
+        self.qs = [_bits16(x, dev) for x in ra.q]
+        self.accepts = [_dev(a.astype(np.int32), dev) for a in ra.accept]
+        self.k = torch.empty_like(self.ks[0]) if ra.passes else None
+        self.v = torch.empty_like(self.vs[0]) if ra.passes else None
+        self.q = torch.empty_like(self.qs[0]) if ra.passes else None
+        self.channel = torch.zeros(L, dtype=torch.int32, device=dev)
+        self.out = torch.zeros((N, ra.H_q, ra.d), dtype=torch.float32, device=dev)
+        self.lse = torch.zeros((N, ra.H_q), dtype=torch.float32, device=dev)
+        nro = int((np.diff(ra.indptr) > 0).sum())
+        self.dst = torch.zeros((nro, ra.H_q * ra.d), dtype=torch.float32, device=dev)
+        ws = api.attend_workspace_bytes(self.pool, self.geom, ra.H_q, None, split)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        if ra.prefix is not None:
+            p = ra.prefix
+            g = _geometry(p, dev)
+            api.append_kv(self.pool, g, _bits16(p.k, dev), _bits16(p.v, dev), ra.theta, self.status)
+            api.fold(self.pool, g, self.status)
+
+    def load(self, t: int, stream=None) -> None:
+        """Copy pass t's inputs into the static buffers (stream-ordered)."""
+        s = torch.cuda.current_stream() if stream is None else stream
+        with torch.cuda.stream(s):
+            self.k.copy_(self.ks[t], non_blocking=True)
+            self.v.copy_(self.vs[t], non_blocking=True)
+            self.q.copy_(self.qs[t], non_blocking=True)
+            self.channel.copy_(self.accepts[t], non_blocking=True)
+
+    def one_pass(self, stream=None) -> None:
+        ra = self.ra
+        api.advance(self.pool, self.geom, self.pos_offset, stream)
+        api.append_kv(self.pool, self.geom, self.k, self.v, ra.theta, self.status, stream)
+        api.attend(self.pool, self.geom, self.q, ra.H_q, ra.theta, ra.sm_scale, self.out, self.workspace,
+                   self.status, self.lse, None, self.split, stream)
+        api.fold(self.pool, self.geom, self.status, self.channel, stream)
+        api.readout(self.geom, self.out, self.dst, self.status, None, stream)
+
+    def pool_logical(self):
+        ra = self.ra
+        raw = self.pool_t.cpu().numpy().view(np.uint16).reshape(ra.num_pages, 2, ra.H_kv, -1)
+        K = raw[:, 0].reshape(ra.num_pages, ra.H_kv, ra.P, ra.d)
+        V = raw[:, 1].reshape(ra.num_pages, ra.H_kv, ra.d, ra.P).transpose(0, 1, 3, 2)
+        return K, V

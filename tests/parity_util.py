@@ -80,7 +80,11 @@ def compare_outputs(ds, ref):
     rows = ref["rows"]
     if rows is not None:
         O, L = O[rows], L[rows]
-    R, RL = ref["O"], ref["LSE"]
+    return compare_arrays(O, L, ref["O"], ref["LSE"])
+
+
+def compare_arrays(O, L, R, RL):
+    """Attention output O / LSE L (float64 arrays from the device) against the oracle's R / RL."""
     assert np.all(np.isfinite(O)), "non-finite output"
     err = float(np.abs(O - R).max()) if O.size else 0.0
     nref = float(np.linalg.norm(R))
@@ -106,3 +110,24 @@ def compare_step(ds, ref, lanes=None):
     assert dst.shape[0] == len(rl)
     assert np.array_equal(dst, out[rl]), "readout gather differs"
     return dict(max_abs=err, rel_l2=rel, k_exact=exact_k)
+
+
+def oracle_run_ahead(ra):
+    """The oracle's repeating decode loop: geometry from committed lengths each pass."""
+    pool = oracle.Pool(ra.num_pages, ra.P, ra.H_kv, ra.d, ra.page_indptr, ra.page_ids)
+    L = ra.num_lanes
+    c = np.zeros(L, np.int32)
+    if ra.prefix is not None:
+        p = ra.prefix
+        oracle.append(pool, c, p.indptr, p.positions, p.slots, p.k, p.v, ra.theta)
+        c, _ = oracle.fold(c, p.indptr, p.fold)
+    fold = np.full(L, oracle.FOLD_CHANNEL)
+    passes, status = [], 0
+    for t in range(ra.passes):
+        pos, slots, kv = oracle.advance(c, ra.indptr, ra.pos_offset)
+        s1 = oracle.append(pool, c, ra.indptr, pos, slots, ra.k[t], ra.v[t], ra.theta)
+        O, LSE, s2 = oracle.attend(pool, ra.indptr, pos, slots, kv, ra.q[t], ra.H_q, ra.theta, ra.sm_scale)
+        c, s3 = oracle.fold(c, ra.indptr, fold, ra.accept[t])
+        passes.append(dict(O=O, LSE=LSE, positions=pos, slots=slots, kv_len=kv, committed=c))
+        status |= s1 | s2 | s3
+    return dict(pool=pool, passes=passes, committed=c, status=status, rows=None)

@@ -339,3 +339,66 @@ def test_kv_len_beyond_capacity_is_clamped_and_flagged():
     wl2 = W.make_config(1)
     base = _oracle_run(wl2)
     assert np.array_equal(res["O"], base["O"])
+
+
+# ----------------------------------------------------------------------------- run-ahead geometry
+
+def test_advance_hand_worked_example():
+    # lane 0: one row after 5 committed slots, positions shifted by 10
+    # lane 1: three rows on an empty lane; lane 2: no rows; lane 3: two rows after 3, shift -3
+    pos, slots, kv = oracle.advance([5, 0, 7, 3], [0, 1, 4, 4, 6], [10, 0, 2, -3])
+    assert slots.tolist() == [5, 0, 1, 2, 3, 4]
+    assert pos.tolist() == [15, 0, 1, 2, 0, 1]
+    assert kv.tolist() == [6, 3, 7, 5]
+    pos0, slots0, _ = oracle.advance([5, 0, 7, 3], [0, 1, 4, 4, 6])
+    assert pos0.tolist() == slots0.tolist()
+
+
+def test_speculative_loop_with_rejections_equals_whole_prompt():
+    """Draft rows after the true ones are appended, attended and then rejected by
+    the fold; the next pass's geometry (from committed_len) rewrites their slots.
+    Rows of the true sequence must see exactly what the single 37-row pass saw."""
+    wl = W.make_config(1)
+    whole = _oracle_run(wl)
+    st = wl.step
+    junk_k, junk_v, junk_q = st.k[::-1].copy(), st.v[::-1].copy(), st.q[::-1].copy()
+    pool = oracle.Pool(wl.num_pages, wl.P, wl.H_kv, wl.d, wl.page_indptr, wl.page_ids)
+    c = np.zeros(1, np.int32)
+    schedule = [(1, 3), (4, 0), (2, 5), (3, 2), (7, 1), (1, 4), (8, 3), (5, 0), (6, 2)]
+    assert sum(a for a, _ in schedule) == 37
+    got = {}
+    j = 0
+    for accept, drafts in schedule:
+        t0 = int(c[0])
+        n = accept + drafts
+        indptr = np.array([0, n], np.int32)
+        pos, slots, kv = oracle.advance(c, indptr)
+        idx = np.arange(t0, t0 + accept)
+        jj = np.arange(j, j + drafts) % 37
+        j += drafts
+        p = W.Pass(indptr=indptr, positions=pos, slots=slots, kv_len=kv, fold=np.array([accept], np.int32),
+                   k=np.concatenate([st.k[idx], junk_k[jj]]), v=np.concatenate([st.v[idx], junk_v[jj]]),
+                   q=np.concatenate([st.q[idx], junk_q[jj]]))
+        r = oracle.step(pool, c, p, wl.H_q, wl.theta, wl.sm_scale)
+        assert r["status"] == 0
+        for i in range(accept):
+            got[t0 + i] = (r["O"][i], r["LSE"][i])
+        c = r["committed"]
+    assert int(c[0]) == 37
+    for t in range(37):
+        assert np.array_equal(got[t][0], whole["O"][t]) and np.array_equal(got[t][1], whole["LSE"][t])
+    K1, V1 = pool.lane_kv(0, 37)
+    K0, V0 = whole["pool"].lane_kv(0, 37)
+    assert np.array_equal(K1, K0) and np.array_equal(V1, V0)
+
+
+def test_run_ahead_positions_are_offset_slots():
+    ra = W.make_run_ahead(3, H_kv=1, G=2, d=16, P=4, num_lanes=6, passes=3, max_prompt=20)
+    c = np.diff(ra.prefix.indptr).astype(np.int32) if ra.prefix is not None else np.zeros(ra.num_lanes, np.int32)
+    pos, slots, kv = oracle.advance(c, ra.indptr, ra.pos_offset)
+    for lane in range(ra.num_lanes):
+        r0, r1 = ra.indptr[lane], ra.indptr[lane + 1]
+        assert np.array_equal(pos[r0:r1] - slots[r0:r1], np.full(r1 - r0, ra.pos_offset[lane]))
+        assert kv[lane] == c[lane] + (r1 - r0)
+        if r1 > r0:
+            assert slots[r1 - 1] == kv[lane] - 1

@@ -10,9 +10,11 @@ from .gen import (  # noqa: F401
     FOLD_ALL,
     FOLD_CHANNEL,
     Pass,
+    RunAhead,
     Workload,
     bf16_bits_from_f32,
     make_config,
     make_random,
+    make_run_ahead,
     CONFIG_NAMES,
 )

@@ -419,3 +419,87 @@ def make_random(seed: int, *, H_kv: int = 2, G: int = 2, d: int = 64, P: int = 1
     return _assemble(f"random_{seed}", rngs, H_q=H_kv * G, H_kv=H_kv, d=d, P=P, lanes=lanes,
                      extra_pages=extra_pages, mask_fn=_make_mask if masked else None,
                      channel_fn=channel_fn)
+
+
+@dataclass
+class RunAhead:
+    """A repeating decode loop: a prompt per lane, then `passes` passes of a fixed
+    shape (indptr) whose geometry each pass takes from the committed lengths.
+
+    Per pass t the arrays k[t], v[t], q[t] hold that pass's rows and accept[t]
+    the per-lane count the fold commits (a device channel, possibly out of
+    range to exercise clamping). Slot s of lane l sits at position
+    pos_offset[l] + s.
+    """
+
+    H_q: int
+    H_kv: int
+    d: int
+    P: int
+    theta: float
+    sm_scale: float
+    num_pages: int
+    page_indptr: np.ndarray   # int32 [L+1]
+    page_ids: np.ndarray      # int32
+    prefix: Optional[Pass]
+    pos_offset: np.ndarray    # int32 [L]
+    indptr: np.ndarray        # int32 [L+1], the shape of every pass
+    k: List[np.ndarray]
+    v: List[np.ndarray]
+    q: List[np.ndarray]
+    accept: List[np.ndarray]  # int32 [L] per pass
+
+    @property
+    def num_lanes(self) -> int:
+        return int(self.indptr.shape[0] - 1)
+
+    @property
+    def passes(self) -> int:
+        return len(self.k)
+
+
+def make_run_ahead(seed: int, *, H_kv: int = 2, G: int = 4, d: int = 128, P: int = 16, num_lanes: int = 8,
+                   passes: int = 6, max_prompt: int = 300, extra_pages: int = 2) -> RunAhead:
+    """Speculative-decoding style loop: each lane drafts 0..8 rows per pass
+    (0 = an idle lane), the channel accepts 0..n of them (sometimes more, to
+    be clamped), prompts 0..max_prompt slots, random position offsets."""
+    rngs = _rngs(seed)
+    g = rngs["lengths"]
+    L = int(num_lanes)
+    n = np.array([int(g.choice([0, 1, 2, 4, 8])) for _ in range(L)], dtype=np.int64)
+    c0 = g.integers(0, max_prompt + 1, size=L).astype(np.int64)
+    off = g.integers(0, 5000, size=L).astype(np.int64)
+    pages = -(-(c0 + passes * n + 1) // P)
+    page_indptr = np.zeros(L + 1, dtype=np.int64)
+    page_indptr[1:] = np.cumsum(pages)
+    num_pages = int(page_indptr[-1]) + int(extra_pages)
+    page_ids = rngs["perm"].permutation(num_pages).astype(np.int32)[: int(page_indptr[-1])].copy()
+    pre_indptr = np.zeros(L + 1, dtype=np.int64)
+    pre_indptr[1:] = np.cumsum(c0)
+    Np = int(pre_indptr[-1])
+    prefix = None
+    if Np:
+        slots = np.concatenate([np.arange(c, dtype=np.int64) for c in c0])
+        pos = np.concatenate([np.arange(c, dtype=np.int64) + o for c, o in zip(c0, off)])
+        prefix = Pass(indptr=pre_indptr.astype(np.int32), positions=pos.astype(np.int32),
+                      slots=slots.astype(np.int32), kv_len=c0.astype(np.int32),
+                      fold=np.full(L, FOLD_ALL, dtype=np.int32),
+                      k=_normal_bf16(rngs["prefix_kv"], (Np, H_kv, d)),
+                      v=_normal_bf16(rngs["prefix_kv"], (Np, H_kv, d)))
+    indptr = np.zeros(L + 1, dtype=np.int64)
+    indptr[1:] = np.cumsum(n)
+    N = int(indptr[-1])
+    H_q = H_kv * G
+    ks, vs, qs, acc = [], [], [], []
+    for _ in range(passes):
+        qs.append(_normal_bf16(rngs["q"], (N, H_q, d)))
+        ks.append(_normal_bf16(rngs["k"], (N, H_kv, d)))
+        vs.append(_normal_bf16(rngs["v"], (N, H_kv, d)))
+        a = np.array([int(rngs["channel"].integers(0, m + 1)) for m in n], dtype=np.int32)
+        if rngs["channel"].random() < 0.3:
+            a[int(rngs["channel"].integers(0, L))] = 99
+        acc.append(a)
+    return RunAhead(H_q=H_q, H_kv=H_kv, d=d, P=P, theta=10000.0, sm_scale=float(1.0 / np.sqrt(d)),
+                    num_pages=num_pages, page_indptr=page_indptr.astype(np.int32), page_ids=page_ids,
+                    prefix=prefix, pos_offset=off.astype(np.int32), indptr=indptr.astype(np.int32),
+                    k=ks, v=vs, q=qs, accept=acc)
