@@ -584,15 +584,24 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char *l
                 q5 = q6;
             }
         };
-        for (int i = 0;; i += kPreStages) {
+        // Whole groups of four steps in a loop whose only exit is at its
+        // bottom, then the remaining steps: exits in the middle of the loop
+        // body would be merged into one block that also leads back to the
+        // loop header, and the loads in flight on that path would then be
+        // waited for at the top of every group.
+        const int T4 = T & ~(kPreStages - 1);
+        for (int i = 0; i < T4; i += kPreStages) {
             step(StepK<0>{}, i);
-            if (i + 1 >= T) break;
             step(StepK<1>{}, i + 1);
-            if (i + 2 >= T) break;
             step(StepK<2>{}, i + 2);
-            if (i + 3 >= T) break;
             step(StepK<3>{}, i + 3);
-            if (i + 4 >= T) break;
+        }
+        if (T4 < T) {
+            step(StepK<0>{}, T4);
+            if (T4 + 1 < T) {
+                step(StepK<1>{}, T4 + 1);
+                if (T4 + 2 < T) step(StepK<2>{}, T4 + 2);
+            }
         }
     }
 
