@@ -360,7 +360,8 @@ def main(argv=None):
         print(json.dumps({"calib_copy_bytes": nbytes}), file=sys.stderr, flush=True)
         del src, dst
     cfg = args.config
-    wl, w, ms_step, attn_avg, host_ms = measure(W, runner, cfg, args.seed, args.split, args.steps, args.warmup)
+    mass = {}
+    wl, w, ms_step, attn_avg, host_ms = measure(W, runner, cfg, args.seed, args.split, args.steps, args.warmup, mass)
     K, Wm = args.steps, args.warmup
     if cfg == 5:
         unit, work_units, scale = "TFLOP/s", w["flops"], 1e12
@@ -394,13 +395,16 @@ def main(argv=None):
                      "kernel": "attention kernels (decode_kernel / prefill_kernel), HIP events per step",
                      "kernel_avg_ms": round(attn_avg, 5)},
     }
+    line["attn_mass"] = {"kernel": "mass_kernel (fp_attn_mass after the step's attention), torch events",
+                         "this_config": mass_line(wl, w, mass["ms"], cfg)}
     if cfg == 3:
         line["config"]["prefill_tflops_step"] = round(w["flops_prefill"] / (ms_step * 1e-3) / 1e12, 3)
     if cfg == 5:
         line["roofline"]["executed_frac"] = round(w["flops_prefill_executed"] / (attn_avg * 1e-3) / 1e12 / peak, 4)
     if cfg == 2 and not args.no_prefill:
         # the prefill half of the metric, on the long-context masked prefill wave
-        wl5, w5, ms5, attn5, _ = measure(W, runner, 5, args.seed, None, 5, 1)
+        mass5 = {}
+        wl5, w5, ms5, attn5, _ = measure(W, runner, 5, args.seed, None, 5, 1, mass5)
         alg = w5["flops"] / (attn5 * 1e-3) / 1e12
         exe = w5["flops_prefill_executed"] / (attn5 * 1e-3) / 1e12
         line["prefill"] = {"workload": "config 5: " + WORKLOAD_TEXT[5], "bound": "mfma", "unit": "TFLOP/s",
@@ -409,6 +413,7 @@ def main(argv=None):
                            "achieved_executed": round(exe, 2), "frac_executed": round(exe / BF16_PEAK_TFLOPS, 4),
                            "algorithmic_flops": w5["flops"], "executed_flops": w5["flops_prefill_executed"],
                            "traffic": measured_traffic(5), "steps": 5, "warmup": 1}
+        line["attn_mass"]["prefill"] = mass_line(wl5, w5, mass5["ms"], 5)
         del wl5
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, cfg, unit)
@@ -416,10 +421,27 @@ def main(argv=None):
     return 0
 
 
-def measure(W, runner, cfg, seed, split, K, Wm):
+def mass_line(wl, w, ms, cfg) -> dict:
+    """Roofline of fp_attn_mass: decode-class lanes read each slot's K once
+    (HBM-bound: kv_len x H_kv x d x 2 B); prefill lanes run Q.K over every
+    attended pair (MFMA-bound: 2 d flops per pair and query head)."""
+    k_bytes = w["kv_bytes_decode"] // 2
+    qk_flops = w["flops"] / 2.0
+    if cfg == 5:
+        ach = qk_flops / (ms * 1e-3) / 1e12
+        return {"ms": round(ms, 4), "bound": "mfma", "unit": "TFLOP/s", "achieved": round(ach, 2),
+                "peak": BF16_PEAK_TFLOPS, "frac": round(ach / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": qk_flops}
+    ach = k_bytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "bound": "hbm", "unit": "GB/s", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+            "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": k_bytes}
+
+
+def measure(W, runner, cfg, seed, split, K, Wm, mass=None):
     """Time K steps (after Wm warm-ups) of one configuration with inputs resident
     in HBM: returns (workload, work, ms per step, attention-kernel ms per step
-    from HIP events on the launch stream, host wall ms per step)."""
+    from HIP events on the launch stream, host wall ms per step). With a dict
+    as `mass`, also times K calls of fp_attn_mass over the last step's
+    attention (torch events on the stream it runs on) into mass["ms"]."""
     import torch
 
     wl = W.make_config(cfg, seed=seed, scale="full")
@@ -451,6 +473,23 @@ def measure(W, runner, cfg, seed, split, K, Wm):
     status = int(ds.status.cpu()[0])
     if status != 0:
         print(f"warning: device status {status} (config {cfg})", file=sys.stderr)
+    if mass is not None:
+        from ragged_paged_kv_fp_amd import api
+
+        buf = torch.zeros((wl.H_kv, int(wl.page_indptr[-1]) * wl.P), dtype=torch.float32, device="cuda")
+        call = lambda: api.attn_mass(ds.pool, ds.geom, wl.H_q, ds.lse, ds.workspace, buf, ds.mask, split)  # noqa: E731
+        for _ in range(Wm):
+            call()
+        torch.cuda.synchronize()
+        m0 = torch.cuda.Event(enable_timing=True)
+        m1 = torch.cuda.Event(enable_timing=True)
+        m0.record(stream)
+        for _ in range(K):
+            call()
+        m1.record(stream)
+        torch.cuda.synchronize()
+        mass["ms"] = m0.elapsed_time(m1) / K
+        del buf
     for a, b in pairs_ev:
         ev.destroy(a)
         ev.destroy(b)

@@ -195,6 +195,32 @@ int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, con
                int32_t num_readout, float *dst, int32_t *status, hipStream_t stream);
 
 /*
+ * fp_attn_mass - attention statistics of the pass, so that an eviction policy
+ * driven by attention scores (TOVA and the like) can run on the device: the
+ * pages' review (section 7) notes that such a policy needs the forward pass to
+ * return the scores, and the Docs' Attention masks section names score-based
+ * KV eviction among the uses of per-row masks. For lane l, KV head g and slot
+ * j below the lane's kv_len (clamped to its capacity):
+ *   slot_mass[g * S + page_indptr[l] * P + j] +=
+ *       sum over the lane's rows r and the query heads h of KV head g of
+ *       exp(score(r, h, j) - lse[r][h])   if row r may read slot j, else 0,
+ * with S = page_indptr_host[L] * P and score the scaled q.k of fp_attend. Each
+ * row's probabilities sum to one over its readable slots, so summed over all
+ * slots and KV heads the pass adds the count of (row, query head) pairs that
+ * read at least one slot.
+ *   Call after fp_attend on the same stream with the same pool, geom,
+ *   num_q_heads, mask, tuning and workspace: it reads the rotated queries that
+ *   fp_attend left in the workspace and fp_attend's lse output (non-null).
+ *   slot_mass: fp32 [H_kv][S] device, accumulated into (zero it for the mass of
+ *   one pass); entries of slots at or past kv_len are not touched.
+ * Deterministic: every output word has one writer and a fixed summation order.
+ * Returns FP_ERR_NULL / FP_ERR_SHAPE / FP_ERR_WORKSPACE like fp_attend.
+ */
+int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_heads, const fp_mask *mask,
+                 const float *lse, const void *workspace, size_t workspace_bytes, const fp_tuning *tuning,
+                 float *slot_mass, hipStream_t stream);
+
+/*
  * fp_advance - the StateGeometry of the next pass of a repeating decode loop,
  * written on the device from committed_len, so a loop that keeps its decode
  * pass in flight (Pipelines and frames: run_ahead) never waits on the host for

@@ -290,6 +290,43 @@ def attend(pool: Pool, indptr, positions, slots, kv_len, q_bits, H_q, theta, sm_
     return O, LSE, status
 
 
+def attn_mass(pool: Pool, indptr, positions, slots, kv_len, q_bits, H_q, theta, sm_scale,
+              mask_bits=None, word_offset=None, lanes=None):
+    """Attention mass each slot received in the pass, per KV head: the scores
+    returned out of the forward pass so that score-driven eviction (TOVA) can
+    use them (review section 7; Docs "Attention masks" names such eviction).
+
+    For lane l, KV head g and slot j below the lane's clamped kv_len, the sum
+    over the lane's rows r and the query heads h of g of the softmax
+    probability of slot j in row r's attention (0 if r may not read j), under
+    the same allowed sets and scaling as attend(). Returns fp64
+    [H][page_indptr[L] * P], slot j of lane l at column page_indptr[l] * P + j;
+    `lanes` limits the lanes computed (the others stay zero).
+    """
+    S = int(pool.page_indptr[-1]) * pool.P
+    mass = np.zeros((pool.H, S))
+    G = H_q // pool.H
+    L = len(indptr) - 1
+    for lane in (range(L) if lanes is None else lanes):
+        r0, r1 = _lane_rows(indptr, lane)
+        if r1 == r0:
+            continue
+        eff = min(max(int(kv_len[lane]), 0), pool.capacity(lane))
+        K, _ = pool.lane_kv(lane, eff)
+        base = int(pool.page_indptr[lane]) * pool.P
+        qr = rope(bf16_to_f64(q_bits[r0:r1]), np.asarray(positions)[r0:r1], theta)
+        for t, row in enumerate(range(r0, r1)):
+            A, _ = allowed_slots(lane, row, eff, slots, indptr, mask_bits, word_offset)
+            if len(A) == 0:
+                continue
+            for g in range(pool.H):
+                s = (K[A, g, :] @ qr[t, g * G:(g + 1) * G, :].T) * sm_scale   # [|A|][G]
+                p = np.exp(s - s.max(axis=0))
+                p /= p.sum(axis=0)
+                mass[g, base + A] += p.sum(axis=1)
+    return mass
+
+
 def fold(committed, indptr, fold_spec, channel=None):
     """committed[l] += k_l with k_l = literal | rows (all) | channel[l], clamped to [0, rows]."""
     out = np.array(committed, dtype=np.int64)

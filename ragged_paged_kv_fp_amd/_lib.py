@@ -34,7 +34,7 @@ FP_ST_PLAN_MISMATCH = 128
 FP_FOLD_ALL = -1
 FP_FOLD_CHANNEL = -2
 
-EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_fold", "fp_readout", "fp_advance",
+EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_fold", "fp_readout", "fp_attn_mass", "fp_advance",
            "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version")
 
 
@@ -87,6 +87,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp_fold.restype = c_i32
     lib.fp_readout.argtypes = [P(FpGeometry), c_ptr, c_i32, c_ptr, c_i32, c_ptr, c_ptr, c_ptr]
     lib.fp_readout.restype = c_i32
+    lib.fp_attn_mass.argtypes = [P(FpKvPool), P(FpGeometry), c_i32, P(FpMask), c_ptr, c_ptr, ctypes.c_size_t, P(FpTuning),
+                                 c_ptr, c_ptr]
+    lib.fp_attn_mass.restype = c_i32
     lib.fp_advance.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
     lib.fp_advance.restype = c_i32
     lib.fp_kv_bytes.argtypes = [c_i32, c_i32, c_i32, c_u64, c_i32]

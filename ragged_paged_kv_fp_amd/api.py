@@ -177,6 +177,21 @@ def readout(geom: Geometry, out: torch.Tensor, dst: torch.Tensor, status: torch.
                                         _ptr(status), _stream(stream)))
 
 
+def attn_mass(pool: Pool, geom: Geometry, num_q_heads: int, lse: torch.Tensor, workspace: torch.Tensor,
+              slot_mass: torch.Tensor, mask: Optional[Mask] = None, split: Optional[int] = None,
+              stream=None) -> None:
+    """fp_attn_mass: add each slot's attention mass of the pass (per KV head) into
+    slot_mass [H_kv][page_indptr[L] * P]; call after attend() with the same
+    pool, geom, mask, split and workspace."""
+    lib = _lib.load()
+    ps, gs = pool.struct(), geom.struct()
+    ms = mask.struct() if mask is not None else None
+    _check("fp_attn_mass", lib.fp_attn_mass(ctypes.byref(ps), ctypes.byref(gs), int(num_q_heads),
+                                            ctypes.byref(ms) if ms is not None else None, _ptr(lse),
+                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _tuning(split), _ptr(slot_mass), _stream(stream)))
+
+
 def advance(pool: Pool, geom: Geometry, pos_offset: Optional[torch.Tensor] = None, stream=None) -> None:
     """fp_advance: write geom's positions / slots / kv_len on the device from the
     pool's committed lengths (rows appended after the frozen prefix)."""

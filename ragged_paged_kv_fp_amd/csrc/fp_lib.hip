@@ -7,6 +7,7 @@
 // counts, mask bits) are taken by the kernels.
 #include "fp_kernels.h"
 
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -376,6 +377,43 @@ int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, con
     const unsigned grid = rows ? (unsigned)num_readout : (unsigned)L;
     hipLaunchKernelGGL(readout_kernel, dim3(grid), dim3(256), 0, stream, geom->indptr, L, (int64_t)geom->num_rows, out,
                        row_elems, rows, num_readout, dst, status);
+    return launch_ok();
+}
+
+int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_heads, const fp_mask *mask,
+                 const float *lse, const void *workspace, size_t workspace_bytes, const fp_tuning *tuning,
+                 float *slot_mass, hipStream_t stream) {
+    Plan p;
+    int rc = make_plan(pool, geom, mask, num_q_heads, tuning, &p);
+    if (rc) return rc;
+    if (p.N == 0) return FP_OK;
+    if (!lse || !workspace || !slot_mass) return FP_ERR_NULL;
+    if (workspace_bytes < p.total) return FP_ERR_WORKSPACE;
+    const int32_t *pp = pool->page_indptr_host;
+    int max_pages = 0;
+    for (int l = 0; l < p.L; ++l) max_pages = std::max(max_pages, pp[l + 1] - pp[l]);
+    const int64_t tiles = ((int64_t)max_pages * p.P + 31) / 32;
+    if (tiles == 0) return FP_OK;
+    MassArgs m;
+    m.pool = static_cast<const uint16_t *>(pool->kv);
+    m.page_elems = 2LL * p.H * p.P * p.D;
+    m.num_pages = pool->num_pages;
+    m.P = p.P; m.H = p.H; m.G = p.G; m.Hq = p.Hq;
+    m.page_indptr = pool->page_indptr;
+    m.page_ids = pool->page_ids;
+    m.indptr = geom->indptr;
+    m.slots = geom->slots;
+    m.kv_len = geom->kv_len;
+    m.qrot = reinterpret_cast<const uint16_t *>(static_cast<const char *>(workspace) + p.off_qrot);
+    m.lse = lse;
+    m.mask_bits = mask ? mask->bits : nullptr;
+    m.mask_off = mask ? mask->word_offset : nullptr;
+    m.mass = slot_mass;
+    m.stride = (int64_t)pp[p.L] * p.P;
+    m.tiles = (int)tiles;
+    const dim3 grid((unsigned)(p.L * p.H), (unsigned)std::min<int64_t>(tiles, 65535)), block(64 * kMassWaves);
+    if (p.D == 128) hipLaunchKernelGGL(mass_kernel<128>, grid, block, 0, stream, m);
+    else hipLaunchKernelGGL(mass_kernel<64>, grid, block, 0, stream, m);
     return launch_ok();
 }
 

@@ -64,7 +64,8 @@ def run(wl_arrays, *, H_q, H_kv, d, theta, sm_scale, cap, prefix=None, committed
     wl_arrays: dict with indptr, positions, slots, kv_len, fold, k, v, q (lists / numpy),
     optional mask (per global row: set of slots, or None for causal), channel.
     cap: per-lane capacity in slots. prefix: same dict shape for a pre-pass (append + fold all).
-    Returns dict(O, LSE, committed, store) with O[row][head] lists.
+    Returns dict(O, LSE, committed, store, mass) with O[row][head] lists and
+    mass[lane][(kv head, slot)] the summed attention probability of the slot.
     """
     L = len(wl_arrays["indptr"]) - 1
     store = [dict() for _ in range(L)]
@@ -109,6 +110,7 @@ def run(wl_arrays, *, H_q, H_kv, d, theta, sm_scale, cap, prefix=None, committed
     O = [[[0.0] * d for _ in range(H_q)] for _ in range(N)]
     LSE = [[-math.inf] * H_q for _ in range(N)]
     masks = w.get("mask")
+    mass = [dict() for _ in range(L)]  # lane -> {(kv head, slot): summed probability}
     for lane in range(L):
         eff = min(max(int(w["kv_len"][lane]), 0), cap[lane])
         for r in range(int(w["indptr"][lane]), int(w["indptr"][lane + 1])):
@@ -128,6 +130,8 @@ def run(wl_arrays, *, H_q, H_kv, d, theta, sm_scale, cap, prefix=None, committed
                 m = max(scores)
                 ps = [math.exp(s - m) for s in scores]
                 tot = sum(ps)
+                for p_, j in zip(ps, allowed):
+                    mass[lane][(g, j)] = mass[lane].get((g, j), 0.0) + p_ / tot
                 acc = [0.0] * d
                 for p_, j in zip(ps, allowed):
                     vj = store[lane][j][1][g]
@@ -136,4 +140,4 @@ def run(wl_arrays, *, H_q, H_kv, d, theta, sm_scale, cap, prefix=None, committed
                 O[r][hq] = [a / tot for a in acc]
                 LSE[r][hq] = m + math.log(tot)
     do_fold(w, w.get("channel"))
-    return dict(O=O, LSE=LSE, committed=committed, store=store)
+    return dict(O=O, LSE=LSE, committed=committed, store=store, mass=mass)

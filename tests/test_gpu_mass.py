@@ -1,0 +1,131 @@
+"""GPU parity of the attention statistics (fp_attn_mass) against the oracle.
+
+After the step runs on the GPU (append, attend, fold, readout), fp_attn_mass
+adds each slot's attention mass per KV head into a zeroed buffer; the oracle
+computes the same sums in fp64 from its own pool. Checks: elementwise against
+the oracle on small copies of the five configurations, random geometries and
+the full-size decode and verify configurations; the conservation law (a row
+and query head with any readable slot contributes exactly one unit) on the
+full-size prefill configurations; determinism and accumulation.
+
+Tolerance: the GPU scores use fp_attend's rotated query, prescaled and rounded
+to bf16 (relative error up to 2^-9 per element), so each probability carries a
+relative error of a few times 2^-9 times the score's magnitude; per-slot sums
+are compared with |gpu - ref| <= 2e-2 * ref + 1e-3 * G, and the whole buffer
+by relative L2 <= 1e-2.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import parity_util as pu
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ragged_paged_kv_fp_amd import _lib
+
+    _lib.load()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _gpu_mass(ds):
+    import torch
+
+    from ragged_paged_kv_fp_amd import api
+
+    wl = ds.wl
+    S = int(wl.page_indptr[-1]) * wl.P
+    mass = torch.zeros((wl.H_kv, S), dtype=torch.float32, device=ds.device)
+    api.attn_mass(ds.pool, ds.geom, wl.H_q, ds.lse, ds.workspace, mass, ds.mask, ds.split)
+    torch.cuda.synchronize()
+    return mass
+
+
+def _oracle_mass(wl, ref, lanes=None):
+    st = wl.step
+    return oracle.attn_mass(ref["pool"], st.indptr, st.positions, st.slots, st.kv_len, st.q, wl.H_q, wl.theta,
+                            wl.sm_scale, wl.mask_bits, wl.mask_word_offset, lanes=lanes)
+
+
+def _compare(wl, got, want):
+    G = wl.H_q // wl.H_kv
+    err = np.abs(got - want)
+    bound = 2e-2 * want + 1e-3 * G
+    worst = float((err - bound).max()) if err.size else 0.0
+    rel = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
+    assert np.all(np.isfinite(got))
+    assert worst <= 0.0, f"per-slot error exceeds bound by {worst}"
+    assert rel <= 1e-2, f"rel-L2 {rel}"
+    return float(err.max()) if err.size else 0.0, rel
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_mass_config_small(cfg):
+    wl = W.make_config(cfg, seed=0, scale="small" if cfg > 1 else "full")
+    _say(f"mass config {cfg}: lanes={wl.num_lanes} rows={wl.step.num_rows}")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)
+    got = _gpu_mass(ds).cpu().numpy().astype(np.float64)
+    _say(_compare(wl, got, _oracle_mass(wl, ref)))
+
+
+@pytest.mark.parametrize("seed,H_kv,G,d,P", [(0, 2, 2, 64, 16), (1, 1, 4, 128, 8), (2, 2, 8, 64, 32),
+                                             (6, 3, 4, 128, 16)])
+def test_mass_random_geometry(seed, H_kv, G, d, P):
+    wl = W.make_random(seed, H_kv=H_kv, G=G, d=d, P=P, num_lanes=7, max_rows=90, max_ctx=400)
+    _say(f"mass random seed {seed}: H_kv={H_kv} G={G} d={d} P={P} rows={wl.step.num_rows}")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)
+    got = _gpu_mass(ds).cpu().numpy().astype(np.float64)
+    _say(_compare(wl, got, _oracle_mass(wl, ref)))
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_mass_full_size_against_oracle(cfg):
+    wl = W.make_config(cfg)
+    _say(f"mass full config {cfg}: lanes={wl.num_lanes} rows={wl.step.num_rows}")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)
+    got = _gpu_mass(ds).cpu().numpy().astype(np.float64)
+    _say(_compare(wl, got, _oracle_mass(wl, ref)))
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_mass_full_size_conservation(cfg):
+    wl = W.make_config(cfg)
+    _say(f"mass conservation config {cfg}: lanes={wl.num_lanes} rows={wl.step.num_rows}")
+    ds = pu.gpu_run(wl)
+    m = _gpu_mass(ds)
+    got = m.double().sum(dim=1).cpu().numpy()
+    lse = ds.lse.cpu().numpy()
+    G = wl.H_q // wl.H_kv
+    pairs = np.isfinite(lse).reshape(lse.shape[0], wl.H_kv, G).sum(axis=(0, 2))
+    _say(got, pairs)
+    np.testing.assert_allclose(got, pairs, rtol=2e-3)
+    assert bool((m >= 0).all())
+
+
+def test_mass_deterministic_and_accumulates():
+    import torch
+
+    wl = W.make_config(3, seed=1, scale="small")
+    ds = pu.gpu_run(wl)
+    a = _gpu_mass(ds)
+    b = _gpu_mass(ds)
+    assert torch.equal(a, b)
+    from ragged_paged_kv_fp_amd import api
+
+    api.attn_mass(ds.pool, ds.geom, wl.H_q, ds.lse, ds.workspace, b, ds.mask, ds.split)
+    torch.cuda.synchronize()
+    assert torch.equal(b, 2 * a)

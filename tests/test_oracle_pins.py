@@ -402,3 +402,50 @@ def test_run_ahead_positions_are_offset_slots():
         assert kv[lane] == c[lane] + (r1 - r0)
         if r1 > r0:
             assert slots[r1 - 1] == kv[lane] - 1
+
+
+# ----------------------------------------------------------------------------- attention mass
+
+def _oracle_mass(wl, res):
+    st = wl.step
+    return oracle.attn_mass(res["pool"], st.indptr, st.positions, st.slots, st.kv_len, st.q, wl.H_q, wl.theta,
+                            wl.sm_scale, wl.mask_bits, wl.mask_word_offset)
+
+
+@pytest.mark.parametrize("seed,P,G,d", [(0, 1, 2, 16), (2, 4, 4, 8), (3, 16, 2, 16), (5, 16, 1, 32)])
+def test_attn_mass_matches_bruteforce(seed, P, G, d):
+    wl = W.make_random(seed, H_kv=2, G=G, d=d, P=P, num_lanes=5, max_rows=20, max_ctx=40)
+    res = _oracle_run(wl)
+    mass = _oracle_mass(wl, res)
+    ref = _bf_run(wl)
+    want = np.zeros_like(mass)
+    for lane, entries in enumerate(ref["mass"]):
+        base = int(wl.page_indptr[lane]) * wl.P
+        for (g, j), v in entries.items():
+            want[g, base + j] += v
+    assert np.max(np.abs(mass - want)) <= 1e-12
+
+
+def test_attn_mass_sums_to_reading_pairs():
+    # each (row, query head) that reads any slot spreads exactly one unit of mass
+    for seed in range(4):
+        wl = W.make_random(40 + seed, H_kv=2, G=4, d=16, P=8, num_lanes=6, max_rows=24, max_ctx=60)
+        res = _oracle_run(wl)
+        mass = _oracle_mass(wl, res)
+        pairs = int(np.isfinite(res["LSE"]).sum())
+        assert abs(mass.sum() - pairs) <= 1e-9 * max(pairs, 1)
+        assert np.all(mass >= 0)
+
+
+def test_attn_mass_zero_query_is_uniform():
+    wl = W.make_config(1)
+    wl.step.q[:] = 0
+    res = _oracle_run(wl)
+    mass = _oracle_mass(wl, res)
+    G = wl.H_q // wl.H_kv
+    # row r reads slots 0..r with probability 1/(r+1) each, for each of the G heads of a group
+    want = np.array([G * sum(1.0 / (r + 1) for r in range(j, 37)) for j in range(37)])
+    base = int(wl.page_indptr[0]) * wl.P
+    for g in range(wl.H_kv):
+        np.testing.assert_allclose(mass[g, base:base + 37], want, rtol=1e-13, atol=0)
+        assert np.all(mass[g, base + 37:] == 0)
