@@ -392,8 +392,9 @@ int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_
     const int32_t *pp = pool->page_indptr_host;
     int max_pages = 0;
     for (int l = 0; l < p.L; ++l) max_pages = std::max(max_pages, pp[l + 1] - pp[l]);
-    const int64_t tiles = ((int64_t)max_pages * p.P + 31) / 32;
-    if (tiles == 0) return FP_OK;
+    const int64_t chunks = ((int64_t)max_pages * p.P + 32 * kMassTiles - 1) / (32 * kMassTiles);
+    if (chunks == 0) return FP_OK;
+    if (chunks > 65535) return FP_ERR_UNSUPPORTED;
     MassArgs m;
     m.pool = static_cast<const uint16_t *>(pool->kv);
     m.page_elems = 2LL * p.H * p.P * p.D;
@@ -410,11 +411,30 @@ int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_
     m.mask_off = mask ? mask->word_offset : nullptr;
     m.mass = slot_mass;
     m.stride = (int64_t)pp[p.L] * p.P;
-    m.tiles = (int)tiles;
-    const dim3 grid((unsigned)(p.L * p.H), (unsigned)std::min<int64_t>(tiles, 65535)), block(64 * kMassWaves);
-    if (p.D == 128) hipLaunchKernelGGL(mass_kernel<128>, grid, block, 0, stream, m);
-    else hipLaunchKernelGGL(mass_kernel<64>, grid, block, 0, stream, m);
-    return launch_ok();
+    m.chunks = (int)chunks;
+    // lanes with rows x G <= 32 go to the decode-class kernel, the others to the chunked one
+    bool any_dec = false, any_pre = false;
+    for (int l = 0; l < p.L; ++l) {
+        const int n = geom->indptr_host[l + 1] - geom->indptr_host[l];
+        if (n > 0 && n * p.G <= 32) any_dec = true;
+        if (n * p.G > 32) any_pre = true;
+    }
+    const dim3 block(64 * kMassWaves);
+    if (any_pre) {
+        const dim3 grid((unsigned)(p.L * p.H), (unsigned)chunks);
+        if (p.D == 128) hipLaunchKernelGGL(mass_kernel<128>, grid, block, 0, stream, m);
+        else hipLaunchKernelGGL(mass_kernel<64>, grid, block, 0, stream, m);
+        if ((rc = launch_ok())) return rc;
+    }
+    if (any_dec) {
+        const int64_t tiles = ((int64_t)max_pages * p.P + 31) / 32;
+        const int64_t per_wg = (int64_t)kMassWaves * kMassWaveTiles;
+        const dim3 grid((unsigned)(p.L * p.H), (unsigned)((tiles + per_wg - 1) / per_wg));
+        if (p.D == 128) hipLaunchKernelGGL(mass_decode_kernel<128>, grid, block, 0, stream, m);
+        else hipLaunchKernelGGL(mass_decode_kernel<64>, grid, block, 0, stream, m);
+        if ((rc = launch_ok())) return rc;
+    }
+    return FP_OK;
 }
 
 int fp_advance(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *pos_offset, int32_t *positions,

@@ -8,15 +8,19 @@
 // Each row's probabilities therefore sum to one over its allowed slots, the
 // same normalisation as the attention output.
 //
-// One workgroup of four waves per (lane, KV head, 32-slot tile): the tile's K
-// stays in registers as the A operand of S^T = K * Q^T (the prefill kernel's
-// slot permutation, so lane half h holds slots 8h..8h+7 and 16+8h..16+8h+7 of
-// its column), and the waves stream the lane's (32-row block, query head)
-// pairs, accumulating p per slot in registers. A pair with no allowed slot in
-// the tile is skipped by the whole wave. The 32 columns of a wave are summed
-// with butterfly shuffles, the four waves through LDS, and one thread per
-// slot adds the total to the output: a single owner per output word, so the
-// result does not depend on scheduling.
+// One workgroup of four waves per (lane, KV head, chunk of eight 32-slot
+// tiles). The chunk's K is staged once in LDS (rows padded by 16 bytes, as in
+// the prefill kernel, so fragment reads are free of bank conflicts); the waves
+// then stream the lane's (32-row block, query head) pairs: a pair's Q
+// fragments are loaded once and serve all eight tiles, each tile computing
+// S^T = K * Q^T with the prefill kernel's slot permutation (lane half h holds
+// slots 8h..8h+7 and 16+8h..16+8h+7 of its column) and adding p to per-lane,
+// per-slot sums held in registers. A pair, or a tile of a pair, with no
+// allowed slot is skipped by the whole wave. At the end the 32 columns of a
+// wave are summed in registers (DPP and a row swap), the four waves through LDS, and one
+// thread per slot adds the total to the output: a single owner per output
+// word and a fixed summation order, so the result does not depend on
+// scheduling.
 #pragma once
 
 #include "fp_kernels.h"
@@ -24,6 +28,7 @@
 namespace fpk {
 
 constexpr int kMassWaves = 4;
+constexpr int kMassTiles = 8;  // 32-slot tiles per workgroup
 
 struct MassArgs {
     const uint16_t *pool;
@@ -37,101 +42,263 @@ struct MassArgs {
     const int64_t *mask_off;          // nullable
     float *mass;                      // [H][stride]
     int64_t stride;                   // page_indptr[L] * P
-    int tiles;                        // 32-slot tiles of the largest working set
+    int chunks;                       // chunks of the largest working set
+};
+
+// Sum over the 32 lanes of each lane half, in registers: two quad swaps, the
+// half-row and row mirrors (every lane of a 16-lane row then holds the row's
+// sum), and one swap of 16-lane rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float half_sum(float v) {
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);  // row_half_mirror
+    v += dpp_f<0x140>(v);  // row_mirror
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+template <int D>
+struct MassLds {
+    static constexpr int KROW = 2 * D + 16;
+    static constexpr int K_BYTES = 32 * kMassTiles * KROW;
 };
 
 template <int D>
 __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
-    __shared__ float s_sum[kMassWaves][32];
+    __shared__ __attribute__((aligned(16))) char s_k[MassLds<D>::K_BYTES];
+    __shared__ float s_sum[kMassWaves][32 * kMassTiles];
+    constexpr int KROW = MassLds<D>::KROW;
+    constexpr int KC = D / 8;  // 16-byte chunks per K row
     const int lane = blockIdx.x / a.H, g = blockIdx.x % a.H;
     const int p0 = a.page_indptr[lane];
     const int cap = (a.page_indptr[lane + 1] - p0) * a.P;
     const int eff = clamp_kv(a.kv_len[lane], cap);
     const int r0 = a.indptr[lane], n = a.indptr[lane + 1] - r0;
-    if (n <= 0 || eff <= 0) return;  // workgroup-uniform
+    const int c0 = 32 * kMassTiles * blockIdx.y;  // first slot of the chunk
+    if (n <= 0 || n * a.G <= 32 || c0 >= eff) return;  // workgroup-uniform; decode-class lanes below
+    const int ntl = min(kMassTiles, (eff - c0 + 31) >> 5);  // tiles of the chunk below kv_len
     const int wv = threadIdx.x / kWave, ln = lane_id(), nn = ln & 31, h = ln >> 5;
     const int pshift = __builtin_ctz(a.P);
-    const int lastpg = (eff - 1) >> pshift;
+
+    // Stage the chunk's K: page ids, then every data load, then every store,
+    // all unconditional, so the workgroup waits for memory once (a condition
+    // would let the compiler sink each load next to its store). Rows at or
+    // past kv_len load the lane's last row below it again (a cache hit); their
+    // scores are dropped.
+    {
+        constexpr int PER = 32 * kMassTiles * KC / (64 * kMassWaves);
+        int pid[PER];
+        uint4 stg[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int slot = min(c0 + (int)(threadIdx.x + u * 64 * kMassWaves) / KC, eff - 1);
+            pid[u] = a.page_ids[p0 + (slot >> pshift)];
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = threadIdx.x + u * 64 * kMassWaves;
+            const int slot = min(c0 + e / KC, eff - 1), ck = e % KC;
+            const int64_t phys = min(max(pid[u], 0), a.num_pages - 1);
+            stg[u] = *reinterpret_cast<const uint4 *>(
+                a.pool + phys * a.page_elems + ((int64_t)g * a.P + (slot & (a.P - 1))) * D + 8 * ck);
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = threadIdx.x + u * 64 * kMassWaves;
+            *reinterpret_cast<uint4 *>(s_k + (e / KC) * KROW + 16 * (e % KC)) = stg[u];
+        }
+    }
+    __syncthreads();
+
     const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
     const int wpr = masked ? (int)((a.mask_off[lane + 1] - a.mask_off[lane]) / n) : 0;
-    const int nrb = (n + 31) >> 5;
-    const int items = nrb * a.G;
+    const int t0 = c0 >> 5;  // first tile of the chunk in the lane
+    const int items = ((n + 31) >> 5) * a.G;
     constexpr float kLog2e = 1.4426950408889634f;
+    const char *krow = s_k + kslot_of_row(nn) * KROW + h * D;
 
-    for (int t = blockIdx.y; t < a.tiles; t += gridDim.y) {
-        const int j0 = 32 * t;
-        if (j0 >= eff) break;  // workgroup-uniform
-        // K rows of the tile as the A operand; slots past the working set read
-        // the last page that holds a slot below kv_len (their scores are dropped)
-        uint4 kf[D / 16];
-        {
-            const int srow = j0 + kslot_of_row(nn);
-            const int pg = min(srow >> pshift, lastpg);
-            const int64_t phys = min(max(a.page_ids[p0 + pg], 0), a.num_pages - 1);
-            const uint4 *src = reinterpret_cast<const uint4 *>(
-                a.pool + phys * a.page_elems + ((int64_t)g * a.P + (srow & (a.P - 1))) * D + h * (D / 2));
+    float msum[kMassTiles][16];
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) kf[s] = src[s];
-        }
-        float msum[16];
+    for (int t = 0; t < kMassTiles; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) msum[i] = 0.0f;
+        for (int i = 0; i < 16; ++i) msum[t][i] = 0.0f;
 
-        for (int it = wv; it < items; it += kMassWaves) {
-            const int rb = it / a.G, head = g * a.G + it % a.G;
-            const int rl = 32 * rb + nn;  // row within the lane (the lane's column)
-            const bool valid = rl < n;
-            const int64_t row = r0 + (valid ? rl : 0);
-            const float lse2 = valid ? a.lse[row * a.Hq + head] * kLog2e : kNegInf;
-            // slots of the tile this column may read, as a 32-bit mask
-            uint32_t bits = 0u;
-            if (valid && lse2 > kNegInf) {
-                const int rem = eff - j0;
-                uint32_t lm = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
-                if (masked) {
-                    bits = t < wpr ? a.mask_bits[a.mask_off[lane] + (int64_t)rl * wpr + t] : 0u;
-                } else {
-                    const int lim = a.slots[row] + 1 - j0;  // causal: slots at or below the row's own
-                    bits = lim >= 32 ? 0xFFFFFFFFu : (lim <= 0 ? 0u : ((1u << lim) - 1u));
-                }
-                bits &= lm;
+    for (int it = wv; it < items; it += kMassWaves) {
+        const int rb = it / a.G, head = g * a.G + it % a.G;
+        const int rl = 32 * rb + nn;  // row within the lane (this lane's column)
+        const bool valid = rl < n;
+        const int64_t row = r0 + (valid ? rl : 0);
+        const float lse2 = valid ? a.lse[row * a.Hq + head] * kLog2e : kNegInf;
+        const bool live = valid && lse2 > kNegInf;
+        // allowed slots of each tile of the chunk for this column
+        uint32_t bits[kMassTiles];
+        if (masked) {
+            const uint32_t *mw = a.mask_bits + a.mask_off[lane] + (int64_t)(valid ? rl : 0) * wpr;
+#pragma unroll
+            for (int t = 0; t < kMassTiles; ++t) bits[t] = (live && t < ntl && t0 + t < wpr) ? mw[t0 + t] : 0u;
+        } else {
+            const int lim = live ? a.slots[row] + 1 - c0 : 0;  // causal: slots at or below the row's own
+#pragma unroll
+            for (int t = 0; t < kMassTiles; ++t) {
+                const int r = lim - 32 * t;
+                bits[t] = r >= 32 ? 0xFFFFFFFFu : (r <= 0 ? 0u : ((1u << r) - 1u));
             }
-            if (!__any(bits != 0u)) continue;  // wave-uniform
+        }
+        {
+            const int rem = eff - c0;  // slots below kv_len from the chunk start
+#pragma unroll
+            for (int t = 0; t < kMassTiles; ++t) {
+                const int r = rem - 32 * t;
+                bits[t] &= r >= 32 ? 0xFFFFFFFFu : (r <= 0 ? 0u : ((1u << r) - 1u));
+            }
+        }
+        uint32_t any = 0u;
+#pragma unroll
+        for (int t = 0; t < kMassTiles; ++t) any |= bits[t];
+        if (!__any(any != 0u)) continue;  // wave-uniform
+        uint4 qf[D / 16];
+        {
             const uint4 *qsrc = reinterpret_cast<const uint4 *>(a.qrot + (row * a.Hq + head) * D + h * (D / 2));
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) qf[s] = qsrc[s];  // row is clamped to the lane's first
+            if (!valid) {
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) qf[s] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kMassTiles; ++t) {
+            if (!__any(bits[t] != 0u)) continue;  // wave-uniform
             f32x16 acc = {};
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) acc = mfma32(kf[s], valid ? qsrc[s] : make_uint4(0, 0, 0, 0), acc);
+            for (int s = 0; s < D / 16; ++s)
+                acc = mfma32(*reinterpret_cast<const uint4 *>(krow + t * 32 * KROW + 16 * s), qf[s], acc);
             // register i holds tile slot 16(i/8) + 8h + i%8 of this column
-            const uint32_t hb = bits >> (8 * h);
+            const uint32_t hb = bits[t] >> (8 * h);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int k = 16 * (i >> 3) + (i & 7);
                 const bool keep = (hb >> k) & 1u;
-                msum[i] += keep ? __builtin_amdgcn_exp2f(acc[i] - lse2) : 0.0f;
+                msum[t][i] += keep ? __builtin_amdgcn_exp2f(acc[i] - lse2) : 0.0f;
             }
         }
-        // sum the 32 columns of each lane half: lane (nn = 0, h) then holds
-        // the wave's totals of its 16 slots
+    }
+    // sum the 32 columns of each lane half; lane (nn = 0, h) then holds the
+    // wave's totals of its 16 slots of every tile
+#pragma unroll
+    for (int t = 0; t < kMassTiles; ++t) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float v = msum[i];
-#pragma unroll
-            for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off);
-            msum[i] = v;
+            const float v = half_sum(msum[t][i]);
+            if (nn == 0) s_sum[wv][32 * t + 16 * (i >> 3) + 8 * h + (i & 7)] = v;
         }
-        if (nn == 0) {
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < 32 * ntl; j += 64 * kMassWaves) {
+        if (c0 + j >= eff) continue;
+        float tot = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s_sum[wv][16 * (i >> 3) + 8 * h + (i & 7)] = msum[i];
-        }
-        __syncthreads();
-        if (threadIdx.x < 32 && j0 + (int)threadIdx.x < eff) {
-            float tot = 0.0f;
+        for (int w = 0; w < kMassWaves; ++w) tot += s_sum[w][j];
+        a.mass[(int64_t)g * a.stride + (int64_t)p0 * a.P + c0 + j] += tot;
+    }
+}
+
+// Decode-class lanes (rows x G <= 32): all the lane's (row, query head)
+// pairs fit in the 32 columns of one MFMA block, so each wave loads its Q
+// once and streams kMassWaveTiles consecutive K tiles straight from memory into
+// registers (the next tile's fragments load while the current one computes),
+// reducing each tile's 32 columns in registers and adding the 32 slot totals
+// to the output (one writer per word). Column c is row c / G, query head
+// g * G + c % G.
+constexpr int kMassWaveTiles = 4;
+
+template <int D>
+__global__ void __launch_bounds__(64 * kMassWaves) mass_decode_kernel(MassArgs a) {
+    const int lane = blockIdx.x / a.H, g = blockIdx.x % a.H;
+    const int r0 = a.indptr[lane], n = a.indptr[lane + 1] - r0;
+    if (n <= 0 || n * a.G > 32) return;  // workgroup-uniform; other lanes take the chunked kernel
+    const int p0 = a.page_indptr[lane];
+    const int cap = (a.page_indptr[lane + 1] - p0) * a.P;
+    const int eff = clamp_kv(a.kv_len[lane], cap);
+    const int wv = threadIdx.x / kWave, ln = lane_id(), nn = ln & 31, h = ln >> 5;
+    const int tb = kMassWaveTiles * (kMassWaves * blockIdx.y + wv);  // first tile of this wave
+    if (32 * tb >= eff) return;  // wave-uniform: no barrier follows
+    const int pshift = __builtin_ctz(a.P);
+    const bool valid = nn < n * a.G;
+    const int rl = valid ? nn / a.G : 0;
+    const int64_t row = r0 + rl;
+    const int head = g * a.G + (valid ? nn % a.G : 0);
+    const float lse2 = valid ? a.lse[row * a.Hq + head] * 1.4426950408889634f : kNegInf;
+    const bool live = valid && lse2 > kNegInf;
+    const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
+    const int wpr = masked ? (int)((a.mask_off[lane + 1] - a.mask_off[lane]) / n) : 0;
+    const int lim = a.slots[row] + 1;  // causal limit of this column's row
+    uint4 qf[D / 16];
+    {
+        const uint4 *qsrc = reinterpret_cast<const uint4 *>(a.qrot + (row * a.Hq + head) * D + h * (D / 2));
 #pragma unroll
-            for (int w = 0; w < kMassWaves; ++w) tot += s_sum[w][threadIdx.x];
-            float *dst = a.mass + (int64_t)g * a.stride + (int64_t)p0 * a.P + j0 + threadIdx.x;
-            *dst += tot;
+        for (int s = 0; s < D / 16; ++s) qf[s] = qsrc[s];
+        if (!valid) {
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) qf[s] = make_uint4(0, 0, 0, 0);
         }
-        __syncthreads();
+    }
+    // K fragment addresses: this lane's row of tile t is slot 32t + kslot_of_row(nn)
+    // (rows at or past kv_len load the last row below it; their scores are dropped)
+    int pid[kMassWaveTiles];
+#pragma unroll
+    for (int u = 0; u < kMassWaveTiles; ++u)
+        pid[u] = a.page_ids[p0 + (min(32 * (tb + u) + kslot_of_row(nn), eff - 1) >> pshift)];
+    auto kload = [&](int u, uint4 (&kf)[D / 16]) {
+        const int slot = min(32 * (tb + u) + kslot_of_row(nn), eff - 1);
+        const int64_t phys = min(max(pid[u], 0), a.num_pages - 1);
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            a.pool + phys * a.page_elems + ((int64_t)g * a.P + (slot & (a.P - 1))) * D + h * (D / 2));
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) kf[s] = src[s];
+    };
+    uint4 kb[2][D / 16];
+    kload(0, kb[0]);
+    if (kMassWaveTiles > 1) kload(1, kb[1]);
+#pragma unroll
+    for (int u = 0; u < kMassWaveTiles; ++u) {
+        const int j0 = 32 * (tb + u);
+        if (j0 >= eff) break;  // wave-uniform
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) acc = mfma32(kb[u & 1][s], qf[s], acc);
+        if (u + 2 < kMassWaveTiles) kload(u + 2, kb[u & 1]);
+        uint32_t bits = 0u;
+        if (live) {
+            if (masked) {
+                const int t = j0 >> 5;
+                bits = t < wpr ? a.mask_bits[a.mask_off[lane] + (int64_t)rl * wpr + t] : 0u;
+            } else {
+                const int r = lim - j0;
+                bits = r >= 32 ? 0xFFFFFFFFu : (r <= 0 ? 0u : ((1u << r) - 1u));
+            }
+            const int r = eff - j0;
+            bits &= r >= 32 ? 0xFFFFFFFFu : ((1u << r) - 1u);
+        }
+        // register i holds tile slot 16(i/8) + 8h + i%8 of this column
+        const uint32_t hb = bits >> (8 * h);
+        float mine = 0.0f;  // lane nn < 16 of half h keeps the total of register nn
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int k = 16 * (i >> 3) + (i & 7);
+            const float p = ((hb >> k) & 1u) ? __builtin_amdgcn_exp2f(acc[i] - lse2) : 0.0f;
+            const float tot = half_sum(p);
+            mine = nn == i ? tot : mine;
+        }
+        if (nn < 16) {
+            const int slot = j0 + 16 * (nn >> 3) + 8 * h + (nn & 7);
+            if (slot < eff) a.mass[(int64_t)g * a.stride + (int64_t)p0 * a.P + slot] += mine;
+        }
     }
 }
 
