@@ -265,7 +265,7 @@ def pmc_summary(fetch_db: str, write_db: str, cfg: int, calib_bytes: int, out: s
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
         rows = per_kernel(db, counter)
         copies = [v for n, v in rows if "copyBuffer" in n]
-        kvals = [v for n, v in rows if kern in n]
+        kvals = [v for n, v in rows if f"fpk::{kern}<" in n]  # exact kernel (not mass_decode_kernel)
         # the calibration copies are the largest copy dispatches of the run
         copies = sorted(copies)[-5:]
         calib_kib = float(np.median(copies))
