@@ -322,6 +322,8 @@ def main(argv=None):
     ap.add_argument("--split", type=int, default=None, help="decode KV slots per work item")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="config 2 only: skip the config 5 prefill measurement")
+    ap.add_argument("--frame", action="store_true",
+                    help="time a two-pass frame (config 3 split per lane) eagerly and as one HIP-graph replay")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run 5 plain device copies of MIB MiB (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -359,6 +361,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": nbytes}), file=sys.stderr, flush=True)
         del src, dst
+    if args.frame:
+        print(json.dumps(frame_bench(W, runner, args.seed, args.steps, args.warmup)), flush=True)
+        return 0
     cfg = args.config
     mass = {}
     wl, w, ms_step, attn_avg, host_ms = measure(W, runner, cfg, args.seed, args.split, args.steps, args.warmup, mass)
@@ -419,6 +424,45 @@ def main(argv=None):
         line["cpu_baseline"] = cpu_baseline(wl, cfg, unit)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def frame_bench(W, runner, seed, K, Wm) -> dict:
+    """A frame of two passes (config 3 with each lane's rows split at a random
+    point: prefix pass folded all, then the continuation) submitted K times
+    eagerly (eight ABI calls per frame from the host) and K times as one HIP
+    graph replay: device ms per frame from torch events and host ms per frame."""
+    import torch
+
+    wl = W.make_config(3, seed=seed, scale="full")
+    rng = np.random.default_rng(seed)
+    first = np.array([int(rng.integers(0, m + 1)) for m in np.diff(wl.step.indptr)])
+    A, B = W.split_pass(wl.step, first)
+    ds = runner.DeviceStep(wl, device="cuda")
+    ds.run_prefix()
+    fr = runner.Frame(ds.pool, [A, B], wl.H_q, wl.theta, wl.sm_scale)
+    res = {}
+    for mode in ("eager", "graph"):
+        go = fr.run if mode == "eager" else fr.replay
+        if mode == "graph":
+            fr.capture()
+        for _ in range(Wm):
+            go()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        e0.record()
+        for _ in range(K):
+            go()
+        e1.record()
+        h1 = time.perf_counter()
+        torch.cuda.synchronize()
+        res[mode] = {"device_ms_per_frame": round(e0.elapsed_time(e1) / K, 4),
+                     "host_ms_per_frame": round((h1 - h0) * 1e3 / K, 4)}
+    st = int(fr.status.cpu()[0])
+    return {"metric": "two-pass frame (prefix pass + continuation), eager vs one HIP-graph replay",
+            "config": {"workload": "config 3 split per lane at a random row: " + WORKLOAD_TEXT[3], "seed": seed,
+                       "rows": [A.num_rows, B.num_rows]},
+            "steps": K, "warmup": Wm, "status": st, **res}
 
 
 def mass_line(wl, w, ms, cfg) -> dict:

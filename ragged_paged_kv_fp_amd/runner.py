@@ -195,3 +195,55 @@ class RunAheadLoop:
         K = raw[:, 0].reshape(ra.num_pages, ra.H_kv, ra.P, ra.d)
         V = raw[:, 1].reshape(ra.num_pages, ra.H_kv, ra.d, ra.P).transpose(0, 1, 3, 2)
         return K, V
+
+
+class Frame:
+    """Several passes over one pool submitted back to back (Pie's submit_frame:
+    passes in consecutive scheduler waves, in order), each pass being the four
+    ABI calls with its own geometry, inputs and outputs.
+
+    run() enqueues the whole frame eagerly; capture() records it once into a
+    HIP graph and replay() then submits it with one launch from the host. The
+    frame restores the committed lengths it started from first, so it can be
+    replayed; that restore is a device-to-device copy, not a memset.
+    """
+
+    def __init__(self, pool: api.Pool, passes, H_q: int, theta: float, sm_scale: float, device="cuda"):
+        self.pool = pool
+        self.H_q, self.theta, self.sm_scale = H_q, float(theta), float(sm_scale)
+        dev = torch.device(device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.committed0 = pool.committed_len.clone()
+        self.items = []
+        for p in passes:
+            g = _geometry(p, dev)
+            N = p.num_rows
+            it = dict(geom=g, k=_bits16(p.k, dev), v=_bits16(p.v, dev), q=_bits16(p.q, dev),
+                      out=torch.zeros((N, H_q, pool.head_dim), dtype=torch.float32, device=dev),
+                      lse=torch.zeros((N, H_q), dtype=torch.float32, device=dev),
+                      dst=torch.zeros((int((np.diff(p.indptr) > 0).sum()), H_q * pool.head_dim),
+                                      dtype=torch.float32, device=dev))
+            ws = api.attend_workspace_bytes(pool, g, H_q)
+            it["ws"] = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+            self.items.append(it)
+        self.graph = None
+
+    def run(self) -> None:
+        self.pool.committed_len.copy_(self.committed0)
+        for it in self.items:
+            g = it["geom"]
+            api.append_kv(self.pool, g, it["k"], it["v"], self.theta, self.status)
+            api.attend(self.pool, g, it["q"], self.H_q, self.theta, self.sm_scale, it["out"], it["ws"], self.status,
+                       it["lse"])
+            api.fold(self.pool, g, self.status)
+            api.readout(g, it["out"], it["dst"], self.status)
+
+    def capture(self) -> None:
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.run()
+        torch.cuda.synchronize()
+
+    def replay(self) -> None:
+        self.graph.replay()

@@ -16,5 +16,6 @@ from .gen import (  # noqa: F401
     make_config,
     make_random,
     make_run_ahead,
+    split_pass,
     CONFIG_NAMES,
 )

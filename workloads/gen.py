@@ -503,3 +503,33 @@ def make_run_ahead(seed: int, *, H_kv: int = 2, G: int = 4, d: int = 128, P: int
                     num_pages=num_pages, page_indptr=page_indptr.astype(np.int32), page_ids=page_ids,
                     prefix=prefix, pos_offset=off.astype(np.int32), indptr=indptr.astype(np.int32),
                     k=ks, v=vs, q=qs, accept=acc)
+
+
+def split_pass(p: Pass, first_rows) -> tuple:
+    """Split a pass into two consecutive passes: lane l's first first_rows[l]
+    rows (folded all, reading up to the last slot they write) and the rest
+    (the original kv_len and fold). Input arrays are copied, not regenerated."""
+    L = p.num_lanes
+    a_rows, b_rows, a_kv, a_ip, b_ip = [], [], [], [0], [0]
+    for lane in range(L):
+        r0, r1 = int(p.indptr[lane]), int(p.indptr[lane + 1])
+        s = min(max(int(first_rows[lane]), 0), r1 - r0)
+        a = list(range(r0, r0 + s))
+        b = list(range(r0 + s, r1))
+        a_rows += a
+        b_rows += b
+        a_ip.append(a_ip[-1] + len(a))
+        b_ip.append(b_ip[-1] + len(b))
+        a_kv.append(int(p.slots[a[-1]]) + 1 if a else 0)
+    a_rows = np.asarray(a_rows, dtype=np.int64)
+    b_rows = np.asarray(b_rows, dtype=np.int64)
+
+    def sub(rows, ip, kv, fold):
+        return Pass(indptr=np.asarray(ip, dtype=np.int32), positions=p.positions[rows].copy(),
+                    slots=p.slots[rows].copy(), kv_len=np.asarray(kv, dtype=np.int32),
+                    fold=np.asarray(fold, dtype=np.int32), k=p.k[rows].copy(), v=p.v[rows].copy(),
+                    q=None if p.q is None else p.q[rows].copy())
+
+    first = sub(a_rows, a_ip, a_kv, [FOLD_ALL] * L)
+    second = sub(b_rows, b_ip, p.kv_len, p.fold)
+    return first, second
