@@ -324,6 +324,9 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true", help="config 2 only: skip the config 5 prefill measurement")
     ap.add_argument("--frame", action="store_true",
                     help="time a two-pass frame (config 3 split per lane) eagerly and as one HIP-graph replay")
+    ap.add_argument("--lora", action="store_true",
+                    help="time projection-site LoRA (rank 16, 8 adapters, d_in = d_out = 4096) on config 3's rows "
+                         "and config 2's rows")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run 5 plain device copies of MIB MiB (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -361,6 +364,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": nbytes}), file=sys.stderr, flush=True)
         del src, dst
+    if args.lora:
+        print(json.dumps(lora_bench(W, args.seed, args.steps, args.warmup)), flush=True)
+        return 0
     if args.frame:
         print(json.dumps(frame_bench(W, runner, args.seed, args.steps, args.warmup)), flush=True)
         return 0
@@ -424,6 +430,54 @@ def main(argv=None):
         line["cpu_baseline"] = cpu_baseline(wl, cfg, unit)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def lora_bench(W, seed, K, Wm) -> dict:
+    """fp_adapter_lora at the q projection (d_in = d_out = 4096, rank 16, 8
+    adapters, a fifth of the lanes without one) over the rows of config 3
+    (mixed wave) and config 2 (decode wave), inputs resident in HBM, timed with
+    torch events over K calls. Algorithmic bytes: x read, y read, out written,
+    and each adapter in use read once (A and B); priced against the HBM peak."""
+    import torch
+
+    from ragged_paged_kv_fp_amd import api
+
+    res = {"metric": "projection-site LoRA, GB/s of algorithmic HBM bytes (1 GPU)", "unit": "GB/s",
+           "peak": HBM_PEAK_GBS, "steps": K, "warmup": Wm, "dtype": "bf16", "data": "synthetic"}
+    for cfg in (3, 2):
+        wl = W.make_config(cfg, seed=seed, scale="full")
+        lw = W.make_lora(seed, wl.step.indptr, d_in=4096, d_out=4096, rank=16, num_adapters=8)
+        dev = "cuda"
+        bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)  # noqa: E731
+        ip = lw.indptr.astype(np.int32)
+        geom = api.Geometry(indptr=torch.from_numpy(ip).to(dev), indptr_host=ip.copy(), positions=None, slots=None,
+                            kv_len=None, fold=None)
+        lora = api.Lora(a=bits(lw.a), b=bits(lw.b), scale=torch.from_numpy(lw.scale).to(dev))
+        x, y = bits(lw.x), bits(lw.y)
+        out = torch.empty_like(y)
+        ws = torch.empty(api.lora_workspace_bytes(geom, lora), dtype=torch.uint8, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        ad = torch.from_numpy(lw.adapter).to(dev)
+        call = lambda: api.adapter_lora(geom, lora, ad, x, y, out, ws, status)  # noqa: E731
+        for _ in range(Wm):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        N = int(ip[-1])
+        used = np.unique(lw.adapter[(lw.adapter >= 0) & (np.diff(ip) > 0)])
+        nbytes = N * 4096 * 2 * 3 + len(used) * 16 * (4096 + 4096) * 2
+        ach = nbytes / (ms * 1e-3) / 1e9
+        res[f"config{cfg}"] = {"workload": f"rows of config {cfg}: " + WORKLOAD_TEXT[cfg], "rows": N,
+                               "adapters_used": int(len(used)), "ms": round(ms, 4), "algorithmic_bytes": nbytes,
+                               "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4),
+                               "status": int(status.cpu()[0])}
+    return res
 
 
 def frame_bench(W, runner, seed, K, Wm) -> dict:

@@ -62,6 +62,7 @@ typedef struct ihipEvent_t *hipEvent_t;
 #define FP_ST_PAGE_RANGE    64    /* page id outside [0, num_pages): write suppressed, read clamped */
 #define FP_ST_PLAN_MISMATCH 128   /* device offset arrays disagree with their host copies:
                                      fp_attend did no attention work (outputs untouched)      */
+#define FP_ST_ADAPTER      256    /* adapter id >= num_adapters: the lane's rows keep y       */
 
 /* ---- fold sentinels (StateGeometry.fold; a value >= 0 is a literal count) ---- */
 #define FP_FOLD_ALL      (-1)     /* freeze every row written this pass                       */
@@ -244,6 +245,43 @@ int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_
  */
 int fp_advance(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *pos_offset, int32_t *positions,
                int32_t *slots, int32_t *kv_len, hipStream_t stream);
+
+/*
+ * Projection-site LoRA adapters (Docs, section Adapters: an adapter attached
+ * at a projection site maps the projection input x and the base output y to
+ * y + b * (a * x), and requests in one batch may use different adapters).
+ * Adapter k is A_k (rank x d_in), B_k (d_out x rank) and a scale s_k.
+ */
+typedef struct fp_lora {
+    int32_t num_adapters;             /* >= 1                                                   */
+    int32_t rank;                     /* r in {16, 32, 48, 64}                                  */
+    int32_t d_in, d_out;              /* projection input / output widths, multiples of 64     */
+    const void *a;                    /* bf16 [num_adapters][rank][d_in] device                 */
+    const void *b;                    /* bf16 [num_adapters][d_out][rank] device                */
+    const float *scale;               /* [num_adapters] device                                  */
+} fp_lora;
+
+/* Workspace bytes fp_adapter_lora needs (host-only): the rank-r projections of every row (two bf16 terms). */
+int64_t fp_lora_workspace_bytes(const fp_geometry *geom, const fp_lora *lora);
+
+/*
+ * fp_adapter_lora - for every row r of lane l with k = adapter[l] >= 0:
+ *     out[r] = bf16( y[r] + s_k * B_k (A_k x[r]) )
+ * and out[r] = y[r] for lanes with adapter[l] < 0.
+ *   geom   : only indptr / indptr_host / num_lanes / num_rows are read.
+ *   adapter: int32 [L] device, per-lane adapter id; an id >= num_adapters sets
+ *            FP_ST_ADAPTER and the lane keeps y.
+ *   x      : bf16 [N][d_in]; y, out: bf16 [N][d_out]; out may equal y (in place).
+ *   Arithmetic: v = A_k x in fp32 (MFMA), kept as two bf16 terms (hi + lo,
+ *   16 significant bits), B_k v in fp32, then y + s_k * (B_k v) in fp32
+ *   rounded to bf16.
+ * Feeding a2: run it on the Q, K or V projection outputs before fp_append_kv /
+ * fp_attend. Returns FP_ERR_NULL / FP_ERR_SHAPE / FP_ERR_UNSUPPORTED /
+ * FP_ERR_WORKSPACE before enqueueing anything.
+ */
+int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t *adapter, const void *x,
+                    const void *y, void *out, void *workspace, size_t workspace_bytes, int32_t *status,
+                    hipStream_t stream);
 
 /* ---- host-only accounting (Pie reviews, Eq. (1) and Eq. (2)) ---- */
 uint64_t fp_kv_bytes(int32_t L, int32_t H_kv, int32_t d, uint64_t T, int32_t b); /* 2*L*H_kv*d*T*b   */

@@ -52,6 +52,7 @@ ST_FOLD_CLAMP = 8      # fold count outside [0, rows]: clamped
 ST_READOUT_RANGE = 16  # readout row outside [0, num_rows): zero row returned
 ST_MASK_SHORT = 32     # mask row holds fewer than kv_len bits: missing bits read as 0
 ST_PAGE_RANGE = 64     # page id outside [0, num_pages): write suppressed, read clamped
+ST_ADAPTER = 256       # adapter id >= number of adapters: the lane keeps y
 
 FOLD_ALL = -1
 FOLD_CHANNEL = -2
@@ -373,6 +374,38 @@ def advance(committed, indptr, pos_offset=None):
             positions[r] = c + i + off
         kv_len[lane] = c + int(ip[lane + 1] - ip[lane])
     return positions.astype(np.int32), slots.astype(np.int32), kv_len.astype(np.int32)
+
+
+def lora(x_bits, y_bits, adapter, indptr, a_bits, b_bits, scale):
+    """Projection-site LoRA adapter (Docs "Adapters": an adapter maps the
+    projection input x and base output y to y + b * (a * x); requests in one
+    batch may use different adapters). For the rows of lane l with
+    k = adapter[l] >= 0 the exact value is y + s_k * B_k (A_k x), rounded once
+    to bf16; lanes with k < 0 keep y, and an id k >= the number of adapters
+    keeps y and sets ST_ADAPTER.
+
+    x_bits [N][d_in], y_bits [N][d_out]: bf16 bits; a_bits [n_ad][r][d_in],
+    b_bits [n_ad][d_out][r]: bf16 bits; scale [n_ad] float.
+    Returns (out bf16 bits [N][d_out], exact fp64 [N][d_out], status).
+    """
+    out = np.array(y_bits, dtype=np.uint16, copy=True)
+    exact = bf16_to_f64(y_bits)
+    n_ad = a_bits.shape[0]
+    status = 0
+    for lane in range(len(indptr) - 1):
+        r0, r1 = _lane_rows(indptr, lane)
+        k = int(adapter[lane])
+        if r1 == r0 or k < 0:
+            continue
+        if k >= n_ad:
+            status |= ST_ADAPTER
+            continue
+        X = bf16_to_f64(x_bits[r0:r1])
+        v = X @ bf16_to_f64(a_bits[k]).T                  # [rows][r]
+        e = exact[r0:r1] + float(scale[k]) * (v @ bf16_to_f64(b_bits[k]).T)
+        exact[r0:r1] = e
+        out[r0:r1] = f64_to_bf16(e)
+    return out, exact, status
 
 
 def readout_rows(indptr, rows=None):

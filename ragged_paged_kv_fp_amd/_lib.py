@@ -30,12 +30,13 @@ FP_ST_READOUT_RANGE = 16
 FP_ST_MASK_SHORT = 32
 FP_ST_PAGE_RANGE = 64
 FP_ST_PLAN_MISMATCH = 128
+FP_ST_ADAPTER = 256
 
 FP_FOLD_ALL = -1
 FP_FOLD_CHANNEL = -2
 
-EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_fold", "fp_readout", "fp_attn_mass", "fp_advance",
-           "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version")
+EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_fold", "fp_readout", "fp_attn_mass",
+           "fp_advance", "fp_lora_workspace_bytes", "fp_adapter_lora", "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version")
 
 
 class FpGeometry(ctypes.Structure):
@@ -51,6 +52,11 @@ class FpKvPool(ctypes.Structure):
 
 class FpMask(ctypes.Structure):
     _fields_ = [("bits", c_ptr), ("word_offset", c_ptr), ("word_offset_host", c_ptr)]
+
+
+class FpLora(ctypes.Structure):
+    _fields_ = [("num_adapters", ctypes.c_int32), ("rank", ctypes.c_int32), ("d_in", ctypes.c_int32),
+                ("d_out", ctypes.c_int32), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
 
 
 class FpTuning(ctypes.Structure):
@@ -90,6 +96,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp_attn_mass.argtypes = [P(FpKvPool), P(FpGeometry), c_i32, P(FpMask), c_ptr, c_ptr, ctypes.c_size_t, P(FpTuning),
                                  c_ptr, c_ptr]
     lib.fp_attn_mass.restype = c_i32
+    lib.fp_lora_workspace_bytes.argtypes = [P(FpGeometry), P(FpLora)]
+    lib.fp_lora_workspace_bytes.restype = ctypes.c_int64
+    lib.fp_adapter_lora.argtypes = [P(FpGeometry), P(FpLora), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, ctypes.c_size_t,
+                                    c_ptr, c_ptr]
+    lib.fp_adapter_lora.restype = c_i32
     lib.fp_advance.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
     lib.fp_advance.restype = c_i32
     lib.fp_kv_bytes.argtypes = [c_i32, c_i32, c_i32, c_u64, c_i32]

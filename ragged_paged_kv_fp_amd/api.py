@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import FpError, FpGeometry, FpKvPool, FpMask, FpTuning
+from ._lib import FpError, FpGeometry, FpKvPool, FpLora, FpMask, FpTuning
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -190,6 +190,36 @@ def attn_mass(pool: Pool, geom: Geometry, num_q_heads: int, lse: torch.Tensor, w
                                             ctypes.byref(ms) if ms is not None else None, _ptr(lse),
                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                                             _tuning(split), _ptr(slot_mass), _stream(stream)))
+
+
+@dataclass
+class Lora:
+    """Adapters of one projection site: A [n][rank][d_in], B [n][d_out][rank] (bf16), scale [n] (fp32)."""
+
+    a: torch.Tensor
+    b: torch.Tensor
+    scale: torch.Tensor
+
+    def struct(self) -> FpLora:
+        n, r, d_in = self.a.shape
+        return FpLora(int(n), int(r), int(d_in), int(self.b.shape[1]), _ptr(self.a), _ptr(self.b), _ptr(self.scale))
+
+
+def lora_workspace_bytes(geom: Geometry, lora: Lora) -> int:
+    lib = _lib.load()
+    gs, ls = geom.struct(), lora.struct()
+    return _check("fp_lora_workspace_bytes", lib.fp_lora_workspace_bytes(ctypes.byref(gs), ctypes.byref(ls)))
+
+
+def adapter_lora(geom: Geometry, lora: Lora, adapter: torch.Tensor, x: torch.Tensor, y: torch.Tensor,
+                 out: torch.Tensor, workspace: torch.Tensor, status: torch.Tensor, stream=None) -> None:
+    """fp_adapter_lora: out = bf16(y + s_k B_k (A_k x)) per lane's adapter k (y kept where k < 0)."""
+    lib = _lib.load()
+    gs, ls = geom.struct(), lora.struct()
+    _check("fp_adapter_lora", lib.fp_adapter_lora(ctypes.byref(gs), ctypes.byref(ls), _ptr(adapter), _ptr(x),
+                                                  _ptr(y), _ptr(out), _ptr(workspace),
+                                                  workspace.numel() * workspace.element_size(), _ptr(status),
+                                                  _stream(stream)))
 
 
 def advance(pool: Pool, geom: Geometry, pos_offset: Optional[torch.Tensor] = None, stream=None) -> None:

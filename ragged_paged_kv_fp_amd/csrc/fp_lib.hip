@@ -437,6 +437,61 @@ int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_
     return FP_OK;
 }
 
+int64_t fp_lora_workspace_bytes(const fp_geometry *geom, const fp_lora *lora) {
+    if (!geom || !lora || !geom->indptr_host) return FP_ERR_NULL;
+    if (geom->num_rows < 0 || lora->rank < 1) return FP_ERR_SHAPE;
+    const int rp = (lora->rank + 31) / 32 * 32;
+    return (int64_t)align256(2 * sizeof(uint16_t) * (size_t)geom->num_rows * rp);
+}
+
+int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t *adapter, const void *x,
+                    const void *y, void *out, void *workspace, size_t workspace_bytes, int32_t *status,
+                    hipStream_t stream) {
+    if (!geom || !lora || !geom->indptr || !geom->indptr_host || !status) return FP_ERR_NULL;
+    if (geom->num_lanes < 1 || geom->num_lanes > kMaxLanes || geom->num_rows < 0) return FP_ERR_SHAPE;
+    const int32_t *ip = geom->indptr_host;
+    if (ip[0] != 0 || ip[geom->num_lanes] != geom->num_rows) return FP_ERR_SHAPE;
+    int max_n = 0;
+    for (int l = 0; l < geom->num_lanes; ++l) {
+        if (ip[l + 1] < ip[l]) return FP_ERR_SHAPE;
+        max_n = std::max(max_n, ip[l + 1] - ip[l]);
+    }
+    if (lora->num_adapters < 1 || lora->d_in < 1 || lora->d_out < 1) return FP_ERR_SHAPE;
+    if (lora->rank % 16 || lora->rank < 16 || lora->rank > 64 || lora->d_in % 64 || lora->d_out % 32)
+        return FP_ERR_UNSUPPORTED;
+    if (geom->num_rows == 0) return FP_OK;
+    if (!adapter || !x || !y || !out || !lora->a || !lora->b || !lora->scale || !workspace) return FP_ERR_NULL;
+    if ((int64_t)workspace_bytes < fp_lora_workspace_bytes(geom, lora)) return FP_ERR_WORKSPACE;
+    LoraArgs a;
+    a.indptr = geom->indptr;
+    a.L = geom->num_lanes;
+    a.adapter = adapter;
+    a.n_ad = lora->num_adapters;
+    a.r = lora->rank;
+    a.rp = (lora->rank + 31) / 32 * 32;
+    a.d_in = lora->d_in;
+    a.d_out = lora->d_out;
+    a.x = static_cast<const uint16_t *>(x);
+    a.y = static_cast<const uint16_t *>(y);
+    a.out = static_cast<uint16_t *>(out);
+    a.a = static_cast<const uint16_t *>(lora->a);
+    a.b = static_cast<const uint16_t *>(lora->b);
+    a.scale = lora->scale;
+    a.v = static_cast<uint16_t *>(workspace);
+    a.N = geom->num_rows;
+    a.status = status;
+    a.in_place = out == y;
+    const unsigned rbs = (unsigned)((max_n + 31) / 32);
+    const dim3 block(64 * kLoraWaves);
+    if (a.rp == 32) hipLaunchKernelGGL(lora_shrink_kernel<1>, dim3(rbs, a.L), block, 0, stream, a);
+    else hipLaunchKernelGGL(lora_shrink_kernel<2>, dim3(rbs, a.L), block, 0, stream, a);
+    int rc = launch_ok();
+    if (rc) return rc;
+    hipLaunchKernelGGL(lora_expand_kernel, dim3((unsigned)((a.d_out + kLoraCols - 1) / kLoraCols), rbs, a.L), block, 0,
+                       stream, a);
+    return launch_ok();
+}
+
 int fp_advance(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *pos_offset, int32_t *positions,
                int32_t *slots, int32_t *kv_len, hipStream_t stream) {
     if (!pool || !pool->committed_len) return FP_ERR_NULL;

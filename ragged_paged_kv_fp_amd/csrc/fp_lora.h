@@ -1,0 +1,147 @@
+// fp_lora.h - projection-site LoRA adapters: out = bf16(y + s_k * B_k (A_k x))
+// for the rows of every lane whose adapter id k is set, in two launches.
+//
+// shrink: one workgroup of four waves per (lane, 32-row block). V^T = A_k X^T
+//   on v_mfma_f32_32x32x16_bf16 (A_k rows as the A operand, the block's x rows
+//   as the B operand), the d_in sum split over the four waves and reduced
+//   through LDS; V (rank values per row) goes to the workspace as two bf16
+//   terms, hi = bf16(v) and lo = bf16(v - hi), which carry 16 significant bits.
+// expand: one workgroup of four waves per (lane, 32-row block, 128 output
+//   columns). Out^T = B_k V^T (B_k rows as the A operand: contiguous rank
+//   vectors; V rows as the B operand, hi and lo terms in two MFMAs), then
+//   y + s_k * acc in fp32 rounded to bf16; lane (row n, half h) holds columns
+//   8(i/4) + 4h + i%4 of row n, so y is read and out written as 8-byte runs.
+// Lanes without an adapter keep y bit for bit (copied unless out is y).
+#pragma once
+
+#include "fp_kernels.h"
+
+namespace fpk {
+
+constexpr int kLoraWaves = 4;
+constexpr int kLoraCols = 32 * kLoraWaves;  // output columns per expand workgroup
+
+struct LoraArgs {
+    const int32_t *indptr;
+    int L;
+    const int32_t *adapter;
+    int n_ad, r, rp, d_in, d_out;  // rp: rank padded to a multiple of 32 (workspace row stride)
+    const uint16_t *x, *y;
+    uint16_t *out;
+    const uint16_t *a, *b;
+    const float *scale;
+    uint16_t *v;                   // workspace bf16 [2][N][rp]: hi terms, then lo terms
+    int64_t N;
+    int32_t *status;
+    bool in_place;
+};
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return (uint16_t)(pack_bf16x2(f, f) & 0xFFFFu); }
+
+template <int MB>
+__global__ void __launch_bounds__(64 * kLoraWaves) lora_shrink_kernel(LoraArgs a) {
+    __shared__ float s_part[kLoraWaves][MB][32][33];
+    const int lane = blockIdx.y, rb = blockIdx.x;
+    const int r0 = a.indptr[lane], n = a.indptr[lane + 1] - r0;
+    if (32 * rb >= n) return;  // workgroup-uniform
+    const int k = a.adapter[lane];
+    if (k < 0 || k >= a.n_ad) return;  // the expand pass handles these lanes
+    const int wv = threadIdx.x / kWave, ln = lane_id(), nn = ln & 31, h = ln >> 5;
+    const int rowl = 32 * rb + nn;
+    const bool rv = rowl < n;
+    const uint16_t *xrow = a.x + (int64_t)(r0 + (rv ? rowl : 0)) * a.d_in + 8 * h;
+    const uint16_t *arow[MB];
+    bool av[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int m = 32 * mb + nn;
+        av[mb] = m < a.r;
+        arow[mb] = a.a + ((int64_t)k * a.r + (av[mb] ? m : 0)) * a.d_in + 8 * h;
+    }
+    f32x16 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+    const int steps = a.d_in / (16 * kLoraWaves);
+    const int kb = wv * steps * 16;  // this wave's share of d_in
+#pragma unroll 4
+    for (int st = 0; st < steps; ++st) {
+        const int kk = kb + 16 * st;
+        uint4 xf = *reinterpret_cast<const uint4 *>(xrow + kk);
+        if (!rv) xf = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            uint4 af = *reinterpret_cast<const uint4 *>(arow[mb] + kk);
+            if (!av[mb]) af = make_uint4(0, 0, 0, 0);
+            acc[mb] = mfma32(af, xf, acc[mb]);
+        }
+    }
+    // register i of lane (n, h) holds V^T[8(i/4) + 4h + i%4 (+32 mb)][n]
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_part[wv][mb][8 * (i >> 2) + 4 * h + (i & 3)][nn] = acc[mb][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 32 * 32 * MB; e += 64 * kLoraWaves) {
+        const int row = e / (32 * MB), m = e % (32 * MB);
+        if (32 * rb + row >= n) continue;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kLoraWaves; ++w) sum += s_part[w][m >> 5][m & 31][row];
+        const uint16_t hi = f32_to_bf16_bits(sum);
+        const int64_t at = (int64_t)(r0 + 32 * rb + row) * a.rp + m;
+        a.v[at] = hi;
+        a.v[a.N * a.rp + at] = f32_to_bf16_bits(sum - __uint_as_float((uint32_t)hi << 16));
+    }
+}
+
+__global__ void __launch_bounds__(64 * kLoraWaves) lora_expand_kernel(LoraArgs a) {
+    const int lane = blockIdx.z, rb = blockIdx.y;
+    const int r0 = a.indptr[lane], n = a.indptr[lane + 1] - r0;
+    if (32 * rb >= n) return;  // workgroup-uniform
+    const int k = a.adapter[lane];
+    const bool bad = k >= a.n_ad;
+    const bool none = k < 0 || bad;
+    if (bad && blockIdx.x == 0 && rb == 0 && threadIdx.x == 0) atomicOr(a.status, FP_ST_ADAPTER);
+    if (none && a.in_place) return;
+    const int wv = threadIdx.x / kWave, ln = lane_id(), nn = ln & 31, h = ln >> 5;
+    const int c0 = kLoraCols * blockIdx.x + 32 * wv;  // this wave's 32 output columns
+    if (c0 >= a.d_out) return;  // wave-uniform; no barrier in this kernel
+    const int rowl = 32 * rb + nn;
+    const bool rv = rowl < n;
+    const int64_t row = r0 + (rv ? rowl : 0);
+    f32x16 acc = {};
+    if (!none) {
+        const uint16_t *brow = a.b + ((int64_t)k * a.d_out + c0 + nn) * a.r + 8 * h;
+        const uint16_t *vrow = a.v + row * a.rp + 8 * h;
+        const int64_t lo = a.N * a.rp;
+        for (int s = 0; s < a.r / 16; ++s) {
+            const uint4 bf = *reinterpret_cast<const uint4 *>(brow + 16 * s);
+            uint4 vh = *reinterpret_cast<const uint4 *>(vrow + 16 * s);
+            uint4 vl = *reinterpret_cast<const uint4 *>(vrow + lo + 16 * s);
+            if (!rv) vh = vl = make_uint4(0, 0, 0, 0);
+            acc = mfma32(bf, vh, acc);
+            acc = mfma32(bf, vl, acc);
+        }
+    }
+    if (!rv) return;
+    const float sc = none ? 0.0f : a.scale[k];
+    const uint16_t *yrow = a.y + row * a.d_out;
+    uint16_t *orow = a.out + row * a.d_out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int col = c0 + 8 * q + 4 * h;
+        const uint2 yv = *reinterpret_cast<const uint2 *>(yrow + col);
+        uint2 ov;
+        if (none) {
+            ov = yv;
+        } else {
+            const float y0 = __uint_as_float(yv.x << 16), y1 = __uint_as_float(yv.x & 0xFFFF0000u);
+            const float y2 = __uint_as_float(yv.y << 16), y3 = __uint_as_float(yv.y & 0xFFFF0000u);
+            ov.x = pack_bf16x2(y0 + sc * acc[4 * q], y1 + sc * acc[4 * q + 1]);
+            ov.y = pack_bf16x2(y2 + sc * acc[4 * q + 2], y3 + sc * acc[4 * q + 3]);
+        }
+        *reinterpret_cast<uint2 *>(orow + col) = ov;
+    }
+}
+
+}  // namespace fpk

@@ -141,3 +141,22 @@ def run(wl_arrays, *, H_q, H_kv, d, theta, sm_scale, cap, prefix=None, committed
                 LSE[r][hq] = m + math.log(tot)
     do_fold(w, w.get("channel"))
     return dict(O=O, LSE=LSE, committed=committed, store=store, mass=mass)
+
+
+def lora(x, y, adapter, indptr, a, b, scale):
+    """Adapter output by explicit loops: out[r][i] = bf16(y + s * sum_j b[i][j] * sum_t a[j][t] x[t]).
+    Arguments are nested lists of bf16 bit patterns (scale: floats). Returns (bits, exact)."""
+    bits = [list(row) for row in y]
+    exact = [[bf16_value(v) for v in row] for row in y]
+    for lane in range(len(indptr) - 1):
+        k = int(adapter[lane])
+        if k < 0 or k >= len(a):
+            continue
+        for r in range(int(indptr[lane]), int(indptr[lane + 1])):
+            xv = [bf16_value(t) for t in x[r]]
+            v = [sum(bf16_value(a[k][j][t]) * xv[t] for t in range(len(xv))) for j in range(len(a[k]))]
+            for i in range(len(y[r])):
+                e = bf16_value(y[r][i]) + scale[k] * sum(bf16_value(b[k][i][j]) * v[j] for j in range(len(v)))
+                exact[r][i] = e
+                bits[r][i] = bf16_round_exact(e)
+    return bits, exact

@@ -57,6 +57,7 @@ def test_header_constants_match_binding_and_oracle():
     assert consts["FP_ST_READOUT_RANGE"] == oracle.ST_READOUT_RANGE
     assert consts["FP_ST_MASK_SHORT"] == oracle.ST_MASK_SHORT
     assert consts["FP_ST_PAGE_RANGE"] == oracle.ST_PAGE_RANGE
+    assert consts["FP_ST_ADAPTER"] == oracle.ST_ADAPTER
     assert consts["FP_FOLD_ALL"] == oracle.FOLD_ALL and consts["FP_FOLD_CHANNEL"] == oracle.FOLD_CHANNEL
 
 

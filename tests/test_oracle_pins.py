@@ -449,3 +449,42 @@ def test_attn_mass_zero_query_is_uniform():
     for g in range(wl.H_kv):
         np.testing.assert_allclose(mass[g, base:base + 37], want, rtol=1e-13, atol=0)
         assert np.all(mass[g, base + 37:] == 0)
+
+
+# ----------------------------------------------------------------------------- projection-site LoRA
+
+def test_lora_matches_bruteforce():
+    ip = np.array([0, 2, 2, 5, 6], dtype=np.int32)
+    lw = W.make_lora(7, ip, d_in=8, d_out=6, rank=3, num_adapters=3, none_frac=0.0)
+    lw.adapter[:] = [2, 0, 1, -1]
+    out, exact, st = oracle.lora(lw.x, lw.y, lw.adapter, ip, lw.a, lw.b, lw.scale)
+    bits, ex = bf.lora(lw.x.tolist(), lw.y.tolist(), lw.adapter, ip, lw.a.tolist(), lw.b.tolist(),
+                       [float(s) for s in lw.scale])
+    assert st == 0
+    assert out.tolist() == bits
+    assert np.max(np.abs(exact - np.array(ex))) <= 1e-12
+    assert np.array_equal(out[5], lw.y[5])  # lane 3 has no adapter
+
+
+def test_lora_zero_b_and_out_of_range_id_keep_y():
+    ip = np.array([0, 3, 7], dtype=np.int32)
+    lw = W.make_lora(3, ip, d_in=16, d_out=8, rank=4, num_adapters=2, none_frac=0.0)
+    lw.adapter[:] = [0, 5]
+    lw.b[0] = 0
+    out, _, st = oracle.lora(lw.x, lw.y, lw.adapter, ip, lw.a, lw.b, lw.scale)
+    assert np.array_equal(out, lw.y) and st == oracle.ST_ADAPTER
+
+
+def test_lora_rank_one_closed_form():
+    # A = e_j (selects x[:, j]), B = a column c: out = y + s * c * x_j, element by element
+    ip = np.array([0, 4], dtype=np.int32)
+    lw = W.make_lora(5, ip, d_in=12, d_out=10, rank=1, num_adapters=1, none_frac=0.0)
+    j = 7
+    lw.a[:] = 0
+    lw.a[0, 0, j] = 0x3F80  # 1.0
+    out, exact, _ = oracle.lora(lw.x, lw.y, lw.adapter, ip, lw.a, lw.b, lw.scale)
+    c = oracle.bf16_to_f64(lw.b[0, :, 0])
+    xj = oracle.bf16_to_f64(lw.x[:, j])
+    want = oracle.bf16_to_f64(lw.y) + float(lw.scale[0]) * np.outer(xj, c)
+    assert np.array_equal(exact, want)
+    assert np.array_equal(out, oracle.f64_to_bf16(want))

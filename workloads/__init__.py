@@ -13,7 +13,9 @@ from .gen import (  # noqa: F401
     RunAhead,
     Workload,
     bf16_bits_from_f32,
+    Lora,
     make_config,
+    make_lora,
     make_random,
     make_run_ahead,
     split_pass,

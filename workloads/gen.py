@@ -533,3 +533,38 @@ def split_pass(p: Pass, first_rows) -> tuple:
     first = sub(a_rows, a_ip, a_kv, [FOLD_ALL] * L)
     second = sub(b_rows, b_ip, p.kv_len, p.fold)
     return first, second
+
+
+@dataclass
+class Lora:
+    """Inputs of a projection-site LoRA step: rows of a pass (x, base output y),
+    per-lane adapter ids (-1: none) and the adapters' weights and scales."""
+
+    indptr: np.ndarray     # int32 [L+1]
+    adapter: np.ndarray    # int32 [L]
+    x: np.ndarray          # uint16 bf16 [N][d_in]
+    y: np.ndarray          # uint16 bf16 [N][d_out]
+    a: np.ndarray          # uint16 bf16 [n_ad][r][d_in]
+    b: np.ndarray          # uint16 bf16 [n_ad][d_out][r]
+    scale: np.ndarray      # float32 [n_ad]
+
+
+def make_lora(seed: int, indptr, *, d_in: int, d_out: int, rank: int, num_adapters: int,
+              none_frac: float = 0.2) -> Lora:
+    """x, y ~ N(0,1); A ~ N(0, 1/d_in), B ~ N(0, 1/rank) so B(Ax) is O(1) like y;
+    scales ~ U[0.5, 2); each lane takes a uniform adapter id, or none with
+    probability none_frac. All rounded to bf16."""
+    rngs = _rngs(seed)
+    indptr = np.asarray(indptr, dtype=np.int32)
+    L, N = len(indptr) - 1, int(indptr[-1])
+    g = rngs["lengths"]
+    adapter = g.integers(0, num_adapters, size=L).astype(np.int32)
+    adapter[g.random(L) < none_frac] = -1
+    x = _normal_bf16(rngs["q"], (N, d_in))
+    y = _normal_bf16(rngs["v"], (N, d_out))
+    a = bf16_bits_from_f32(rngs["k"].standard_normal((num_adapters, rank, d_in), dtype=np.float32)
+                           / np.float32(np.sqrt(d_in)))
+    b = bf16_bits_from_f32(rngs["prefix_kv"].standard_normal((num_adapters, d_out, rank), dtype=np.float32)
+                           / np.float32(np.sqrt(rank)))
+    scale = rngs["channel"].uniform(0.5, 2.0, size=num_adapters).astype(np.float32)
+    return Lora(indptr=indptr, adapter=adapter, x=x, y=y, a=a, b=b, scale=scale)
