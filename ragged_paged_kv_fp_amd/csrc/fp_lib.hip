@@ -437,11 +437,24 @@ int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_
     return FP_OK;
 }
 
+namespace {
+// (lane, 32-row block) work items of a pass, from the host copy of indptr
+int64_t lora_items(const fp_geometry *geom) {
+    int64_t t = 0;
+    for (int l = 0; l < geom->num_lanes; ++l) {
+        const int n = geom->indptr_host[l + 1] - geom->indptr_host[l];
+        if (n > 0) t += (n + 31) / 32;
+    }
+    return t;
+}
+}  // namespace
+
 int64_t fp_lora_workspace_bytes(const fp_geometry *geom, const fp_lora *lora) {
     if (!geom || !lora || !geom->indptr_host) return FP_ERR_NULL;
-    if (geom->num_rows < 0 || lora->rank < 1) return FP_ERR_SHAPE;
+    if (geom->num_rows < 0 || geom->num_lanes < 1 || lora->rank < 1) return FP_ERR_SHAPE;
     const int rp = (lora->rank + 31) / 32 * 32;
-    return (int64_t)align256(2 * sizeof(uint16_t) * (size_t)geom->num_rows * rp);
+    return (int64_t)(align256(2 * sizeof(uint16_t) * (size_t)geom->num_rows * rp) +
+                     align256(sizeof(int2) * (size_t)lora_items(geom)));
 }
 
 int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t *adapter, const void *x,
@@ -451,13 +464,11 @@ int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t 
     if (geom->num_lanes < 1 || geom->num_lanes > kMaxLanes || geom->num_rows < 0) return FP_ERR_SHAPE;
     const int32_t *ip = geom->indptr_host;
     if (ip[0] != 0 || ip[geom->num_lanes] != geom->num_rows) return FP_ERR_SHAPE;
-    int max_n = 0;
-    for (int l = 0; l < geom->num_lanes; ++l) {
+    for (int l = 0; l < geom->num_lanes; ++l)
         if (ip[l + 1] < ip[l]) return FP_ERR_SHAPE;
-        max_n = std::max(max_n, ip[l + 1] - ip[l]);
-    }
     if (lora->num_adapters < 1 || lora->d_in < 1 || lora->d_out < 1) return FP_ERR_SHAPE;
-    if (lora->rank % 16 || lora->rank < 16 || lora->rank > 64 || lora->d_in % 64 || lora->d_out % 32)
+    if (lora->rank % 16 || lora->rank < 16 || lora->rank > 64 || lora->d_in % 64 || lora->d_out % 32 ||
+        lora->d_out > 65535 * kLoraCols)
         return FP_ERR_UNSUPPORTED;
     if (geom->num_rows == 0) return FP_OK;
     if (!adapter || !x || !y || !out || !lora->a || !lora->b || !lora->scale || !workspace) return FP_ERR_NULL;
@@ -477,18 +488,26 @@ int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t 
     a.a = static_cast<const uint16_t *>(lora->a);
     a.b = static_cast<const uint16_t *>(lora->b);
     a.scale = lora->scale;
+    const int64_t n_items = lora_items(geom);
+    if (n_items > INT32_MAX / 2) return FP_ERR_UNSUPPORTED;
     a.v = static_cast<uint16_t *>(workspace);
     a.N = geom->num_rows;
+    int2 *items = reinterpret_cast<int2 *>(static_cast<char *>(workspace) +
+                                           align256(2 * sizeof(uint16_t) * (size_t)geom->num_rows * a.rp));
+    a.items = items;
+    a.n_items = (int)n_items;
     a.status = status;
     a.in_place = out == y;
-    const unsigned rbs = (unsigned)((max_n + 31) / 32);
-    const dim3 block(64 * kLoraWaves);
-    if (a.rp == 32) hipLaunchKernelGGL(lora_shrink_kernel<1>, dim3(rbs, a.L), block, 0, stream, a);
-    else hipLaunchKernelGGL(lora_shrink_kernel<2>, dim3(rbs, a.L), block, 0, stream, a);
+    hipLaunchKernelGGL(lora_plan_kernel, dim3(1), dim3(kLoraPlanThreads), 0, stream, geom->indptr, a.L, items,
+                       a.n_items, status);
     int rc = launch_ok();
     if (rc) return rc;
-    hipLaunchKernelGGL(lora_expand_kernel, dim3((unsigned)((a.d_out + kLoraCols - 1) / kLoraCols), rbs, a.L), block, 0,
-                       stream, a);
+    const dim3 block(64 * kLoraWaves);
+    if (a.rp == 32) hipLaunchKernelGGL(lora_shrink_kernel<1>, dim3((unsigned)n_items), block, 0, stream, a);
+    else hipLaunchKernelGGL(lora_shrink_kernel<2>, dim3((unsigned)n_items), block, 0, stream, a);
+    if ((rc = launch_ok())) return rc;
+    hipLaunchKernelGGL(lora_expand_kernel, dim3((unsigned)n_items, (unsigned)((a.d_out + kLoraCols - 1) / kLoraCols)),
+                       block, 0, stream, a);
     return launch_ok();
 }
 

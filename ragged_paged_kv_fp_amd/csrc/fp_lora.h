@@ -12,6 +12,8 @@
 //   y + s_k * acc in fp32 rounded to bf16; lane (row n, half h) holds columns
 //   8(i/4) + 4h + i%4 of row n, so y is read and out written as 8-byte runs.
 // Lanes without an adapter keep y bit for bit (copied unless out is y).
+// A plan kernel first lists the (lane, 32-row block) work items in the
+// workspace, so both launches cover exactly the pass's row blocks.
 #pragma once
 
 #include "fp_kernels.h"
@@ -32,18 +34,61 @@ struct LoraArgs {
     const float *scale;
     uint16_t *v;                   // workspace bf16 [2][N][rp]: hi terms, then lo terms
     int64_t N;
+    const int2 *items;             // workspace: (lane, row block) per work item, lane -1 past the list
+    int n_items;                   // work items the host counted from its copy of indptr
     int32_t *status;
     bool in_place;
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return (uint16_t)(pack_bf16x2(f, f) & 0xFFFFu); }
 
+constexpr int kLoraPlanThreads = 1024;
+
+// One workgroup: items in lane order, a lane of n rows giving ceil(n/32)
+// blocks. If the device offsets disagree with the host's count, the list is
+// cut (or padded with lane -1) to the host's length and FP_ST_PLAN_MISMATCH set.
+__global__ void __launch_bounds__(kLoraPlanThreads) lora_plan_kernel(const int32_t *indptr, int L, int2 *items,
+                                                                       int n_items, int32_t *status) {
+    __shared__ int s_tot[kLoraPlanThreads];
+    constexpr int PER = kMaxLanes / kLoraPlanThreads;  // lanes per thread
+    const int t = threadIdx.x;
+    int cnt[PER], mine = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int l = t * PER + u;
+        const int n = l < L ? indptr[l + 1] - indptr[l] : 0;
+        cnt[u] = n > 0 ? min((n + 31) >> 5, n_items) : 0;
+        mine = min(mine + cnt[u], n_items);
+    }
+    // inclusive scan saturating at n_items: no sum can overflow and every
+    // start below stays in [0, n_items]
+    s_tot[t] = mine;
+    __syncthreads();
+    for (int off = 1; off < kLoraPlanThreads; off <<= 1) {
+        const int v = t >= off ? s_tot[t - off] : 0;
+        __syncthreads();
+        s_tot[t] = min(s_tot[t] + v, n_items);
+        __syncthreads();
+    }
+    int base = s_tot[t] - mine;
+    const int total = s_tot[kLoraPlanThreads - 1];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        for (int b = 0; b < cnt[u] && base + b < n_items; ++b) items[base + b] = make_int2(t * PER + u, b);
+        base += cnt[u];
+    }
+    for (int i = total + t; i < n_items; i += kLoraPlanThreads) items[i] = make_int2(-1, 0);
+    if (t == 0 && total != n_items) atomicOr(status, FP_ST_PLAN_MISMATCH);
+}
+
 template <int MB>
 __global__ void __launch_bounds__(64 * kLoraWaves) lora_shrink_kernel(LoraArgs a) {
     __shared__ float s_part[kLoraWaves][MB][32][33];
-    const int lane = blockIdx.y, rb = blockIdx.x;
+    const int2 item = a.items[blockIdx.x];
+    const int lane = item.x, rb = item.y;
+    if (lane < 0) return;  // workgroup-uniform
     const int r0 = a.indptr[lane], n = a.indptr[lane + 1] - r0;
-    if (32 * rb >= n) return;  // workgroup-uniform
+    if (32 * rb >= n) return;
     const int k = a.adapter[lane];
     if (k < 0 || k >= a.n_ad) return;  // the expand pass handles these lanes
     const int wv = threadIdx.x / kWave, ln = lane_id(), nn = ln & 31, h = ln >> 5;
@@ -95,16 +140,18 @@ __global__ void __launch_bounds__(64 * kLoraWaves) lora_shrink_kernel(LoraArgs a
 }
 
 __global__ void __launch_bounds__(64 * kLoraWaves) lora_expand_kernel(LoraArgs a) {
-    const int lane = blockIdx.z, rb = blockIdx.y;
+    const int2 item = a.items[blockIdx.x];
+    const int lane = item.x, rb = item.y;
+    if (lane < 0) return;  // workgroup-uniform
     const int r0 = a.indptr[lane], n = a.indptr[lane + 1] - r0;
-    if (32 * rb >= n) return;  // workgroup-uniform
+    if (32 * rb >= n) return;
     const int k = a.adapter[lane];
     const bool bad = k >= a.n_ad;
     const bool none = k < 0 || bad;
-    if (bad && blockIdx.x == 0 && rb == 0 && threadIdx.x == 0) atomicOr(a.status, FP_ST_ADAPTER);
+    if (bad && blockIdx.y == 0 && rb == 0 && threadIdx.x == 0) atomicOr(a.status, FP_ST_ADAPTER);
     if (none && a.in_place) return;
     const int wv = threadIdx.x / kWave, ln = lane_id(), nn = ln & 31, h = ln >> 5;
-    const int c0 = kLoraCols * blockIdx.x + 32 * wv;  // this wave's 32 output columns
+    const int c0 = kLoraCols * blockIdx.y + 32 * wv;  // this wave's 32 output columns
     if (c0 >= a.d_out) return;  // wave-uniform; no barrier in this kernel
     const int rowl = 32 * rb + nn;
     const bool rv = rowl < n;
