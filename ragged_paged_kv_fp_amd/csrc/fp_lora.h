@@ -8,9 +8,9 @@
 //   terms, hi = bf16(v) and lo = bf16(v - hi), which carry 16 significant bits.
 // expand: one workgroup of four waves per (lane, 32-row block, 128 output
 //   columns). Out^T = B_k V^T (B_k rows as the A operand: contiguous rank
-//   vectors; V rows as the B operand, hi and lo terms in two MFMAs), then
-//   y + s_k * acc in fp32 rounded to bf16; lane (row n, half h) holds columns
-//   8(i/4) + 4h + i%4 of row n, so y is read and out written as 8-byte runs.
+//   vectors; V rows as the B operand, hi and lo terms in two MFMAs); the
+//   scaled products pass through LDS so that y is read and out written as
+//   whole 256-byte row runs, y + s_k * (B_k v) in fp32 rounded to bf16.
 // Lanes without an adapter keep y bit for bit (copied unless out is y).
 // A plan kernel first lists the (lane, 32-row block) work items in the
 // workspace, so both launches cover exactly the pass's row blocks.
@@ -140,6 +140,7 @@ __global__ void __launch_bounds__(64 * kLoraWaves) lora_shrink_kernel(LoraArgs a
 }
 
 __global__ void __launch_bounds__(64 * kLoraWaves) lora_expand_kernel(LoraArgs a) {
+    __shared__ __attribute__((aligned(16))) float s_d[32][kLoraCols + 4];  // s_k * (B_k v), [row][column]
     const int2 item = a.items[blockIdx.x];
     const int lane = item.x, rb = item.y;
     if (lane < 0) return;  // workgroup-uniform
@@ -150,45 +151,53 @@ __global__ void __launch_bounds__(64 * kLoraWaves) lora_expand_kernel(LoraArgs a
     const bool none = k < 0 || bad;
     if (bad && blockIdx.y == 0 && rb == 0 && threadIdx.x == 0) atomicOr(a.status, FP_ST_ADAPTER);
     if (none && a.in_place) return;
-    const int wv = threadIdx.x / kWave, ln = lane_id(), nn = ln & 31, h = ln >> 5;
-    const int c0 = kLoraCols * blockIdx.y + 32 * wv;  // this wave's 32 output columns
-    if (c0 >= a.d_out) return;  // wave-uniform; no barrier in this kernel
-    const int rowl = 32 * rb + nn;
-    const bool rv = rowl < n;
-    const int64_t row = r0 + (rv ? rowl : 0);
-    f32x16 acc = {};
+    const int cw = kLoraCols * blockIdx.y;  // the workgroup's first output column
     if (!none) {
-        const uint16_t *brow = a.b + ((int64_t)k * a.d_out + c0 + nn) * a.r + 8 * h;
-        const uint16_t *vrow = a.v + row * a.rp + 8 * h;
-        const int64_t lo = a.N * a.rp;
-        for (int s = 0; s < a.r / 16; ++s) {
-            const uint4 bf = *reinterpret_cast<const uint4 *>(brow + 16 * s);
-            uint4 vh = *reinterpret_cast<const uint4 *>(vrow + 16 * s);
-            uint4 vl = *reinterpret_cast<const uint4 *>(vrow + lo + 16 * s);
-            if (!rv) vh = vl = make_uint4(0, 0, 0, 0);
-            acc = mfma32(bf, vh, acc);
-            acc = mfma32(bf, vl, acc);
+        const int wv = threadIdx.x / kWave, ln = lane_id(), nn = ln & 31, h = ln >> 5;
+        const int c0 = cw + 32 * wv;  // this wave's 32 output columns
+        const int rowl = 32 * rb + nn;
+        const bool rv = rowl < n;
+        const int64_t row = r0 + (rv ? rowl : 0);
+        f32x16 acc = {};
+        if (c0 < a.d_out) {  // wave-uniform
+            const uint16_t *brow = a.b + ((int64_t)k * a.d_out + c0 + nn) * a.r + 8 * h;
+            const uint16_t *vrow = a.v + row * a.rp + 8 * h;
+            const int64_t lo = a.N * a.rp;
+            for (int s = 0; s < a.r / 16; ++s) {
+                const uint4 bf = *reinterpret_cast<const uint4 *>(brow + 16 * s);
+                uint4 vh = *reinterpret_cast<const uint4 *>(vrow + 16 * s);
+                uint4 vl = *reinterpret_cast<const uint4 *>(vrow + lo + 16 * s);
+                if (!rv) vh = vl = make_uint4(0, 0, 0, 0);
+                acc = mfma32(bf, vh, acc);
+                acc = mfma32(bf, vl, acc);
+            }
         }
-    }
-    if (!rv) return;
-    const float sc = none ? 0.0f : a.scale[k];
-    const uint16_t *yrow = a.y + row * a.d_out;
-    uint16_t *orow = a.out + row * a.d_out;
+        const float sc = a.scale[k];
+        // register i of lane (n, h): column 8(i/4) + 4h + i%4 of row n
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int col = c0 + 8 * q + 4 * h;
-        const uint2 yv = *reinterpret_cast<const uint2 *>(yrow + col);
-        uint2 ov;
-        if (none) {
-            ov = yv;
-        } else {
-            const float y0 = __uint_as_float(yv.x << 16), y1 = __uint_as_float(yv.x & 0xFFFF0000u);
-            const float y2 = __uint_as_float(yv.y << 16), y3 = __uint_as_float(yv.y & 0xFFFF0000u);
-            ov.x = pack_bf16x2(y0 + sc * acc[4 * q], y1 + sc * acc[4 * q + 1]);
-            ov.y = pack_bf16x2(y2 + sc * acc[4 * q + 2], y3 + sc * acc[4 * q + 3]);
-        }
-        *reinterpret_cast<uint2 *>(orow + col) = ov;
+        for (int i = 0; i < 16; ++i) s_d[nn][32 * wv + 8 * (i >> 2) + 4 * h + (i & 3)] = sc * acc[i];
+        __syncthreads();
     }
+    // each thread: 16 consecutive columns of one row, so a row's 256 bytes
+    // are read and written by eight neighbouring threads
+    const int rr = threadIdx.x >> 3, cs = 16 * (threadIdx.x & 7);
+    const int col = cw + cs;
+    if (32 * rb + rr >= n || col >= a.d_out) return;
+    const int64_t at = (int64_t)(r0 + 32 * rb + rr) * a.d_out + col;
+    const uint4 y0 = *reinterpret_cast<const uint4 *>(a.y + at);
+    const uint4 y1 = *reinterpret_cast<const uint4 *>(a.y + at + 8);
+    if (none) {
+        *reinterpret_cast<uint4 *>(a.out + at) = y0;
+        *reinterpret_cast<uint4 *>(a.out + at + 8) = y1;
+        return;
+    }
+    const float *d = &s_d[rr][cs];
+    auto mix = [&](uint32_t w, int j) {  // two bf16 of y plus two deltas, rounded to bf16
+        return pack_bf16x2(__uint_as_float(w << 16) + d[j], __uint_as_float(w & 0xFFFF0000u) + d[j + 1]);
+    };
+    *reinterpret_cast<uint4 *>(a.out + at) = make_uint4(mix(y0.x, 0), mix(y0.y, 2), mix(y0.z, 4), mix(y0.w, 6));
+    *reinterpret_cast<uint4 *>(a.out + at + 8) =
+        make_uint4(mix(y1.x, 8), mix(y1.y, 10), mix(y1.z, 12), mix(y1.w, 14));
 }
 
 }  // namespace fpk
