@@ -327,6 +327,9 @@ def main(argv=None):
     ap.add_argument("--lora", action="store_true",
                     help="time projection-site LoRA (rank 16, 8 adapters, d_in = d_out = 4096) on config 3's rows "
                          "and config 2's rows")
+    ap.add_argument("--run-ahead", action="store_true",
+                    help="time a repeating speculative decode loop (geometry advanced on the device) eagerly and "
+                         "as one HIP-graph replay per pass")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run 5 plain device copies of MIB MiB (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -364,6 +367,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": nbytes}), file=sys.stderr, flush=True)
         del src, dst
+    if args.run_ahead:
+        print(json.dumps(run_ahead_bench(W, runner, args.seed, args.steps, args.warmup)), flush=True)
+        return 0
     if args.lora:
         print(json.dumps(lora_bench(W, args.seed, args.steps, args.warmup)), flush=True)
         return 0
@@ -430,6 +436,49 @@ def main(argv=None):
         line["cpu_baseline"] = cpu_baseline(wl, cfg, unit)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def run_ahead_bench(W, runner, seed, K, Wm) -> dict:
+    """A repeating decode loop at the decode-wave shape (64 lanes, prompts up to
+    8192 slots, 32/8 heads, d=128, P=16, each lane drafting 0/1/2/4/8 rows per
+    pass and the fold committing a device-channel count), every pass taking
+    its geometry from fp_advance. K passes enqueued eagerly (five ABI calls per
+    pass) and K as one HIP-graph replay per pass, each after the copies of that
+    pass's inputs into the loop's buffers: device and host ms per pass."""
+    import torch
+
+    ra = W.make_run_ahead(seed, H_kv=8, G=4, d=128, P=16, num_lanes=64, passes=Wm + K, max_prompt=8192)
+    res = {"metric": "run-ahead decode pass (geometry advanced on the device), eager vs HIP-graph replay",
+           "config": {"workload": "64 lanes, prompts U{0..8192}, H_q=32 H_kv=8 d=128 P=16, drafts 0/1/2/4/8 rows "
+                                  "per lane, channel fold", "rows_per_pass": int(ra.indptr[-1]), "seed": seed},
+           "steps": K, "warmup": Wm}
+    for mode in ("eager", "graph"):
+        lp = runner.RunAheadLoop(ra)
+        go = lp.one_pass
+        if mode == "graph":
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):  # recording runs nothing: the loop state is unchanged
+                lp.one_pass()
+            torch.cuda.synchronize()
+            go = graph.replay
+        for t in range(Wm):
+            lp.load(t)
+            go()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        e0.record()
+        for t in range(Wm, Wm + K):
+            lp.load(t)
+            go()
+        e1.record()
+        h1 = time.perf_counter()
+        torch.cuda.synchronize()
+        res[mode] = {"device_ms_per_pass": round(e0.elapsed_time(e1) / K, 4),
+                     "host_ms_per_pass": round((h1 - h0) * 1e3 / K, 4), "status": int(lp.status.cpu()[0])}
+        del lp
+    return res
 
 
 def lora_bench(W, seed, K, Wm) -> dict:
