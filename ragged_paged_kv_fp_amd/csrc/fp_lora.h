@@ -108,16 +108,47 @@ __global__ void __launch_bounds__(64 * kLoraWaves) lora_shrink_kernel(LoraArgs a
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
     const int steps = a.d_in / (16 * kLoraWaves);
     const int kb = wv * steps * 16;  // this wave's share of d_in
-#pragma unroll 4
-    for (int st = 0; st < steps; ++st) {
+    // groups of four 16-wide steps in two register buffers: the next group's
+    // loads are in flight while the current group's MFMAs run
+    constexpr int GS = 4;
+    struct Grp {
+        uint4 x[GS], a[MB][GS];
+    };
+    auto load = [&](int g, Grp &b) {
+#pragma unroll
+        for (int j = 0; j < GS; ++j) {
+            const int kk = kb + 16 * (GS * g + j);
+            b.x[j] = *reinterpret_cast<const uint4 *>(xrow + kk);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) b.a[mb][j] = *reinterpret_cast<const uint4 *>(arow[mb] + kk);
+        }
+    };
+    auto compute = [&](const Grp &b) {
+#pragma unroll
+        for (int j = 0; j < GS; ++j) {
+            const uint4 xf = rv ? b.x[j] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32(av[mb] ? b.a[mb][j] : make_uint4(0, 0, 0, 0), xf, acc[mb]);
+        }
+    };
+    const int groups = steps / GS;
+    Grp b0, b1;
+    int g = 0;
+    if (groups > 0) load(0, b0);
+    for (; g + 1 < groups; g += 2) {
+        load(g + 1, b1);
+        compute(b0);
+        if (g + 2 < groups) load(g + 2, b0);
+        compute(b1);
+    }
+    if (g < groups) compute(b0);
+    for (int st = GS * groups; st < steps; ++st) {  // the last steps of a d_in that is not a multiple of 256
         const int kk = kb + 16 * st;
-        uint4 xf = *reinterpret_cast<const uint4 *>(xrow + kk);
-        if (!rv) xf = make_uint4(0, 0, 0, 0);
+        const uint4 xf = rv ? *reinterpret_cast<const uint4 *>(xrow + kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            uint4 af = *reinterpret_cast<const uint4 *>(arow[mb] + kk);
-            if (!av[mb]) af = make_uint4(0, 0, 0, 0);
-            acc[mb] = mfma32(af, xf, acc[mb]);
+            const uint4 af = *reinterpret_cast<const uint4 *>(arow[mb] + kk);
+            acc[mb] = mfma32(av[mb] ? af : make_uint4(0, 0, 0, 0), xf, acc[mb]);
         }
     }
     // register i of lane (n, h) holds V^T[8(i/4) + 4h + i%4 (+32 mb)][n]
