@@ -346,7 +346,7 @@ def main(argv=None):
         print(json.dumps(rec))
         return 0
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: this library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         return 2
 
     import torch

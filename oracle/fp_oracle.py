@@ -23,7 +23,7 @@ accounting of the two Pie reviews (section 2.1/2.2, Eqs. (1) and (2)):
   readout  by default the last row of each lane, or caller-chosen rows
            ("Readouts").
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * RoPE pairs interleaved dims (2i, 2i+1) with w_i = theta^(-2i/d) (the
     RoFormer definition); K is stored rotated, Q is rotated at use, unrounded.
   * Rotated K is rounded once, to nearest-even, from fp64 to bf16.
