@@ -210,8 +210,10 @@ int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, con
  * slots and KV heads the pass adds the count of (row, query head) pairs that
  * read at least one slot.
  *   Call after fp_attend on the same stream with the same pool, geom,
- *   num_q_heads, mask, tuning and workspace: it reads the rotated queries that
- *   fp_attend left in the workspace and fp_attend's lse output (non-null).
+ *   num_q_heads, mask and workspace: it reads the rotated queries that
+ *   fp_attend left at the start of the workspace and fp_attend's lse output
+ *   (non-null); tuning may differ from fp_attend's (it is only validated).
+ *   The workspace must hold at least the rotated queries, N * H_q * d * 2 bytes.
  *   slot_mass: fp32 [H_kv][S] device, accumulated into (zero it for the mass of
  *   one pass); entries of slots at or past kv_len are not touched.
  * Deterministic: every output word has one writer and a fixed summation order.

@@ -149,11 +149,13 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
         }
     }
     if (p.n_dec > INT32_MAX / 2 || p.n_pre > INT32_MAX / 2 || p.sum_words > INT32_MAX / 2) return FP_ERR_UNSUPPORTED;
+    // the rotated Q comes first: its place depends only on the rows and heads,
+    // so fp_attn_mass finds it whatever tuning or mask the plan had
     size_t off = 0;
+    p.off_qrot = off; off = align256(off + sizeof(uint16_t) * (size_t)p.N * Hq * p.D);
     p.off_lane = off; off = align256(off + sizeof(LaneInfo) * (size_t)p.L);
     p.off_dec = off;  off = align256(off + sizeof(int4) * (size_t)p.n_dec);
     p.off_pre = off;  off = align256(off + sizeof(int4) * (size_t)p.n_pre);
-    p.off_qrot = off; off = align256(off + sizeof(uint16_t) * (size_t)p.N * Hq * p.D);
     p.off_po = off;   off = align256(off + (p.merge ? sizeof(float) * (size_t)p.n_dec * p.ncols_max * p.D : 0));
     p.off_pml = off;  off = align256(off + (p.merge ? sizeof(float) * (size_t)p.n_dec * 64 : 0));
     p.off_sum = off;  off = align256(off + sizeof(uint32_t) * (size_t)p.sum_words);
@@ -388,7 +390,7 @@ int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_
     if (rc) return rc;
     if (p.N == 0) return FP_OK;
     if (!lse || !workspace || !slot_mass) return FP_ERR_NULL;
-    if (workspace_bytes < p.total) return FP_ERR_WORKSPACE;
+    if (workspace_bytes < sizeof(uint16_t) * (size_t)p.N * p.Hq * p.D) return FP_ERR_WORKSPACE;  // the rotated Q
     const int32_t *pp = pool->page_indptr_host;
     int max_pages = 0;
     for (int l = 0; l < p.L; ++l) max_pages = std::max(max_pages, pp[l + 1] - pp[l]);

@@ -129,3 +129,20 @@ def test_mass_deterministic_and_accumulates():
     api.attn_mass(ds.pool, ds.geom, wl.H_q, ds.lse, ds.workspace, b, ds.mask, ds.split)
     torch.cuda.synchronize()
     assert torch.equal(b, 2 * a)
+
+
+def test_mass_does_not_depend_on_tuning():
+    import torch
+
+    from ragged_paged_kv_fp_amd import api
+
+    wl = W.make_config(2, seed=2, scale="small")
+    ds = pu.gpu_run(wl, split=64)
+    S = int(wl.page_indptr[-1]) * wl.P
+    outs = []
+    for split in (64, None, 4096):
+        m = torch.zeros((wl.H_kv, S), dtype=torch.float32, device=ds.device)
+        api.attn_mass(ds.pool, ds.geom, wl.H_q, ds.lse, ds.workspace, m, ds.mask, split)
+        outs.append(m)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
