@@ -158,3 +158,54 @@ def test_readout_default_count_checked(lib):
     st = ctypes.c_int32(0)
     assert lib.fp_readout(ctypes.byref(g), FAKE, 8, None, 3, FAKE, ctypes.addressof(st), None) == -2
     assert lib.fp_readout(ctypes.byref(g), FAKE, 8, None, 2, FAKE, None, None) == -1
+
+
+def test_attn_mass_and_advance_validation(lib):
+    g, p, keep = _structs()
+    st = ctypes.c_int32(0)
+    # mass: lse, workspace and output are required; the workspace must hold the rotated Q
+    assert lib.fp_attn_mass(ctypes.byref(p), ctypes.byref(g), 4, None, None, FAKE, 1 << 20, None, FAKE, None) == -1
+    assert lib.fp_attn_mass(ctypes.byref(p), ctypes.byref(g), 4, None, FAKE, FAKE, 1 << 20, None, None, None) == -1
+    assert lib.fp_attn_mass(ctypes.byref(p), ctypes.byref(g), 4, None, FAKE, FAKE, 16, None, FAKE, None) == -4
+    assert lib.fp_attn_mass(ctypes.byref(p), ctypes.byref(g), 5, None, FAKE, FAKE, 1 << 20, None, FAKE, None) == -2
+    # advance: outputs and the pool's committed lengths are required; the host offsets must be consistent
+    assert lib.fp_advance(ctypes.byref(p), ctypes.byref(g), None, FAKE, FAKE, None, None) == -1
+    assert lib.fp_advance(ctypes.byref(p), ctypes.byref(g), None, None, FAKE, FAKE, None) == -1
+    g.num_rows = 9
+    assert lib.fp_advance(ctypes.byref(p), ctypes.byref(g), None, FAKE, FAKE, FAKE, None) == -2
+
+
+@pytest.mark.parametrize("mut,code", [
+    ("rank=8", -3), ("rank=80", -3), ("rank=24", -3), ("d_in=96", -3), ("d_out=48", -3),
+    ("num_adapters=0", -2), ("d_in=0", -2), ("workspace=16", -4), ("status=0", -1), ("x=0", -1),
+])
+def test_lora_validation(lib, mut, code):
+    from ragged_paged_kv_fp_amd import _lib
+
+    g, p, keep = _structs()
+    lo = _lib.FpLora(3, 16, 256, 128, FAKE, FAKE, FAKE)
+    ws, status, x = 1 << 20, FAKE, FAKE
+    k, v = mut.split("=")
+    v = int(v)
+    if k == "workspace":
+        ws = v
+    elif k == "status":
+        status = None
+    elif k == "x":
+        x = None
+    else:
+        setattr(lo, k, v)
+    rc = lib.fp_adapter_lora(ctypes.byref(g), ctypes.byref(lo), FAKE, x, FAKE, FAKE, FAKE, ws, status, None)
+    assert rc == code
+
+
+def test_lora_workspace_size(lib):
+    from ragged_paged_kv_fp_amd import _lib
+
+    g, p, keep = _structs(L=3, rows=(70, 0, 5), pages=(1, 1, 1))
+    for rank, rp in ((16, 32), (48, 64), (64, 64)):
+        lo = _lib.FpLora(2, rank, 256, 128, FAKE, FAKE, FAKE)
+        n = lib.fp_lora_workspace_bytes(ctypes.byref(g), ctypes.byref(lo))
+        items = 3 + 1  # ceil(70/32) + ceil(5/32)
+        want = -(-(2 * 2 * 75 * rp) // 256) * 256 + -(-(8 * items) // 256) * 256
+        assert n == want, (rank, n, want)
