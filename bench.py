@@ -483,7 +483,8 @@ def run_ahead_bench(W, runner, seed, K, Wm) -> dict:
 
 def lora_bench(W, seed, K, Wm) -> dict:
     """fp_adapter_lora at the q projection (d_in = d_out = 4096, rank 16, 8
-    adapters, a fifth of the lanes without one) over the rows of config 3
+    adapters, a fifth of the lanes without one), and fp_adapter_ia3 at the
+    same site, over the rows of config 3
     (mixed wave) and config 2 (decode wave), inputs resident in HBM, timed with
     torch events over K calls. Algorithmic bytes: x read, y read, out written,
     and each adapter in use read once (A and B); priced against the HBM peak."""
@@ -522,9 +523,25 @@ def lora_bench(W, seed, K, Wm) -> dict:
         used = np.unique(lw.adapter[(lw.adapter >= 0) & (np.diff(ip) > 0)])
         nbytes = N * 4096 * 2 * 3 + len(used) * 16 * (4096 + 4096) * 2
         ach = nbytes / (ms * 1e-3) / 1e9
+        # IA3 at the same site: y read, out written, each scale vector in use read once
+        sc3 = bits(W.bf16_bits_from_f32(np.random.default_rng(seed).uniform(0.5, 2.0, (8, 4096)).astype(np.float32)))
+        call3 = lambda: api.adapter_ia3(geom, sc3, ad, y, out, status)  # noqa: E731
+        for _ in range(Wm):
+            call3()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            call3()
+        e1.record()
+        torch.cuda.synchronize()
+        ms3 = e0.elapsed_time(e1) / K
+        nb3 = N * 4096 * 2 * 2 + len(used) * 4096 * 2
+        ach3 = nb3 / (ms3 * 1e-3) / 1e9
         res[f"config{cfg}"] = {"workload": f"rows of config {cfg}: " + WORKLOAD_TEXT[cfg], "rows": N,
                                "adapters_used": int(len(used)), "ms": round(ms, 4), "algorithmic_bytes": nbytes,
                                "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4),
+                               "ia3": {"ms": round(ms3, 4), "algorithmic_bytes": nb3, "achieved": round(ach3, 1),
+                                       "frac": round(ach3 / HBM_PEAK_GBS, 4)},
                                "status": int(status.cpu()[0])}
     return res
 

@@ -285,6 +285,20 @@ int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t 
                     const void *y, void *out, void *workspace, size_t workspace_bytes, int32_t *status,
                     hipStream_t stream);
 
+/*
+ * fp_adapter_ia3 - the IA3 form of a projection-site adapter (Docs, section
+ * Adapters: IA3 scales the base output y): for every row r of lane l with
+ * k = adapter[l] >= 0,
+ *     out[r][c] = bf16( y[r][c] * scale_k[c] )
+ * and out[r] = y[r] for lanes with adapter[l] < 0 (an id >= num_adapters sets
+ * FP_ST_ADAPTER and keeps y). The product of two bf16 values is exact in fp32,
+ * so the result is the correctly rounded product.
+ *   scale  : bf16 [num_adapters][d_out] device; y, out: bf16 [N][d_out] (out may equal y);
+ *   d_out a multiple of 8. geom: only indptr / indptr_host / num_lanes / num_rows are read.
+ */
+int fp_adapter_ia3(const fp_geometry *geom, int32_t num_adapters, int32_t d_out, const void *scale,
+                   const int32_t *adapter, const void *y, void *out, int32_t *status, hipStream_t stream);
+
 /* ---- host-only accounting (Pie reviews, Eq. (1) and Eq. (2)) ---- */
 uint64_t fp_kv_bytes(int32_t L, int32_t H_kv, int32_t d, uint64_t T, int32_t b); /* 2*L*H_kv*d*T*b   */
 uint64_t fp_pages_for(uint64_t T, int32_t P);                                   /* ceil(T/P)        */

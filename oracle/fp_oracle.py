@@ -408,6 +408,25 @@ def lora(x_bits, y_bits, adapter, indptr, a_bits, b_bits, scale):
     return out, exact, status
 
 
+def ia3(y_bits, adapter, indptr, scale_bits):
+    """IA3 adapter (Docs "Adapters": IA3 scales the base output y): rows of a
+    lane with k = adapter[l] >= 0 become bf16(y * scale_k) per output column;
+    others keep y, an id past the table also sets ST_ADAPTER.
+    Returns (out bf16 bits [N][d_out], status)."""
+    out = np.array(y_bits, dtype=np.uint16, copy=True)
+    status = 0
+    for lane in range(len(indptr) - 1):
+        r0, r1 = _lane_rows(indptr, lane)
+        k = int(adapter[lane])
+        if r1 == r0 or k < 0:
+            continue
+        if k >= scale_bits.shape[0]:
+            status |= ST_ADAPTER
+            continue
+        out[r0:r1] = f64_to_bf16(bf16_to_f64(y_bits[r0:r1]) * bf16_to_f64(scale_bits[k])[None, :])
+    return out, status
+
+
 def readout_rows(indptr, rows=None):
     """Readout list: given rows in the given order, or the last row of each non-empty lane."""
     if rows is not None:

@@ -36,7 +36,8 @@ FP_FOLD_ALL = -1
 FP_FOLD_CHANNEL = -2
 
 EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_fold", "fp_readout", "fp_attn_mass",
-           "fp_advance", "fp_lora_workspace_bytes", "fp_adapter_lora", "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version")
+           "fp_advance", "fp_lora_workspace_bytes", "fp_adapter_lora", "fp_adapter_ia3",
+           "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version")
 
 
 class FpGeometry(ctypes.Structure):
@@ -101,6 +102,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp_adapter_lora.argtypes = [P(FpGeometry), P(FpLora), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, ctypes.c_size_t,
                                     c_ptr, c_ptr]
     lib.fp_adapter_lora.restype = c_i32
+    lib.fp_adapter_ia3.argtypes = [P(FpGeometry), c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
+    lib.fp_adapter_ia3.restype = c_i32
     lib.fp_advance.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
     lib.fp_advance.restype = c_i32
     lib.fp_kv_bytes.argtypes = [c_i32, c_i32, c_i32, c_u64, c_i32]

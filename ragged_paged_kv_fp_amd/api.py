@@ -222,6 +222,16 @@ def adapter_lora(geom: Geometry, lora: Lora, adapter: torch.Tensor, x: torch.Ten
                                                   _stream(stream)))
 
 
+def adapter_ia3(geom: Geometry, scale: torch.Tensor, adapter: torch.Tensor, y: torch.Tensor, out: torch.Tensor,
+                status: torch.Tensor, stream=None) -> None:
+    """fp_adapter_ia3: out = bf16(y * scale[k]) per lane's adapter k (y kept where k < 0); scale [n][d_out] bf16."""
+    lib = _lib.load()
+    gs = geom.struct()
+    n, d_out = scale.shape
+    _check("fp_adapter_ia3", lib.fp_adapter_ia3(ctypes.byref(gs), int(n), int(d_out), _ptr(scale), _ptr(adapter),
+                                                _ptr(y), _ptr(out), _ptr(status), _stream(stream)))
+
+
 def advance(pool: Pool, geom: Geometry, pos_offset: Optional[torch.Tensor] = None, stream=None) -> None:
     """fp_advance: write geom's positions / slots / kv_len on the device from the
     pool's committed lengths (rows appended after the frozen prefix)."""

@@ -513,6 +513,23 @@ int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t 
     return launch_ok();
 }
 
+int fp_adapter_ia3(const fp_geometry *geom, int32_t num_adapters, int32_t d_out, const void *scale,
+                   const int32_t *adapter, const void *y, void *out, int32_t *status, hipStream_t stream) {
+    if (!geom || !geom->indptr || !geom->indptr_host || !status) return FP_ERR_NULL;
+    if (geom->num_lanes < 1 || geom->num_rows < 0 || num_adapters < 1 || d_out < 1) return FP_ERR_SHAPE;
+    if (d_out % 8) return FP_ERR_UNSUPPORTED;
+    const int32_t *ip = geom->indptr_host;
+    if (ip[0] != 0 || ip[geom->num_lanes] != geom->num_rows) return FP_ERR_SHAPE;
+    for (int l = 0; l < geom->num_lanes; ++l)
+        if (ip[l + 1] < ip[l]) return FP_ERR_SHAPE;
+    if (geom->num_rows == 0) return FP_OK;
+    if (!scale || !adapter || !y || !out) return FP_ERR_NULL;
+    hipLaunchKernelGGL(ia3_kernel, dim3((unsigned)geom->num_rows), dim3(kIa3Threads), 0, stream, geom->indptr,
+                       geom->num_lanes, adapter, num_adapters, d_out, static_cast<const uint16_t *>(scale),
+                       static_cast<const uint16_t *>(y), static_cast<uint16_t *>(out), status);
+    return launch_ok();
+}
+
 int fp_advance(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *pos_offset, int32_t *positions,
                int32_t *slots, int32_t *kv_len, hipStream_t stream) {
     if (!pool || !pool->committed_len) return FP_ERR_NULL;

@@ -231,4 +231,37 @@ __global__ void __launch_bounds__(64 * kLoraWaves) lora_expand_kernel(LoraArgs a
         make_uint4(mix(y1.x, 8), mix(y1.y, 10), mix(y1.z, 12), mix(y1.w, 14));
 }
 
+// IA3: one workgroup per row (its lane found once, from uniform addresses),
+// each thread taking 8 output columns per round; y * scale in fp32 is exact,
+// so one rounding to bf16.
+constexpr int kIa3Threads = 256;
+
+__global__ void __launch_bounds__(kIa3Threads) ia3_kernel(const int32_t *indptr, int L, const int32_t *adapter, int n_ad,
+                                                          int d_out, const uint16_t *scale, const uint16_t *y,
+                                                          uint16_t *out, int32_t *status) {
+    const int64_t row = blockIdx.x;
+    const int lane = find_lane(indptr, L, row);
+    const int k = adapter[lane];
+    const bool none = k < 0 || k >= n_ad;
+    if (k >= n_ad && threadIdx.x == 0 && row == indptr[lane]) atomicOr(status, FP_ST_ADAPTER);
+    if (none && out == y) return;  // workgroup-uniform
+    auto mul = [](uint32_t a, uint32_t b) {
+        return pack_bf16x2(__uint_as_float(a << 16) * __uint_as_float(b << 16),
+                           __uint_as_float(a & 0xFFFF0000u) * __uint_as_float(b & 0xFFFF0000u));
+    };
+    const uint16_t *yr = y + row * d_out;
+    uint16_t *orow = out + row * d_out;
+    const uint16_t *sr = scale + (int64_t)(none ? 0 : k) * d_out;
+    for (int c = 8 * threadIdx.x; c < d_out; c += 8 * kIa3Threads) {
+        const uint4 yv = *reinterpret_cast<const uint4 *>(yr + c);
+        if (none) {
+            *reinterpret_cast<uint4 *>(orow + c) = yv;
+            continue;
+        }
+        const uint4 sv = *reinterpret_cast<const uint4 *>(sr + c);
+        *reinterpret_cast<uint4 *>(orow + c) =
+            make_uint4(mul(yv.x, sv.x), mul(yv.y, sv.y), mul(yv.z, sv.z), mul(yv.w, sv.w));
+    }
+}
+
 }  // namespace fpk

@@ -30,7 +30,7 @@ def lib():
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(fp_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -209,3 +209,14 @@ def test_lora_workspace_size(lib):
         items = 3 + 1  # ceil(70/32) + ceil(5/32)
         want = -(-(2 * 2 * 75 * rp) // 256) * 256 + -(-(8 * items) // 256) * 256
         assert n == want, (rank, n, want)
+
+
+def test_ia3_validation(lib):
+    g, p, keep = _structs()
+    st = FAKE
+    assert lib.fp_adapter_ia3(ctypes.byref(g), 2, 12, FAKE, FAKE, FAKE, FAKE, st, None) == -3
+    assert lib.fp_adapter_ia3(ctypes.byref(g), 0, 64, FAKE, FAKE, FAKE, FAKE, st, None) == -2
+    assert lib.fp_adapter_ia3(ctypes.byref(g), 2, 64, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert lib.fp_adapter_ia3(ctypes.byref(g), 2, 64, None, FAKE, FAKE, FAKE, st, None) == -1
+    g.num_rows = 9
+    assert lib.fp_adapter_ia3(ctypes.byref(g), 2, 64, FAKE, FAKE, FAKE, FAKE, st, None) == -2

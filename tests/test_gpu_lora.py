@@ -123,3 +123,31 @@ def test_lora_full_size_mixed_wave_sampled():
     for lane in np.nonzero(lw.adapter < 0)[0]:
         r0, r1 = int(lw.indptr[lane]), int(lw.indptr[lane + 1])
         assert np.array_equal(got[r0:r1], lw.y[r0:r1])
+
+
+def test_ia3_bit_exact():
+    import torch
+
+    from ragged_paged_kv_fp_amd import api
+
+    wl = W.make_config(3, seed=0)
+    ip = wl.step.indptr.astype(np.int32)
+    N, d_out = int(ip[-1]), 1024
+    rng = np.random.default_rng(3)
+    y = W.bf16_bits_from_f32(rng.standard_normal((N, d_out)).astype(np.float32))
+    scale = W.bf16_bits_from_f32(rng.uniform(0.25, 4.0, (6, d_out)).astype(np.float32))
+    adapter = rng.integers(-1, 6, size=len(ip) - 1).astype(np.int32)
+    adapter[5] = 9  # out of range: flagged, lane keeps y
+    want, want_st = oracle.ia3(y, adapter, ip, scale)
+    dev = "cuda"
+    geom = api.Geometry(indptr=torch.from_numpy(ip).to(dev), indptr_host=ip.copy(), positions=None, slots=None,
+                        kv_len=None, fold=None)
+    for in_place in (False, True):
+        yt = _bits(y, dev)
+        out = yt if in_place else torch.full_like(yt, 0x7FC0)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        api.adapter_ia3(geom, _bits(scale, dev), torch.from_numpy(adapter).to(dev), yt, out, status)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), f"in_place={in_place}"
+        assert int(status.cpu()[0]) == want_st == oracle.ST_ADAPTER

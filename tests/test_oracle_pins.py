@@ -488,3 +488,27 @@ def test_lora_rank_one_closed_form():
     want = oracle.bf16_to_f64(lw.y) + float(lw.scale[0]) * np.outer(xj, c)
     assert np.array_equal(exact, want)
     assert np.array_equal(out, oracle.f64_to_bf16(want))
+
+
+def test_ia3_matches_exact_rounding_and_closed_forms():
+    ip = np.array([0, 3, 3, 7, 9], dtype=np.int32)
+    rng = np.random.default_rng(11)
+    y = W.bf16_bits_from_f32(rng.standard_normal((9, 16)).astype(np.float32))
+    scale = W.bf16_bits_from_f32(rng.uniform(0.1, 3.0, (2, 16)).astype(np.float32))
+    adapter = np.array([1, 0, -1, 0], dtype=np.int32)
+    out, st = oracle.ia3(y, adapter, ip, scale)
+    assert st == 0
+    for lane in range(4):
+        for r in range(ip[lane], ip[lane + 1]):
+            for c in range(16):
+                k = adapter[lane]
+                want = int(y[r, c]) if k < 0 else bf.bf16_round_exact(bf.bf16_value(y[r, c]) * bf.bf16_value(scale[k, c]))
+                assert int(out[r, c]) == want
+    ones = np.full((1, 16), 0x3F80, np.uint16)          # 1.0: y unchanged, bit for bit
+    assert np.array_equal(oracle.ia3(y, np.zeros(4, np.int32), ip, ones)[0], y)
+    twos = np.full((1, 16), 0x4000, np.uint16)          # 2.0: exponent + 1
+    o2, _ = oracle.ia3(y, np.zeros(4, np.int32), ip, twos)
+    nz = (y & 0x7FFF) != 0
+    assert np.array_equal(o2[nz], (y[nz] + 0x80).astype(np.uint16))
+    _, st = oracle.ia3(y, np.array([0, 0, 5, 0], np.int32), ip, ones)
+    assert st == oracle.ST_ADAPTER
