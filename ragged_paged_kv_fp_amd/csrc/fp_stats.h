@@ -15,8 +15,13 @@
 // fragments are loaded once and serve all eight tiles, each tile computing
 // S^T = K * Q^T with the prefill kernel's slot permutation (lane half h holds
 // slots 8h..8h+7 and 16+8h..16+8h+7 of its column) and adding p to per-lane,
-// per-slot sums held in registers. A pair, or a tile of a pair, with no
-// allowed slot is skipped by the whole wave. At the end the 32 columns of a
+// per-slot sums held in registers. Before that, the workgroup marks in LDS
+// the row blocks that may read any slot of the chunk (every row's mask words
+// or causal limit loaded at once), so the waves skip the other pairs without
+// waiting on memory for each. A pair with no allowed slot in the chunk is
+// skipped by the whole wave; otherwise all eight tiles are computed (dropped
+// slots add zero), so the MFMA chain of one tile overlaps the exponentials of
+// the one before. At the end the 32 columns of a
 // wave are summed in registers (DPP and a row swap), the four waves through LDS, and one
 // thread per slot adds the total to the output: a single owner per output
 // word and a fixed summation order, so the result does not depend on
@@ -29,6 +34,7 @@ namespace fpk {
 
 constexpr int kMassWaves = 4;
 constexpr int kMassTiles = 8;  // 32-slot tiles per workgroup
+constexpr int kMassMaxBlocks = 4096;  // row blocks a lane may have for the LDS skip flags
 
 struct MassArgs {
     const uint16_t *pool;
@@ -72,6 +78,7 @@ template <int D>
 __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
     __shared__ __attribute__((aligned(16))) char s_k[MassLds<D>::K_BYTES];
     __shared__ float s_sum[kMassWaves][32 * kMassTiles];
+    __shared__ uint8_t s_live[kMassMaxBlocks];  // row block may read a slot of the chunk
     constexpr int KROW = MassLds<D>::KROW;
     constexpr int KC = D / 8;  // 16-byte chunks per K row
     const int lane = blockIdx.x / a.H, g = blockIdx.x % a.H;
@@ -118,6 +125,29 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
     const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
     const int wpr = masked ? (int)((a.mask_off[lane + 1] - a.mask_off[lane]) / n) : 0;
     const int t0 = c0 >> 5;  // first tile of the chunk in the lane
+    const int nrb = (n + 31) >> 5;
+    const bool flags = nrb <= kMassMaxBlocks;  // workgroup-uniform; otherwise every pair is tried
+    if (flags) {
+        for (int b = threadIdx.x; b < nrb; b += 64 * kMassWaves) s_live[b] = 0;
+        __syncthreads();
+        const int rem = eff - c0;
+        for (int r = threadIdx.x; r < n; r += 64 * kMassWaves) {
+            bool live;
+            if (masked) {
+                const uint32_t *mw = a.mask_bits + a.mask_off[lane] + (int64_t)r * wpr;
+                uint32_t any = 0u;
+                for (int t = 0; t < ntl && t0 + t < wpr; ++t) {
+                    const int q = rem - 32 * t;
+                    any |= mw[t0 + t] & (q >= 32 ? 0xFFFFFFFFu : ((1u << q) - 1u));
+                }
+                live = any != 0u;
+            } else {
+                live = a.slots[r0 + r] + 1 > c0;
+            }
+            if (live) s_live[r >> 5] = 1;  // every writer stores the same value
+        }
+        __syncthreads();
+    }
     const int items = ((n + 31) >> 5) * a.G;
     constexpr float kLog2e = 1.4426950408889634f;
     const char *krow = s_k + kslot_of_row(nn) * KROW + h * D;
@@ -130,6 +160,7 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
 
     for (int it = wv; it < items; it += kMassWaves) {
         const int rb = it / a.G, head = g * a.G + it % a.G;
+        if (flags && !s_live[rb]) continue;  // workgroup-uniform
         const int rl = 32 * rb + nn;  // row within the lane (this lane's column)
         const bool valid = rl < n;
         const int64_t row = r0 + (valid ? rl : 0);
@@ -173,7 +204,6 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < kMassTiles; ++t) {
-            if (!__any(bits[t] != 0u)) continue;  // wave-uniform
             f32x16 acc = {};
 #pragma unroll
             for (int s = 0; s < D / 16; ++s)
