@@ -263,7 +263,8 @@ typedef struct fp_lora {
     const float *scale;               /* [num_adapters] device                                  */
 } fp_lora;
 
-/* Workspace bytes fp_adapter_lora needs (host-only): the rank-r projections of every row (two bf16 terms). */
+/* Workspace bytes fp_adapter_lora needs (host-only): the rank-r projections of every row (two bf16 terms),
+ * then 16 bytes per (lane, 32-row block) work item. */
 int64_t fp_lora_workspace_bytes(const fp_geometry *geom, const fp_lora *lora);
 
 /*

@@ -456,7 +456,7 @@ int64_t fp_lora_workspace_bytes(const fp_geometry *geom, const fp_lora *lora) {
     if (geom->num_rows < 0 || geom->num_lanes < 1 || lora->rank < 1) return FP_ERR_SHAPE;
     const int rp = (lora->rank + 31) / 32 * 32;
     return (int64_t)(align256(2 * sizeof(uint16_t) * (size_t)geom->num_rows * rp) +
-                     align256(sizeof(int2) * (size_t)lora_items(geom)));
+                     align256(sizeof(int4) * (size_t)lora_items(geom)));
 }
 
 int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t *adapter, const void *x,
@@ -494,22 +494,32 @@ int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t 
     if (n_items > INT32_MAX / 2) return FP_ERR_UNSUPPORTED;
     a.v = static_cast<uint16_t *>(workspace);
     a.N = geom->num_rows;
-    int2 *items = reinterpret_cast<int2 *>(static_cast<char *>(workspace) +
+    int4 *items = reinterpret_cast<int4 *>(static_cast<char *>(workspace) +
                                            align256(2 * sizeof(uint16_t) * (size_t)geom->num_rows * a.rp));
     a.items = items;
     a.n_items = (int)n_items;
     a.status = status;
     a.in_place = out == y;
-    hipLaunchKernelGGL(lora_plan_kernel, dim3(1), dim3(kLoraPlanThreads), 0, stream, geom->indptr, a.L, items,
-                       a.n_items, status);
+    hipLaunchKernelGGL(lora_plan_kernel, dim3(1), dim3(kLoraPlanThreads), 0, stream, geom->indptr, a.L, adapter,
+                       items, a.n_items, status);
     int rc = launch_ok();
     if (rc) return rc;
     const dim3 block(64 * kLoraWaves);
-    if (a.rp == 32) hipLaunchKernelGGL(lora_shrink_kernel<1>, dim3((unsigned)n_items), block, 0, stream, a);
-    else hipLaunchKernelGGL(lora_shrink_kernel<2>, dim3((unsigned)n_items), block, 0, stream, a);
+    const dim3 grid((unsigned)n_items);
+    switch (a.r / 16) {
+        case 1: hipLaunchKernelGGL(lora_shrink_kernel<1>, grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(lora_shrink_kernel<2>, grid, block, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL(lora_shrink_kernel<3>, grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL(lora_shrink_kernel<4>, grid, block, 0, stream, a); break;
+    }
     if ((rc = launch_ok())) return rc;
-    hipLaunchKernelGGL(lora_expand_kernel, dim3((unsigned)n_items, (unsigned)((a.d_out + kLoraCols - 1) / kLoraCols)),
-                       block, 0, stream, a);
+    const dim3 egrid((unsigned)n_items, (unsigned)((a.d_out + kLoraCols * kLoraBlocks - 1) / (kLoraCols * kLoraBlocks)));
+    switch (a.r / 16) {
+        case 1: hipLaunchKernelGGL(lora_expand_kernel<1>, egrid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(lora_expand_kernel<2>, egrid, block, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL(lora_expand_kernel<3>, egrid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL(lora_expand_kernel<4>, egrid, block, 0, stream, a); break;
+    }
     return launch_ok();
 }
 

@@ -207,7 +207,7 @@ def test_lora_workspace_size(lib):
         lo = _lib.FpLora(2, rank, 256, 128, FAKE, FAKE, FAKE)
         n = lib.fp_lora_workspace_bytes(ctypes.byref(g), ctypes.byref(lo))
         items = 3 + 1  # ceil(70/32) + ceil(5/32)
-        want = -(-(2 * 2 * 75 * rp) // 256) * 256 + -(-(8 * items) // 256) * 256
+        want = -(-(2 * 2 * 75 * rp) // 256) * 256 + -(-(16 * items) // 256) * 256
         assert n == want, (rank, n, want)
 
 
