@@ -257,7 +257,8 @@ int fp_advance(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *p
 typedef struct fp_lora {
     int32_t num_adapters;             /* >= 1                                                   */
     int32_t rank;                     /* r in {16, 32, 48, 64}                                  */
-    int32_t d_in, d_out;              /* projection input / output widths, multiples of 64     */
+    int32_t d_in, d_out;              /* projection widths: d_in a multiple of 64, d_out a       */
+                                      /* multiple of 32 and at most 65535 * 512                  */
     const void *a;                    /* bf16 [num_adapters][rank][d_in] device                 */
     const void *b;                    /* bf16 [num_adapters][d_out][rank] device                */
     const float *scale;               /* [num_adapters] device                                  */

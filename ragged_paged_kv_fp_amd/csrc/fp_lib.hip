@@ -470,7 +470,7 @@ int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t 
         if (ip[l + 1] < ip[l]) return FP_ERR_SHAPE;
     if (lora->num_adapters < 1 || lora->d_in < 1 || lora->d_out < 1) return FP_ERR_SHAPE;
     if (lora->rank % 16 || lora->rank < 16 || lora->rank > 64 || lora->d_in % 64 || lora->d_out % 32 ||
-        lora->d_out > 65535 * kLoraCols)
+        (int64_t)lora->d_out > (int64_t)65535 * kLoraCols * kLoraBlocks)
         return FP_ERR_UNSUPPORTED;
     if (geom->num_rows == 0) return FP_OK;
     if (!adapter || !x || !y || !out || !lora->a || !lora->b || !lora->scale || !workspace) return FP_ERR_NULL;

@@ -87,7 +87,10 @@ def _check(lw, got, lanes=None):
     return float((g == wb).mean()), st
 
 
-@pytest.mark.parametrize("rank,d_in,d_out", [(16, 4096, 1024), (32, 512, 4096), (48, 1024, 96), (64, 2048, 512)])
+# the last three: d_in steps that do not divide evenly over the four waves
+# (some waves with one step or none), and d_out with a partial column block
+@pytest.mark.parametrize("rank,d_in,d_out", [(16, 4096, 1024), (32, 512, 4096), (48, 1024, 96), (64, 2048, 512),
+                                             (16, 192, 544), (48, 64, 32), (32, 320, 1056)])
 def test_lora_small_pass(rank, d_in, d_out):
     wl = W.make_config(3, seed=1, scale="small")
     lw = W.make_lora(rank, wl.step.indptr, d_in=d_in, d_out=d_out, rank=rank, num_adapters=5)
