@@ -282,6 +282,7 @@ __device__ __forceinline__ void rope_q_body(const RopeQArgs &a, int block) {
 
 // ============================================================================ plan
 
+constexpr int kXcds = 8;  // accelerator complex dies: workgroups go to them round robin by launch index
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxLanes = 4096;
 constexpr int kDecodeCols = 32;  // query row-heads one decode wave holds (MFMA N)

@@ -414,6 +414,7 @@ int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_
     m.mass = slot_mass;
     m.stride = (int64_t)pp[p.L] * p.P;
     m.chunks = (int)chunks;
+    m.L = p.L;
     // lanes with rows x G <= 32 go to the decode-class kernel, the others to the chunked one
     bool any_dec = false, any_pre = false;
     for (int l = 0; l < p.L; ++l) {
@@ -423,7 +424,8 @@ int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_
     }
     const dim3 block(64 * kMassWaves);
     if (any_pre) {
-        const dim3 grid((unsigned)(p.L * p.H), (unsigned)chunks);
+        const int64_t rounds = ((int64_t)p.L * p.H + kXcds - 1) / kXcds;  // pairs per XCD
+        const dim3 grid((unsigned)(kXcds * rounds * chunks));
         if (p.D == 128) hipLaunchKernelGGL(mass_kernel<128>, grid, block, 0, stream, m);
         else hipLaunchKernelGGL(mass_kernel<64>, grid, block, 0, stream, m);
         if ((rc = launch_ok())) return rc;

@@ -49,6 +49,7 @@ struct MassArgs {
     float *mass;                      // [H][stride]
     int64_t stride;                   // page_indptr[L] * P
     int chunks;                       // chunks of the largest working set
+    int L;                            // lanes
 };
 
 // Sum over the 32 lanes of each lane half, in registers: two quad swaps, the
@@ -81,12 +82,19 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
     __shared__ uint8_t s_live[kMassMaxBlocks];  // row block may read a slot of the chunk
     constexpr int KROW = MassLds<D>::KROW;
     constexpr int KC = D / 8;  // 16-byte chunks per K row
-    const int lane = blockIdx.x / a.H, g = blockIdx.x % a.H;
+    // Workgroups go to the XCDs round robin by launch index; index i runs on
+    // XCD i % 8. Each XCD takes (lane, KV head) pairs x, x + 8, ... one after
+    // the other with all their chunks, so the workgroups resident on an XCD
+    // at one time mostly share one pair's Q, which then stays in that XCD's L2.
+    const int xcd = blockIdx.x % kXcds, kx = blockIdx.x / kXcds;
+    const int pair = kXcds * (kx / a.chunks) + xcd;
+    if (pair >= a.L * a.H) return;
+    const int lane = pair / a.H, g = pair % a.H;
     const int p0 = a.page_indptr[lane];
     const int cap = (a.page_indptr[lane + 1] - p0) * a.P;
     const int eff = clamp_kv(a.kv_len[lane], cap);
     const int r0 = a.indptr[lane], n = a.indptr[lane + 1] - r0;
-    const int c0 = 32 * kMassTiles * blockIdx.y;  // first slot of the chunk
+    const int c0 = 32 * kMassTiles * (kx % a.chunks);  // first slot of the chunk
     if (n <= 0 || n * a.G <= 32 || c0 >= eff) return;  // workgroup-uniform; decode-class lanes below
     const int ntl = min(kMassTiles, (eff - c0 + 31) >> 5);  // tiles of the chunk below kv_len
     const int wv = threadIdx.x / kWave, ln = lane_id(), nn = ln & 31, h = ln >> 5;
