@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfp.so")
 SOURCES = [os.path.join(HERE, "csrc", "fp_lib.hip")]
-DEPS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("fp_kernels.h", "fp_device.h", "fp_decode.h", "fp_prefill.h")] + [
+DEPS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("fp_kernels.h", "fp_device.h", "fp_decode.h", "fp_prefill.h",
+                                                                "fp_stats.h", "fp_lora.h")] + [
     os.path.join(ROOT, "include", "fp.h")]
 
 HIPCC_FLAGS = [
@@ -21,6 +22,11 @@ HIPCC_FLAGS = [
     "-shared",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs rather than AGPRs: the attention-mass kernel reads
+    # every score with VALU instructions, which cannot take AGPR operands, so
+    # AGPR results would cost one copy per score (the attention kernels are
+    # unchanged by it)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

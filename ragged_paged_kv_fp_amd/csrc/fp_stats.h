@@ -210,19 +210,34 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
                 for (int s = 0; s < D / 16; ++s) qf[s] = make_uint4(0, 0, 0, 0);
             }
         }
+        // -lse2 enters the accumulation as one more MFMA, its two bf16 terms
+        // (hi + lo, 16 significant bits) in rows 0 and 1 of B against ones in
+        // columns 0 and 1 of A, so no subtraction per score is needed
+        uint4 bias_a, bias_b;
+        {
+            const float nl = live ? -lse2 : 0.0f;
+            const uint32_t hi = pack_bf16x2(nl, nl) & 0xFFFFu;
+            const float rest = nl - __uint_as_float(hi << 16);
+            const uint32_t lo = pack_bf16x2(rest, rest) & 0xFFFFu;
+            bias_a = make_uint4(h == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u);
+            bias_b = make_uint4(h == 0 ? (hi | (lo << 16)) : 0u, 0u, 0u, 0u);
+        }
 #pragma unroll
         for (int t = 0; t < kMassTiles; ++t) {
             f32x16 acc = {};
 #pragma unroll
             for (int s = 0; s < D / 16; ++s)
                 acc = mfma32(*reinterpret_cast<const uint4 *>(krow + t * 32 * KROW + 16 * s), qf[s], acc);
-            // register i holds tile slot 16(i/8) + 8h + i%8 of this column
+            acc = mfma32(bias_a, bias_b, acc);
+            // register i holds tile slot 16(i/8) + 8h + i%8 of this column;
+            // a dropped slot's weight is cleared by a sign-extended bit mask
             const uint32_t hb = bits[t] >> (8 * h);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int k = 16 * (i >> 3) + (i & 7);
-                const bool keep = (hb >> k) & 1u;
-                msum[t][i] += keep ? __builtin_amdgcn_exp2f(acc[i] - lse2) : 0.0f;
+                uint32_t keep;  // all ones if slot k is allowed (kept opaque: a select would take three instructions)
+                asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(keep) : "v"(hb), "i"(k));
+                msum[t][i] += __uint_as_float(__float_as_uint(__builtin_amdgcn_exp2f(acc[i])) & keep);
             }
         }
     }
