@@ -322,11 +322,6 @@ __device__ __forceinline__ void pre_main(const char *stc, const char *stn, const
     const char *krow = stn + kslot_of_row(n) * PreLds<D>::KROW + h * D;
     const char *vrow = stc + PreLds<D>::K_BYTES + n * PreLds<D>::VROW + 16 * h;
     uint4 kf[NQK], vf[NDB][2];
-    // A wave starting its step (fragment reads, the QK^T chain and the first
-    // P*V half) goes ahead of the other wave on its SIMD, which is then in
-    // the VALU-heavy end of its own step: the two waves drift half a step
-    // apart, and one's MFMAs run under the other's VALU work.
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < NQK; ++s) kf[s] = *reinterpret_cast<const uint4 *>(krow + 16 * s);
 #pragma unroll
@@ -359,7 +354,6 @@ __device__ __forceinline__ void pre_main(const char *stc, const char *stn, const
         if (s == NQK - 1) bias.load(0);  // the K fragments are all consumed now
         __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_setprio(0);
     const uint4 pb1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
