@@ -130,9 +130,11 @@ __global__ void __launch_bounds__(64 * kLoraWaves) lora_shrink_kernel(LoraArgs a
     f32x4 acc[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[rb][0] = acc[rb][1] = f32x4{};
-    // 32-wide steps of d_in dealt round robin: wave wv takes steps wv, wv + 4, ...
-    const int steps = (a.d_in / 32 - wv + kLoraWaves - 1) / kLoraWaves;
-    auto col = [&](int st) { return 32 * (wv + kLoraWaves * st); };
+    // pairs of 32-wide steps (64 columns: one 128-byte line of each row) dealt
+    // round robin: wave wv takes pairs wv, wv + 4, ..., so each line of x is
+    // read whole by one wave in two consecutive loads
+    const int steps = 2 * max(0, (a.d_in / 64 - wv + kLoraWaves - 1) / kLoraWaves);
+    auto col = [&](int st) { return 64 * (wv + kLoraWaves * (st >> 1)) + 32 * (st & 1); };
     // groups of GS 32-wide steps in a ring of NB register buffers: NB - 1
     // groups' loads are in flight while a group's MFMAs run (every load is
     // unconditional, the group index clamped to the last, so the compiler
@@ -179,7 +181,7 @@ __global__ void __launch_bounds__(64 * kLoraWaves) lora_shrink_kernel(LoraArgs a
             }
         }
     }
-    for (int st = GS * groups; st < steps; ++st) {  // a step left over from the groups
+    for (int st = GS * groups; st < steps; ++st) {  // a step left over from the groups (none while GS is 2)
         Grp t;
         const int kk = col(st);
 #pragma unroll
