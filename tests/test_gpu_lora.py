@@ -154,3 +154,34 @@ def test_ia3_bit_exact():
         got = out.cpu().numpy().view(np.uint16)
         assert np.array_equal(got, want), f"in_place={in_place}"
         assert int(status.cpu()[0]) == want_st == oracle.ST_ADAPTER
+
+
+def test_lora_and_ia3_at_the_lane_limit():
+    """4096 lanes (the library's limit), mostly empty or one row with a few
+    long ones: every thread of the plan scans four lanes and the item list
+    comes from the binary search over the lanes' starts."""
+    rng = np.random.default_rng(11)
+    L = 4096
+    n = rng.choice([0, 0, 1, 1, 1, 2, 5], size=L)
+    n[rng.choice(L, 6, replace=False)] = rng.integers(33, 200, size=6)
+    ip = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    lw = W.make_lora(12, ip, d_in=256, d_out=128, rank=32, num_adapters=7)
+    got, st = _run(lw)
+    exact_frac, want_st = _check(lw, got)
+    assert st == want_st == 0
+    assert exact_frac >= 0.99
+    want, want_st = oracle.ia3(lw.y, lw.adapter, ip, lw.b[:, :, 0].copy())
+    import torch
+
+    from ragged_paged_kv_fp_amd import api
+
+    dev = "cuda"
+    geom = api.Geometry(indptr=torch.from_numpy(ip).to(dev), indptr_host=ip.copy(), positions=None, slots=None,
+                        kv_len=None, fold=None)
+    out = torch.full_like(_bits(lw.y, dev), 0x7FC0)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    api.adapter_ia3(geom, _bits(lw.b[:, :, 0].copy(), dev), torch.from_numpy(lw.adapter).to(dev), _bits(lw.y, dev),
+                    out, status)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), want)
+    assert int(status.cpu()[0]) == want_st == 0
