@@ -263,8 +263,8 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
 
 // Decode-class lanes (rows x G <= 32): all the lane's (row, query head)
 // pairs fit in the 32 columns of one MFMA block, so each wave loads its Q
-// once and streams kMassWaveTiles consecutive K tiles straight from memory into
-// registers (the next tile's fragments load while the current one computes),
+// once and streams kMassWaveTiles consecutive K tiles from memory (the next
+// tile's K runs load while the current one computes),
 // reducing each tile's 32 columns in registers and adding the 32 slot totals
 // to the output (one writer per word). Column c is row c / G, query head
 // g * G + c % G.
@@ -272,6 +272,7 @@ constexpr int kMassWaveTiles = 8;  // 2, 4, 8 and 16 measured: 8 (and 2) about 4
 
 template <int D>
 __global__ void __launch_bounds__(64 * kMassWaves) mass_decode_kernel(MassArgs a) {
+    __shared__ __attribute__((aligned(16))) char s_k[kMassWaves][DecLds<D>::BYTES];
     const int lane = blockIdx.x / a.H, g = blockIdx.x % a.H;
     const int r0 = a.indptr[lane], n = a.indptr[lane + 1] - r0;
     if (n <= 0 || n * a.G > 32) return;  // workgroup-uniform; other lanes take the chunked kernel
@@ -291,6 +292,8 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_decode_kernel(MassArgs a
     const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
     const int wpr = masked ? (int)((a.mask_off[lane + 1] - a.mask_off[lane]) / n) : 0;
     const int lim = a.slots[row] + 1;  // causal limit of this column's row
+    const uint32_t *mwp = masked ? a.mask_bits + a.mask_off[lane] + (int64_t)rl * wpr
+                                 : reinterpret_cast<const uint32_t *>(a.indptr);
     uint4 qf[D / 16];
     {
         const uint4 *qsrc = reinterpret_cast<const uint4 *>(a.qrot + (row * a.Hq + head) * D + h * (D / 2));
@@ -301,43 +304,61 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_decode_kernel(MassArgs a
             for (int s = 0; s < D / 16; ++s) qf[s] = make_uint4(0, 0, 0, 0);
         }
     }
-    // K fragment addresses: this lane's row of tile t is slot 32t + kslot_of_row(nn)
-    // (rows at or past kv_len load the last row below it; their scores are dropped)
-    int pid[kMassWaveTiles];
-#pragma unroll
-    for (int u = 0; u < kMassWaveTiles; ++u)
-        pid[u] = a.page_ids[p0 + (min(32 * (tb + u) + kslot_of_row(nn), eff - 1) >> pshift)];
-    auto kload = [&](int u, uint4 (&kf)[D / 16]) {
-        const int slot = min(32 * (tb + u) + kslot_of_row(nn), eff - 1);
-        const int64_t phys = min(max(pid[u], 0), a.num_pages - 1);
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            a.pool + phys * a.page_elems + ((int64_t)g * a.P + (slot & (a.P - 1))) * D + h * (D / 2));
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) kf[s] = src[s];
+    // K arrives as whole 1 KB runs of the pages (every load instruction covers
+    // complete cache lines, like the decode kernel's K) and passes through the
+    // wave's LDS buffer into the MFMA fragment layout: lane (n, h) then holds
+    // tile row kslot_of_row(n), half h of the head dimension. Lane l keeps the
+    // physical page of the tile's (l & 3)-th page; rows at or past kv_len read
+    // the lane's last page (their scores are dropped).
+    constexpr int RPR = 512 / D, LPR = D / 8;  // tile rows per run, lanes per row
+    const int lastpg = (eff - 1) >> pshift;
+    auto tile_kp = [&](int u) {
+        const int pg = min((32 * (tb + u) >> pshift) + (ln & 3), lastpg);
+        return min(max(a.page_ids[p0 + pg], 0), a.num_pages - 1);
     };
-    uint4 kb[2][D / 16];
-    kload(0, kb[0]);
-    if (kMassWaveTiles > 1) kload(1, kb[1]);
+    const int64_t kcol = (int64_t)g * a.P * D + 8 * (ln % LPR);
+    auto kload = [&](int kp, KvFrags<D> &f) {
+#pragma unroll
+        for (int u = 0; u < D / 16; ++u) {
+            const int r = u * RPR + ln / LPR;
+            const int64_t page = __builtin_amdgcn_readlane(kp, (u * RPR) >> pshift);
+            f.k[u] = load_nt(a.pool + page * a.page_elems + kcol + (int64_t)(r & (a.P - 1)) * D);
+        }
+    };
+    const uint32_t mm = masked ? 0xFFFFFFFFu : 0u;
+    uint32_t mw_next = mwp[masked ? min(tb, wpr - 1) : 0];  // mask word of the wave's first tile
+    int kp[2];
+    kp[0] = tile_kp(0);
+    kp[1] = tile_kp(min(1, kMassWaveTiles - 1));
+    KvFrags<D> kb[2];
+    kload(kp[0], kb[0]);
+    kp[0] = tile_kp(min(2, kMassWaveTiles - 1));
 #pragma unroll
     for (int u = 0; u < kMassWaveTiles; ++u) {
         const int j0 = 32 * (tb + u);
         if (j0 >= eff) break;  // wave-uniform
+        if (u + 1 < kMassWaveTiles) {
+            kload(kp[(u + 1) & 1], kb[(u + 1) & 1]);
+            kp[(u + 1) & 1] = tile_kp(min(u + 3, kMassWaveTiles - 1));
+        }
+        uint4 kf[D / 16];
+        stage_k<D, 32>(kb[u & 1], s_k[wv], kf);
         f32x16 acc = {};
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) acc = mfma32(kb[u & 1][s], qf[s], acc);
-        if (u + 2 < kMassWaveTiles) kload(u + 2, kb[u & 1]);
-        uint32_t bits = 0u;
-        if (live) {
-            if (masked) {
-                const int t = j0 >> 5;
-                bits = t < wpr ? a.mask_bits[a.mask_off[lane] + (int64_t)rl * wpr + t] : 0u;
-            } else {
-                const int r = lim - j0;
-                bits = r >= 32 ? 0xFFFFFFFFu : (r <= 0 ? 0u : ((1u << r) - 1u));
-            }
-            const int r = eff - j0;
-            bits &= r >= 32 ? 0xFFFFFFFFu : ((1u << r) - 1u);
-        }
+        for (int s = 0; s < D / 16; ++s) acc = mfma32(kf[s], qf[s], acc);
+        // allowed slots of the tile for this column: the row's mask word
+        // (loaded a tile ahead) on masked lanes, the causal limit on the
+        // others; both enter through masks so the word is used on every path
+        // (a load used only behind a branch would be sunk into it and waited
+        // for right there)
+        const uint32_t mwv = mw_next;
+        mw_next = mwp[masked ? min((j0 >> 5) + 1, wpr - 1) : 0];
+        const int rl_ = lim - j0, rk = eff - j0;
+        const uint32_t lm = rl_ >= 32 ? 0xFFFFFFFFu : (rl_ <= 0 ? 0u : ((1u << rl_) - 1u));
+        const uint32_t km = rk >= 32 ? 0xFFFFFFFFu : ((1u << rk) - 1u);
+        const uint32_t wm = (!masked || (j0 >> 5) < wpr) ? mwv : 0u;
+        uint32_t bits = (wm | ~mm) & (lm | mm) & km;
+        bits = live ? bits : 0u;
         // register i holds tile slot 16(i/8) + 8h + i%8 of this column
         const uint32_t hb = bits >> (8 * h);
         float mine = 0.0f;  // lane nn < 16 of half h keeps the total of register nn
