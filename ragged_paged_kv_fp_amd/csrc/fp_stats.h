@@ -158,7 +158,11 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
     }
     const int items = ((n + 31) >> 5) * a.G;
     constexpr float kLog2e = 1.4426950408889634f;
-    const char *krow = s_k + kslot_of_row(nn) * KROW + h * D;
+    // Step s of the QK^T chain takes head-dimension elements 16s + 8kg ..
+    // 16s + 8kg + 7 for lane group kg (= h) on both operands, so each Q load
+    // instruction reads 32 contiguous bytes of every row it touches rather
+    // than two 16-byte pieces half a row apart.
+    const char *krow = s_k + kslot_of_row(nn) * KROW + 16 * h;
 
     float msum[kMassTiles][16];
 #pragma unroll
@@ -202,9 +206,10 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
         if (!__any(any != 0u)) continue;  // wave-uniform
         uint4 qf[D / 16];
         {
-            const uint4 *qsrc = reinterpret_cast<const uint4 *>(a.qrot + (row * a.Hq + head) * D + h * (D / 2));
+            const uint16_t *qsrc = a.qrot + (row * a.Hq + head) * D + 8 * h;
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) qf[s] = qsrc[s];  // row is clamped to the lane's first
+            for (int s = 0; s < D / 16; ++s)  // row is clamped to the lane's first
+                qf[s] = *reinterpret_cast<const uint4 *>(qsrc + 16 * s);
             if (!valid) {
 #pragma unroll
                 for (int s = 0; s < D / 16; ++s) qf[s] = make_uint4(0, 0, 0, 0);
@@ -227,7 +232,7 @@ __global__ void __launch_bounds__(64 * kMassWaves) mass_kernel(MassArgs a) {
             f32x16 acc = {};
 #pragma unroll
             for (int s = 0; s < D / 16; ++s)
-                acc = mfma32(*reinterpret_cast<const uint4 *>(krow + t * 32 * KROW + 16 * s), qf[s], acc);
+                acc = mfma32(*reinterpret_cast<const uint4 *>(krow + t * 32 * KROW + 32 * s), qf[s], acc);
             acc = mfma32(bias_a, bias_b, acc);
             // register i holds tile slot 16(i/8) + 8h + i%8 of this column;
             // a dropped slot's weight is cleared by a sign-extended bit mask
