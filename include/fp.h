@@ -21,7 +21,8 @@
  *  - Pointers are DEVICE pointers unless the name ends in `_host`.
  *  - bf16 values are passed as 16-bit storage (bit patterns).
  *  - The caller owns every buffer; the library allocates no memory, keeps no
- *    state between calls and never synchronizes. Buffers must stay valid until
+ *    state between calls (apart from the static device scratch of
+ *    fp_attend_noalloc) and never synchronizes. Buffers must stay valid until
  *    the work enqueued on `stream` has completed. `stream` may be NULL (the
  *    default stream).
  *  - Errors the host can see are returned synchronously, before anything is
@@ -170,6 +171,33 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
               float rope_theta, float sm_scale, const fp_mask *mask, float *out, float *lse,
               void *workspace, size_t workspace_bytes, const fp_tuning *tuning,
               int32_t *status, hipStream_t stream);
+
+/*
+ * fp_attend_noalloc - fp_attend for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and results as fp_attend, but
+ * the workspace is the library's own static device scratch of
+ * fp_attend_noalloc_max_bytes() bytes (64 MiB) per device, which every device
+ * the library runs on holds until the process ends. The caller still passes
+ * inputs and outputs.
+ *   - Makes no hipMalloc / hipFree call and calls no allocating routine. The
+ *     first call on a device looks up that device's scratch address once
+ *     (hipGetSymbolAddress); make that first call outside graph capture.
+ *   - Returns FP_ERR_WORKSPACE, with nothing enqueued, when the pass needs more
+ *     than the scratch holds (fp_attend_workspace_bytes() > the maximum), and
+ *     the other FP_ERR_* codes of fp_attend.
+ *   - Every call on one device shares that device's scratch, which keeps the
+ *     last call's contents (nothing in it needs to start at zero). Calls that
+ *     overlap on one device (two streams, or two host threads without ordering)
+ *     race on it; calls in order on one stream do not. fp_attn_mass cannot follow
+ *     it (that needs the rotated queries in a caller workspace).
+ */
+int fp_attend_noalloc(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, int32_t num_q_heads,
+                      float rope_theta, float sm_scale, const fp_mask *mask, float *out, float *lse,
+                      const fp_tuning *tuning, int32_t *status, hipStream_t stream);
+
+/* Bytes of the static scratch fp_attend_noalloc uses (the largest workspace it accepts). */
+int64_t fp_attend_noalloc_max_bytes(void);
 
 /*
  * fp_fold - after the pass, freeze k_l newly written slots of every lane:

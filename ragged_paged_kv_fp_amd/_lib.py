@@ -35,7 +35,8 @@ FP_ST_ADAPTER = 256
 FP_FOLD_ALL = -1
 FP_FOLD_CHANNEL = -2
 
-EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_fold", "fp_readout", "fp_attn_mass",
+EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_attend_noalloc",
+           "fp_attend_noalloc_max_bytes", "fp_fold", "fp_readout", "fp_attn_mass",
            "fp_advance", "fp_lora_workspace_bytes", "fp_adapter_lora", "fp_adapter_ia3",
            "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version")
 
@@ -90,6 +91,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp_attend.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_i32, ctypes.c_float, ctypes.c_float, P(FpMask),
                               c_ptr, c_ptr, c_ptr, ctypes.c_size_t, P(FpTuning), c_ptr, c_ptr]
     lib.fp_attend.restype = c_i32
+    lib.fp_attend_noalloc.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_i32, ctypes.c_float, ctypes.c_float,
+                                      P(FpMask), c_ptr, c_ptr, P(FpTuning), c_ptr, c_ptr]
+    lib.fp_attend_noalloc.restype = c_i32
+    lib.fp_attend_noalloc_max_bytes.argtypes = []
+    lib.fp_attend_noalloc_max_bytes.restype = c_i64
     lib.fp_fold.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, c_ptr]
     lib.fp_fold.restype = c_i32
     lib.fp_readout.argtypes = [P(FpGeometry), c_ptr, c_i32, c_ptr, c_i32, c_ptr, c_ptr, c_ptr]

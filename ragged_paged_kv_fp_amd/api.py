@@ -157,6 +157,24 @@ def attend(pool: Pool, geom: Geometry, q: torch.Tensor, num_q_heads: int, rope_t
                                       _ptr(status), _stream(stream)))
 
 
+def attend_noalloc(pool: Pool, geom: Geometry, q: torch.Tensor, num_q_heads: int, rope_theta: float,
+                   sm_scale: float, out: torch.Tensor, status: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                   mask: Optional[Mask] = None, split: Optional[int] = None, stream=None, events=None) -> None:
+    """fp_attend_noalloc: fp_attend on the library's static device scratch (no workspace argument)."""
+    lib = _lib.load()
+    ps, gs = pool.struct(), geom.struct()
+    ms = mask.struct() if mask is not None else None
+    _check("fp_attend_noalloc", lib.fp_attend_noalloc(ctypes.byref(ps), ctypes.byref(gs), _ptr(q), int(num_q_heads),
+                                                      float(rope_theta), float(sm_scale),
+                                                      ctypes.byref(ms) if ms is not None else None,
+                                                      _ptr(out), _ptr(lse), _tuning(split, events), _ptr(status),
+                                                      _stream(stream)))
+
+
+def attend_noalloc_max_bytes() -> int:
+    return int(_lib.load().fp_attend_noalloc_max_bytes())
+
+
 def fold(pool: Pool, geom: Geometry, status: torch.Tensor, channel: Optional[torch.Tensor] = None,
          stream=None) -> None:
     """fp_fold: committed_len += none | all | literal | channel count, clamped."""

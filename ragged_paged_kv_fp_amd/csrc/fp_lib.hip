@@ -9,8 +9,15 @@
 
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 #include <string.h>
+
+// The library's own device scratch (fp_attend_noalloc): 64 MiB per device,
+// file scope, held until the process ends. Host code must use the address
+// hipGetSymbolAddress returns for the current device, never this name.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -188,53 +195,36 @@ void launch_prefill_g(const AttnArgs &a, int G, int64_t n, hipStream_t s) {
     }
 }
 
-}  // namespace
+// Scratch memory of fp_attend_noalloc: the workspace fp_attend would take
+// from the caller (rotated Q, plan records, work lists, split partials, tile
+// lists), held by the library on every device it runs on until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory:
+// kernels get the device address that hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept in scratch_dev.
 
-extern "C" {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_dev[kMaxDevices] = {};
 
-int fp_append_kv(const fp_kv_pool *pool, const fp_geometry *geom, const void *k, const void *v, float rope_theta,
-                 int32_t *status, hipStream_t stream) {
-    int rc = check_pool(pool);
-    if (rc) return rc;
-    if ((rc = check_geom(geom, pool))) return rc;
-    if (!status) return FP_ERR_NULL;
-    if (geom->num_rows == 0) return FP_OK;
-    if (!k || !v) return FP_ERR_NULL;
-    AppendArgs a;
-    a.pool = static_cast<uint16_t *>(pool->kv);
-    a.num_pages = pool->num_pages;
-    a.P = pool->page_size;
-    a.H = pool->num_kv_heads;
-    a.D = pool->head_dim;
-    a.page_elems = 2LL * a.H * a.P * a.D;
-    a.page_indptr = pool->page_indptr;
-    a.page_ids = pool->page_ids;
-    a.committed = pool->committed_len;
-    a.indptr = geom->indptr;
-    a.L = geom->num_lanes;
-    a.N = geom->num_rows;
-    a.positions = geom->positions;
-    a.slots = geom->slots;
-    a.k = static_cast<const uint16_t *>(k);
-    a.v = static_cast<const uint16_t *>(v);
-    a.status = status;
-    a.freqs = rope_freqs(rope_theta, a.D);
-    row_grouping(a.N, a.D / 2, a.H, &a.rows, &a.chunks);
-    hipLaunchKernelGGL(append_kernel, dim3((unsigned)((a.N + a.rows - 1) / a.rows)), dim3(256), 0, stream, a);
-    return launch_ok();
+// Device address of this device's scratch array (FP_ERR_HIP if the lookup fails).
+int scratch_ptr(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FP_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FP_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FP_ERR_HIP;
+        scratch_dev[dev] = ptr;
+    }
+    *out = scratch_dev[dev];
+    return FP_OK;
 }
 
-int64_t fp_attend_workspace_bytes(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *mask,
-                                  int32_t num_q_heads, const fp_tuning *tuning) {
-    Plan p;
-    const int rc = make_plan(pool, geom, mask, num_q_heads, tuning, &p);
-    if (rc) return rc;
-    return (int64_t)p.total;
-}
-
-int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, int32_t num_q_heads, float rope_theta,
-              float sm_scale, const fp_mask *mask, float *out, float *lse, void *workspace, size_t workspace_bytes,
-              const fp_tuning *tuning, int32_t *status, hipStream_t stream) {
+// fp_attend on a given workspace (the caller's, or the library's static scratch).
+int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, int32_t num_q_heads, float rope_theta,
+                float sm_scale, const fp_mask *mask, float *out, float *lse, void *workspace, size_t workspace_bytes,
+                const fp_tuning *tuning, int32_t *status, hipStream_t stream) {
     Plan p;
     int rc = make_plan(pool, geom, mask, num_q_heads, tuning, &p);
     if (rc) return rc;
@@ -345,6 +335,72 @@ int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, in
     }
     return FP_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int fp_append_kv(const fp_kv_pool *pool, const fp_geometry *geom, const void *k, const void *v, float rope_theta,
+                 int32_t *status, hipStream_t stream) {
+    int rc = check_pool(pool);
+    if (rc) return rc;
+    if ((rc = check_geom(geom, pool))) return rc;
+    if (!status) return FP_ERR_NULL;
+    if (geom->num_rows == 0) return FP_OK;
+    if (!k || !v) return FP_ERR_NULL;
+    AppendArgs a;
+    a.pool = static_cast<uint16_t *>(pool->kv);
+    a.num_pages = pool->num_pages;
+    a.P = pool->page_size;
+    a.H = pool->num_kv_heads;
+    a.D = pool->head_dim;
+    a.page_elems = 2LL * a.H * a.P * a.D;
+    a.page_indptr = pool->page_indptr;
+    a.page_ids = pool->page_ids;
+    a.committed = pool->committed_len;
+    a.indptr = geom->indptr;
+    a.L = geom->num_lanes;
+    a.N = geom->num_rows;
+    a.positions = geom->positions;
+    a.slots = geom->slots;
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.status = status;
+    a.freqs = rope_freqs(rope_theta, a.D);
+    row_grouping(a.N, a.D / 2, a.H, &a.rows, &a.chunks);
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)((a.N + a.rows - 1) / a.rows)), dim3(256), 0, stream, a);
+    return launch_ok();
+}
+
+int64_t fp_attend_workspace_bytes(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *mask,
+                                  int32_t num_q_heads, const fp_tuning *tuning) {
+    Plan p;
+    const int rc = make_plan(pool, geom, mask, num_q_heads, tuning, &p);
+    if (rc) return rc;
+    return (int64_t)p.total;
+}
+
+int fp_attend(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, int32_t num_q_heads, float rope_theta,
+              float sm_scale, const fp_mask *mask, float *out, float *lse, void *workspace, size_t workspace_bytes,
+              const fp_tuning *tuning, int32_t *status, hipStream_t stream) {
+    return attend_impl(pool, geom, q, num_q_heads, rope_theta, sm_scale, mask, out, lse, workspace, workspace_bytes,
+                       tuning, status, stream);
+}
+
+int fp_attend_noalloc(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, int32_t num_q_heads,
+                      float rope_theta, float sm_scale, const fp_mask *mask, float *out, float *lse,
+                      const fp_tuning *tuning, int32_t *status, hipStream_t stream) {
+    Plan p;
+    int rc = make_plan(pool, geom, mask, num_q_heads, tuning, &p);
+    if (rc) return rc;
+    if (p.total > kScratchBytes) return FP_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if ((rc = scratch_ptr(&ws))) return rc;
+    return attend_impl(pool, geom, q, num_q_heads, rope_theta, sm_scale, mask, out, lse, ws, kScratchBytes, tuning,
+                       status, stream);
+}
+
+int64_t fp_attend_noalloc_max_bytes(void) { return (int64_t)kScratchBytes; }
 
 int fp_fold(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *channel, int32_t *status,
             hipStream_t stream) {
