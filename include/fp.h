@@ -64,6 +64,9 @@ typedef struct ihipEvent_t *hipEvent_t;
 #define FP_ST_PLAN_MISMATCH 128   /* device offset arrays disagree with their host copies:
                                      fp_attend did no attention work (outputs untouched)      */
 #define FP_ST_ADAPTER      256    /* adapter id >= num_adapters: the lane's rows keep y       */
+#define FP_ST_DUP_WRITE    512    /* fp_check_hazards: a KV cell is written twice in one pass */
+#define FP_ST_SHARED_CELL 1024    /* fp_check_hazards: a KV cell one lane writes is read or
+                                     written by another lane (Eq. (4) violated)               */
 
 /* ---- fold sentinels (StateGeometry.fold; a value >= 0 is a literal count) ---- */
 #define FP_FOLD_ALL      (-1)     /* freeze every row written this pass                       */
@@ -223,6 +226,31 @@ int fp_fold(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *chan
 int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, const int32_t *rows,
                int32_t num_readout, float *dst, int32_t *status, hipStream_t stream);
 
+/* Workspace bytes fp_check_hazards needs: three int32 per KV cell (num_pages * P cells). */
+int64_t fp_hazard_workspace_bytes(const fp_kv_pool *pool);
+
+/*
+ * fp_check_hazards - debug check of one pass's geometry against the reviews'
+ * Eq. (4) (section 5: calls batched together must keep their meaning, i.e.
+ * W(a) ∩ (R(b) ∪ W(b)) = ∅ for two calls a ≠ b), with lanes as the calls and
+ * KV cells (physical page, offset) as the state:
+ *   W(l) = cells lane l's rows write (the writes fp_append_kv performs: slot
+ *          inside the capacity, not below committed_len, page id in the pool);
+ *   R(l) = cells of lane l's slots below its kv_len (clamped to the capacity)
+ *          whose page id is in the pool.
+ * Sets FP_ST_DUP_WRITE in *status if some cell is written more than once in
+ * the pass (two rows naming one slot, which fp_append_kv leaves undefined, or
+ * two lanes whose pages overlap), and FP_ST_SHARED_CELL if a cell one lane
+ * writes is read or written by another lane. Reads the geometry, the page
+ * table and committed_len only: enqueue it before fp_append_kv of the pass.
+ *   workspace: fp_hazard_workspace_bytes(pool) bytes of device memory (its
+ *   contents are overwritten). Four launches; nothing else is modified.
+ * Returns FP_ERR_NULL / FP_ERR_SHAPE / FP_ERR_UNSUPPORTED / FP_ERR_WORKSPACE
+ * before enqueueing anything, FP_ERR_HIP on a launch error.
+ */
+int fp_check_hazards(const fp_kv_pool *pool, const fp_geometry *geom, void *workspace, size_t workspace_bytes,
+                     int32_t *status, hipStream_t stream);
+
 /*
  * fp_attn_mass - attention statistics of the pass, so that an eviction policy
  * driven by attention scores (TOVA and the like) can run on the device: the
@@ -337,6 +365,10 @@ uint64_t fp_page_bytes(int32_t P, int32_t H_kv, int32_t d);                     
 
 /* Library version string (static storage). */
 const char *fp_version(void);
+
+/* SHA-256 (hex) of the library's source files as they were compiled (static
+ * storage): a binding compares it with its sources to refuse a stale build. */
+const char *fp_source_hash(void);
 
 #ifdef __cplusplus
 }

@@ -53,6 +53,8 @@ ST_READOUT_RANGE = 16  # readout row outside [0, num_rows): zero row returned
 ST_MASK_SHORT = 32     # mask row holds fewer than kv_len bits: missing bits read as 0
 ST_PAGE_RANGE = 64     # page id outside [0, num_pages): write suppressed, read clamped
 ST_ADAPTER = 256       # adapter id >= number of adapters: the lane keeps y
+ST_DUP_WRITE = 512     # a KV cell receives two writes in one pass
+ST_SHARED_CELL = 1024  # a KV cell one lane writes is read or written by another lane
 
 FOLD_ALL = -1
 FOLD_CHANNEL = -2
@@ -221,6 +223,53 @@ def append(pool: Pool, committed, indptr, positions, slots, k_bits, v_bits, thet
     return status
 
 
+def hazards(pool: Pool, committed, indptr, slots, kv_len) -> int:
+    """Conflicts of one pass between what its rows write and what its lanes read.
+
+    The reviews' Eq. (4) (section 5, batching that keeps meaning) asks that
+    calls batched together do not touch each other's state:
+    W(a) ∩ (R(b) ∪ W(b)) = ∅ for two calls a ≠ b. Here a call is a lane, and
+    the state is KV cells (physical page, offset):
+      W(a): the cells lane a's rows write this pass (writes that append()
+            performs: slot inside the lane's capacity, not frozen, page id in
+            the pool);
+      R(b): the cells of lane b's slots below its kv_len (clamped to its
+            capacity) whose page id is in the pool.
+    Returns ST_DUP_WRITE if some cell is written more than once in the pass
+    (two rows with one slot, or two lanes' writes landing in one cell), and
+    ST_SHARED_CELL if a cell lane a writes is read or written by another lane.
+    """
+    writers = {}
+    L = len(indptr) - 1
+    for lane in range(L):
+        r0, r1 = _lane_rows(indptr, lane)
+        cap = pool.capacity(lane)
+        for r in range(r0, r1):
+            s = int(slots[r])
+            if s < 0 or s >= cap or s < int(committed[lane]):
+                continue
+            page = int(pool.page_ids[pool.page_indptr[lane] + s // pool.P])
+            if page < 0 or page >= pool.num_pages:
+                continue
+            writers.setdefault((page, s % pool.P), []).append(lane)
+    status = 0
+    for lanes in writers.values():
+        if len(lanes) > 1:
+            status |= ST_DUP_WRITE
+        if len(set(lanes)) > 1:
+            status |= ST_SHARED_CELL
+    for lane in range(L):
+        eff = min(max(int(kv_len[lane]), 0), pool.capacity(lane))
+        for j in range(eff):
+            page = int(pool.page_ids[pool.page_indptr[lane] + j // pool.P])
+            if page < 0 or page >= pool.num_pages:
+                continue
+            w = writers.get((page, j % pool.P))
+            if w is not None and any(a != lane for a in w):
+                status |= ST_SHARED_CELL
+    return status
+
+
 def _mask_span(mask_bits, word_offset, indptr, lane):
     if mask_bits is None or word_offset is None:
         return None
@@ -272,6 +321,10 @@ def attend(pool: Pool, indptr, positions, slots, kv_len, q_bits, H_q, theta, sm_
         if eff != kvl:
             status |= ST_KVLEN
         K, V = pool.lane_kv(lane, eff)
+        if not (np.isfinite(K).all() and np.isfinite(V).all()):
+            # every slot below kv_len must hold finite K/V (written by append or
+            # filled by the caller); such a pass is outside the step's domain
+            raise ValueError(f"lane {lane}: a slot below kv_len holds a non-finite K or V")
         idx = np.nonzero(lane_of == lane)[0]
         qr = rope(bf16_to_f64(q_bits[rows[idx]]), np.asarray(positions)[rows[idx]], theta)
         for t, i in enumerate(idx):

@@ -31,14 +31,17 @@ FP_ST_MASK_SHORT = 32
 FP_ST_PAGE_RANGE = 64
 FP_ST_PLAN_MISMATCH = 128
 FP_ST_ADAPTER = 256
+FP_ST_DUP_WRITE = 512
+FP_ST_SHARED_CELL = 1024
 
 FP_FOLD_ALL = -1
 FP_FOLD_CHANNEL = -2
 
 EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_attend_noalloc",
-           "fp_attend_noalloc_max_bytes", "fp_fold", "fp_readout", "fp_attn_mass",
+           "fp_attend_noalloc_max_bytes", "fp_hazard_workspace_bytes",
+           "fp_check_hazards", "fp_fold", "fp_readout", "fp_attn_mass",
            "fp_advance", "fp_lora_workspace_bytes", "fp_adapter_lora", "fp_adapter_ia3",
-           "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version")
+           "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version", "fp_source_hash")
 
 
 class FpGeometry(ctypes.Structure):
@@ -74,8 +77,27 @@ class FpError(RuntimeError):
 _lib = None
 
 
+class StaleLibraryError(ImportError):
+    """libfp.so was compiled from other sources than the ones in the tree."""
+
+
+def check_fresh(lib: ctypes.CDLL, sources=None) -> None:
+    """Raise StaleLibraryError unless the library's compiled-in source hash equals
+    the hash of the current sources (so no test or benchmark runs an old binary)."""
+    from . import build
+
+    lib.fp_source_hash.argtypes = []
+    lib.fp_source_hash.restype = ctypes.c_char_p
+    built = lib.fp_source_hash().decode()
+    now = build.source_hash(sources)
+    if built != now:
+        raise StaleLibraryError(f"libfp.so was built from other sources (built {built[:12]}, tree {now[:12]}): "
+                                "rebuild it with `python -m ragged_paged_kv_fp_amd.build` or __graft_entry__.build()")
+
+
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libfp.so; raises if it has not been built (there is no fallback path)."""
+    """Load libfp.so; raises if it has not been built or is older than its
+    sources (there is no fallback path)."""
     global _lib
     if _lib is not None:
         return _lib
@@ -83,6 +105,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise ImportError(f"{path} is missing: build it with `python -m ragged_paged_kv_fp_amd.build` "
                           "(or __graft_entry__.build()); the step has no CPU fallback")
     lib = ctypes.CDLL(path)
+    check_fresh(lib)
     P = ctypes.POINTER
     lib.fp_append_kv.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, ctypes.c_float, c_ptr, c_ptr]
     lib.fp_append_kv.restype = c_i32
@@ -96,6 +119,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp_attend_noalloc.restype = c_i32
     lib.fp_attend_noalloc_max_bytes.argtypes = []
     lib.fp_attend_noalloc_max_bytes.restype = c_i64
+    lib.fp_hazard_workspace_bytes.argtypes = [P(FpKvPool)]
+    lib.fp_hazard_workspace_bytes.restype = c_i64
+    lib.fp_check_hazards.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, ctypes.c_size_t, c_ptr, c_ptr]
+    lib.fp_check_hazards.restype = c_i32
     lib.fp_fold.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, c_ptr]
     lib.fp_fold.restype = c_i32
     lib.fp_readout.argtypes = [P(FpGeometry), c_ptr, c_i32, c_ptr, c_i32, c_ptr, c_ptr, c_ptr]

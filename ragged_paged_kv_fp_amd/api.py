@@ -175,6 +175,21 @@ def attend_noalloc_max_bytes() -> int:
     return int(_lib.load().fp_attend_noalloc_max_bytes())
 
 
+def hazard_workspace_bytes(pool: Pool) -> int:
+    lib = _lib.load()
+    ps = pool.struct()
+    return _check("fp_hazard_workspace_bytes", lib.fp_hazard_workspace_bytes(ctypes.byref(ps)))
+
+
+def check_hazards(pool: Pool, geom: Geometry, workspace: torch.Tensor, status: torch.Tensor, stream=None) -> None:
+    """fp_check_hazards: Eq. (4) write/read conflicts of the pass's lanes (debug; before append_kv)."""
+    lib = _lib.load()
+    ps, gs = pool.struct(), geom.struct()
+    _check("fp_check_hazards", lib.fp_check_hazards(ctypes.byref(ps), ctypes.byref(gs), _ptr(workspace),
+                                                    workspace.numel() * workspace.element_size(), _ptr(status),
+                                                    _stream(stream)))
+
+
 def fold(pool: Pool, geom: Geometry, status: torch.Tensor, channel: Optional[torch.Tensor] = None,
          stream=None) -> None:
     """fp_fold: committed_len += none | all | literal | channel count, clamped."""

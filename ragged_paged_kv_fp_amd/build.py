@@ -2,6 +2,7 @@
 
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -36,10 +37,20 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
+def source_hash(paths=None) -> str:
+    """SHA-256 over the library's source files (DEPS, in order), as compiled into fp_source_hash()."""
+    h = hashlib.sha256()
+    for p in (DEPS if paths is None else paths):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False, extra_flags=None) -> str:
     """Compile libfp.so (always recompiles). Returns the library path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags or []) + ["-I", os.path.join(ROOT, "include")] + SOURCES + ["-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags or []) + [f'-DFP_SOURCE_HASH="{source_hash()}"',
+                                                               "-I", os.path.join(ROOT, "include")] + SOURCES + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,11 +61,6 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
-def is_stale() -> bool:
-    if not os.path.exists(LIB):
-        return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(d) > t for d in DEPS)
 
 
 if __name__ == "__main__":

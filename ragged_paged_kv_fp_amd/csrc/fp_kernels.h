@@ -144,6 +144,80 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     }
 }
 
+// ============================================================================ hazards
+
+// Write/read conflicts of one pass (the reviews' Eq. (4): what one lane writes
+// must not be read or written by another lane), on KV cells (physical page,
+// offset). Three words per cell: how many rows write it this pass, and the
+// smallest and largest lane that does. A cell written twice sets
+// FP_ST_DUP_WRITE; a cell whose writers are not all the lane that writes or
+// reads it sets FP_ST_SHARED_CELL. Debug path: four small launches.
+struct HazardArgs {
+    const int32_t *indptr, *slots, *kv_len, *page_indptr, *page_ids, *committed;
+    int L, num_pages, P;
+    int64_t N, cells;
+    int32_t *cnt, *lmin, *lmax;  // [cells] each
+    int32_t *status;
+};
+
+__global__ void __launch_bounds__(256) hazard_init_kernel(HazardArgs a) {
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < a.cells; c += (int64_t)gridDim.x * blockDim.x) {
+        a.cnt[c] = 0;
+        a.lmin[c] = 0x7FFFFFFF;
+        a.lmax[c] = -1;
+    }
+}
+
+// Cell row `row` writes this pass (the write fp_append_kv performs), or -1 if
+// that write is suppressed; *lane_out gets the row's lane.
+__device__ __forceinline__ int64_t hazard_write_cell(const HazardArgs &a, int64_t row, int *lane_out) {
+    const int lane = find_lane(a.indptr, a.L, row);
+    *lane_out = lane;
+    const int slot = a.slots[row];
+    const int p0 = a.page_indptr[lane];
+    const int cap = (a.page_indptr[lane + 1] - p0) * a.P;
+    if (slot < 0 || slot >= cap || slot < a.committed[lane]) return -1;
+    const int page = a.page_ids[p0 + slot / a.P];
+    if (page < 0 || page >= a.num_pages) return -1;
+    return (int64_t)page * a.P + slot % a.P;
+}
+
+__global__ void __launch_bounds__(256) hazard_mark_kernel(HazardArgs a) {
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= a.N) return;
+    int lane;
+    const int64_t c = hazard_write_cell(a, row, &lane);
+    if (c < 0) return;
+    atomicAdd(&a.cnt[c], 1);
+    atomicMin(&a.lmin[c], lane);
+    atomicMax(&a.lmax[c], lane);
+}
+
+__global__ void __launch_bounds__(256) hazard_rows_kernel(HazardArgs a) {
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= a.N) return;
+    int lane;
+    const int64_t c = hazard_write_cell(a, row, &lane);
+    if (c < 0) return;
+    int bits = 0;
+    if (a.cnt[c] > 1) bits |= FP_ST_DUP_WRITE;
+    if (a.lmin[c] != a.lmax[c]) bits |= FP_ST_SHARED_CELL;
+    if (bits) atomicOr(a.status, bits);
+}
+
+// Block (x, lane): slots [256 x, 256 x + 256) of the lane that it reads.
+__global__ void __launch_bounds__(256) hazard_reads_kernel(HazardArgs a) {
+    const int lane = blockIdx.y;
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    const int p0 = a.page_indptr[lane];
+    const int cap = (a.page_indptr[lane + 1] - p0) * a.P;
+    if (j >= clamp_kv(a.kv_len[lane], cap)) return;
+    const int page = a.page_ids[p0 + j / a.P];
+    if (page < 0 || page >= a.num_pages) return;
+    const int64_t c = (int64_t)page * a.P + j % a.P;
+    if (a.cnt[c] > 0 && (a.lmin[c] != lane || a.lmax[c] != lane)) atomicOr(a.status, FP_ST_SHARED_CELL);
+}
+
 // ============================================================================ fold
 
 __global__ void __launch_bounds__(256) fold_kernel(const int32_t *indptr, const int32_t *fold, const int32_t *channel,

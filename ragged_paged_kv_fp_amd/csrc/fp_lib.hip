@@ -393,6 +393,9 @@ int fp_attend_noalloc(const fp_kv_pool *pool, const fp_geometry *geom, const voi
     Plan p;
     int rc = make_plan(pool, geom, mask, num_q_heads, tuning, &p);
     if (rc) return rc;
+    if (!status) return FP_ERR_NULL;
+    if (p.N == 0) return FP_OK;
+    if (!q || !out) return FP_ERR_NULL;
     if (p.total > kScratchBytes) return FP_ERR_WORKSPACE;
     void *ws = nullptr;
     if ((rc = scratch_ptr(&ws))) return rc;
@@ -401,6 +404,58 @@ int fp_attend_noalloc(const fp_kv_pool *pool, const fp_geometry *geom, const voi
 }
 
 int64_t fp_attend_noalloc_max_bytes(void) { return (int64_t)kScratchBytes; }
+
+int64_t fp_hazard_workspace_bytes(const fp_kv_pool *pool) {
+    const int rc = check_pool(pool);
+    if (rc) return rc;
+    return (int64_t)3 * sizeof(int32_t) * pool->num_pages * pool->page_size;
+}
+
+int fp_check_hazards(const fp_kv_pool *pool, const fp_geometry *geom, void *workspace, size_t workspace_bytes,
+                     int32_t *status, hipStream_t stream) {
+    int rc = check_pool(pool);
+    if (rc) return rc;
+    if ((rc = check_geom(geom, pool))) return rc;
+    if (geom->num_lanes > 65535) return FP_ERR_UNSUPPORTED;
+    if (!status || !workspace) return FP_ERR_NULL;
+    const int64_t cells = (int64_t)pool->num_pages * pool->page_size;
+    if ((int64_t)workspace_bytes < fp_hazard_workspace_bytes(pool)) return FP_ERR_WORKSPACE;
+    HazardArgs a;
+    a.indptr = geom->indptr;
+    a.slots = geom->slots;
+    a.kv_len = geom->kv_len;
+    a.page_indptr = pool->page_indptr;
+    a.page_ids = pool->page_ids;
+    a.committed = pool->committed_len;
+    a.L = geom->num_lanes;
+    a.num_pages = pool->num_pages;
+    a.P = pool->page_size;
+    a.N = geom->num_rows;
+    a.cells = cells;
+    a.cnt = static_cast<int32_t *>(workspace);
+    a.lmin = a.cnt + cells;
+    a.lmax = a.lmin + cells;
+    a.status = status;
+    int max_cap = 0;
+    for (int l = 0; l < a.L; ++l)
+        max_cap = std::max(max_cap, (pool->page_indptr_host[l + 1] - pool->page_indptr_host[l]) * a.P);
+    const int64_t init_blocks = std::min<int64_t>((cells + 255) / 256, 4096);
+    hipLaunchKernelGGL(hazard_init_kernel, dim3((unsigned)init_blocks), dim3(256), 0, stream, a);
+    if ((rc = launch_ok())) return rc;
+    if (a.N > 0) {
+        const unsigned rb = (unsigned)((a.N + 255) / 256);
+        hipLaunchKernelGGL(hazard_mark_kernel, dim3(rb), dim3(256), 0, stream, a);
+        if ((rc = launch_ok())) return rc;
+        hipLaunchKernelGGL(hazard_rows_kernel, dim3(rb), dim3(256), 0, stream, a);
+        if ((rc = launch_ok())) return rc;
+        if (max_cap > 0) {
+            hipLaunchKernelGGL(hazard_reads_kernel, dim3((unsigned)((max_cap + 255) / 256), (unsigned)a.L), dim3(256), 0,
+                               stream, a);
+            if ((rc = launch_ok())) return rc;
+        }
+    }
+    return FP_OK;
+}
 
 int fp_fold(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *channel, int32_t *status,
             hipStream_t stream) {
@@ -624,6 +679,11 @@ uint64_t fp_page_waste(uint64_t T, int32_t P) { return P > 0 ? fp_pages_for(T, P
 
 uint64_t fp_page_bytes(int32_t P, int32_t H_kv, int32_t d) { return 2ull * (uint64_t)H_kv * (uint64_t)P * (uint64_t)d * 2ull; }
 
-const char *fp_version(void) { return "ragged_paged_kv_fp_amd 0.1 (gfx950)"; }
+const char *fp_version(void) { return "ragged_paged_kv_fp_amd 0.2 (gfx950)"; }
+
+#ifndef FP_SOURCE_HASH
+#define FP_SOURCE_HASH "unknown"
+#endif
+const char *fp_source_hash(void) { return FP_SOURCE_HASH; }
 
 }  // extern "C"

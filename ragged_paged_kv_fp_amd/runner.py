@@ -64,7 +64,7 @@ class DeviceStep:
         self.out = torch.zeros((N, wl.H_q, wl.d), dtype=torch.float32, device=dev)
         self.lse = torch.zeros((N, wl.H_q), dtype=torch.float32, device=dev) if with_lse else None
         self.mask = None
-        if wl.mask_bits is not None:
+        if wl.mask_bits is not None and wl.mask_bits.size > 0:  # all spans empty: every lane causal
             self.mask = api.Mask(bits=_dev(wl.mask_bits.view(np.int32), dev),
                                  word_offset=_dev(wl.mask_word_offset.astype(np.int64), dev),
                                  word_offset_host=wl.mask_word_offset.astype(np.int64).copy())

@@ -58,12 +58,14 @@ def rope_complex(vec, pos, theta):
     return out
 
 
-def run(wl_arrays, *, H_q, H_kv, d, theta, sm_scale, cap, prefix=None, committed0=None):
+def run(wl_arrays, *, H_q, H_kv, d, theta, sm_scale, cap, prefix=None, committed0=None, hole_bits=None):
     """Dense brute force of one pass.
 
     wl_arrays: dict with indptr, positions, slots, kv_len, fold, k, v, q (lists / numpy),
     optional mask (per global row: set of slots, or None for causal), channel.
-    cap: per-lane capacity in slots. prefix: same dict shape for a pre-pass (append + fold all).
+    cap: per-lane capacity in slots. prefix: same dict shape for a pre-pass (append, then its fold).
+    hole_bits: bf16 bit pattern every never-written slot holds (K and V alike);
+    None means no row may read such a slot.
     Returns dict(O, LSE, committed, store, mass) with O[row][head] lists and
     mass[lane][(kv head, slot)] the summed attention probability of the slot.
     """
@@ -103,6 +105,14 @@ def run(wl_arrays, *, H_q, H_kv, d, theta, sm_scale, cap, prefix=None, committed
         do_append(prefix)
         do_fold(prefix, None)
 
+    def slot_kv(lane, j):
+        if j in store[lane]:
+            return store[lane][j]
+        if hole_bits is None:
+            raise KeyError(f"lane {lane} reads slot {j}, which was never written")
+        hv = [bf16_value(hole_bits)] * d
+        return [hv] * H_kv, [hv] * H_kv
+
     w = wl_arrays
     do_append(w)
     G = H_q // H_kv
@@ -125,7 +135,7 @@ def run(wl_arrays, *, H_q, H_kv, d, theta, sm_scale, cap, prefix=None, committed
                 qv = rope_complex([bf16_value(b) for b in w["q"][r][hq]], int(w["positions"][r]), theta)
                 scores = []
                 for j in allowed:
-                    kj = store[lane][j][0][g]
+                    kj = slot_kv(lane, j)[0][g]
                     scores.append(sum(a * b for a, b in zip(qv, kj)) * sm_scale)
                 m = max(scores)
                 ps = [math.exp(s - m) for s in scores]
@@ -134,7 +144,7 @@ def run(wl_arrays, *, H_q, H_kv, d, theta, sm_scale, cap, prefix=None, committed
                     mass[lane][(g, j)] = mass[lane].get((g, j), 0.0) + p_ / tot
                 acc = [0.0] * d
                 for p_, j in zip(ps, allowed):
-                    vj = store[lane][j][1][g]
+                    vj = slot_kv(lane, j)[1][g]
                     for t in range(d):
                         acc[t] += p_ * vj[t]
                 O[r][hq] = [a / tot for a in acc]

@@ -58,6 +58,8 @@ def test_header_constants_match_binding_and_oracle():
     assert consts["FP_ST_MASK_SHORT"] == oracle.ST_MASK_SHORT
     assert consts["FP_ST_PAGE_RANGE"] == oracle.ST_PAGE_RANGE
     assert consts["FP_ST_ADAPTER"] == oracle.ST_ADAPTER
+    assert consts["FP_ST_DUP_WRITE"] == oracle.ST_DUP_WRITE
+    assert consts["FP_ST_SHARED_CELL"] == oracle.ST_SHARED_CELL
     assert consts["FP_FOLD_ALL"] == oracle.FOLD_ALL and consts["FP_FOLD_CHANNEL"] == oracle.FOLD_CHANNEL
 
 
@@ -220,3 +222,54 @@ def test_ia3_validation(lib):
     assert lib.fp_adapter_ia3(ctypes.byref(g), 2, 64, None, FAKE, FAKE, FAKE, st, None) == -1
     g.num_rows = 9
     assert lib.fp_adapter_ia3(ctypes.byref(g), 2, 64, FAKE, FAKE, FAKE, FAKE, st, None) == -2
+
+
+def test_noalloc_validation_before_any_device_call(lib):
+    g, p, keep = _structs()
+    st = ctypes.c_int32(0)
+    call = lambda g_, hq=4, status=ctypes.addressof(st), q=FAKE: lib.fp_attend_noalloc(  # noqa: E731
+        ctypes.byref(p), ctypes.byref(g_), q, hq, 1e4, 0.125, None, FAKE, None, None, status, None)
+    assert call(g, status=None) == -1
+    assert call(g, q=None) == -1
+    assert call(g, hq=5) == -2
+    assert lib.fp_attend_noalloc_max_bytes() == 64 << 20
+    # a pass whose workspace exceeds the scratch (rotated Q of 300k rows alone) is refused
+    big, pb, keep2 = _structs(L=1, rows=(300000,), pages=(1,))
+    assert _ws(lib, pb, big) > lib.fp_attend_noalloc_max_bytes()
+    assert lib.fp_attend_noalloc(ctypes.byref(pb), ctypes.byref(big), FAKE, 4, 1e4, 0.125, None, FAKE, None, None,
+                                 ctypes.addressof(st), None) == -4
+
+
+def test_hazard_check_validation(lib):
+    g, p, keep = _structs(P=16)
+    st = ctypes.c_int32(0)
+    need = lib.fp_hazard_workspace_bytes(ctypes.byref(p))
+    assert need == 3 * 4 * p.num_pages * 16
+    assert lib.fp_check_hazards(ctypes.byref(p), ctypes.byref(g), FAKE, need - 1, ctypes.addressof(st), None) == -4
+    assert lib.fp_check_hazards(ctypes.byref(p), ctypes.byref(g), None, need, ctypes.addressof(st), None) == -1
+    assert lib.fp_check_hazards(ctypes.byref(p), ctypes.byref(g), FAKE, need, None, None) == -1
+    p.page_size = 12
+    assert lib.fp_hazard_workspace_bytes(ctypes.byref(p)) == -3
+
+
+def test_stale_library_is_refused(lib, tmp_path):
+    """The binding compares the library's compiled-in source hash with the tree's:
+    the built library matches, and a changed source makes the check raise."""
+    from ragged_paged_kv_fp_amd import _lib, build
+
+    _lib.check_fresh(lib)  # the library under test was built from these sources
+    changed = []
+    for src in build.DEPS:
+        dst = tmp_path / os.path.basename(src)
+        data = open(src, "rb").read()
+        if src.endswith("fp_decode.h"):
+            data += b"\n// edited\n"
+        dst.write_bytes(data)
+        changed.append(str(dst))
+    with pytest.raises(_lib.StaleLibraryError):
+        _lib.check_fresh(lib, changed)
+    same = [str(tmp_path / ("same_" + os.path.basename(s))) for s in build.DEPS]
+    for src, dst in zip(build.DEPS, same):
+        open(dst, "wb").write(open(src, "rb").read())
+    with pytest.raises(_lib.StaleLibraryError):  # file names are part of the hash
+        _lib.check_fresh(lib, same)

@@ -56,6 +56,94 @@ def test_random_geometry(seed, H_kv, G, d, P):
     _say(pu.compare_step(ds, ref))
 
 
+HOLE_BITS = 0x3FC0  # bf16 1.5: what a slot no pass wrote holds (finite, as the step requires below kv_len)
+
+
+@pytest.mark.parametrize("seed,H_kv,G,d,P,kinds,masked", [
+    (0, 2, 2, 64, 16, None, True), (1, 1, 4, 128, 8, [2, 2, 1, 0], True), (2, 2, 8, 64, 32, [1, 1, 2, 0], True),
+    (3, 4, 1, 128, 16, [2, 1, 0], True), (4, 2, 4, 128, 32, [0, 0, 1, 1, 2], False),
+    (5, 1, 2, 64, 8, None, False), (6, 8, 4, 128, 16, [2, 2, 2, 1, 0, 0], True), (7, 2, 8, 128, 8, [2, 1], True),
+    (8, 2, 4, 128, 16, [2, 2, 2, 2], False), (9, 2, 4, 128, 16, [1, 1, 1, 1, 0, 0, 0, 0], True),
+])
+def test_explicit_slot_geometry(seed, H_kv, G, d, P, kinds, masked):
+    """Rows naming their slots (State geometry, for algorithms that manage KV
+    slots directly): permuted and gapped slots, prefix slots above the frozen
+    count rewritten, kv_len below some rows' slots, holes below kv_len holding
+    the pool's fill; decode-, verify- and prefill-class lanes, causal and bitmap."""
+    wl = W.make_explicit(seed, H_kv=H_kv, G=G, d=d, P=P, num_lanes=len(kinds) if kinds else 7, max_rows=120,
+                         max_ctx=500, masked=masked, kinds=kinds)
+    n = np.diff(wl.step.indptr)
+    _say(f"explicit seed {seed}: H_kv={H_kv} G={G} d={d} P={P} rows={wl.step.num_rows} "
+         f"decode-class={int(((n > 0) & (n * G <= 32)).sum())} prefill-class={int((n * G > 32).sum())}")
+    ref = pu.oracle_run(wl, fill=HOLE_BITS)
+    ds = pu.gpu_run(wl, fill=HOLE_BITS)
+    _say(pu.compare_step(ds, ref))
+
+
+def _hazard_bits(wl):
+    """fp_check_hazards on the GPU and oracle.hazards, both after the prefix pass and its fold."""
+    import torch
+
+    from ragged_paged_kv_fp_amd import api, runner
+
+    ds = runner.DeviceStep(wl)
+    ds.run_prefix()
+    torch.cuda.synchronize()
+    ws = torch.empty(api.hazard_workspace_bytes(ds.pool), dtype=torch.uint8, device=ds.device)
+    st = torch.zeros(1, dtype=torch.int32, device=ds.device)
+    api.check_hazards(ds.pool, ds.geom, ws, st)
+    torch.cuda.synchronize()
+    pool = oracle.Pool(wl.num_pages, wl.P, wl.H_kv, wl.d, wl.page_indptr, wl.page_ids)
+    c = np.zeros(wl.num_lanes, np.int32)
+    if wl.prefix is not None:
+        c, _ = oracle.fold(c, wl.prefix.indptr, wl.prefix.fold)
+    assert ds.pool.committed_len.cpu().numpy().tolist() == c.tolist()
+    return int(st.cpu()[0]), oracle.hazards(pool, c, wl.step.indptr, wl.step.slots, wl.step.kv_len)
+
+
+def test_hazard_check_matches_oracle():
+    """Eq. (4) (reviews, section 5) conflicts between lanes, and cells written twice:
+    the GPU check and the oracle agree bit for bit on valid passes (no bits) and
+    on passes with planted conflicts (the bits they expect)."""
+    DUP, SH = oracle.ST_DUP_WRITE, oracle.ST_SHARED_CELL
+    for wl in (W.make_explicit(11, num_lanes=6), W.make_config(3, seed=2, scale="small"),
+               W.make_random(12, num_lanes=6)):
+        got, want = _hazard_bits(wl)
+        assert got == want == 0, (wl.name, got, want)
+    # a duplicate slot within one lane
+    wl = W.make_explicit(13, num_lanes=6, kinds=[2, 1, 0, 2, 1, 0])
+    st = wl.step
+    lane = next(l for l in range(wl.num_lanes) if st.indptr[l + 1] - st.indptr[l] >= 2)
+    st.slots = st.slots.copy()
+    st.slots[st.indptr[lane] + 1] = st.slots[st.indptr[lane]]
+    got, want = _hazard_bits(wl)
+    assert want & DUP and got == want, (got, want)
+    # lane b's first page replaced by the page lane a writes into: b reads a's fresh cell
+    wl = W.make_config(3, seed=3, scale="small")
+    st = wl.step
+    n = np.diff(st.indptr)
+    a = int(np.argmax(n))
+    b = next(l for l in range(wl.num_lanes) if l != a and st.kv_len[l] >= wl.P)
+    s_a = int(st.slots[st.indptr[a]])
+    wl.page_ids = wl.page_ids.copy()
+    wl.page_ids[wl.page_indptr[b]] = wl.page_ids[wl.page_indptr[a] + s_a // wl.P]
+    got, want = _hazard_bits(wl)
+    assert want & SH and got == want, (got, want)
+    # two lanes whose rows write one cell
+    wl = W.make_config(2, seed=6, scale="small")
+    st = wl.step
+    wl.page_ids = wl.page_ids.copy()
+    last1 = (int(st.slots[1]) // wl.P)
+    last0 = (int(st.slots[0]) // wl.P)
+    st.slots = st.slots.copy()
+    st.slots[1] = last1 * wl.P + int(st.slots[0]) % wl.P
+    st.kv_len = st.kv_len.copy()
+    st.kv_len[1] = max(int(st.kv_len[1]), int(st.slots[1]) + 1)
+    wl.page_ids[wl.page_indptr[1] + last1] = wl.page_ids[wl.page_indptr[0] + last0]
+    got, want = _hazard_bits(wl)
+    assert want == DUP | SH and got == want, (got, want)
+
+
 def test_page_permutation_bit_identical_with_nan_decoys():
     wl = W.make_random(21, H_kv=2, G=4, d=128, P=16, num_lanes=6, max_rows=70, max_ctx=300, extra_pages=9)
     a = pu.gpu_run(wl, fill=NAN_BF16)

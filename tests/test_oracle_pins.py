@@ -147,13 +147,13 @@ def _oracle_run(wl, fill=0):
     return res
 
 
-def _bf_run(wl):
+def _bf_run(wl, hole_bits=None):
     st = _as_bf_inputs(wl, wl.step)
     st["mask"] = _mask_sets(wl)
     st["channel"] = wl.channel
     pre = _as_bf_inputs(wl, wl.prefix) if wl.prefix is not None else None
     return bf.run(st, H_q=wl.H_q, H_kv=wl.H_kv, d=wl.d, theta=wl.theta, sm_scale=wl.sm_scale,
-                  cap=[int(c) for c in wl.capacity()], prefix=pre)
+                  cap=[int(c) for c in wl.capacity()], prefix=pre, hole_bits=hole_bits)
 
 
 def _compare_to_bruteforce(wl, res, ref):
@@ -203,6 +203,112 @@ def test_random_passes_match_bruteforce(seed, P, G, d):
     res = _oracle_run(wl)
     ref = _bf_run(wl)
     _compare_to_bruteforce(wl, res, ref)
+
+
+HOLE_BITS = 0x3FC0  # bf16 1.5: what a never-written slot holds in the explicit-slot pins
+
+
+@pytest.mark.parametrize("seed,P,G,d", [(0, 4, 2, 16), (1, 8, 1, 8), (2, 2, 4, 16), (3, 16, 2, 8), (4, 1, 8, 8)])
+def test_explicit_slots_match_bruteforce(seed, P, G, d):
+    """Rows that name their slots (State geometry): permuted and gapped slots,
+    prefix slots above the frozen count rewritten, kv_len below some rows'
+    slots, holes that keep the pool's fill, random positions; the paged oracle
+    equals the dense brute force, which has no page table."""
+    wl = W.make_explicit(seed, H_kv=2, G=G, d=d, P=P, num_lanes=5, max_rows=14, max_ctx=30)
+    res = _oracle_run(wl, fill=HOLE_BITS)
+    ref = _bf_run(wl, hole_bits=HOLE_BITS)
+    _compare_to_bruteforce(wl, res, ref)
+
+
+def test_explicit_generator_covers_the_geometry_cases():
+    """Over a few seeds, make_explicit writes out of order, writes past kv_len,
+    leaves holes below kv_len and rewrites prefix slots above the frozen count."""
+    out_of_order = past = hole = rewrite = False
+    for seed in range(5):
+        _explicit_cases(W.make_explicit(seed, num_lanes=7), flags := {})
+        out_of_order |= flags["out_of_order"]
+        past |= flags["past"]
+        hole |= flags["hole"]
+        rewrite |= flags["rewrite"]
+    assert out_of_order and past and hole and rewrite
+
+
+def _explicit_cases(wl, flags):
+    st, pre = wl.step, wl.prefix
+    c = np.zeros(wl.num_lanes, np.int32)
+    c, _ = oracle.fold(c, pre.indptr, pre.fold)
+    out_of_order = past = hole = rewrite = False
+    for lane in range(wl.num_lanes):
+        r0, r1 = int(st.indptr[lane]), int(st.indptr[lane + 1])
+        s_ = st.slots[r0:r1].astype(np.int64)
+        ps = pre.slots[int(pre.indptr[lane]):int(pre.indptr[lane + 1])].astype(np.int64)
+        k = int(c[lane])
+        out_of_order |= bool(np.any(np.diff(s_) != 1))
+        past |= bool(np.any(s_ >= int(st.kv_len[lane])))
+        written = set(s_.tolist()) | set(ps.tolist())
+        hole |= any(j not in written for j in range(int(st.kv_len[lane])))
+        rewrite |= bool(set(s_.tolist()) & set(ps[ps >= k].tolist()))
+    flags.update(out_of_order=out_of_order, past=past, hole=hole, rewrite=rewrite)
+
+
+def test_nonfinite_slot_below_kv_len_is_outside_the_domain():
+    """The step's precondition: slots below kv_len hold finite K/V. The oracle
+    refuses a pass that breaks it and accepts non-finite bytes at or past kv_len."""
+    wl = W.make_config(1)
+    pool = oracle.Pool(wl.num_pages, wl.P, wl.H_kv, wl.d, wl.page_indptr, wl.page_ids, fill_bits=0x7FC0)
+    st = wl.step
+    c = np.zeros(1, np.int32)
+    oracle.append(pool, c, st.indptr, st.positions, st.slots, st.k, st.v, wl.theta)
+    O, _, _ = oracle.attend(pool, st.indptr, st.positions, st.slots, st.kv_len, st.q, wl.H_q, wl.theta, wl.sm_scale)
+    assert np.isfinite(O).all()  # slots 37..47 hold NaN but lie past kv_len
+    pg, off = pool.locate(0, 20)
+    pool.v[pg, 1, off, 3] = 0x7FC0
+    with pytest.raises(ValueError):
+        oracle.attend(pool, st.indptr, st.positions, st.slots, st.kv_len, st.q, wl.H_q, wl.theta, wl.sm_scale)
+
+
+def _hz(page_indptr, page_ids, indptr, slots, kv_len, committed=None, num_pages=8, P=4):
+    pool = oracle.Pool(num_pages, P, 1, 2, page_indptr, page_ids)
+    L = len(indptr) - 1
+    return oracle.hazards(pool, np.zeros(L, np.int32) if committed is None else np.asarray(committed),
+                          np.asarray(indptr), np.asarray(slots), np.asarray(kv_len))
+
+
+def test_hazards_hand_worked():
+    """Eq. (4) (reviews, section 5): W(a) and R(b) ∪ W(b) disjoint for lanes a ≠ b,
+    on (page, offset) cells, and no cell written twice; pages of 4 slots."""
+    DUP, SH = oracle.ST_DUP_WRITE, oracle.ST_SHARED_CELL
+    # two lanes on disjoint pages, each writing and reading its own cells: no hazard
+    assert _hz([0, 2, 3], [5, 1, 7], [0, 2, 3], [6, 7, 2], [8, 3]) == 0
+    # one lane, two rows naming slot 3: a cell written twice
+    assert _hz([0, 1], [2], [0, 2], [3, 3], [4]) == DUP
+    # the same page listed twice in one lane: slots 1 and 5 are one cell
+    assert _hz([0, 2], [6, 6], [0, 2], [1, 5], [6]) == DUP
+    # lane 1 (no rows) shares page 3 read-only with lane 0 and reads slots 0..2; lane 0
+    # writes offset 3 of that page (its slot 7): lane 1 does not read offset 3, no hazard ...
+    assert _hz([0, 2, 3], [0, 3, 3], [0, 1, 1], [7], [8, 3]) == 0
+    # ... but with kv_len 4 it does
+    assert _hz([0, 2, 3], [0, 3, 3], [0, 1, 1], [7], [8, 4]) == SH
+    # lane 1 writes that shared cell itself (slot 3 of its page 3), lane 0 reads it too
+    assert _hz([0, 2, 3], [0, 3, 3], [0, 1, 2], [1, 3], [8, 4]) == SH
+    # both lanes write the same cell: written twice, and by two lanes
+    assert _hz([0, 1, 2], [4, 4], [0, 1, 2], [2, 2], [0, 0]) == DUP | SH
+    # a suppressed write (frozen, or past capacity) is no write
+    assert _hz([0, 1, 2], [4, 4], [0, 1, 2], [2, 2], [0, 0], committed=[3, 0]) == 0
+    assert _hz([0, 1, 2], [4, 4], [0, 1, 2], [2, 9], [0, 0]) == 0
+    # a lane reading cells it writes itself is the normal case
+    assert _hz([0, 2], [1, 0], [0, 3], [4, 5, 6], [8]) == 0
+    # every valid pass the generators build is hazard-free
+    for seed in range(3):
+        for wl in (W.make_explicit(seed), W.make_random(seed), W.make_config(3, seed=seed, scale="small")):
+            pool = oracle.Pool(wl.num_pages, wl.P, wl.H_kv, wl.d, wl.page_indptr, wl.page_ids)
+            c = np.zeros(wl.num_lanes, np.int32)
+            if wl.prefix is not None:
+                p = wl.prefix
+                assert oracle.hazards(pool, c, p.indptr, p.slots, p.kv_len) == 0
+                c, _ = oracle.fold(c, p.indptr, p.fold)
+            st = wl.step
+            assert oracle.hazards(pool, c, st.indptr, st.slots, st.kv_len) == 0
 
 
 # ----------------------------------------------------------------------------- invariants

@@ -15,6 +15,7 @@ from .gen import (  # noqa: F401
     bf16_bits_from_f32,
     Lora,
     make_config,
+    make_explicit,
     make_lora,
     make_random,
     make_run_ahead,

@@ -568,3 +568,91 @@ def make_lora(seed: int, indptr, *, d_in: int, d_out: int, rank: int, num_adapte
                            / np.float32(np.sqrt(rank)))
     scale = rngs["channel"].uniform(0.5, 2.0, size=num_adapters).astype(np.float32)
     return Lora(indptr=indptr, adapter=adapter, x=x, y=y, a=a, b=b, scale=scale)
+
+
+def make_explicit(seed: int, *, H_kv: int = 2, G: int = 2, d: int = 64, P: int = 16, num_lanes: int = 6,
+                  max_rows: int = 80, max_ctx: int = 300, masked: bool = True, extra_pages: int = 3,
+                  kinds=None, density: float = 0.7) -> Workload:
+    """A pass whose rows name their slots explicitly, the way algorithms that
+    manage KV slots directly use StateGeometry (Docs, State geometry), instead
+    of appending after the committed prefix.
+
+    Per lane: an untimed prefix pass writes a random subset (about `density`)
+    of the lane's slots in random order at random positions, and its fold
+    freezes the slots below a random k (a literal count). The step's rows
+    then write distinct slots drawn from [k, capacity) in random order: some
+    rewrite slots the prefix wrote above k, some are fresh, and gaps are left.
+    kv_len is the capacity, the largest written slot + 1, or a value between
+    the smallest and largest written slot + 1, so some rows write past what
+    the lane reads. Slots below kv_len that neither pass writes are holes:
+    they keep whatever the pool held (the caller's fill). Positions are random
+    and unrelated to slots. Lane kinds: 0 decode (1 row), 1 verify (2..8
+    rows), 2 prefill (9..max_rows rows); masks as in make_random; fold modes,
+    channel and an explicit readout list (random rows, repeats allowed) too.
+    """
+    rngs = _rngs(seed)
+    g = rngs["lengths"]
+    L = int(num_lanes)
+    spec = []
+    for i in range(L):
+        kind = int(kinds[i % len(kinds)]) if kinds is not None else int(g.integers(0, 3))
+        n = 1 if kind == 0 else (int(g.integers(2, 9)) if kind == 1 else int(g.integers(9, max_rows + 1)))
+        cap = -(-(n + int(g.integers(0, max_ctx + 1)) + int(g.integers(0, 2 * P))) // P) * P
+        pre = np.nonzero(g.random(cap) < density)[0].astype(np.int64)
+        pre = pre[g.permutation(len(pre))]
+        k = int(g.integers(0, min(len(pre), cap - n) + 1))
+        step = g.choice(np.arange(k, cap, dtype=np.int64), size=n, replace=False)
+        hi = int(step.max()) + 1
+        mode = int(g.integers(0, 3))
+        kvl = cap if mode == 0 else (hi if mode == 1 else int(g.integers(int(step.min()) + 1, hi + 1)))
+        fm = int(g.integers(0, 4))
+        fold = [FOLD_ALL, FOLD_CHANNEL, int(g.integers(0, n + 1)), 0][fm]
+        mask = None
+        if masked and g.random() < 0.5:
+            mk = ["window", "tova", "causal", "random"][int(g.integers(0, 4))]
+            mask = dict(kind=mk, window=int(g.integers(1, 70)), sinks=int(g.integers(0, 5)), drop=0.3, density=0.4)
+        spec.append(dict(n=n, cap=cap, pre=pre, k=k, step=step, kv_len=kvl, fold=fold, mask=mask, kind=kind))
+    order = rngs["perm"].permutation(L) if L > 1 else np.arange(L)
+    spec = [spec[i] for i in order]
+    pages = np.array([s["cap"] // P for s in spec], dtype=np.int64)
+    page_indptr = np.zeros(L + 1, dtype=np.int64)
+    page_indptr[1:] = np.cumsum(pages)
+    num_pages = int(page_indptr[-1]) + int(extra_pages)
+    page_ids = rngs["perm"].permutation(num_pages).astype(np.int32)[: int(page_indptr[-1])].copy()
+
+    def cat(arrs):
+        return np.concatenate(arrs).astype(np.int64) if arrs else np.zeros(0, np.int64)
+
+    pre_counts = np.array([len(s["pre"]) for s in spec], dtype=np.int64)
+    pre_indptr = np.concatenate([[0], np.cumsum(pre_counts)])
+    Np = int(pre_indptr[-1])
+    pre_pos = g.integers(0, 20000, size=Np)
+    prefix = None
+    if Np:
+        prefix = Pass(indptr=pre_indptr.astype(np.int32), positions=pre_pos.astype(np.int32),
+                      slots=cat([s["pre"] for s in spec]).astype(np.int32),
+                      kv_len=np.array([s["cap"] for s in spec], dtype=np.int32),
+                      fold=np.array([s["k"] for s in spec], dtype=np.int32),
+                      k=_normal_bf16(rngs["prefix_kv"], (Np, H_kv, d)),
+                      v=_normal_bf16(rngs["prefix_kv"], (Np, H_kv, d)))
+    counts = np.array([s["n"] for s in spec], dtype=np.int64)
+    indptr = np.concatenate([[0], np.cumsum(counts)])
+    N = int(indptr[-1])
+    H_q = H_kv * G
+    step = Pass(indptr=indptr.astype(np.int32), positions=g.integers(0, 20000, size=N).astype(np.int32),
+                slots=cat([s["step"] for s in spec]).astype(np.int32),
+                kv_len=np.array([s["kv_len"] for s in spec], dtype=np.int32),
+                fold=np.array([s["fold"] for s in spec], dtype=np.int32),
+                k=_normal_bf16(rngs["k"], (N, H_kv, d)), v=_normal_bf16(rngs["v"], (N, H_kv, d)),
+                q=_normal_bf16(rngs["q"], (N, H_q, d)))
+    wl = Workload(name=f"explicit_{seed}", H_q=H_q, H_kv=H_kv, d=d, P=P, theta=10000.0,
+                  sm_scale=float(1.0 / np.sqrt(d)), num_pages=num_pages,
+                  page_indptr=page_indptr.astype(np.int32), page_ids=page_ids, prefix=prefix, step=step,
+                  meta={"lanes": [{k_: v_ for k_, v_ in s.items() if k_ not in ("pre", "step")} for s in spec]})
+    if masked:
+        lanes_m = [dict(n=s["n"], kv_len=s["kv_len"], mask=s["mask"]) for s in spec]
+        wl.mask_bits, wl.mask_word_offset = _bitmap_rows(lanes_m, step, rngs["mask"])
+    wl.channel = np.array([int(rngs["channel"].integers(-2, 12)) for _ in range(L)], dtype=np.int32)
+    if N:
+        wl.readout_rows = rngs["channel"].integers(0, N, size=int(rngs["channel"].integers(1, 2 * L + 1))).astype(np.int32)
+    return wl
