@@ -165,14 +165,35 @@ class HipEvents:
 
 # --------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(wl, cfg: int, unit: str, budget_s: float = 20.0):
-    """Time the fp64 oracle on a bounded sample of the same step, one host thread."""
+_CPU_JOB = {}  # what the forked oracle workers read (inherited copy-on-write)
+
+
+def _cpu_attend(rows):
+    import oracle
+
+    j = _CPU_JOB
+    st, wl = j["st"], j["wl"]
+    oracle.attend(j["pool"], st.indptr, st.positions, st.slots, st.kv_len, st.q, wl.H_q, wl.theta, wl.sm_scale,
+                  wl.mask_bits, wl.mask_word_offset, rows=rows)
+    return len(rows)
+
+
+def cpu_baseline(wl, cfg: int, unit: str):
+    """Time the fp64 oracle on a bounded sample of the same step on the host's
+    cores: the append of the sampled lanes, then their attention split by lane
+    over a pool of worker processes (one per core of this process's CPU set,
+    at most 16, the CPU share of one GPU; BLAS limited to one thread each),
+    then fold and readout. Must run before anything in the process touches the
+    GPU: the workers are forked from it."""
+    import multiprocessing as mp
+
     import oracle
 
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
     st = wl.step
     n = np.diff(st.indptr).astype(np.int64)
     order = [l for l in range(wl.num_lanes) if n[l] > 0]
@@ -182,7 +203,7 @@ def cpu_baseline(wl, cfg: int, unit: str, budget_s: float = 20.0):
         lanes, rows = order, None
     else:
         rng = np.random.default_rng(7)
-        lanes = sorted(rng.choice(order, size=min(4, len(order)), replace=False).tolist())
+        lanes = sorted(rng.choice(order, size=min(2 * cores, len(order)), replace=False).tolist())
         rows = []
         for l in lanes:
             r0, r1 = int(st.indptr[l]), int(st.indptr[l + 1])
@@ -198,18 +219,23 @@ def cpu_baseline(wl, cfg: int, unit: str, budget_s: float = 20.0):
             p = wl.prefix
             oracle.append(pool, c, p.indptr, p.positions, p.slots, p.k, p.v, wl.theta, lanes=lanes)
             c, _ = oracle.fold(c, p.indptr, p.fold)
-        t0 = time.perf_counter()
-        oracle.append(pool, c, st.indptr, st.positions, st.slots, st.k, st.v, wl.theta, lanes=lanes)
         sample_rows = rows if rows is not None else np.concatenate(
             [np.arange(st.indptr[l], st.indptr[l + 1]) for l in lanes]).astype(np.int64)
-        O, LSE, _ = oracle.attend(pool, st.indptr, st.positions, st.slots, st.kv_len, st.q, wl.H_q, wl.theta,
-                                  wl.sm_scale, wl.mask_bits, wl.mask_word_offset, rows=sample_rows)
+        lane_of = np.searchsorted(st.indptr, sample_rows, side="right") - 1
+        groups = [sample_rows[lane_of == l] for l in lanes]
+        groups = sorted([g for g in groups if len(g)], key=len, reverse=True)
+        t0 = time.perf_counter()
+        oracle.append(pool, c, st.indptr, st.positions, st.slots, st.k, st.v, wl.theta, lanes=lanes)
+        _CPU_JOB.update(pool=pool, st=st, wl=wl)
+        with mp.get_context("fork").Pool(cores) as workers:
+            workers.map(_cpu_attend, groups, chunksize=1)
         oracle.fold(c, st.indptr, st.fold, wl.channel)
         if rows is None:
             rl = oracle.readout_rows(st.indptr, wl.readout_rows)
             oracle.readout(np.zeros((st.num_rows, 1)), st.num_rows, rl)
         dt = time.perf_counter() - t0
     finally:
+        _CPU_JOB.clear()
         if ctx:
             ctx.__exit__(None, None, None)
     eff = np.minimum(np.maximum(st.kv_len.astype(np.int64), 0), wl.capacity())
@@ -222,8 +248,9 @@ def cpu_baseline(wl, cfg: int, unit: str, budget_s: float = 20.0):
         work_units = 4.0 * wl.d * wl.H_q * float(pairs.sum())
         val = work_units / dt / 1e12
         what = f"{len(sample_rows)} sampled rows of {len(lanes)} lanes, {work_units:.3e} algorithmic flop"
-    return {"value": val, "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": f"{what}; append+attend+fold+readout in {dt:.2f} s (fp64 numpy, one thread)"}
+    return {"value": val, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{what}; append+attend+fold+readout in {dt:.2f} s, worker start included (fp64 numpy "
+                      f"oracle, attention split by lane over {cores} forked processes, BLAS 1 thread each)"}
 
 
 # --------------------------------------------------------------------------- measured traffic
@@ -282,18 +309,32 @@ def pmc_summary(fetch_db: str, write_db: str, cfg: int, calib_bytes: int, out: s
     return rec
 
 
-def trace_summary(db: str, command: str) -> str:
-    """Markdown table of per-kernel durations from a rocprofv3 --kernel-trace results db."""
+def trace_summary(db: str, command: str, last: int = 0) -> str:
+    """Markdown table of per-kernel durations from a rocprofv3 --kernel-trace
+    results db: all launches, and (last > 0) the last `last` launches of each
+    kernel by start time, which are the flushed timed steps of bench.py's
+    final phase when last = --steps."""
     import sqlite3
 
     c = sqlite3.connect(db)
-    q = ("select name, count(*), avg(duration)/1000.0, min(duration)/1000.0, max(duration)/1000.0, "
-         "sum(duration)/1000.0 from kernels group by name order by sum(duration) desc")
-    lines = [f"Command: `{command}`", "",
-             "| kernel | calls | avg us | min us | max us | total us |", "|---|---|---|---|---|---|"]
-    for name, n, avg, mn, mx, tot in c.execute(q):
-        name = name.replace("|", "/")
-        lines.append(f"| `{name[:90]}` | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {tot:.1f} |")
+    rows = c.execute("select name, start, duration, vgpr_count, lds_size from kernels order by start").fetchall()
+    by = {}
+    for name, start, dur, vgpr, lds in rows:
+        by.setdefault(name, []).append((dur / 1000.0, vgpr, lds))
+    head = "| kernel | calls | avg us | min us | max us | total us | VGPRs | LDS B |"
+    sep = "|---|---|---|---|---|---|---|---|"
+    if last:
+        head += f" avg us, last {last} |"
+        sep += "---|"
+    lines = [f"Command: `{command}`", "", head, sep]
+    for name, v in sorted(by.items(), key=lambda kv: -sum(x[0] for x in kv[1])):
+        d = np.array([x[0] for x in v])
+        cell = name.replace("|", "/")[:90]
+        line = (f"| `{cell}` | {len(d)} | {d.mean():.2f} | {d.min():.2f} | {d.max():.2f} | {d.sum():.1f} | "
+                f"{v[0][1]} | {v[0][2]} |")
+        if last:
+            line += f" {d[-last:].mean():.2f} |"
+        lines.append(line)
     return "\n".join(lines) + "\n"
 
 
@@ -321,7 +362,10 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--split", type=int, default=None, help="decode KV slots per work item")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true", help="config 2 only: skip the config 5 prefill measurement")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="config 2 only: skip configs 5, 3 and 4 and the other seeds")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured read-stream and MFMA peaks")
+    ap.add_argument("--no-flush", action="store_true", help="no 1 GiB read between timed steps")
     ap.add_argument("--frame", action="store_true",
                     help="time a two-pass frame (config 3 split per lane) eagerly and as one HIP-graph replay")
     ap.add_argument("--lora", action="store_true",
@@ -335,10 +379,12 @@ def main(argv=None):
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write the measured-traffic record for --config from two rocprofv3 --pmc result dbs")
     ap.add_argument("--trace-summary", nargs=2, metavar=("DB", "COMMAND"),
-                    help="print a markdown per-kernel summary of a rocprofv3 --kernel-trace results db")
+                    help="print a markdown per-kernel summary of a rocprofv3 --kernel-trace results db "
+                         "(with --trace-last N: also the mean of each kernel's last N launches)")
+    ap.add_argument("--trace-last", type=int, default=0)
     args = ap.parse_args(argv)
     if args.trace_summary:
-        print(trace_summary(*args.trace_summary), end="")
+        print(trace_summary(*args.trace_summary, last=args.trace_last), end="")
         return 0
     if args.pmc_summary:
         rec = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, (args.calib_copy or 1024) << 20,
@@ -349,9 +395,19 @@ def main(argv=None):
         print("bench.py measures one GPU: this library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         return 2
 
+    import workloads as W
+
+    cpu = None
+    pre_wl = None
+    if not (args.no_cpu_baseline or args.run_ahead or args.lora or args.frame):
+        # the oracle's workers are forked, so this runs before anything touches the GPU
+        pre_wl = W.make_config(args.config, seed=args.seed, scale="full")
+        unit0 = "TFLOP/s" if args.config == 5 else "GB/s"
+        cpu = cpu_baseline(pre_wl, args.config, unit0)
+        print(json.dumps({"cpu_baseline": cpu}), file=sys.stderr, flush=True)
+
     import torch
 
-    import workloads as W
     from ragged_paged_kv_fp_amd import _lib, runner
 
     _lib.load()
@@ -377,19 +433,23 @@ def main(argv=None):
         print(json.dumps(frame_bench(W, runner, args.seed, args.steps, args.warmup)), flush=True)
         return 0
     cfg = args.config
-    mass = {}
-    wl, w, ms_step, attn_avg, host_ms = measure(W, runner, cfg, args.seed, args.split, args.steps, args.warmup, mass)
     K, Wm = args.steps, args.warmup
+    peaks = None if args.no_peaks else measure_peaks()
+    pk_hbm = peaks["hbm_read_GB/s"] if peaks else None
+    pk_mfma = peaks["mfma_bf16_TFLOP/s"] if peaks else None
+    mass = {}
+    wl, w, r = measure(W, runner, cfg, args.seed, args.split, K, Wm, mass, flush=not args.no_flush, wl=pre_wl)
+    pre_wl = None
+    step_ms = float(np.mean(r["step_ms"]))
     if cfg == 5:
         unit, work_units, scale = "TFLOP/s", w["flops"], 1e12
-        bound, peak, r_unit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
+        bound, peak, r_unit, win, kname = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s", "prefill_ms", "prefill_kernel"
     else:
         unit, work_units, scale = "GB/s", w["kv_bytes_all"] if cfg == 1 else w["kv_bytes_decode"], 1e9
         bound, peak, r_unit = "hbm", HBM_PEAK_GBS, "GB/s"
-        if cfg == 3:
-            work_units = w["kv_bytes_decode"]
-    value = work_units / (ms_step * 1e-3) / scale
-    achieved = work_units / (attn_avg * 1e-3) / scale
+        win, kname = ("attn_ms", "prefill_kernel") if cfg == 1 else ("decode_ms", "decode_kernel")
+    value = work_units / (step_ms * 1e-3) / scale
+    achieved = rate(work_units, r[win], scale)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -397,7 +457,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -405,37 +465,76 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": f"config {cfg}: " + WORKLOAD_TEXT[cfg], "seed": args.seed,
                    "lanes": wl.num_lanes, "rows": wl.step.num_rows, "kv_bytes_decode": w["kv_bytes_decode"],
-                   "attn_flops": w["flops"], "attended_pairs": w["pairs"], "host_wall_ms_per_step":
-                   round(host_ms, 4)},
+                   "attn_flops": w["flops"], "attended_pairs": w["pairs"]},
+        "timing": {"protocol": ("per step: untimed 1 GiB read of other data (evicts L2 and MALL), then events around "
+                                "reset->append->attend->fold->readout; value and ms_per_step are the mean of the K "
+                                "flushed steps" if not args.no_flush else "no flush between steps"),
+                   "step_ms": _stats(r["step_ms"]),
+                   "unflushed_ms_per_step": round(r["unflushed_ms_per_step"], 4),
+                   "unflushed_value": round(work_units / (r["unflushed_ms_per_step"] * 1e-3) / scale, 3),
+                   "host_wall_ms_per_step_unflushed": round(r["host_ms_per_step"], 4)},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": r_unit,
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(cfg),
-                     "kernel": "attention kernels (decode_kernel / prefill_kernel), HIP events per step",
-                     "kernel_avg_ms": round(attn_avg, 5)},
+                     "kernel": f"{kname}: HIP events recorded by fp_attend around it, per flushed step",
+                     "kernel_avg_ms": round(float(np.mean(r[win])), 5), "kernel_ms": _stats(r[win])},
     }
+    if peaks:
+        line["peaks_measured"] = peaks
+        line["roofline"]["measured_peak"] = pk_mfma if bound == "mfma" else pk_hbm
+        line["roofline"]["frac_of_measured_peak"] = round(achieved / line["roofline"]["measured_peak"], 4)
+    if bound == "hbm" and cfg != 1:
+        line["roofline"]["windows"] = decode_windows(w, r, pk_hbm)
+    if cfg in (3, 5):
+        line["roofline"]["prefill"] = prefill_window(w, r, pk_mfma)
     line["attn_mass"] = {"kernel": "mass_kernel (fp_attn_mass after the step's attention), torch events",
                          "this_config": mass_line(wl, w, mass["ms"], cfg)}
-    if cfg == 3:
-        line["config"]["prefill_tflops_step"] = round(w["flops_prefill"] / (ms_step * 1e-3) / 1e12, 3)
-    if cfg == 5:
-        line["roofline"]["executed_frac"] = round(w["flops_prefill_executed"] / (attn_avg * 1e-3) / 1e12 / peak, 4)
-    if cfg == 2 and not args.no_prefill:
-        # the prefill half of the metric, on the long-context masked prefill wave
-        mass5 = {}
-        wl5, w5, ms5, attn5, _ = measure(W, runner, 5, args.seed, None, 5, 1, mass5)
-        alg = w5["flops"] / (attn5 * 1e-3) / 1e12
-        exe = w5["flops_prefill_executed"] / (attn5 * 1e-3) / 1e12
-        line["prefill"] = {"workload": "config 5: " + WORKLOAD_TEXT[5], "bound": "mfma", "unit": "TFLOP/s",
-                           "peak": BF16_PEAK_TFLOPS, "attn_ms": round(attn5, 4), "ms_per_step": round(ms5, 4),
-                           "achieved": round(alg, 2), "frac": round(alg / BF16_PEAK_TFLOPS, 4),
-                           "achieved_executed": round(exe, 2), "frac_executed": round(exe / BF16_PEAK_TFLOPS, 4),
-                           "algorithmic_flops": w5["flops"], "executed_flops": w5["flops_prefill_executed"],
-                           "traffic": measured_traffic(5), "steps": 5, "warmup": 1}
-        line["attn_mass"]["prefill"] = mass_line(wl5, w5, mass5["ms"], 5)
-        del wl5
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, cfg, unit)
+    if cfg == 2 and not args.no_extra:
+        line.update(extra_configs(W, runner, args.seed, pk_hbm, pk_mfma))
+        line["seeds"] = {str(args.seed): round(value, 3)}
+        for sd in (1, 2):
+            if sd == args.seed:
+                continue
+            wls, ws_, rs = measure(W, runner, cfg, sd, args.split, 10, 2, None, flush=not args.no_flush)
+            line["seeds"][str(sd)] = round(ws_["kv_bytes_decode"] / (float(np.mean(rs["step_ms"])) * 1e-3) / 1e9, 3)
+            del wls
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
     return 0
+
+
+def extra_configs(W, runner, seed, pk_hbm, pk_mfma) -> dict:
+    """The other measured configurations of the default run: the prefill half of
+    the metric on config 5 (long-context masked prefill), config 3 (mixed wave:
+    its prefill lanes in TFLOP/s and its decode lanes in GB/s, each on its own
+    kernel window) and config 4 (guidance + speculative verify, HBM-bound).
+    Each runs 1 warm-up and 5 flushed steps."""
+    out = {}
+    mass5 = {}
+    wl5, w5, r5 = measure(W, runner, 5, seed, None, 5, 1, mass5)
+    out["prefill"] = {"workload": "config 5: " + WORKLOAD_TEXT[5], "bound": "mfma", "unit": "TFLOP/s",
+                      "peak": BF16_PEAK_TFLOPS, "ms_per_step": round(float(np.mean(r5["step_ms"])), 4),
+                      **prefill_window(w5, r5, pk_mfma), "traffic": measured_traffic(5), "steps": 5, "warmup": 1,
+                      "attn_mass": mass_line(wl5, w5, mass5["ms"], 5)}
+    del wl5
+    wl3, w3, r3 = measure(W, runner, 3, seed, None, 5, 1)
+    t_pre = w3["flops_prefill"] / (BF16_PEAK_TFLOPS * 1e12) * 1e3
+    t_dec = w3["kv_bytes_decode"] / (HBM_PEAK_GBS * 1e9) * 1e3
+    t3 = float(np.mean(r3["step_ms"]))
+    out["config3"] = {"workload": "config 3: " + WORKLOAD_TEXT[3], "steps": 5, "warmup": 1,
+                      "prefill": prefill_window(w3, r3, pk_mfma), "decode": decode_windows(w3, r3, pk_hbm),
+                      "step_ms": _stats(r3["step_ms"]),
+                      "t_bound_ms": {"prefill_at_peak": round(t_pre, 4), "decode_at_peak": round(t_dec, 4)},
+                      "t_bound_over_t_measured": round(max(t_pre, t_dec) / t3, 4),
+                      "t_bound_serial_over_t_measured": round((t_pre + t_dec) / t3, 4),
+                      "traffic": measured_traffic(3)}
+    del wl3
+    wl4, w4, r4 = measure(W, runner, 4, seed, None, 5, 1)
+    out["config4"] = {"workload": "config 4: " + WORKLOAD_TEXT[4], "steps": 5, "warmup": 1,
+                      "decode": decode_windows(w4, r4, pk_hbm), "step_ms": _stats(r4["step_ms"]),
+                      "unflushed_step_ms": round(r4["unflushed_ms_per_step"], 4), "traffic": measured_traffic(4)}
+    del wl4
+    return out
 
 
 def run_ahead_bench(W, runner, seed, K, Wm) -> dict:
@@ -600,43 +699,119 @@ def mass_line(wl, w, ms, cfg) -> dict:
             "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": k_bytes}
 
 
-def measure(W, runner, cfg, seed, split, K, Wm, mass=None):
-    """Time K steps (after Wm warm-ups) of one configuration with inputs resident
-    in HBM: returns (workload, work, ms per step, attention-kernel ms per step
-    from HIP events on the launch stream, host wall ms per step). With a dict
-    as `mass`, also times K calls of fp_attn_mass over the last step's
-    attention (torch events on the stream it runs on) into mass["ms"]."""
+FLUSH_BYTES = 1 << 30  # read before every flushed step: L2 (8 x 4 MB) and the 256 MB MALL then hold none of its inputs
+
+
+class Flusher:
+    """Evicts the caches between timed steps by reading FLUSH_BYTES of other
+    data with the read-stream kernel of libfp_peaks.so (a read leaves no dirty
+    lines whose write-back could overlap the next step)."""
+
+    def __init__(self):
+        import ctypes
+
+        import torch
+
+        from ragged_paged_kv_fp_amd import build
+
+        if not os.path.exists(build.PEAKS_LIB):
+            raise ImportError(f"{build.PEAKS_LIB} is missing: build it with __graft_entry__.build()")
+        self.lib = ctypes.CDLL(build.PEAKS_LIB)
+        self.lib.fp_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+        self.blocks = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+
+    def __call__(self, stream):
+        rc = self.lib.fp_peak_read(self.buf.data_ptr(), FLUSH_BYTES, self.blocks, self.sink.data_ptr(),
+                                   stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"flush read failed: {rc}")
+
+
+def _stats(xs) -> dict:
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "min": round(float(a.min()), 5), "max": round(float(a.max()), 5)}
+
+
+def measure(W, runner, cfg, seed, split, K, Wm, mass=None, flush=True, wl=None):
+    """Time one configuration with inputs resident in HBM.
+
+    Phase 1 (unflushed): Wm warm-up steps, then K steps back to back between
+    two events; gives the back-to-back rate.
+    Phase 2 (flushed, the reported figures): Wm warm-up steps, then K steps,
+    each after an untimed 1 GiB read of other data that evicts L2 and the MALL. Per step,
+    events on the launch stream bracket the whole step (reset of
+    committed_len -> append -> attend -> fold -> readout) and the fp_attend
+    call, and HIP events the library records inside fp_attend split it into
+    the prefill kernel, the decode kernel and the split merge.
+    Both phases are bracketed by torch.cuda.synchronize(). Returns
+    (workload, work, dict of per-step millisecond lists and phase-1 totals)."""
     import torch
 
-    wl = W.make_config(cfg, seed=seed, scale="full")
+    print(f"[bench] config {cfg} seed {seed}: {K} steps after {Wm} warm-ups", file=sys.stderr, flush=True)
+    if wl is None:
+        wl = W.make_config(cfg, seed=seed, scale="full")
     w = work(wl)
     ds = runner.DeviceStep(wl, device="cuda", split=split)
     ds.run_prefix()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = HipEvents()
-    pairs_ev = [(ev.create(), ev.create()) for _ in range(K)]
+    hip_ev = [tuple(ev.create() for _ in range(4)) for _ in range(K)]  # begin, end, prefill_end, merge_end
+    tev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    # ---- phase 1: back to back
     for _ in range(Wm):
         ds.reset()
         ds.step()
     torch.cuda.synchronize()
-    ds.status.zero_()
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    b0, b1 = tev(), tev()
     h0 = time.perf_counter()
-    t_begin.record(stream)
-    for i in range(K):
+    b0.record(stream)
+    for _ in range(K):
         ds.reset()
-        ds.step(events=pairs_ev[i])
-    t_end.record(stream)
+        ds.step()
+    b1.record(stream)
     torch.cuda.synchronize()
     h1 = time.perf_counter()
-    total_ms = t_begin.elapsed_time(t_end)
-    attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs_ev]
+    res = {"unflushed_ms_per_step": b0.elapsed_time(b1) / K, "host_ms_per_step": (h1 - h0) * 1e3 / K}
+    # ---- phase 2: flushed steps with per-step windows
+    flusher = Flusher() if flush else None
+    step_ev = [(tev(), tev(), tev(), tev()) for _ in range(K)]  # step begin, call begin, call end, step end
+    for i in range(Wm):
+        if flusher is not None:
+            flusher(stream)
+        ds.reset()
+        ds.step()
+    torch.cuda.synchronize()
+    ds.status.zero_()
+    torch.cuda.synchronize()
+    for i in range(K):
+        if flusher is not None:
+            flusher(stream)
+        sb, cb, ce, se = step_ev[i]
+        sb.record(stream)
+        ds.reset()
+        ds.append()
+        cb.record(stream)
+        ds.attend(events=hip_ev[i])
+        ce.record(stream)
+        ds.fold()
+        ds.readout()
+        se.record(stream)
+    torch.cuda.synchronize()
+    res["step_ms"] = [sb.elapsed_time(se) for sb, _, _, se in step_ev]
+    res["call_ms"] = [cb.elapsed_time(ce) for _, cb, ce, _ in step_ev]
+    res["attn_ms"] = [ev.elapsed_ms(b, e) for b, e, _, _ in hip_ev]
+    res["prefill_ms"] = [ev.elapsed_ms(b, p) for b, _, p, _ in hip_ev]
+    res["decode_ms"] = [ev.elapsed_ms(p, e) for _, e, p, _ in hip_ev]
+    res["a4_ms"] = [ev.elapsed_ms(p, m) for _, _, p, m in hip_ev]  # decode kernel + split merge
     status = int(ds.status.cpu()[0])
     if status != 0:
         print(f"warning: device status {status} (config {cfg})", file=sys.stderr)
+    del flusher
     if mass is not None:
         from ragged_paged_kv_fp_amd import api
 
@@ -645,8 +820,7 @@ def measure(W, runner, cfg, seed, split, K, Wm, mass=None):
         for _ in range(Wm):
             call()
         torch.cuda.synchronize()
-        m0 = torch.cuda.Event(enable_timing=True)
-        m1 = torch.cuda.Event(enable_timing=True)
+        m0, m1 = tev(), tev()
         m0.record(stream)
         for _ in range(K):
             call()
@@ -654,12 +828,98 @@ def measure(W, runner, cfg, seed, split, K, Wm, mass=None):
         torch.cuda.synchronize()
         mass["ms"] = m0.elapsed_time(m1) / K
         del buf
-    for a, b in pairs_ev:
-        ev.destroy(a)
-        ev.destroy(b)
+    for evs in hip_ev:
+        for e in evs:
+            ev.destroy(e)
     del ds
     torch.cuda.empty_cache()
-    return wl, w, total_ms / K, float(np.mean(attn_ms)), (h1 - h0) * 1e3 / K
+    return wl, w, res
+
+
+def rate(units: float, ms_list, scale: float) -> float:
+    return units / (float(np.mean(ms_list)) * 1e-3) / scale
+
+
+def decode_windows(w, r, peak_meas=None) -> dict:
+    """HBM-bound decode figures of one measurement: algorithmic KV bytes of the
+    decode-class lanes over the decode kernel alone, decode + split merge
+    (survey row a4), the whole fp_attend call (plan, Q rotation, tile lists,
+    attention, merge) and the whole step."""
+    b = w["kv_bytes_decode"]
+    out = {}
+    for name, key in (("decode_kernel", "decode_ms"), ("decode_plus_merge", "a4_ms"), ("fp_attend", "call_ms"),
+                      ("step", "step_ms")):
+        gbs = rate(b, r[key], 1e9)
+        out[name] = {"ms": _stats(r[key]), "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if peak_meas:
+            out[name]["frac_of_measured_peak"] = round(gbs / peak_meas, 4)
+    return out
+
+
+def prefill_window(w, r, peak_meas=None) -> dict:
+    """MFMA-bound prefill figures: algorithmic flops (allowed pairs only) and
+    executed flops (every 32-slot tile a work item visits) over the prefill kernel."""
+    alg = rate(w["flops_prefill"], r["prefill_ms"], 1e12)
+    exe = rate(w["flops_prefill_executed"], r["prefill_ms"], 1e12)
+    out = {"ms": _stats(r["prefill_ms"]), "TFLOP/s": round(alg, 2), "frac": round(alg / BF16_PEAK_TFLOPS, 4),
+           "TFLOP/s_executed": round(exe, 2), "frac_executed": round(exe / BF16_PEAK_TFLOPS, 4),
+           "algorithmic_flops": w["flops_prefill"], "executed_flops": w["flops_prefill_executed"]}
+    if peak_meas:
+        out["frac_of_measured_peak"] = round(alg / peak_meas, 4)
+    return out
+
+
+# --------------------------------------------------------------------------- measured peaks
+
+def measure_peaks(reps: int = 10) -> dict:
+    """The device's own peaks from libfp_peaks.so: a read-only stream of 4 GiB
+    (16-byte non-temporal loads, contiguous chunks per workgroup) and a loop of
+    independent v_mfma_f32_32x32x16_bf16 chains on every SIMD, each timed with
+    events on the launch stream; best of `reps` launches."""
+    import ctypes
+
+    import torch
+
+    from ragged_paged_kv_fp_amd import build
+
+    if not os.path.exists(build.PEAKS_LIB):
+        raise ImportError(f"{build.PEAKS_LIB} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(build.PEAKS_LIB)
+    lib.fp_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fp_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fp_peak_mfma_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.fp_peak_mfma_flop.restype = ctypes.c_double
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def timed(fn):
+        best = float("inf")
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = fn()
+            e1.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"peak kernel launch failed: {rc}")
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    read_ms = timed(lambda: lib.fp_peak_read(buf.data_ptr(), nbytes, 8 * cus, sink.data_ptr(), stream.cuda_stream))
+    del buf
+    iters, blocks = 4096, 2 * cus  # eight waves per CU, two per SIMD
+    mfma_ms = timed(lambda: lib.fp_peak_mfma(iters, blocks, sink.data_ptr(), stream.cuda_stream))
+    gbs = nbytes / (read_ms * 1e-3) / 1e9
+    tf = lib.fp_peak_mfma_flop(iters, blocks) / (mfma_ms * 1e-3) / 1e12
+    torch.cuda.empty_cache()
+    return {"hbm_read_GB/s": round(gbs, 1), "hbm_frac_of_vendor": round(gbs / HBM_PEAK_GBS, 4),
+            "mfma_bf16_TFLOP/s": round(tf, 1), "mfma_frac_of_vendor": round(tf / BF16_PEAK_TFLOPS, 4),
+            "read_ms": round(read_ms, 4), "mfma_ms": round(mfma_ms, 4), "reps": reps,
+            "how": "libfp_peaks.so: 4 GiB read stream (16-byte non-temporal loads, contiguous chunks), "
+                   "4 chains of v_mfma_f32_32x32x16_bf16 per wave on 2 waves/SIMD; best of reps"}
 
 
 if __name__ == "__main__":

@@ -134,9 +134,13 @@ typedef struct fp_tuning {
                                          decode workgroup of the device about two items      */
     int32_t reserved[7];              /* must be zero                                          */
     hipEvent_t attn_begin;            /* nullable: recorded on the stream right before the
-                                         attention kernels (prefill and decode)              */
+                                         attention kernels (prefill, then decode)             */
     hipEvent_t attn_end;              /* nullable: recorded right after them (before the merge of
                                          decode splits)                                       */
+    hipEvent_t prefill_end;           /* nullable: recorded between the prefill and the decode
+                                         kernels (right after attn_begin if no prefill lane)  */
+    hipEvent_t merge_end;             /* nullable: recorded after the merge of decode splits
+                                         (right after attn_end if nothing is merged)          */
 } fp_tuning;
 
 /*

@@ -65,7 +65,8 @@ class FpLora(ctypes.Structure):
 
 
 class FpTuning(ctypes.Structure):
-    _fields_ = [("decode_split_slots", c_i32), ("reserved", c_i32 * 7), ("attn_begin", c_ptr), ("attn_end", c_ptr)]
+    _fields_ = [("decode_split_slots", c_i32), ("reserved", c_i32 * 7), ("attn_begin", c_ptr), ("attn_end", c_ptr),
+                ("prefill_end", c_ptr), ("merge_end", c_ptr)]
 
 
 class FpError(RuntimeError):

@@ -110,6 +110,8 @@ def _tuning(split: Optional[int], events=None):
     t.decode_split_slots = int(split or 0)
     if events is not None:
         t.attn_begin, t.attn_end = int(events[0]), int(events[1])
+        if len(events) > 2:  # (begin, end, prefill_end, merge_end)
+            t.prefill_end, t.merge_end = int(events[2]), int(events[3])
     return ctypes.byref(t)
 
 
@@ -144,7 +146,8 @@ def attend(pool: Pool, geom: Geometry, q: torch.Tensor, num_q_heads: int, rope_t
            mask: Optional[Mask] = None, split: Optional[int] = None, stream=None, events=None) -> None:
     """fp_attend: attention of every row over its lane's kv_len slots (causal or bitmap).
 
-    events: optional (begin, end) raw hipEvent_t handles recorded around the attention kernels.
+    events: optional raw hipEvent_t handles (begin, end) recorded around the attention kernels, or
+    (begin, end, prefill_end, merge_end) to also split prefill from decode and time the split merge.
     """
     lib = _lib.load()
     ps, gs = pool.struct(), geom.struct()

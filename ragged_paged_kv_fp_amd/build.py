@@ -11,6 +11,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfp.so")
 SOURCES = [os.path.join(HERE, "csrc", "fp_lib.hip")]
+# measurement microbenchmarks (read stream, MFMA loop), a library of their own
+PEAKS_LIB = os.path.join(HERE, "libfp_peaks.so")
+PEAKS_SOURCES = [os.path.join(HERE, "csrc", "fp_peaks.hip")]
 DEPS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("fp_kernels.h", "fp_device.h", "fp_decode.h", "fp_prefill.h",
                                                                 "fp_stats.h", "fp_lora.h")] + [
     os.path.join(ROOT, "include", "fp.h")]
@@ -58,6 +61,15 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libfp.so")
     os.replace(tmp, LIB)
+    ptmp = PEAKS_LIB + ".tmp"
+    pcmd = [hipcc()] + HIPCC_FLAGS + PEAKS_SOURCES + ["-o", ptmp]
+    if verbose:
+        print(" ".join(pcmd), flush=True)
+    res = subprocess.run(pcmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libfp_peaks.so")
+    os.replace(ptmp, PEAKS_LIB)
     return LIB
 
 

@@ -315,6 +315,7 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
         else launch_prefill_g<64>(a, p.G, p.n_pre, stream);
         if ((rc = launch_ok())) return rc;
     }
+    if (tuning && tuning->prefill_end && hipEventRecord(tuning->prefill_end, stream) != hipSuccess) return FP_ERR_HIP;
     if (p.n_dec) {
         const dim3 grid((unsigned)p.n_dec), block(kDecThreads);
         if (p.D == 128) {
@@ -333,6 +334,7 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
         else hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, a);
         if ((rc = launch_ok())) return rc;
     }
+    if (tuning && tuning->merge_end && hipEventRecord(tuning->merge_end, stream) != hipSuccess) return FP_ERR_HIP;
     return FP_OK;
 }
 
