@@ -29,17 +29,32 @@ __device__ __forceinline__ uint4 load_nt(const void *p) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Nearest-even bf16 of a double in one rounding: truncate to float (toward
-// zero), set the last float bit if anything was dropped (round-to-odd), then
-// round that float to bf16 nearest-even. Float keeps enough extra bits for
-// the two steps to equal one correct rounding.
-__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+// Nearest-even bf16 of a double in one rounding, the general path: truncate
+// to float (toward zero), set the last float bit if anything was dropped
+// (round-to-odd), then round that float to bf16 nearest-even. Float keeps
+// enough extra bits for the two steps to equal one correct rounding.
+__device__ __forceinline__ uint32_t f64_to_bf16_slow(double x) {
     float f = __double2float_rz(x);
     uint32_t u = __float_as_uint(f);
     if ((double)f != x) u |= 1u;
     if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u;  // NaN
     u += 0x7FFFu + ((u >> 16) & 1u);
     return u >> 16;
+}
+
+// Nearest-even bf16 of a double in one rounding. When the double's exponent
+// lies in bf16's normal range, rounding its 52-bit significand to 7 bits at
+// bit 45 (adding 2^44 - 1 plus the kept last bit) is that rounding, a carry
+// into the exponent included (up to infinity); the exponent is then rebiased
+// from 1023 to 127. Zeros, bf16 subnormals, infinities and NaN take the
+// general path.
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t e = (uint32_t)(b >> 52) & 0x7FFu;
+    if (e - 897u > 1150u - 897u) return f64_to_bf16_slow(x);
+    const uint64_t mag = b & 0x7FFFFFFFFFFFFFFFull;
+    const uint32_t r = (uint32_t)((mag + 0x00000FFFFFFFFFFFull + ((mag >> 45) & 1ull)) >> 45);  // exponent | 7 bits
+    return (r - (896u << 7)) | ((uint32_t)(b >> 48) & 0x8000u);
 }
 
 constexpr int kMaxPairs = 64;  // head_dim / 2 for head_dim <= 128

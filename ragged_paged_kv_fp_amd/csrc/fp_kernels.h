@@ -10,7 +10,7 @@
 
 namespace fpk {
 
-// Per-lane plan record written by the plan (prep_kernel, block 0).
+// Per-lane plan record written by the plan (plan_kernel).
 struct LaneInfo {
     int dec_off;   // first decode work item of the lane, -1 if the lane is not a decode lane
     int nsplit;    // decode KV splits of the lane (items per KV head)
@@ -29,7 +29,7 @@ __device__ __forceinline__ void rotate_pair_f64(double x0, double x1, double c, 
 struct AppendArgs {
     uint16_t *pool;
     int64_t page_elems;
-    int num_pages, P, H, D;
+    int num_pages, P, H;
     const int32_t *page_indptr, *page_ids, *committed;
     const int32_t *indptr;
     int L;
@@ -37,39 +37,59 @@ struct AppendArgs {
     const int32_t *positions, *slots;
     const uint16_t *k, *v;
     int32_t *status;
-    int rows, chunks;  // rows per workgroup (<= kAppendRows), KV-head chunks per (row, pair)
+    int rshift;  // log2 of the rows per workgroup (<= kAppendRows)
     RopeFreqs freqs;
 };
 
-constexpr int kAppendRows = 16;      // most consecutive rows one append workgroup writes
-constexpr int kAppendVWords = 8320;  // LDS words staging V: 8 heads of 16 rows at head dim 128
+constexpr int kAppendRows = 16;        // most consecutive rows one append workgroup writes
+constexpr int kBatch = 8;              // 16-byte loads a thread of the row kernels issues before using them
+constexpr int kAppendVBytes = 33024;   // LDS staging V: 16 rows x (8 heads x 128 dims + 8 padding) bf16
 
-// Rows per workgroup and head chunks per (row, RoPE pair) for the row-grouped
-// kernels: many rows share a workgroup when there are enough rows to fill the
-// chip, few rows get all their heads spread over the workgroup's threads.
-__host__ __forceinline__ void row_grouping(int64_t N, int pairs, int heads, int *rows, int *chunks, int threads = 256) {
-    int r = 1;
-    while (r < kAppendRows && N / (2 * r) >= 1024) r *= 2;
-    int c = threads / (r * pairs);
-    c = c < 1 ? 1 : (c > heads ? heads : c);
-    *rows = r;
-    *chunks = c;
+// log2 of the rows per workgroup of the row-grouped kernels (append, Q
+// rotation): many rows share a workgroup when there are enough rows to fill
+// the chip, one row per workgroup for a short pass.
+__host__ __forceinline__ int row_group_shift(int64_t N, int max_rows) {
+    int s = 0;
+    while ((1 << s) < max_rows && N / (2LL << s) >= 1024) ++s;
+    return s;
 }
 
-// One workgroup per a.rows consecutive rows. The rows are validated once
-// (lane, slot, freeze, page); K is rotated by one thread per (row, RoPE pair,
-// head chunk) looping over the chunk's KV heads, which share the angle, each 4-byte pair store
-// coalescing with its neighbours in the K row; V goes through LDS one head at
-// a group of heads at a time so that consecutive threads store consecutive rows of one V^T row:
-// the rows of a prefill chunk sit in consecutive slots of a page, and their
-// 2-byte stores then merge into one contiguous segment per V^T row.
+// One 16-byte chunk of a head row (four RoPE pairs) rotated in fp64 by the
+// pairs' (cos, sin) and rounded once to nearest-even bf16.
+__device__ __forceinline__ uint4 rotate_chunk(uint4 x, const double2 *cs) {
+    uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        double y0, y1;
+        rotate_pair_f64((double)bf16_lo(w[q]), (double)bf16_hi(w[q]), cs[q].x, cs[q].y, &y0, &y1);
+        w[q] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// One workgroup per 2^rshift consecutive rows.
+//  1. The rows are validated once (lane, slot, freeze, page).
+//  2. The fp64 (cos, sin) of every (row, RoPE pair) goes to LDS: the KV heads
+//     of a row share them.
+//  3. K: one thread per 16-byte chunk (four pairs) of a (row, head) row, chunk
+//     index fastest, so a wave reads and writes whole 256-byte head rows.
+//  4. V goes through LDS a group of heads at a time (16-byte loads), rows
+//     padded by 16 bytes so the transposed reads below are free of bank
+//     conflicts, then is stored into the V^T block with the row index fastest:
+//     rows of a prefill chunk sit in consecutive slots of a page, so one
+//     wave's 2-byte stores cover consecutive bytes of consecutive V^T rows.
+template <int D>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+    constexpr int PAIRS = D / 2, C8 = D / 8, CSH = D == 128 ? 4 : 3, DSH = D == 128 ? 7 : 6;
     __shared__ int64_t s_base[kAppendRows];  // element offset of the row's page, -1: row not written
     __shared__ int s_off[kAppendRows];
-    __shared__ uint32_t s_vw[kAppendVWords];  // V of the rows for a group of heads, padded head rows
-    const int64_t r0 = (int64_t)blockIdx.x * a.rows;
-    const int nr = (int)(a.N - r0 < a.rows ? a.N - r0 : a.rows);
+    __shared__ double2 s_cs[kAppendRows * PAIRS];
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[kAppendVBytes / 2];
+    const int R = 1 << a.rshift;
+    const int64_t r0 = (int64_t)blockIdx.x << a.rshift;
+    const int nr = (int)(a.N - r0 < R ? a.N - r0 : R);
     const int tid = threadIdx.x;
+    const int H = a.H;
     if (tid < kAppendRows) {
         int64_t base = -1;
         int off = 0;
@@ -96,49 +116,68 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
         s_base[tid] = base;
         s_off[tid] = off;
     }
+    for (int e = tid; e < nr * PAIRS; e += blockDim.x) {
+        double c, sn;
+        rope_cos_sin(a.positions[r0 + (e / PAIRS)], a.freqs.w[e % PAIRS], &c, &sn);
+        s_cs[e] = make_double2(c, sn);
+    }
     __syncthreads();
-    const int pairs = a.D >> 1;
-    const int hpc = (a.H + a.chunks - 1) / a.chunks;
-    for (int idx = tid; idx < nr * a.chunks * pairs; idx += blockDim.x) {
-        const int rc = idx / pairs, i = idx - rc * pairs;
-        const int j = rc / a.chunks, h0 = (rc - j * a.chunks) * hpc, h1 = min(a.H, h0 + hpc);
-        const int64_t base = s_base[j];
-        if (base < 0) continue;
-        const int64_t row = r0 + j;
-        double c, s;
-        rope_cos_sin(a.positions[row], a.freqs.w[i], &c, &s);
-        uint32_t *kb = reinterpret_cast<uint32_t *>(a.pool + base + (int64_t)s_off[j] * a.D) + i;  // K block [H][P][D]
-        const uint32_t *kin = reinterpret_cast<const uint32_t *>(a.k + row * a.H * a.D) + i;
-#pragma unroll 4
-        for (int h = h0; h < h1; ++h) {
-            const uint32_t kw = kin[h * pairs];
-            double y0, y1;
-            rotate_pair_f64((double)bf16_lo(kw), (double)bf16_hi(kw), c, s, &y0, &y1);
-            kb[(int64_t)h * a.P * pairs] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+    // K chunks kBatch at a time per thread: all loads of a batch are issued
+    // before the first rotation, so a thread keeps kBatch loads in flight
+    const int nk = nr * H * C8;
+    for (int e0 = tid; e0 < nk; e0 += kBatch * 256) {
+        uint4 x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + 256 * u;
+            const int rh = e >> CSH;  // (row - r0) * H + head: the row's K rows are contiguous
+            x[u] = e < nk ? *reinterpret_cast<const uint4 *>(a.k + (r0 * H + rh) * D + 8 * (e & (C8 - 1)))
+                          : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + 256 * u;
+            if (e >= nk) break;
+            const int c = e & (C8 - 1), rh = e >> CSH;
+            const int j = rh / H, h = rh - j * H;
+            const int64_t base = s_base[j];
+            if (base >= 0)
+                *reinterpret_cast<uint4 *>(a.pool + base + ((int64_t)h * a.P + s_off[j]) * D + 8 * c) =
+                    rotate_chunk(x[u], &s_cs[j * PAIRS + 4 * c]);
         }
     }
-    const int64_t vblock = (int64_t)a.H * a.P * a.D;  // V block [H][D][P] follows the K block
-    // V goes through LDS a group of heads at a time (all heads of a decode
-    // row in one round); stores then run with the row index fastest.
-    const int hg = max(1, min(a.H, kAppendVWords / (a.rows * (pairs + 1))));
-    for (int h0 = 0; h0 < a.H; h0 += hg) {
-        const int hn = min(hg, a.H - h0);
-        for (int e = tid; e < nr * hn * pairs; e += blockDim.x) {
-            const int j = e / (hn * pairs), rem = e - j * hn * pairs;
-            const int hh = rem / pairs, i = rem - hh * pairs;
-            s_vw[(j * hn + hh) * (pairs + 1) + i] =
-                reinterpret_cast<const uint32_t *>(a.v + ((r0 + j) * a.H + h0 + hh) * a.D)[i];
+    const int64_t vblock = (int64_t)H * a.P * D;  // V block [H][D][P] follows the K block
+    const int hg = max(1, min(H, (kAppendVBytes / 2 - 8 * R) / (R * D)));  // heads per round
+    for (int h0 = 0; h0 < H; h0 += hg) {
+        const int hn = min(hg, H - h0);
+        const int rs = hn * D + 8;  // LDS row stride (elements): 16 bytes of padding per row
+        const int nv = nr * hn * C8;
+        for (int e0 = tid; e0 < nv; e0 += kBatch * 256) {
+            uint4 x[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int e = e0 + 256 * u;
+                const int c = e & (C8 - 1), rh = e >> CSH;
+                const int j = rh / hn, hh = rh - j * hn;
+                x[u] = e < nv ? *reinterpret_cast<const uint4 *>(a.v + (r0 + j) * H * D + (int64_t)(h0 + hh) * D + 8 * c)
+                              : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int e = e0 + 256 * u;
+                if (e >= nv) break;
+                const int c = e & (C8 - 1), rh = e >> CSH;
+                const int j = rh / hn, hh = rh - j * hn;
+                *reinterpret_cast<uint4 *>(&s_v[j * rs + hh * D + 8 * c]) = x[u];
+            }
         }
         __syncthreads();
-        for (int e = tid; e < hn * a.D * a.rows; e += blockDim.x) {
-            const int j = e % a.rows, dh = e / a.rows;
-            const int hh = dh / a.D, d = dh - hh * a.D;
+        for (int e = tid; e < (hn * D) << a.rshift; e += blockDim.x) {
+            const int j = e & (R - 1), dh = e >> a.rshift;
+            const int hh = dh >> DSH, d = dh & (D - 1);
             const int64_t base = s_base[j];
-            if (j < nr && base >= 0) {
-                const uint32_t w = s_vw[(j * hn + hh) * (pairs + 1) + (d >> 1)];
-                a.pool[base + vblock + ((int64_t)(h0 + hh) * a.D + d) * a.P + s_off[j]] =
-                    (uint16_t)((d & 1) ? (w >> 16) : (w & 0xFFFFu));
-            }
+            if (j < nr && base >= 0)
+                a.pool[base + vblock + ((int64_t)(h0 + hh) * D + d) * a.P + s_off[j]] = s_v[j * rs + hh * D + d];
         }
         __syncthreads();
     }
@@ -319,37 +358,51 @@ struct RopeQArgs {
     uint16_t *qrot;
     const int32_t *positions;
     int64_t N;
-    int Hq, D;
+    int Hq;
     double qscale;  // sm_scale * log2(e): scores come out in base-2 units
-    int rows, chunks;  // rows per workgroup, query-head chunks per (row, pair)
+    int rshift;     // log2 of the rows per workgroup (<= kQRows)
     RopeFreqs freqs;
 };
 
-// One workgroup per a.rows rows, one thread per (row, RoPE pair, head chunk)
-// looping over the chunk's query heads, which share the angle; the 4-byte pair
-// loads and stores of a wave cover whole Q rows. Output is the rotated,
-// prescaled Q in bf16, same [N][Hq][D] layout as q.
+constexpr int kQRows = 16;  // most rows one Q-rotation workgroup handles
+
+// One workgroup per 2^rshift rows: the fp64 (cos, sin) of every (row, pair),
+// prescaled by qscale, go to LDS (all query heads of a row share them), then
+// one thread per 16-byte chunk (four pairs) of a (row, head) row rotates it
+// and rounds it once to bf16; consecutive threads take consecutive chunks, so
+// a wave reads and writes whole head rows. Output: the rotated, prescaled Q in
+// bf16, same [N][Hq][D] layout as q.
+template <int D>
 __device__ __forceinline__ void rope_q_body(const RopeQArgs &a, int block) {
-    const int64_t r0 = (int64_t)block * a.rows;
-    const int nr = (int)(a.N - r0 < a.rows ? a.N - r0 : a.rows);
-    const int pairs = a.D >> 1;
-    const int hpc = (a.Hq + a.chunks - 1) / a.chunks;
-    for (int idx = threadIdx.x; idx < nr * a.chunks * pairs; idx += blockDim.x) {
-        const int rc = idx / pairs, i = idx - rc * pairs;
-        const int j = rc / a.chunks, h0 = (rc - j * a.chunks) * hpc, h1 = min(a.Hq, h0 + hpc);
-        const int64_t row = r0 + j;
-        double c, s;
-        rope_cos_sin(a.positions[row], a.freqs.w[i], &c, &s);
-        c *= a.qscale;
-        s *= a.qscale;
-        const uint32_t *qin = reinterpret_cast<const uint32_t *>(a.q + row * a.Hq * a.D) + i;
-        uint32_t *qo = reinterpret_cast<uint32_t *>(a.qrot + row * a.Hq * a.D) + i;
-#pragma unroll 8
-        for (int h = h0; h < h1; ++h) {
-            const uint32_t w = qin[h * pairs];
-            double y0, y1;
-            rotate_pair_f64((double)bf16_lo(w), (double)bf16_hi(w), c, s, &y0, &y1);
-            qo[h * pairs] = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+    constexpr int PAIRS = D / 2, C8 = D / 8, CSH = D == 128 ? 4 : 3;
+    __shared__ double2 s_cs[kQRows * PAIRS];
+    const int R = 1 << a.rshift;
+    const int64_t r0 = (int64_t)block << a.rshift;
+    const int nr = (int)(a.N - r0 < R ? a.N - r0 : R);
+    for (int e = threadIdx.x; e < nr * PAIRS; e += blockDim.x) {
+        double c, sn;
+        rope_cos_sin(a.positions[r0 + (e / PAIRS)], a.freqs.w[e % PAIRS], &c, &sn);
+        s_cs[e] = make_double2(c * a.qscale, sn * a.qscale);
+    }
+    __syncthreads();
+    const int Hq = a.Hq;
+    const int nq = nr * Hq * C8;
+    const int nt = blockDim.x;
+    for (int e0 = threadIdx.x; e0 < nq; e0 += kBatch * nt) {
+        uint4 x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + nt * u;
+            x[u] = e < nq ? *reinterpret_cast<const uint4 *>(a.q + (r0 * Hq + (e >> CSH)) * D + 8 * (e & (C8 - 1)))
+                          : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + nt * u;
+            if (e >= nq) break;
+            const int c = e & (C8 - 1), rh = e >> CSH;
+            const int j = rh / Hq;
+            *reinterpret_cast<uint4 *>(a.qrot + (r0 * Hq + rh) * D + 8 * c) = rotate_chunk(x[u], &s_cs[j * PAIRS + 4 * c]);
         }
     }
 }
@@ -533,12 +586,16 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
     }
 }
 
-// Plan and Q rotation in one launch (they read only the inputs): block 0
-// builds the plan, blocks 1.. rotate the rows of Q.
-__global__ void __launch_bounds__(kPlanThreads) prep_kernel(PlanArgs pa, RopeQArgs ra) {
-    if (blockIdx.x == 0) plan_body(pa);
-    else rope_q_body(ra, (int)blockIdx.x - 1);
-}
+// The plan: one workgroup.
+__global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs pa) { plan_body(pa); }
+
+// Q rotation: a launch of its own with small workgroups, so that many of them
+// (each with its own loads in flight) share a compute unit; the plan's large
+// LDS footprint would allow one per compute unit.
+constexpr int kRopeThreads = 256;
+
+template <int D>
+__global__ void __launch_bounds__(kRopeThreads) rope_q_kernel(RopeQArgs ra) { rope_q_body<D>(ra, (int)blockIdx.x); }
 
 // ============================================================================ mask summary
 

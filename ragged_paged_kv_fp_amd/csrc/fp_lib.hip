@@ -46,8 +46,11 @@ int device_cus() {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+inline bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
 int check_pool(const fp_kv_pool *p) {
     if (!p || !p->kv || !p->page_indptr || !p->page_indptr_host || !p->page_ids || !p->committed_len) return FP_ERR_NULL;
+    if (!aligned16(p->kv)) return FP_ERR_UNSUPPORTED;
     if (p->num_pages < 1 || p->num_kv_heads < 1) return FP_ERR_SHAPE;
     if (p->page_size != 8 && p->page_size != 16 && p->page_size != 32) return FP_ERR_UNSUPPORTED;
     if (p->head_dim != 64 && p->head_dim != 128) return FP_ERR_UNSUPPORTED;
@@ -231,6 +234,7 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
     if (!status) return FP_ERR_NULL;
     if (p.N == 0) return FP_OK;
     if (!q || !out) return FP_ERR_NULL;
+    if (!aligned16(q)) return FP_ERR_UNSUPPORTED;
     if (!workspace) return FP_ERR_NULL;
     if (workspace_bytes < p.total) return FP_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
@@ -262,12 +266,14 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
     ra.positions = geom->positions;
     ra.N = p.N;
     ra.Hq = p.Hq;
-    ra.D = p.D;
     ra.qscale = (double)sm_scale * 1.4426950408889634;  // log2(e)
     ra.freqs = rope_freqs(rope_theta, p.D);
-    row_grouping(p.N, p.D / 2, p.Hq, &ra.rows, &ra.chunks, kPlanThreads);
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(1 + (p.N + ra.rows - 1) / ra.rows)), dim3(kPlanThreads), 0, stream,
-                       pa, ra);
+    ra.rshift = row_group_shift(p.N, kQRows);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, pa);
+    if ((rc = launch_ok())) return rc;
+    const dim3 rgrid((unsigned)((p.N + (1 << ra.rshift) - 1) >> ra.rshift));
+    if (p.D == 128) hipLaunchKernelGGL(rope_q_kernel<128>, rgrid, dim3(kRopeThreads), 0, stream, ra);
+    else hipLaunchKernelGGL(rope_q_kernel<64>, rgrid, dim3(kRopeThreads), 0, stream, ra);
     if ((rc = launch_ok())) return rc;
 
     AttnArgs a;
@@ -350,13 +356,13 @@ int fp_append_kv(const fp_kv_pool *pool, const fp_geometry *geom, const void *k,
     if (!status) return FP_ERR_NULL;
     if (geom->num_rows == 0) return FP_OK;
     if (!k || !v) return FP_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v)) return FP_ERR_UNSUPPORTED;
     AppendArgs a;
     a.pool = static_cast<uint16_t *>(pool->kv);
     a.num_pages = pool->num_pages;
     a.P = pool->page_size;
     a.H = pool->num_kv_heads;
-    a.D = pool->head_dim;
-    a.page_elems = 2LL * a.H * a.P * a.D;
+    a.page_elems = 2LL * a.H * a.P * pool->head_dim;
     a.page_indptr = pool->page_indptr;
     a.page_ids = pool->page_ids;
     a.committed = pool->committed_len;
@@ -368,9 +374,11 @@ int fp_append_kv(const fp_kv_pool *pool, const fp_geometry *geom, const void *k,
     a.k = static_cast<const uint16_t *>(k);
     a.v = static_cast<const uint16_t *>(v);
     a.status = status;
-    a.freqs = rope_freqs(rope_theta, a.D);
-    row_grouping(a.N, a.D / 2, a.H, &a.rows, &a.chunks);
-    hipLaunchKernelGGL(append_kernel, dim3((unsigned)((a.N + a.rows - 1) / a.rows)), dim3(256), 0, stream, a);
+    a.freqs = rope_freqs(rope_theta, pool->head_dim);
+    a.rshift = row_group_shift(a.N, kAppendRows);
+    const dim3 grid((unsigned)((a.N + (1 << a.rshift) - 1) >> a.rshift));
+    if (pool->head_dim == 128) hipLaunchKernelGGL(append_kernel<128>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(append_kernel<64>, grid, dim3(256), 0, stream, a);
     return launch_ok();
 }
 
