@@ -288,16 +288,26 @@ __device__ __forceinline__ void stage_o(const DecState<D, NC> &w, int c, float s
     }
 }
 
+// LDS of one decode workgroup. The K staging buffers (used by the tile loop)
+// and the output combine rows (used after it, past a barrier) share storage.
 template <int D, int NC>
-__global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(AttnArgs a) {
-    __shared__ float s_ml[kDecWaves][2][32];
-    __shared__ float s_fin[2][32];
-    __shared__ float s_o[kDecWaves][NC][kLdsRow];
-    __shared__ __attribute__((aligned(16))) char s_k[kDecWaves][DecLds<D>::BYTES];
+struct DecShared {
+    float ml[kDecWaves][2][32];
+    float fin[2][32];
+    union {
+        float o[kDecWaves][NC][kLdsRow];
+        char k[kDecWaves][DecLds<D>::BYTES];
+    } u;
+};
 
-    const int item = blockIdx.x;
-    const int4 it = a.dec_items[item];
-    if (it.x < 0) return;
+// One work item (lane, KV head, KV split): every barrier inside is reached by
+// all threads of the workgroup.
+template <int D, int NC>
+__device__ __forceinline__ void decode_item(const AttnArgs &a, const int4 it, DecShared<D, NC> &sh) {
+    auto &s_ml = sh.ml;
+    auto &s_fin = sh.fin;
+    auto &s_o = sh.u.o;
+    auto &s_k = sh.u.k;
     const int lane = it.x, g = it.y, s0 = it.z, s1 = it.w;
     const LaneInfo li = a.lane_info[lane];
     const int r0 = a.indptr[lane];
@@ -418,62 +428,136 @@ __global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(A
     }
 }
 
-// Combine the KV splits of one (decode lane, KV head, query column): block of
-// D threads, one output element each. Split statistics go through LDS so the
-// partial-output loads of all splits are issued back to back.
-constexpr int kMergeChunk = 256;
+// One workgroup per work item of its column class's list. The hardware
+// dispatcher starts workgroups in launch order as others finish, so the long
+// items at the head of the list go first and the short partial splits set the
+// tail.
+template <int D, int NC>
+__global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) DecShared<D, NC> sh;
+    const int4 it = a.dec_list[blockIdx.x];
+    if (it.x >= 0) decode_item<D, NC>(a, it, sh);
+}
+
+// Combine the KV splits of one (decode lane, KV head), all its query
+// columns at once: a workgroup of kMergeThreads. Every split's (max, sum) of
+// every column goes to LDS at once, and each thread issues the loads of its
+// first kMergeBatch splits' partial outputs before waiting on anything, so
+// the work is two memory round trips deep rather than one per step. Then the
+// column maxima and denominators are read from LDS and every thread
+// accumulates four float4 output groups over the splits.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxSplits = 128;  // splits whose statistics fit the LDS arrays at once
+constexpr int kMergeBatch = 4;        // splits of partial outputs in flight per thread
 
 template <int D>
-__global__ void __launch_bounds__(D) merge_kernel(AttnArgs a) {
-    __shared__ float s_w[kMergeChunk];
-    __shared__ float s_red[D / kWave];
-    __shared__ float s_stat[2];
-    const int lane = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(AttnArgs a) {
+    __shared__ float s_m[kMergeMaxSplits][32], s_l[kMergeMaxSplits][32];
+    __shared__ float s_M[32], s_den[32];
+    const int lane = blockIdx.x, g = blockIdx.y;
     const LaneInfo li = a.lane_info[lane];
-    if (li.dec_off < 0 || li.nsplit <= 1) return;
+    if (li.dec_off < 0 || li.nsplit <= 1) return;  // workgroup-uniform
     const int r0 = a.indptr[lane];
     const int ncols = (a.indptr[lane + 1] - r0) * a.G;
-    if (n >= ncols) return;
-    const int tid = threadIdx.x, dd = tid;
     const int64_t first = (int64_t)li.dec_off + (int64_t)g * li.nsplit;
     const int ns = li.nsplit;
-    // global max over splits
-    float mloc = kNegInf;
-    for (int s = tid; s < ns; s += D) mloc = fmaxf(mloc, a.part_ml[(first + s) * 64 + n]);
-    mloc = wave_max(mloc);
-    if (lane_id() == 0) s_red[tid / kWave] = mloc;
-    __syncthreads();
-    if (tid == 0) {
-        float M = kNegInf;
-        for (int v = 0; v < D / kWave; ++v) M = fmaxf(M, s_red[v]);
-        s_stat[0] = M;
-    }
-    __syncthreads();
-    const float M = s_stat[0];
-    float num = 0.0f, den = 0.0f;
-    for (int c0 = 0; c0 < ns; c0 += kMergeChunk) {
-        const int cn = min(kMergeChunk, ns - c0);
-        for (int s = tid; s < cn; s += D)
-            s_w[s] = (M == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(a.part_ml[(first + c0 + s) * 64 + n] - M);
-        __syncthreads();
-        for (int s = 0; s < cn; ++s) den += s_w[s] * a.part_ml[(first + c0 + s) * 64 + 32 + n];
-        const float *po = a.part_o + ((first + c0) * a.ncols_max + n) * D + dd;
-        const int64_t stride = (int64_t)a.ncols_max * D;
-        int s = 0;
-        for (; s + 8 <= cn; s += 8) {
-            float v[8];
+    const int tid = threadIdx.x;
+    const float *ml = a.part_ml + first * 64;
+    constexpr int D4 = D / 4;
+    const int n4 = ncols * D4;                              // float4 groups of the lane's outputs
+    const int64_t ostride4 = (int64_t)a.ncols_max * D4;     // float4 groups per split of partial outputs
+    const float4 *po = reinterpret_cast<const float4 *>(a.part_o) + first * ostride4;
+    // partial outputs of the first kMergeBatch splits: issued before any wait
+    float4 pre[kMergeBatch][4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = po[(s + u) * stride];
+    for (int b = 0; b < kMergeBatch; ++b)
 #pragma unroll
-            for (int u = 0; u < 8; ++u) num += s_w[s + u] * v[u];
+        for (int k = 0; k < 4; ++k) {
+            const int e4 = tid + kMergeThreads * k;
+            pre[b][k] = (b < ns && e4 < n4) ? po[b * ostride4 + e4] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        for (; s < cn; ++s) num += s_w[s] * po[s * stride];
+    // per-column maximum and denominator over every split, kMergeMaxSplits at a time
+    float M = kNegInf, den = 0.0f;
+    for (int c0 = 0; c0 < ns; c0 += kMergeMaxSplits) {
+        const int cn = min(kMergeMaxSplits, ns - c0);
         __syncthreads();
+        for (int e = tid; e < cn * 32; e += kMergeThreads) {
+            const int sp = e >> 5, cc = e & 31;
+            s_m[sp][cc] = ml[(c0 + sp) * 64 + cc];
+            s_l[sp][cc] = ml[(c0 + sp) * 64 + 32 + cc];
+        }
+        __syncthreads();
+        if (tid < 32) {
+            float Mc = M;
+            for (int sp = 0; sp < cn; ++sp) Mc = fmaxf(Mc, s_m[sp][tid]);
+            if (Mc != kNegInf) {
+                den = M == kNegInf ? 0.0f : den * __builtin_amdgcn_exp2f(M - Mc);
+                for (int sp = 0; sp < cn; ++sp) den += __builtin_amdgcn_exp2f(s_m[sp][tid] - Mc) * s_l[sp][tid];
+            }
+            M = Mc;
+        }
     }
-    const int64_t orow = r0 + n / a.G;
-    const int ohead = g * a.G + n % a.G;
-    a.out[(orow * a.Hq + ohead) * D + dd] = den > 0.0f ? num / den : 0.0f;
-    if (dd == 0 && a.lse) a.lse[orow * a.Hq + ohead] = den > 0.0f ? (M + __log2f(den)) * 0.69314718055994531f : kNegInf;
+    if (tid < 32) {
+        s_M[tid] = M;
+        s_den[tid] = den;
+    }
+    // weighted sum of the partial outputs; a refilled slot takes the split
+    // kMergeBatch further on, so kMergeBatch splits stay in flight
+    float4 acc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = 0; c0 < ns; c0 += kMergeMaxSplits) {
+        const int cn = min(kMergeMaxSplits, ns - c0);
+        if (ns > kMergeMaxSplits) {  // LDS holds the last chunk's maxima: bring this chunk's back
+            __syncthreads();
+            for (int e = tid; e < cn * 32; e += kMergeThreads) s_m[e >> 5][e & 31] = ml[(c0 + (e >> 5)) * 64 + (e & 31)];
+        }
+        __syncthreads();
+        for (int b0 = 0; b0 < cn; b0 += kMergeBatch) {
+#pragma unroll
+            for (int b = 0; b < kMergeBatch; ++b) {
+                const int sp = c0 + b0 + b;
+                if (sp >= ns) break;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int e4 = tid + kMergeThreads * k;
+                    if (e4 >= n4) continue;
+                    const int n = e4 / D4;
+                    const float Mn = s_M[n];
+                    const float w = Mn == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_m[b0 + b][n] - Mn);
+                    const float4 v = pre[b][k];
+                    acc[k].x += w * v.x;
+                    acc[k].y += w * v.y;
+                    acc[k].z += w * v.z;
+                    acc[k].w += w * v.w;
+                }
+                const int nx = sp + kMergeBatch;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int e4 = tid + kMergeThreads * k;
+                    if (nx < ns && e4 < n4) pre[b][k] = po[nx * ostride4 + e4];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e4 = tid + kMergeThreads * k;
+        if (e4 >= n4) continue;
+        const int n = e4 / D4, d4 = e4 - n * D4;
+        const float dn = s_den[n];
+        const float inv = dn > 0.0f ? 1.0f / dn : 0.0f;
+        const int64_t orow = r0 + n / a.G;
+        const int ohead = g * a.G + n % a.G;
+        *reinterpret_cast<float4 *>(a.out + (orow * a.Hq + ohead) * D + 4 * d4) =
+            make_float4(acc[k].x * inv, acc[k].y * inv, acc[k].z * inv, acc[k].w * inv);
+    }
+    if (tid < ncols && a.lse) {
+        const float dn = s_den[tid];
+        const int64_t orow = r0 + tid / a.G;
+        const int ohead = g * a.G + tid % a.G;
+        a.lse[orow * a.Hq + ohead] = dn > 0.0f ? (s_M[tid] + __log2f(dn)) * 0.69314718055994531f : kNegInf;
+    }
 }
 
 }  // namespace fpk

@@ -418,25 +418,28 @@ constexpr int kPreCols = 256;    // query row-heads per prefill workgroup (8 wav
 // Rows of one prefill work item: all GQA heads of those rows fill the workgroup.
 __host__ __device__ __forceinline__ int prefill_rows(int G) { return kPreCols / G; }
 
+constexpr int kDecodeCols16 = 16;  // decode lanes up to this many row-heads take the 16-column kernel
+
 struct PlanArgs {
     const int32_t *indptr, *page_indptr, *kv_len;
     const int64_t *mask_off;  // nullable
     int L, H, G, P, split;
-    int64_t n_dec_host, n_pre_host, sum_host, N_host;
+    int64_t n_dec_host[2];  // decode items of each column class (<= 16, <= 32 row-heads)
+    int64_t n_pre_host, sum_host, N_host;
     int ncols_host;
     int merge_host;     // the host allotted split-merge buffers
     LaneInfo *lane_info;
-    int4 *dec_items;   // {lane, kv head, first slot, end slot}
+    int4 *dec_items;   // class-0 items, then class-1 items: {lane, kv head, first slot, end slot}
     int4 *pre_items;   // {lane, kv head, first local row, rows}
     int32_t *status;
 };
 
 struct LaneCounts {
-    int dec, pre, sum, nsplit, nrb, stride, ncols;
+    int dec, pre, sum, nsplit, nrb, stride, ncols, cls;
 };
 
 __device__ __forceinline__ LaneCounts lane_counts(const PlanArgs &a, int l, int32_t *st) {
-    LaneCounts r = {0, 0, 0, 0, 0, 0, 0};
+    LaneCounts r = {0, 0, 0, 0, 0, 0, 0, 0};
     const int n = a.indptr[l + 1] - a.indptr[l];
     const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
     const int kv = a.kv_len[l];
@@ -451,6 +454,7 @@ __device__ __forceinline__ LaneCounts lane_counts(const PlanArgs &a, int l, int3
         r.nsplit = cap > 0 ? (cap + a.split - 1) / a.split : 1;
         r.dec = a.H * r.nsplit;
         r.ncols = n * a.G;
+        r.cls = r.ncols <= kDecodeCols16 ? 0 : 1;
     } else {
         r.nrb = (n + prefill_rows(a.G) - 1) / prefill_rows(a.G);
         r.pre = a.H * r.nrb;
@@ -471,61 +475,98 @@ __device__ __forceinline__ int upper_lane(const int *offs, int L, int idx) {
     return lo;
 }
 
+// Exclusive prefix sum over the workgroup's threads (in thread order); *total
+// gets the sum of all. s_w: one int per wave.
+__device__ __forceinline__ int block_excl_scan(int v, int *s_w, int *total) {
+    const int ln = lane_id(), wv = threadIdx.x / kWave;
+    int x = v;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (ln >= o) x += y;
+    }
+    if (ln == kWave - 1) s_w[wv] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < kPlanThreads / kWave; ++w) {
+        const int t = s_w[w];
+        before += w < wv ? t : 0;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + x - v;
+}
+
 // Single workgroup: per-lane classification (decode if all rows x GQA heads fit
-// one MFMA tile, prefill otherwise), prefix offsets, and the work-item lists.
+// one MFMA tile, prefill otherwise; decode lanes in two column classes),
+// prefix offsets, and the work-item lists. The decode list holds the items of
+// column class 0 (<= 16 row-heads), then those of class 1 (<= 32); within a
+// class, first every split but each (lane, KV head)'s last, then the last
+// splits (the partial ones), so that the long items are dispatched first. Split outputs are stored by (lane, KV head, split): lane_info's
+// dec_off counts every decode item of the lanes before, in lane order.
 __device__ __forceinline__ void plan_body(const PlanArgs &a) {
-    __shared__ int s_dec[kMaxLanes + 1];
-    __shared__ int s_pre[kMaxLanes + 1];
-    __shared__ int s_nd[kMaxLanes + 1];  // decode lanes before lane l
-    __shared__ int s_scan[4][kPlanThreads];
+    __shared__ int s_pre[kMaxLanes + 1];    // prefill items before lane l
+    __shared__ int s_full[2][kMaxLanes + 1];  // non-last decode items of class c before lane l
+    __shared__ int s_nd[2][kMaxLanes + 1];    // decode lanes of class c before lane l
+    __shared__ int s_w[kPlanThreads / kWave];
     __shared__ int s_bad;
     const int tid = threadIdx.x;
     if (tid == 0) s_bad = 0;
     const int per = (a.L + kPlanThreads - 1) / kPlanThreads;
     const int l0 = tid * per, l1 = min(a.L, l0 + per);
     int32_t st = 0;
-    int td = 0, tp = 0, ts = 0, tc = 0, tn = 0;
+    int td = 0, tp = 0, ts = 0, tc = 0, tf0 = 0, tf1 = 0, tn0 = 0, tn1 = 0;
     for (int l = l0; l < l1; ++l) {
         const LaneCounts c = lane_counts(a, l, &st);
-        td += c.dec; tp += c.pre; ts += c.sum; tn += c.dec ? 1 : 0;
+        td += c.dec; tp += c.pre; ts += c.sum;
+        if (c.dec) {
+            if (c.cls == 0) { tf0 += c.dec - a.H; tn0 += 1; }
+            else { tf1 += c.dec - a.H; tn1 += 1; }
+        }
         tc = max(tc, c.ncols);
         if (c.nsplit > 1 && !a.merge_host) tc = kDecodeCols + 1;  // forces the mismatch path
     }
     if (st) atomicOr(a.status, st);
-    __syncthreads();
+    int Td, Tp, Ts, Tf0, Tf1, Tn0, Tn1;
+    int od = block_excl_scan(td, s_w, &Td);  // its barriers also order s_bad's initialisation
     if (tc > a.ncols_host) atomicOr(&s_bad, 1);
-    s_scan[0][tid] = td; s_scan[1][tid] = tp; s_scan[2][tid] = ts; s_scan[3][tid] = tn;
-    __syncthreads();
-    for (int o = 1; o < kPlanThreads; o <<= 1) {
-        int v0 = 0, v1 = 0, v2 = 0, v3 = 0;
-        if (tid >= o) { v0 = s_scan[0][tid - o]; v1 = s_scan[1][tid - o]; v2 = s_scan[2][tid - o]; v3 = s_scan[3][tid - o]; }
-        __syncthreads();
-        s_scan[0][tid] += v0; s_scan[1][tid] += v1; s_scan[2][tid] += v2; s_scan[3][tid] += v3;
-        __syncthreads();
-    }
-    int od = s_scan[0][tid] - td, op = s_scan[1][tid] - tp, os = s_scan[2][tid] - ts, on = s_scan[3][tid] - tn;
+    int op = block_excl_scan(tp, s_w, &Tp);
+    int os = block_excl_scan(ts, s_w, &Ts);
+    int of0 = block_excl_scan(tf0, s_w, &Tf0);
+    int of1 = block_excl_scan(tf1, s_w, &Tf1);
+    int on0 = block_excl_scan(tn0, s_w, &Tn0);
+    int on1 = block_excl_scan(tn1, s_w, &Tn1);
     int32_t dummy = 0;
     for (int l = l0; l < l1; ++l) {
         const LaneCounts c = lane_counts(a, l, &dummy);
-        s_dec[l] = od;
         s_pre[l] = op;
-        s_nd[l] = on;
+        s_full[0][l] = of0;
+        s_full[1][l] = of1;
+        s_nd[0][l] = on0;
+        s_nd[1][l] = on1;
         LaneInfo li;
         li.dec_off = c.dec ? od : -1;
         li.nsplit = c.nsplit;
         li.sum_off = c.sum ? os : -1;
         li.sum_stride = c.stride;
         a.lane_info[l] = li;
-        od += c.dec; op += c.pre; os += c.sum; on += c.dec ? 1 : 0;
+        od += c.dec; op += c.pre; os += c.sum;
+        if (c.dec) {
+            if (c.cls == 0) { of0 += c.dec - a.H; on0 += 1; }
+            else { of1 += c.dec - a.H; on1 += 1; }
+        }
     }
-    if (tid == kPlanThreads - 1) {
-        s_dec[a.L] = s_scan[0][tid];
-        s_pre[a.L] = s_scan[1][tid];
-        s_nd[a.L] = s_scan[3][tid];
+    const int n0 = Tf0 + a.H * Tn0, n1 = Tf1 + a.H * Tn1;  // decode items of each class
+    if (tid == 0) {
+        s_pre[a.L] = Tp;
+        s_full[0][a.L] = Tf0;
+        s_full[1][a.L] = Tf1;
+        s_nd[0][a.L] = Tn0;
+        s_nd[1][a.L] = Tn1;
         // Launch grids and workspace were sized from the host copies; device
         // offsets that disagree would index past them, so no work is emitted.
-        if (s_scan[0][tid] != a.n_dec_host || s_scan[1][tid] != a.n_pre_host || s_scan[2][tid] != a.sum_host ||
-            (int64_t)a.indptr[a.L] != a.N_host)
+        if (n0 != a.n_dec_host[0] || n1 != a.n_dec_host[1] || Td != n0 + n1 || Tp != a.n_pre_host ||
+            Ts != a.sum_host || (int64_t)a.indptr[a.L] != a.N_host)
             atomicOr(&s_bad, 1);
     }
     __syncthreads();
@@ -534,32 +575,24 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
         for (int l = tid; l < a.L; l += kPlanThreads) a.lane_info[l] = LaneInfo{-1, 0, -1, 0};
         if (tid == 0) atomicOr(a.status, FP_ST_PLAN_MISMATCH);
     }
-    const int tot_d = bad ? 0 : s_dec[a.L], tot_p = bad ? 0 : s_pre[a.L];
-    // Decode items in launch order: first every split but each (lane, KV
-    // head)'s last, then the last splits (the partial ones). Workgroups are
-    // dispatched in this order, so the short items fill the end of the grid.
-    // Split outputs are stored by (lane, KV head, split), not by launch order.
-    const int tot_last = a.H * s_nd[a.L];
-    const int tot_full = tot_d - tot_last;
-    for (int64_t idx = tid; idx < a.n_dec_host; idx += kPlanThreads) {
+    const int64_t n_dec = a.n_dec_host[0] + a.n_dec_host[1];
+    for (int64_t idx = tid; idx < n_dec; idx += kPlanThreads) {
         int4 it = make_int4(-1, 0, 0, 0);
-        if (idx < tot_d) {
+        if (!bad) {
+            const int cls = idx < n0 ? 0 : 1;
+            const int local = (int)idx - (cls ? n0 : 0);
+            const int tf = cls ? Tf1 : Tf0;
             int l, g, sp;
-            if (idx < tot_full) {
-                // largest lane whose first non-last split is at or before idx
-                int lo = 0, hi = a.L;
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (s_dec[mid] - a.H * s_nd[mid] <= idx) lo = mid; else hi = mid;
-                }
-                l = lo;
-                const int local = (int)idx - (s_dec[l] - a.H * s_nd[l]);
-                const LaneInfo li = a.lane_info[l];
-                g = local / (li.nsplit - 1);
-                sp = local - g * (li.nsplit - 1);
+            if (local < tf) {
+                // a non-last split: the largest lane whose first such item is at or before local
+                l = upper_lane(s_full[cls], a.L, local);
+                const int j = local - s_full[cls][l];
+                const int ns = a.lane_info[l].nsplit;
+                g = j / (ns - 1);
+                sp = j - g * (ns - 1);
             } else {
-                const int j = (int)idx - tot_full;
-                l = upper_lane(s_nd, a.L, j / a.H);
+                const int j = local - tf;
+                l = upper_lane(s_nd[cls], a.L, j / a.H);
                 g = j % a.H;
                 sp = a.lane_info[l].nsplit - 1;
             }
@@ -568,6 +601,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
         }
         a.dec_items[idx] = it;
     }
+    const int tot_p = bad ? 0 : Tp;
     for (int64_t idx = tid; idx < a.n_pre_host; idx += kPlanThreads) {
         int4 it = make_int4(-1, 0, 0, 0);
         if (idx < tot_p) {
@@ -689,6 +723,7 @@ struct AttnArgs {
     const int64_t *mask_off;          // nullable
     float *out, *lse;                 // lse nullable
     const int4 *dec_items, *pre_items;
+    const int4 *dec_list;             // the decode items of one launch (one column class)
     const LaneInfo *lane_info;
     float *part_o;                    // [items][ncols_max][D] unnormalized split outputs
     float *part_ml;                   // [items][2][32] split max (base 2) and sum

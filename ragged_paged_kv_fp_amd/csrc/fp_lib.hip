@@ -91,11 +91,26 @@ int check_mask(const fp_mask *m, const fp_geometry *g) {
 
 struct Plan {
     int L = 0, H = 0, G = 0, Hq = 0, D = 0, P = 0, split = 0, ncols_max = 1;
-    int64_t N = 0, n_dec = 0, n_pre = 0, sum_words = 0;
+    int64_t N = 0, n_dec = 0, n_dec_cls[2] = {0, 0}, n_pre = 0, sum_words = 0;
     bool merge = false, summaries = false;
     size_t off_lane = 0, off_dec = 0, off_pre = 0, off_qrot = 0, off_po = 0, off_pml = 0, off_sum = 0;
     size_t total = 0;
 };
+
+// Workgroups of a kernel resident on the device at once (occupancy query,
+// cached per device and kernel).
+template <class Kernel>
+int resident_blocks(Kernel kernel, int threads) {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess || nb < 1) nb = 1;
+        cached[dev] = nb * device_cus();
+    }
+    return cached[dev];
+}
 
 // Shape-only plan: mirrors lane_counts() of the device plan from the host copies.
 int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *mask, int32_t Hq,
@@ -118,7 +133,16 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
         }
     }
     if (split == 0) {
-        const double slots = 2.0 * device_cus();  // decode workgroups resident at once (about two per CU)
+        // decode workgroups resident at once, for the kernel the pass will run
+        // (the 32-column kernel as soon as one decode lane has more than 16
+        // query row-heads)
+        bool wide = false;
+        for (int l = 0; l < geom->num_lanes; ++l) {
+            const int n = geom->indptr_host[l + 1] - geom->indptr_host[l];
+            if (n * G > kDecodeCols16 && n * G <= kDecodeCols) wide = true;
+        }
+        const double slots = (double)(wide ? resident_blocks(decode_kernel<128, 32>, kDecThreads)
+                                           : resident_blocks(decode_kernel<128, 16>, kDecThreads));
         for (const int cand : kSplitChoices) {
             split = cand;
             int64_t items = 0;
@@ -147,6 +171,7 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
         if (n * G <= kDecodeCols) {
             const int nsplit = cap > 0 ? (cap + split - 1) / split : 1;
             p.n_dec += (int64_t)p.H * nsplit;
+            p.n_dec_cls[n * G <= kDecodeCols16 ? 0 : 1] += (int64_t)p.H * nsplit;
             if (nsplit > 1) p.merge = true;
             if (n * G > p.ncols_max) p.ncols_max = n * G;
         } else {
@@ -249,7 +274,8 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
     pa.kv_len = geom->kv_len;
     pa.mask_off = mask ? mask->word_offset : nullptr;
     pa.L = p.L; pa.H = p.H; pa.G = p.G; pa.P = p.P; pa.split = p.split;
-    pa.n_dec_host = p.n_dec;
+    pa.n_dec_host[0] = p.n_dec_cls[0];
+    pa.n_dec_host[1] = p.n_dec_cls[1];
     pa.n_pre_host = p.n_pre;
     pa.sum_host = p.sum_words;
     pa.N_host = p.N;
@@ -322,22 +348,29 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
         if ((rc = launch_ok())) return rc;
     }
     if (tuning && tuning->prefill_end && hipEventRecord(tuning->prefill_end, stream) != hipSuccess) return FP_ERR_HIP;
+    // decode: lanes with up to 16 query row-heads run the 16-column kernel
+    // (two waves per SIMD); when the pass also has wider lanes, every decode
+    // item runs in one launch of the 32-column kernel: two launches would
+    // each pay their own start and tail, one after the other.
     if (p.n_dec) {
+        const bool wide = p.n_dec_cls[1] > 0;
+        AttnArgs ac = a;
+        ac.dec_list = dec_items;
         const dim3 grid((unsigned)p.n_dec), block(kDecThreads);
         if (p.D == 128) {
-            if (p.ncols_max <= 16) hipLaunchKernelGGL((decode_kernel<128, 16>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((decode_kernel<128, 32>), grid, block, 0, stream, a);
+            if (!wide) hipLaunchKernelGGL((decode_kernel<128, 16>), grid, block, 0, stream, ac);
+            else hipLaunchKernelGGL((decode_kernel<128, 32>), grid, block, 0, stream, ac);
         } else {
-            if (p.ncols_max <= 16) hipLaunchKernelGGL((decode_kernel<64, 16>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((decode_kernel<64, 32>), grid, block, 0, stream, a);
+            if (!wide) hipLaunchKernelGGL((decode_kernel<64, 16>), grid, block, 0, stream, ac);
+            else hipLaunchKernelGGL((decode_kernel<64, 32>), grid, block, 0, stream, ac);
         }
         if ((rc = launch_ok())) return rc;
     }
     if (tuning && tuning->attn_end && hipEventRecord(tuning->attn_end, stream) != hipSuccess) return FP_ERR_HIP;
     if (p.merge) {
-        const dim3 grid(p.L, p.H, p.ncols_max);
-        if (p.D == 128) hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, a);
-        else hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, a);
+        const dim3 grid(p.L, p.H);
+        if (p.D == 128) hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, a);
+        else hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, a);
         if ((rc = launch_ok())) return rc;
     }
     if (tuning && tuning->merge_end && hipEventRecord(tuning->merge_end, stream) != hipSuccess) return FP_ERR_HIP;
