@@ -529,6 +529,21 @@ def extra_configs(W, runner, seed, pk_hbm, pk_mfma) -> dict:
                       "t_bound_serial_over_t_measured": round((t_pre + t_dec) / t3, 4),
                       "traffic": measured_traffic(3)}
     del wl3
+    # a decode wave under a sliding window with sinks: masked decode lanes walk tile lists
+    wlw = W.make_window_decode(seed, L=64, kv=32768, window=1024, sinks=4)
+    ww, rw = measure(W, runner, None, seed, None, 5, 1, wl=wlw)[1:]
+    kvb = 2 * wlw.H_kv * wlw.d * 2  # bytes per slot
+    attended = int(attended_pairs(wlw).sum()) * kvb
+    tiles = 64 * (len(range(0, 4, 32)) + (1024 + 31) // 32 + 1) * 32 * kvb  # the tiles a lane touches (upper bound)
+    gbs = rate(attended, rw["decode_ms"], 1e9)
+    out["window_decode"] = {"workload": "64 decode lanes x 1 row at kv_len 32768, window 1024 + 4 sinks bitmaps, "
+                                        "H_q=32 H_kv=8 d=128, P=16", "steps": 5, "warmup": 1,
+                            "attended_kv_bytes": attended, "kv_bytes_if_unmasked": int(ww["kv_bytes_decode"]),
+                            "tile_bytes_upper_bound": tiles,
+                            "decode_ms": _stats(rw["decode_ms"]), "a4_ms": _stats(rw["a4_ms"]),
+                            "fp_attend_ms": _stats(rw["call_ms"]), "step_ms": _stats(rw["step_ms"]),
+                            "GB/s_attended": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del wlw
     wl4, w4, r4 = measure(W, runner, 4, seed, None, 5, 1)
     out["config4"] = {"workload": "config 4: " + WORKLOAD_TEXT[4], "steps": 5, "warmup": 1,
                       "decode": decode_windows(w4, r4, pk_hbm), "step_ms": _stats(r4["step_ms"]),
@@ -751,7 +766,8 @@ def measure(W, runner, cfg, seed, split, K, Wm, mass=None, flush=True, wl=None):
     (workload, work, dict of per-step millisecond lists and phase-1 totals)."""
     import torch
 
-    print(f"[bench] config {cfg} seed {seed}: {K} steps after {Wm} warm-ups", file=sys.stderr, flush=True)
+    print(f"[bench] config {cfg if wl is None else wl.name} seed {seed}: {K} steps after {Wm} warm-ups", file=sys.stderr,
+          flush=True)
     if wl is None:
         wl = W.make_config(cfg, seed=seed, scale="full")
     w = work(wl)

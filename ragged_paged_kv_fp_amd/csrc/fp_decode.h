@@ -302,7 +302,7 @@ struct DecShared {
 
 // One work item (lane, KV head, KV split): every barrier inside is reached by
 // all threads of the workgroup.
-template <int D, int NC>
+template <int D, int NC, bool MASKED>
 __device__ __forceinline__ void decode_item(const AttnArgs &a, const int4 it, DecShared<D, NC> &sh) {
     auto &s_ml = sh.ml;
     auto &s_fin = sh.fin;
@@ -334,45 +334,72 @@ __device__ __forceinline__ void decode_item(const AttnArgs &a, const int4 it, De
         w.m = kNegInf;
         w.l = 0.0f;
     }
-    const bool masked = a.mask_off && a.mask_off[lane + 1] > a.mask_off[lane];
+    constexpr bool masked = MASKED;  // a masked lane (the launch holds only those) walks its tile list
     const uint32_t *mrow = nullptr;
     int64_t wpr = 0;
-    if (masked) {
+    if constexpr (MASKED) {
         wpr = (a.mask_off[lane + 1] - a.mask_off[lane]) / nrows;
         mrow = a.mask_bits + a.mask_off[lane] + (colv ? (col / a.G) : 0) * wpr;
     }
     const int lim = !colv ? 0 : (masked ? kv.eff : min(a.slots[row] + 1, kv.eff));
-    const int jend = __builtin_amdgcn_readfirstlane(min(s1, wave_max_i(lim)));
-
-    // ---- stream this wave's tiles (every kDecWaves-th of the split). While
-    // tile c is computed, tile c+S is in flight and the page ids of c+2S are
-    // being read; a tile index past the wave's range maps to the wave's last
-    // real tile (a cache hit), so every load is unconditional and the
-    // compiler's memory waits only cover the data actually needed.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // Q has landed before the pipeline starts
+    // Tiles of this wave: without a tile list, every kDecWaves-th 32-slot tile
+    // of the split below the wave's furthest limit; with one (a masked lane,
+    // built by summary_kernel: only the tiles where some row of the lane may
+    // read a slot), every kDecWaves-th entry of the split's share of the list,
+    // each lane of the wave holding one entry.
     constexpr int kStep = 32 * kDecWaves;
     const int first = s0 + 32 * wv;
-    if (first < jend) {  // wave-uniform
-        const int last = first + kStep * ((jend - 1 - first) / kStep);
-        auto clampt = [&](int t) { return t <= last ? t : last; };
-        int cur = first;
+    int nsteps;
+    uint32_t ent = 0;
+    if constexpr (MASKED) {
+        const int32_t *lst = a.summary + li.sum_off;
+        const int p0 = s0 >> 5, p1 = (s1 + 31) >> 5;
+        const int pl = min(p0 + wv + kDecWaves * l, li.sum_stride - 2);  // stays inside the record
+        ent = (uint32_t)lst[1 + pl];
+        const int cnt = __builtin_amdgcn_readfirstlane(min(lst[0], p1));
+        nsteps = cnt > p0 + wv ? (cnt - p0 - wv + kDecWaves - 1) / kDecWaves : 0;
+    } else {
+        const int jend = __builtin_amdgcn_readfirstlane(min(s1, wave_max_i(lim)));
+        nsteps = first < jend ? (jend - 1 - first) / kStep + 1 : 0;
+    }
+
+    // ---- stream this wave's tiles. While tile i is computed, tile i+1 is in
+    // flight and the page ids of tile i+2 are being read; a step past the
+    // wave's last maps to its last tile (a cache hit), so every load is
+    // unconditional and the compiler's memory waits only cover the data
+    // actually needed.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // Q (and the list entries) have landed before the pipeline starts
+    // the pipeline over steps 0..ilast, the tile of step i starting at slot jof(i)
+    auto stream_tiles = [&](int ilast, auto jof) {
+        auto mword = [&](int j0) { return (masked && colv && (j0 >> 5) < wpr) ? mrow[j0 >> 5] : 0u; };
+        int i = 0;
         KvFrags<D> fa, fb;
-        TilePages pa = tile_pages<NC>(kv, clampt(cur));
-        TilePages pb = tile_pages<NC>(kv, clampt(cur + kStep));
-        tile_load<D, NC>(kv, clampt(cur), pa, fa);
-        pa = tile_pages<NC>(kv, clampt(cur + 2 * kStep));
+        TilePages pa = tile_pages<NC>(kv, jof(0));
+        TilePages pb = tile_pages<NC>(kv, jof(1));
+        tile_load<D, NC>(kv, jof(0), pa, fa);
+        pa = tile_pages<NC>(kv, jof(2));
         for (;;) {
-            tile_load<D, NC>(kv, clampt(cur + kStep), pb, fb);
-            pb = tile_pages<NC>(kv, clampt(cur + 3 * kStep));
-            uint32_t mw = (masked && colv && (cur >> 5) < wpr) ? mrow[cur >> 5] : 0u;
-            tile_compute<D>(fa, s_k[wv], cur, lim, mw, masked, w);
-            if (cur + kStep > last) break;
-            tile_load<D, NC>(kv, clampt(cur + 2 * kStep), pa, fa);
-            pa = tile_pages<NC>(kv, clampt(cur + 4 * kStep));
-            mw = (masked && colv && ((cur + kStep) >> 5) < wpr) ? mrow[(cur + kStep) >> 5] : 0u;
-            tile_compute<D>(fb, s_k[wv], cur + kStep, lim, mw, masked, w);
-            if (cur + 2 * kStep > last) break;
-            cur += 2 * kStep;
+            tile_load<D, NC>(kv, jof(i + 1), pb, fb);
+            pb = tile_pages<NC>(kv, jof(i + 3));
+            const int j0 = jof(i);
+            tile_compute<D>(fa, s_k[wv], j0, lim, mword(j0), masked, w);
+            if (i + 1 > ilast) break;
+            tile_load<D, NC>(kv, jof(i + 2), pa, fa);
+            pa = tile_pages<NC>(kv, jof(i + 4));
+            const int j1 = jof(i + 1);
+            tile_compute<D>(fb, s_k[wv], j1, lim, mword(j1), masked, w);
+            if (i + 2 > ilast) break;
+            i += 2;
+        }
+    };
+    if (nsteps > 0) {  // wave-uniform
+        const int ilast = nsteps - 1;
+        if constexpr (MASKED) {
+            stream_tiles(ilast, [&](int i) {
+                return 32 * (int)(__builtin_amdgcn_readlane(ent, i < ilast ? i : ilast) & 0x7FFFFFFFu);
+            });
+        } else {
+            stream_tiles(ilast, [&](int i) { return first + kStep * (i < ilast ? i : ilast); });
         }
     }
 
@@ -428,15 +455,15 @@ __device__ __forceinline__ void decode_item(const AttnArgs &a, const int4 it, De
     }
 }
 
-// One workgroup per work item of its column class's list. The hardware
-// dispatcher starts workgroups in launch order as others finish, so the long
-// items at the head of the list go first and the short partial splits set the
-// tail.
-template <int D, int NC>
+// One workgroup per work item of the launch's list (the decode items of the
+// pass's unmasked lanes, or of its masked lanes). The hardware dispatcher
+// starts workgroups in launch order as others finish, so the long items at
+// the head of the list go first and the short partial splits set the tail.
+template <int D, int NC, bool MASKED>
 __global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) DecShared<D, NC> sh;
     const int4 it = a.dec_list[blockIdx.x];
-    if (it.x >= 0) decode_item<D, NC>(a, it, sh);
+    if (it.x >= 0) decode_item<D, NC, MASKED>(a, it, sh);
 }
 
 // Combine the KV splits of one (decode lane, KV head), all its query

@@ -418,24 +418,24 @@ constexpr int kPreCols = 256;    // query row-heads per prefill workgroup (8 wav
 // Rows of one prefill work item: all GQA heads of those rows fill the workgroup.
 __host__ __device__ __forceinline__ int prefill_rows(int G) { return kPreCols / G; }
 
-constexpr int kDecodeCols16 = 16;  // decode lanes up to this many row-heads take the 16-column kernel
+constexpr int kDecodeCols16 = 16;  // passes whose decode lanes have at most this many row-heads run the 16-column kernel
 
 struct PlanArgs {
     const int32_t *indptr, *page_indptr, *kv_len;
     const int64_t *mask_off;  // nullable
     int L, H, G, P, split;
-    int64_t n_dec_host[2];  // decode items of each column class (<= 16, <= 32 row-heads)
+    int64_t n_dec_host[2];  // decode items of the unmasked lanes, of the masked lanes
     int64_t n_pre_host, sum_host, N_host;
     int ncols_host;
     int merge_host;     // the host allotted split-merge buffers
     LaneInfo *lane_info;
-    int4 *dec_items;   // class-0 items, then class-1 items: {lane, kv head, first slot, end slot}
+    int4 *dec_items;   // unmasked lanes' items, then masked lanes': {lane, kv head, first slot, end slot}
     int4 *pre_items;   // {lane, kv head, first local row, rows}
     int32_t *status;
 };
 
 struct LaneCounts {
-    int dec, pre, sum, nsplit, nrb, stride, ncols, cls;
+    int dec, pre, sum, nsplit, nrb, stride, ncols, cls;  // cls: 1 for a masked decode lane
 };
 
 __device__ __forceinline__ LaneCounts lane_counts(const PlanArgs &a, int l, int32_t *st) {
@@ -454,7 +454,11 @@ __device__ __forceinline__ LaneCounts lane_counts(const PlanArgs &a, int l, int3
         r.nsplit = cap > 0 ? (cap + a.split - 1) / a.split : 1;
         r.dec = a.H * r.nsplit;
         r.ncols = n * a.G;
-        r.cls = r.ncols <= kDecodeCols16 ? 0 : 1;
+        if (masked) {  // one tile list for the lane (all its rows); its items go to the masked launch
+            r.stride = (cap + 31) / 32 + 1;
+            r.sum = r.stride;
+            r.cls = 1;
+        }
     } else {
         r.nrb = (n + prefill_rows(a.G) - 1) / prefill_rows(a.G);
         r.pre = a.H * r.nrb;
@@ -498,16 +502,16 @@ __device__ __forceinline__ int block_excl_scan(int v, int *s_w, int *total) {
 }
 
 // Single workgroup: per-lane classification (decode if all rows x GQA heads fit
-// one MFMA tile, prefill otherwise; decode lanes in two column classes),
-// prefix offsets, and the work-item lists. The decode list holds the items of
-// column class 0 (<= 16 row-heads), then those of class 1 (<= 32); within a
-// class, first every split but each (lane, KV head)'s last, then the last
+// one MFMA tile, prefill otherwise), prefix offsets, and the work-item lists.
+// The decode list holds the items of the unmasked decode lanes, then those of
+// the masked ones (a launch each: masked lanes walk tile lists); within each
+// part, first every split but each (lane, KV head)'s last, then the last
 // splits (the partial ones), so that the long items are dispatched first. Split outputs are stored by (lane, KV head, split): lane_info's
 // dec_off counts every decode item of the lanes before, in lane order.
 __device__ __forceinline__ void plan_body(const PlanArgs &a) {
     __shared__ int s_pre[kMaxLanes + 1];    // prefill items before lane l
-    __shared__ int s_full[2][kMaxLanes + 1];  // non-last decode items of class c before lane l
-    __shared__ int s_nd[2][kMaxLanes + 1];    // decode lanes of class c before lane l
+    __shared__ int s_full[2][kMaxLanes + 1];  // non-last decode items of part c (unmasked, masked) before lane l
+    __shared__ int s_nd[2][kMaxLanes + 1];    // decode lanes of part c before lane l
     __shared__ int s_w[kPlanThreads / kWave];
     __shared__ int s_bad;
     const int tid = threadIdx.x;
@@ -556,7 +560,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
             else { of1 += c.dec - a.H; on1 += 1; }
         }
     }
-    const int n0 = Tf0 + a.H * Tn0, n1 = Tf1 + a.H * Tn1;  // decode items of each class
+    const int n0 = Tf0 + a.H * Tn0, n1 = Tf1 + a.H * Tn1;  // decode items of each part
     if (tid == 0) {
         s_pre[a.L] = Tp;
         s_full[0][a.L] = Tf0;
@@ -634,6 +638,8 @@ __global__ void __launch_bounds__(kRopeThreads) rope_q_kernel(RopeQArgs ra) { ro
 // ============================================================================ mask summary
 
 struct SummaryArgs {
+    int64_t n_pre;  // prefill items; workgroups past them take decode lane blockIdx.x - n_pre
+    int L;
     const int4 *pre_items;
     const LaneInfo *lane_info;
     const int32_t *indptr, *page_indptr, *kv_len;
@@ -644,7 +650,8 @@ struct SummaryArgs {
 };
 
 // Tile list of one row block of a masked prefill lane (the rows of one prefill
-// work item): the 32-slot KV tiles below kv_len in which some row of the block
+// work item), or of all rows of a masked decode lane: the 32-slot KV tiles
+// below kv_len in which some row of the block
 // has an allowed slot, in increasing order, each entry tagged in bit 31 when
 // every row of the block may read every slot of the tile. Record layout:
 // [count, entry 0, entry 1, ...]. The prefill kernel walks this list, so
@@ -653,17 +660,31 @@ constexpr int kSumThreads = 256;
 
 __global__ void __launch_bounds__(kSumThreads) summary_kernel(SummaryArgs a) {
     __shared__ int s_wc[kSumThreads / kWave];
-    const int4 it = a.pre_items[blockIdx.x];
-    if (it.x < 0 || it.y != 0) return;
-    const int l = it.x;
-    const LaneInfo li = a.lane_info[l];
-    if (li.sum_off < 0) return;
+    int l, rstart, nr;
+    LaneInfo li;
+    int32_t *rec;
+    if ((int64_t)blockIdx.x < a.n_pre) {  // a row block of a masked prefill lane (its KV head 0 item)
+        const int4 it = a.pre_items[blockIdx.x];
+        if (it.x < 0 || it.y != 0) return;
+        l = it.x;
+        li = a.lane_info[l];
+        if (li.sum_off < 0) return;
+        rstart = it.z;
+        nr = it.w;
+        rec = a.summary + li.sum_off + (int64_t)(rstart / prefill_rows(a.G)) * li.sum_stride;
+    } else {  // a masked decode lane: one list over all its rows
+        l = (int)(blockIdx.x - a.n_pre);
+        if (l >= a.L) return;
+        li = a.lane_info[l];
+        if (li.sum_off < 0 || li.dec_off < 0) return;
+        rstart = 0;
+        nr = a.indptr[l + 1] - a.indptr[l];
+        rec = a.summary + li.sum_off;
+    }
     const int nl = a.indptr[l + 1] - a.indptr[l];
     const int64_t wpr = (a.mask_off[l + 1] - a.mask_off[l]) / nl;
     const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
     const int eff = clamp_kv(a.kv_len[l], cap);
-    const int rstart = it.z, nr = it.w;
-    int32_t *rec = a.summary + li.sum_off + (int64_t)(rstart / prefill_rows(a.G)) * li.sum_stride;
     const uint32_t *rb = a.bits + a.mask_off[l] + (int64_t)rstart * wpr;
     // tiles holding slots below kv_len whose mask word exists (a short row reads 0 beyond its words)
     const int ntiles = (int)min((int64_t)((eff + 31) >> 5), wpr);

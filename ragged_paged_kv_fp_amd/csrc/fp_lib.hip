@@ -92,7 +92,7 @@ int check_mask(const fp_mask *m, const fp_geometry *g) {
 struct Plan {
     int L = 0, H = 0, G = 0, Hq = 0, D = 0, P = 0, split = 0, ncols_max = 1;
     int64_t N = 0, n_dec = 0, n_dec_cls[2] = {0, 0}, n_pre = 0, sum_words = 0;
-    bool merge = false, summaries = false;
+    bool merge = false, summaries = false, dec_lists = false, wide = false;
     size_t off_lane = 0, off_dec = 0, off_pre = 0, off_qrot = 0, off_po = 0, off_pml = 0, off_sum = 0;
     size_t total = 0;
 };
@@ -136,13 +136,13 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
         // decode workgroups resident at once, for the kernel the pass will run
         // (the 32-column kernel as soon as one decode lane has more than 16
         // query row-heads)
-        bool wide = false;
+        bool wide = false;  // (Plan::wide, known before the loop below fills it)
         for (int l = 0; l < geom->num_lanes; ++l) {
             const int n = geom->indptr_host[l + 1] - geom->indptr_host[l];
             if (n * G > kDecodeCols16 && n * G <= kDecodeCols) wide = true;
         }
-        const double slots = (double)(wide ? resident_blocks(decode_kernel<128, 32>, kDecThreads)
-                                           : resident_blocks(decode_kernel<128, 16>, kDecThreads));
+        const double slots = (double)(wide ? resident_blocks(decode_kernel<128, 32, false>, kDecThreads)
+                                           : resident_blocks(decode_kernel<128, 16, false>, kDecThreads));
         for (const int cand : kSplitChoices) {
             split = cand;
             int64_t items = 0;
@@ -171,9 +171,15 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
         if (n * G <= kDecodeCols) {
             const int nsplit = cap > 0 ? (cap + split - 1) / split : 1;
             p.n_dec += (int64_t)p.H * nsplit;
-            p.n_dec_cls[n * G <= kDecodeCols16 ? 0 : 1] += (int64_t)p.H * nsplit;
+            p.n_dec_cls[masked ? 1 : 0] += (int64_t)p.H * nsplit;
+            if (n * G > kDecodeCols16) p.wide = true;
             if (nsplit > 1) p.merge = true;
             if (n * G > p.ncols_max) p.ncols_max = n * G;
+            if (masked) {
+                p.sum_words += (cap + 31) / 32 + 1;
+                p.summaries = true;
+                p.dec_lists = true;
+            }
         } else {
             const int nrb = (n + prefill_rows(G) - 1) / prefill_rows(G);
             p.n_pre += (int64_t)p.H * nrb;
@@ -328,6 +334,8 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
 
     if (p.summaries) {
         SummaryArgs sa;
+        sa.n_pre = p.n_pre;
+        sa.L = p.L;
         sa.pre_items = pre_items;
         sa.lane_info = lane_info;
         sa.indptr = geom->indptr;
@@ -338,7 +346,8 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
         sa.P = p.P;
         sa.G = p.G;
         sa.summary = reinterpret_cast<int32_t *>(ws + p.off_sum);
-        hipLaunchKernelGGL(summary_kernel, dim3((unsigned)p.n_pre), dim3(kSumThreads), 0, stream, sa);
+        hipLaunchKernelGGL(summary_kernel, dim3((unsigned)(p.n_pre + (p.dec_lists ? p.L : 0))), dim3(kSumThreads), 0,
+                           stream, sa);
         if ((rc = launch_ok())) return rc;
     }
     if (tuning && tuning->attn_begin && hipEventRecord(tuning->attn_begin, stream) != hipSuccess) return FP_ERR_HIP;
@@ -348,21 +357,33 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
         if ((rc = launch_ok())) return rc;
     }
     if (tuning && tuning->prefill_end && hipEventRecord(tuning->prefill_end, stream) != hipSuccess) return FP_ERR_HIP;
-    // decode: lanes with up to 16 query row-heads run the 16-column kernel
-    // (two waves per SIMD); when the pass also has wider lanes, every decode
-    // item runs in one launch of the 32-column kernel: two launches would
-    // each pay their own start and tail, one after the other.
-    if (p.n_dec) {
-        const bool wide = p.n_dec_cls[1] > 0;
+    // decode: the 16-column kernel (two waves per SIMD) when every decode lane
+    // has at most 16 query row-heads, else the 32-column kernel for all of
+    // them (two launches of different widths would each pay their own start
+    // and tail, one after the other); the unmasked lanes' items in one
+    // launch, the masked lanes' (which walk tile lists) in a second
+    for (int part = 0; part < 2; ++part) {
+        const int64_t n = p.n_dec_cls[part];
+        if (n == 0) continue;
         AttnArgs ac = a;
-        ac.dec_list = dec_items;
-        const dim3 grid((unsigned)p.n_dec), block(kDecThreads);
+        ac.dec_list = dec_items + (part ? p.n_dec_cls[0] : 0);
+        const dim3 grid((unsigned)n), block(kDecThreads);
         if (p.D == 128) {
-            if (!wide) hipLaunchKernelGGL((decode_kernel<128, 16>), grid, block, 0, stream, ac);
-            else hipLaunchKernelGGL((decode_kernel<128, 32>), grid, block, 0, stream, ac);
+            if (!p.wide) {
+                if (part == 0) hipLaunchKernelGGL((decode_kernel<128, 16, false>), grid, block, 0, stream, ac);
+                else hipLaunchKernelGGL((decode_kernel<128, 16, true>), grid, block, 0, stream, ac);
+            } else {
+                if (part == 0) hipLaunchKernelGGL((decode_kernel<128, 32, false>), grid, block, 0, stream, ac);
+                else hipLaunchKernelGGL((decode_kernel<128, 32, true>), grid, block, 0, stream, ac);
+            }
         } else {
-            if (!wide) hipLaunchKernelGGL((decode_kernel<64, 16>), grid, block, 0, stream, ac);
-            else hipLaunchKernelGGL((decode_kernel<64, 32>), grid, block, 0, stream, ac);
+            if (!p.wide) {
+                if (part == 0) hipLaunchKernelGGL((decode_kernel<64, 16, false>), grid, block, 0, stream, ac);
+                else hipLaunchKernelGGL((decode_kernel<64, 16, true>), grid, block, 0, stream, ac);
+            } else {
+                if (part == 0) hipLaunchKernelGGL((decode_kernel<64, 32, false>), grid, block, 0, stream, ac);
+                else hipLaunchKernelGGL((decode_kernel<64, 32, true>), grid, block, 0, stream, ac);
+            }
         }
         if ((rc = launch_ok())) return rc;
     }

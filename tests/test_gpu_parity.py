@@ -80,6 +80,20 @@ def test_explicit_slot_geometry(seed, H_kv, G, d, P, kinds, masked):
     _say(pu.compare_step(ds, ref))
 
 
+@pytest.mark.parametrize("seed,L,kv,window,sinks,P", [(0, 4, 32768, 1024, 4, 16), (1, 3, 30001, 1000, 3, 32),
+                                                       (2, 5, 5000, 77, 0, 8)])
+def test_window_decode_lanes_walk_tile_lists(seed, L, kv, window, sinks, P):
+    """Masked decode lanes read only the tiles their bitmap touches (Docs,
+    Attention masks: sliding window with attention sinks): at kv_len 32768 a
+    window of 1024 plus 4 sinks is 33 of 1024 tiles. The slots in between are
+    holes the prefix never wrote; the result equals the oracle's."""
+    wl = W.make_window_decode(seed, L=L, kv=kv, window=window, sinks=sinks, H_q=16, H_kv=4, d=128, P=P)
+    _say(f"window decode seed {seed}: lanes={L} kv={kv} window={window} sinks={sinks} P={P}")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)
+    _say(pu.compare_step(ds, ref))
+
+
 def _hazard_bits(wl):
     """fp_check_hazards on the GPU and oracle.hazards, both after the prefix pass and its fold."""
     import torch

@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     Lora,
     make_config,
     make_explicit,
+    make_window_decode,
     make_lora,
     make_random,
     make_run_ahead,

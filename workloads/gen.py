@@ -656,3 +656,33 @@ def make_explicit(seed: int, *, H_kv: int = 2, G: int = 2, d: int = 64, P: int =
     if N:
         wl.readout_rows = rngs["channel"].integers(0, N, size=int(rngs["channel"].integers(1, 2 * L + 1))).astype(np.int32)
     return wl
+
+
+def make_window_decode(seed: int, *, L: int = 64, kv: int = 32768, window: int = 1024, sinks: int = 4,
+                       H_q: int = 32, H_kv: int = 8, d: int = 128, P: int = 16) -> Workload:
+    """A decode wave under a sliding window with attention sinks (Docs,
+    Attention masks), the StreamingLLM shape: L lanes of one row at slot
+    kv - 1 (position kv - 1) whose bitmap allows slots j < sinks and the
+    window kv - window < j <= kv - 1. The prefix pass writes only the slots
+    the rows may read (sinks and window, positions = slots, nothing frozen);
+    the others are holes that keep the pool's fill. Lane order and physical
+    pages are permuted as in the configurations."""
+    rngs = _rngs(seed)
+    read = np.concatenate([np.arange(sinks), np.arange(kv - window, kv - 1)]).astype(np.int64)
+    n_pre = len(read)
+    lanes = [dict(c=0, n=1, kv_len=kv, fold=FOLD_ALL, pos_of_slot=_ident_pos(kv),
+                  mask=dict(kind="window", window=window, sinks=sinks)) for _ in range(L)]
+    wl = _assemble(f"window_decode_{L}x{kv}", rngs, H_q=H_q, H_kv=H_kv, d=d, P=P, lanes=lanes,
+                   mask_fn=_make_mask)
+    # the step's single row sits at slot kv - 1; the prefix writes the readable slots only
+    st = wl.step
+    st.slots = np.full(L, kv - 1, dtype=np.int32)
+    st.positions = np.full(L, kv - 1, dtype=np.int32)
+    wl.mask_bits, wl.mask_word_offset = _bitmap_rows(lanes, st, rngs["mask"])
+    pre_indptr = (np.arange(L + 1, dtype=np.int64) * n_pre).astype(np.int32)
+    wl.prefix = Pass(indptr=pre_indptr, positions=np.tile(read, L).astype(np.int32),
+                     slots=np.tile(read, L).astype(np.int32), kv_len=np.full(L, kv, dtype=np.int32),
+                     fold=np.zeros(L, dtype=np.int32), k=_normal_bf16(rngs["prefix_kv"], (L * n_pre, H_kv, d)),
+                     v=_normal_bf16(rngs["prefix_kv"], (L * n_pre, H_kv, d)))
+    wl.meta.update(window=window, sinks=sinks)
+    return wl
