@@ -43,8 +43,8 @@ struct PreLds {
     static constexpr int V_BYTES = D * VROW;
     static constexpr int MW_OFF = K_BYTES + V_BYTES;  // mask words of the block's rows (masked lanes)
     static constexpr int STAGE = MW_OFF + 4 * 256;
-    static constexpr int LUT_OFF = kPreStages * STAGE;  // [256][4] uint32: bf16 keep masks of a mask byte
-    static constexpr int AOP_OFF = LUT_OFF + 256 * 16;   // [2][64] uint4: A operands of the bias MFMAs
+    static constexpr int LUT_OFF = kPreStages * STAGE;  // [16][2] uint32: bf16 keep masks of a mask nibble
+    static constexpr int AOP_OFF = LUT_OFF + 16 * 8;     // [2][64] uint4: A operands of the bias MFMAs
     static constexpr int TOTAL = AOP_OFF + 2 * 64 * 16;
 };
 
@@ -171,8 +171,9 @@ __device__ __forceinline__ uint32_t neg_m2(const PreWave<D> &w) {
 //    is the slot permutation of the score rows (row m holds slot
 //    kslot_of_row(m), so A[m][k] = (kslot_of_row(m) == k)) and whose B operand
 //    holds -m for a slot the row may read and -2^126 for one it may not. The
-//    B operand is built from the row's mask bytes through a 256-entry table
-//    of bf16 keep masks in LDS.
+//    B operand is built from the row's mask bytes, a nibble at a time,
+//    through a 16-entry table of bf16 keep masks in LDS (128 bytes: the
+//    entries sit in distinct banks, so the lanes' lookups never conflict).
 // A score the row may not read then sits near -2^126 and its weight is 0; the
 // column max of a tile therefore covers allowed slots only. Slots at or past
 // kv_len can hold stale K (even NaN), so the one tile that crosses kv_len
@@ -206,7 +207,10 @@ struct MaskBias {
         const int ln = lane_id(), kg = ln >> 5;
         if (k == 0) bits = full ? 0xFFFFFFFFu : (bits & lm);
         // B lane (n, kg) of MFMA k holds slots 16k + 8kg .. 16k + 8kg + 7
-        b = *reinterpret_cast<const uint4 *>(lds + lut_off + 16 * ((bits >> (16 * k + 8 * kg)) & 0xFFu));
+        const uint32_t byte = (bits >> (16 * k + 8 * kg)) & 0xFFu;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(lds + lut_off + 8 * (byte & 15u));
+        const uint2 hi = *reinterpret_cast<const uint2 *>(lds + lut_off + 8 * (byte >> 4));
+        b = make_uint4(lo.x, lo.y, hi.x, hi.y);
         a = *reinterpret_cast<const uint4 *>(lds + aop_off + 1024 * k + 16 * ln);
     }
     __device__ __forceinline__ void build() { b = make_uint4(bfi(b.x), bfi(b.y), bfi(b.z), bfi(b.w)); }
@@ -214,12 +218,12 @@ struct MaskBias {
     __device__ __forceinline__ f32x16 apply(f32x16 acc, int) const { return mfma32(a, b, acc); }
 };
 
-// Fills the keep-mask table (entry e: word q keeps bf16 half 0 if bit 2q of e
-// is set and half 1 if bit 2q+1 is) and the A operands of MaskBias.
+// Fills the keep-mask table (entry e, a nibble: word q keeps bf16 half 0 if
+// bit 2q of e is set and half 1 if bit 2q+1 is) and the A operands of MaskBias.
 template <int D>
 __device__ __forceinline__ void fill_bias_tables(char *lds) {
-    for (int wi = threadIdx.x; wi < 256 * 4; wi += kPreThreads) {
-        const int e = wi >> 2, q = wi & 3;
+    for (int wi = threadIdx.x; wi < 16 * 2; wi += kPreThreads) {
+        const int e = wi >> 1, q = wi & 1;
         const uint32_t v = (((e >> (2 * q)) & 1) ? 0x0000FFFFu : 0u) | (((e >> (2 * q + 1)) & 1) ? 0xFFFF0000u : 0u);
         reinterpret_cast<uint32_t *>(lds + PreLds<D>::LUT_OFF)[wi] = v;
     }
