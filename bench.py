@@ -673,11 +673,16 @@ def frame_bench(W, runner, seed, K, Wm) -> dict:
     A, B = W.split_pass(wl.step, first)
     ds = runner.DeviceStep(wl, device="cuda")
     ds.run_prefix()
-    fr = runner.Frame(ds.pool, [A, B], wl.H_q, wl.theta, wl.sm_scale)
+    frames = {"eager": runner.Frame(ds.pool, [A, B], wl.H_q, wl.theta, wl.sm_scale),
+              "vertical": runner.Frame(ds.pool, [A, B], wl.H_q, wl.theta, wl.sm_scale, vertical=True)}
+    frames["graph"] = frames["eager"]
+    frames["vertical_graph"] = frames["vertical"]
+    assert len(frames["vertical"].items) == 1
     res = {}
-    for mode in ("eager", "graph"):
-        go = fr.run if mode == "eager" else fr.replay
-        if mode == "graph":
+    for mode in ("eager", "graph", "vertical", "vertical_graph"):
+        fr = frames[mode]
+        go = fr.replay if mode.endswith("graph") else fr.run
+        if mode.endswith("graph"):
             fr.capture()
         for _ in range(Wm):
             go()
@@ -692,8 +697,9 @@ def frame_bench(W, runner, seed, K, Wm) -> dict:
         torch.cuda.synchronize()
         res[mode] = {"device_ms_per_frame": round(e0.elapsed_time(e1) / K, 4),
                      "host_ms_per_frame": round((h1 - h0) * 1e3 / K, 4)}
-    st = int(fr.status.cpu()[0])
-    return {"metric": "two-pass frame (prefix pass + continuation), eager vs one HIP-graph replay",
+    st = int(frames["eager"].status.cpu()[0]) | int(frames["vertical"].status.cpu()[0])
+    return {"metric": "two-pass frame (prefix pass + continuation): eager and one HIP-graph replay, each as two "
+                      "passes and vertically batched into one pass (fp_vertical_merge)",
             "config": {"workload": "config 3 split per lane at a random row: " + WORKLOAD_TEXT[3], "seed": seed,
                        "rows": [A.num_rows, B.num_rows]},
             "steps": K, "warmup": Wm, "status": st, **res}

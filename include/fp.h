@@ -363,6 +363,48 @@ int fp_adapter_lora(const fp_geometry *geom, const fp_lora *lora, const int32_t 
 int fp_adapter_ia3(const fp_geometry *geom, int32_t num_adapters, int32_t d_out, const void *scale,
                    const int32_t *adapter, const void *y, void *out, int32_t *status, hipStream_t stream);
 
+/*
+ * fp_vertical_merge - vertical batching of a frame (the reviews' section 5:
+ * a prefix forward and its continuation can be combined into one dispatch
+ * when their order is preserved inside it; Docs, Pipelines and frames:
+ * submit_frame runs passes back to back). Host-only: from the host copies of
+ * two consecutive passes A then B over the same lanes and pool, decide
+ * whether one pass M does exactly what A then B do, and if so describe M.
+ *
+ * Eligible when, for every lane l with c = committed[l] (before A), nA / nB
+ * rows in A / B and capacity cap = (page_indptr_host[l+1] -
+ * page_indptr_host[l]) * page_size:
+ *   - A's rows take slots c, c+1, ..., c+nA-1 in order (rows appended
+ *     causally after the frozen prefix), and A folds all of them (FP_FOLD_ALL
+ *     or the literal nA), so B's rows see them as frozen history;
+ *   - every B slot is >= c + nA (B never rewrites what A froze);
+ *   - A's and B's kv_len lie in [0, cap], A's covers its rows (>= c + nA) and,
+ *     when B has rows, so does B's (the merged pass reads B's kv_len);
+ *   - B folds all its rows or a literal count in [0, nB];
+ *   - no lane carries a mask (the caller passes passes without bitmaps).
+ * Then M has, per lane, A's rows followed by B's, kv_len = B's (A's if B has
+ * no rows), and fold = FP_FOLD_ALL if B folds all, else the literal nA + k.
+ * Under the causal rule an A row reads j <= its slot, none of B's slots, and a
+ * B row reads A's slots as freshly appended K/V: the same attention as A then
+ * B, in one append and one attend.
+ *
+ * Inputs (host arrays): L lanes; indptr_a/indptr_b [L+1]; slots_a [NA],
+ * slots_b [NB]; kv_len_a/kv_len_b/fold_a/fold_b [L]; committed [L];
+ * page_indptr_host [L+1]; page_size.
+ * Outputs (host arrays, written only when eligible): indptr_m [L+1];
+ * src_row [NA+NB]: merged row i is row src_row[i] of A if < NA, else row
+ * src_row[i] - NA of B; row_of_a [NA], row_of_b [NB]: merged row of each
+ * input row (for readout lists); kv_len_m, fold_m [L]. Positions, slots and
+ * K/V/Q rows of M are A's and B's gathered by src_row.
+ * Returns FP_OK when eligible, 1 when not (outputs untouched), FP_ERR_NULL /
+ * FP_ERR_SHAPE for bad arguments.
+ */
+int fp_vertical_merge(int32_t L, const int32_t *indptr_a, const int32_t *slots_a, const int32_t *kv_len_a,
+                      const int32_t *fold_a, const int32_t *indptr_b, const int32_t *slots_b,
+                      const int32_t *kv_len_b, const int32_t *fold_b, const int32_t *committed,
+                      const int32_t *page_indptr_host, int32_t page_size, int32_t *indptr_m, int32_t *src_row,
+                      int32_t *row_of_a, int32_t *row_of_b, int32_t *kv_len_m, int32_t *fold_m);
+
 /* ---- host-only accounting (Pie reviews, Eq. (1) and Eq. (2)) ---- */
 uint64_t fp_kv_bytes(int32_t L, int32_t H_kv, int32_t d, uint64_t T, int32_t b); /* 2*L*H_kv*d*T*b   */
 uint64_t fp_pages_for(uint64_t T, int32_t P);                                   /* ceil(T/P)        */

@@ -512,7 +512,7 @@ def step(pool: Pool, committed, geom, H_q, theta, sm_scale, mask_bits=None, word
     res = dict(O=O, LSE=LSE, committed=new_c, status=st | st_a | st_f)
     if rows is None:
         rl = readout_rows(geom.indptr, readout_list)
-        ro, st_r = readout(O.reshape(O.shape[0], -1), int(geom.indptr[-1]), rl)
+        ro, st_r = readout(O.reshape(O.shape[0], O.shape[1] * O.shape[2]), int(geom.indptr[-1]), rl)
         res.update(readout=ro, readout_rows=rl)
         res["status"] |= st_r
     return res

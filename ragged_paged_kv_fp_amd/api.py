@@ -277,6 +277,32 @@ def advance(pool: Pool, geom: Geometry, pos_offset: Optional[torch.Tensor] = Non
                                         _ptr(geom.slots), _ptr(geom.kv_len), _stream(stream)))
 
 
+def vertical_merge(a, b, committed: np.ndarray, page_indptr_host: np.ndarray, page_size: int):
+    """fp_vertical_merge on host copies of two consecutive passes a, b (objects
+    with indptr, slots, kv_len, fold as numpy int32 arrays). Returns None when
+    one pass cannot do what a then b do, else a dict with the merged pass's
+    indptr, kv_len, fold and the row maps src_row, row_of_a, row_of_b."""
+    lib = _lib.load()
+    L = int(len(a.indptr) - 1)
+    i32 = lambda x: np.ascontiguousarray(x, dtype=np.int32)  # noqa: E731
+    ia, sa, ka, fa = i32(a.indptr), i32(a.slots), i32(a.kv_len), i32(a.fold)
+    ib, sb, kb, fb = i32(b.indptr), i32(b.slots), i32(b.kv_len), i32(b.fold)
+    c, pp = i32(committed), i32(page_indptr_host)
+    NA, NB = int(ia[-1]), int(ib[-1])
+    out = dict(indptr=np.zeros(L + 1, np.int32), src_row=np.zeros(max(NA + NB, 1), np.int32),
+               row_of_a=np.zeros(max(NA, 1), np.int32), row_of_b=np.zeros(max(NB, 1), np.int32),
+               kv_len=np.zeros(L, np.int32), fold=np.zeros(L, np.int32))
+    rc = lib.fp_vertical_merge(L, _hptr(ia), _hptr(sa), _hptr(ka), _hptr(fa), _hptr(ib), _hptr(sb), _hptr(kb),
+                               _hptr(fb), _hptr(c), _hptr(pp), int(page_size), _hptr(out["indptr"]),
+                               _hptr(out["src_row"]), _hptr(out["row_of_a"]), _hptr(out["row_of_b"]),
+                               _hptr(out["kv_len"]), _hptr(out["fold"]))
+    if rc == 1:
+        return None
+    _check("fp_vertical_merge", rc)
+    out["src_row"], out["row_of_a"], out["row_of_b"] = out["src_row"][:NA + NB], out["row_of_a"][:NA], out["row_of_b"][:NB]
+    return out
+
+
 def kv_bytes(L: int, H_kv: int, d: int, T: int, b: int) -> int:
     return int(_lib.load().fp_kv_bytes(L, H_kv, d, T, b))
 

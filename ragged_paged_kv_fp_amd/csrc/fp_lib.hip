@@ -733,6 +733,55 @@ int fp_advance(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *p
     return launch_ok();
 }
 
+int fp_vertical_merge(int32_t L, const int32_t *indptr_a, const int32_t *slots_a, const int32_t *kv_len_a,
+                      const int32_t *fold_a, const int32_t *indptr_b, const int32_t *slots_b,
+                      const int32_t *kv_len_b, const int32_t *fold_b, const int32_t *committed,
+                      const int32_t *page_indptr_host, int32_t page_size, int32_t *indptr_m, int32_t *src_row,
+                      int32_t *row_of_a, int32_t *row_of_b, int32_t *kv_len_m, int32_t *fold_m) {
+    if (!indptr_a || !indptr_b || !kv_len_a || !kv_len_b || !fold_a || !fold_b || !committed || !page_indptr_host ||
+        !indptr_m || !src_row || !row_of_a || !row_of_b || !kv_len_m || !fold_m)
+        return FP_ERR_NULL;
+    if (L < 1 || page_size < 1 || indptr_a[0] != 0 || indptr_b[0] != 0) return FP_ERR_SHAPE;
+    for (int l = 0; l < L; ++l)
+        if (indptr_a[l + 1] < indptr_a[l] || indptr_b[l + 1] < indptr_b[l]) return FP_ERR_SHAPE;
+    const int32_t NA = indptr_a[L], NB = indptr_b[L];
+    if ((NA > 0 && !slots_a) || (NB > 0 && !slots_b)) return FP_ERR_NULL;
+    // eligibility first: nothing is written unless every lane qualifies
+    for (int l = 0; l < L; ++l) {
+        const int a0 = indptr_a[l], na = indptr_a[l + 1] - a0;
+        const int b0 = indptr_b[l], nb = indptr_b[l + 1] - b0;
+        const int64_t c = committed[l];
+        const int64_t cap = (int64_t)(page_indptr_host[l + 1] - page_indptr_host[l]) * page_size;
+        if (kv_len_a[l] < 0 || kv_len_a[l] > cap || kv_len_b[l] < 0 || kv_len_b[l] > cap) return 1;
+        if (!(fold_a[l] == FP_FOLD_ALL || fold_a[l] == na)) return 1;
+        if (!(fold_b[l] == FP_FOLD_ALL || (fold_b[l] >= 0 && fold_b[l] <= nb))) return 1;
+        for (int i = 0; i < na; ++i)
+            if (slots_a[a0 + i] != c + i) return 1;
+        if (na > 0 && kv_len_a[l] < c + na) return 1;
+        if (nb > 0 && na > 0 && kv_len_b[l] < c + na) return 1;
+        for (int i = 0; i < nb; ++i)
+            if (slots_b[b0 + i] < c + na) return 1;
+    }
+    indptr_m[0] = 0;
+    for (int l = 0; l < L; ++l) {
+        const int a0 = indptr_a[l], na = indptr_a[l + 1] - a0;
+        const int b0 = indptr_b[l], nb = indptr_b[l + 1] - b0;
+        int m = indptr_m[l];
+        for (int i = 0; i < na; ++i, ++m) {
+            src_row[m] = a0 + i;
+            row_of_a[a0 + i] = m;
+        }
+        for (int i = 0; i < nb; ++i, ++m) {
+            src_row[m] = NA + b0 + i;
+            row_of_b[b0 + i] = m;
+        }
+        indptr_m[l + 1] = m;
+        kv_len_m[l] = nb > 0 ? kv_len_b[l] : kv_len_a[l];
+        fold_m[l] = fold_b[l] == FP_FOLD_ALL ? FP_FOLD_ALL : na + fold_b[l];
+    }
+    return FP_OK;
+}
+
 uint64_t fp_kv_bytes(int32_t L, int32_t H_kv, int32_t d, uint64_t T, int32_t b) {
     return 2ull * (uint64_t)L * (uint64_t)H_kv * (uint64_t)d * T * (uint64_t)b;
 }

@@ -197,10 +197,75 @@ class RunAheadLoop:
         return K, V
 
 
+class _Rows:
+    """Host description of one pass (the fields the ABI calls take)."""
+
+    def __init__(self, indptr, positions, slots, kv_len, fold, k, v, q):
+        self.indptr, self.positions, self.slots = indptr, positions, slots
+        self.kv_len, self.fold, self.k, self.v, self.q = kv_len, fold, k, v, q
+
+    @property
+    def num_lanes(self) -> int:
+        return int(self.indptr.shape[0] - 1)
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.indptr[-1])
+
+
+def _committed_after(c: np.ndarray, p) -> Optional[np.ndarray]:
+    """Committed lengths after pass p's fold, when they follow from its host
+    arrays (all or a literal count; a channel count is only known on the device)."""
+    n = np.diff(p.indptr).astype(np.int64)
+    f = np.asarray(p.fold, dtype=np.int64)
+    if np.any(f < -1):
+        return None
+    k = np.where(f == -1, n, np.clip(f, 0, n))
+    return (c.astype(np.int64) + k).astype(np.int32)
+
+
+def vertical_groups(passes, committed0: np.ndarray, page_indptr_host: np.ndarray, page_size: int):
+    """Vertical batching of a frame (the reviews' section 5: a prefix forward
+    and its continuation combined into one dispatch, order kept inside it):
+    consecutive passes are merged greedily for as long as fp_vertical_merge
+    finds the merged pass equivalent. Returns a list of groups, each a dict
+    with the pass to run ('pass') and, per original pass of the group, its
+    index and the merged rows of its rows ('parts': [(index, rows)])."""
+    groups = []
+    c_next = np.asarray(committed0, dtype=np.int32)  # committed lengths before the next group (None: unknown)
+    cur, c_cur = None, None
+    for idx, p in enumerate(passes):
+        if cur is not None and c_cur is not None:
+            m = api.vertical_merge(cur["pass"], p, c_cur, page_indptr_host, page_size)
+            if m is not None:
+                a = cur["pass"]
+                pick = lambda x, y: np.concatenate([x, y])[m["src_row"]]  # noqa: E731
+                cur["pass"] = _Rows(m["indptr"], pick(a.positions, p.positions), pick(a.slots, p.slots), m["kv_len"],
+                                    m["fold"], pick(a.k, p.k), pick(a.v, p.v), pick(a.q, p.q))
+                cur["parts"] = [(i, m["row_of_a"][rows]) for i, rows in cur["parts"]] + [(idx, m["row_of_b"])]
+                continue
+        if cur is not None:
+            groups.append(cur)
+            c_next = None if c_cur is None else _committed_after(c_cur, cur["pass"])
+        cur = {"pass": _Rows(np.asarray(p.indptr, np.int32), p.positions, p.slots, p.kv_len, p.fold, p.k, p.v, p.q),
+               "parts": [(idx, np.arange(p.num_rows, dtype=np.int32))]}
+        c_cur = c_next
+    if cur is not None:
+        groups.append(cur)
+    return groups
+
+
 class Frame:
     """Several passes over one pool submitted back to back (Pie's submit_frame:
     passes in consecutive scheduler waves, in order), each pass being the four
     ABI calls with its own geometry, inputs and outputs.
+
+    With vertical=True, consecutive passes that one pass can replace exactly
+    (fp_vertical_merge: a prefix and its continuation on the same lanes) are
+    merged first, so the frame issues one append and one attend for them; the
+    readout rows of every original pass are gathered by the merged pass's
+    explicit readout list, and parts()/readout_of() map the merged outputs
+    back to the original passes.
 
     run() enqueues the whole frame eagerly; capture() records it once into a
     HIP graph and replay() then submits it with one launch from the host. The
@@ -208,21 +273,36 @@ class Frame:
     replayed; that restore is a device-to-device copy, not a memset.
     """
 
-    def __init__(self, pool: api.Pool, passes, H_q: int, theta: float, sm_scale: float, device="cuda"):
+    def __init__(self, pool: api.Pool, passes, H_q: int, theta: float, sm_scale: float, device="cuda",
+                 vertical: bool = False):
         self.pool = pool
         self.H_q, self.theta, self.sm_scale = H_q, float(theta), float(sm_scale)
         dev = torch.device(device)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.committed0 = pool.committed_len.clone()
+        if vertical:
+            groups = vertical_groups(passes, self.committed0.cpu().numpy(), pool.page_indptr_host, pool.page_size)
+        else:
+            groups = [{"pass": p, "parts": [(i, np.arange(p.num_rows, dtype=np.int32))]} for i, p in enumerate(passes)]
         self.items = []
-        for p in passes:
+        for grp in groups:
+            p = grp["pass"]
             g = _geometry(p, dev)
             N = p.num_rows
             it = dict(geom=g, k=_bits16(p.k, dev), v=_bits16(p.v, dev), q=_bits16(p.q, dev),
                       out=torch.zeros((N, H_q, pool.head_dim), dtype=torch.float32, device=dev),
-                      lse=torch.zeros((N, H_q), dtype=torch.float32, device=dev),
-                      dst=torch.zeros((int((np.diff(p.indptr) > 0).sum()), H_q * pool.head_dim),
-                                      dtype=torch.float32, device=dev))
+                      lse=torch.zeros((N, H_q), dtype=torch.float32, device=dev), parts=grp["parts"])
+            # readout: every original pass's default rows (the last row of each lane it has rows in)
+            rl, spans = [], []
+            for idx, rows in grp["parts"]:
+                ip = np.asarray(passes[idx].indptr, dtype=np.int64)
+                last = (ip[1:] - 1)[np.diff(ip) > 0]
+                spans.append((idx, len(rl), len(rl) + len(last)))
+                rl.extend(rows[last].tolist())
+            it["readout_rows"] = None if len(grp["parts"]) == 1 else _dev(np.asarray(rl, np.int32), dev)
+            it["spans"] = spans
+            it["dst"] = torch.zeros((max(len(rl), 1), H_q * pool.head_dim), dtype=torch.float32, device=dev)
+            it["nro"] = len(rl)
             ws = api.attend_workspace_bytes(pool, g, H_q)
             it["ws"] = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
             self.items.append(it)
@@ -236,7 +316,24 @@ class Frame:
             api.attend(self.pool, g, it["q"], self.H_q, self.theta, self.sm_scale, it["out"], it["ws"], self.status,
                        it["lse"])
             api.fold(self.pool, g, self.status)
-            api.readout(g, it["out"], it["dst"], self.status)
+            api.readout(g, it["out"], it["dst"][:it["nro"]], self.status, it["readout_rows"])
+
+    def parts(self):
+        """(original pass index, its rows' out, its rows' lse) for every original pass, in frame order."""
+        res = []
+        for it in self.items:
+            for idx, rows in it["parts"]:
+                r = torch.from_numpy(rows.astype(np.int64)).to(it["out"].device)
+                res.append((idx, it["out"][r], it["lse"][r]))
+        return sorted(res, key=lambda x: x[0])
+
+    def readout_of(self, idx: int) -> torch.Tensor:
+        """The readout rows of original pass idx (its default: last row of each lane with rows)."""
+        for it in self.items:
+            for j, lo, hi in it["spans"]:
+                if j == idx:
+                    return it["dst"][lo:hi]
+        raise KeyError(idx)
 
     def capture(self) -> None:
         torch.cuda.synchronize()

@@ -81,3 +81,52 @@ def test_frame_prefix_and_continuation(cfg, seed):
             assert torch.equal(o, it["out"]) and torch.equal(l, it["lse"]) and torch.equal(d, it["dst"]), rep
         assert torch.equal(pool0, ds.pool_t)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cfg,seed", [(1, 0), (3, 2), (3, 5), (2, 1)])
+def test_vertical_frame_one_pass(cfg, seed):
+    """The same split frame with vertical batching: the prefix pass and its
+    continuation run as one pass (one append, one attend); outputs equal the
+    oracle's whole pass, the stored K/V and committed lengths equal it bit for
+    bit, each original pass's readout rows are its default ones, and the
+    merged frame replayed from a HIP graph reproduces the eager one."""
+    import torch
+
+    from ragged_paged_kv_fp_amd import runner
+
+    wl = W.make_config(cfg, seed=seed, scale="small" if cfg > 1 else "full")
+    st = wl.step
+    rng = np.random.default_rng(seed)
+    first = np.array([int(rng.integers(0, m + 1)) for m in np.diff(st.indptr)])
+    A, B = W.split_pass(st, first)
+    a_rows, b_rows = _split_rows(st, first)
+    ref = pu.oracle_run(wl)
+    ds = runner.DeviceStep(wl)
+    ds.run_prefix()
+    fr = runner.Frame(ds.pool, [A, B], wl.H_q, wl.theta, wl.sm_scale, vertical=True)
+    assert len(fr.items) == 1, "prefix + continuation should merge into one pass"
+    fr.run()
+    torch.cuda.synchronize()
+    O = np.zeros((st.num_rows, wl.H_q, wl.d))
+    L = np.zeros((st.num_rows, wl.H_q))
+    parts = fr.parts()
+    for (idx, out, lse), rows in zip(parts, (a_rows, b_rows)):
+        O[rows] = out.cpu().numpy()
+        L[rows] = lse.cpu().numpy()
+    pu.compare_arrays(O, L, ref["O"], ref["LSE"])
+    ds.geom = fr.items[0]["geom"]
+    pu.compare_pool(ds, ref)
+    assert ds.pool.committed_len.cpu().numpy().tolist() == ref["committed"].tolist()
+    assert int(fr.status.cpu()[0]) == 0
+    for idx, out, _ in parts:
+        p = (A, B)[idx]
+        ip = np.asarray(p.indptr, np.int64)
+        last = (ip[1:] - 1)[np.diff(ip) > 0]
+        assert torch.equal(fr.readout_of(idx), out.reshape(out.shape[0], -1)[torch.as_tensor(last, device=out.device)])
+    eager = (fr.items[0]["out"].clone(), fr.items[0]["lse"].clone(), fr.items[0]["dst"].clone())
+    fr.capture()
+    for rep in range(3):
+        fr.items[0]["out"].zero_()
+        fr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(eager[0], fr.items[0]["out"]) and torch.equal(eager[2], fr.items[0]["dst"]), rep
