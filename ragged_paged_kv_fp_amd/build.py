@@ -35,6 +35,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# The host code (validation, planning, accounting, frame merging) built with
+# AddressSanitizer and UndefinedBehaviorSanitizer for the CPU tests; device
+# code is compiled as usual and never instrumented.
+ASAN_LIB = os.path.join(HERE, "libfp_hostsan.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     return os.path.join(rocm, "bin", "hipcc")
@@ -73,6 +81,32 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Compile libfp_hostsan.so: libfp.so with its host code under ASan + UBSan."""
+    tmp = ASAN_LIB + ".tmp"
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1"]
+    cmd = [hipcc()] + flags + SANITIZE_FLAGS + [f'-DFP_SOURCE_HASH="{source_hash()}"',
+                                                "-I", os.path.join(ROOT, "include")] + SOURCES + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libfp_hostsan.so")
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime (preloaded into the process that loads libfp_hostsan.so)."""
+    res = subprocess.run([os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang"),
+                          "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang's AddressSanitizer runtime was not found")
+    return path
 
 
 if __name__ == "__main__":

@@ -9,10 +9,12 @@ and query head with any readable slot contributes exactly one unit) on the
 full-size prefill configurations; determinism and accumulation.
 
 Tolerance: the GPU scores use fp_attend's rotated query, prescaled and rounded
-to bf16 (relative error up to 2^-9 per element), so each probability carries a
-relative error of a few times 2^-9 times the score's magnitude; per-slot sums
-are compared with |gpu - ref| <= 2e-2 * ref + 1e-3 * G, and the whole buffer
-by relative L2 <= 1e-2.
+to bf16 (relative error up to 2^-9 per element), so each score is off by at
+most about 2^-9 times the sum of |q_i k_i|, a few times 2^-9 for these
+N(0, 1) inputs, and each probability by that much relatively: per-slot sums
+are compared with |gpu - ref| <= 1e-2 * ref + 5e-4 * G (1e-2 is about
+5 * 2^-9; the absolute term covers sums of many tiny probabilities), and the
+whole buffer by relative L2 <= 5e-3, the attention output's own bound.
 """
 
 import numpy as np
@@ -61,13 +63,14 @@ def _oracle_mass(wl, ref, lanes=None):
 def _compare(wl, got, want):
     G = wl.H_q // wl.H_kv
     err = np.abs(got - want)
-    bound = 2e-2 * want + 1e-3 * G
+    bound = 1e-2 * want + 5e-4 * G
     worst = float((err - bound).max()) if err.size else 0.0
     rel = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
     assert np.all(np.isfinite(got))
     assert worst <= 0.0, f"per-slot error exceeds bound by {worst}"
-    assert rel <= 1e-2, f"rel-L2 {rel}"
-    return float(err.max()) if err.size else 0.0, rel
+    assert rel <= 5e-3, f"rel-L2 {rel}"
+    used = float((err / bound).max()) if err.size else 0.0  # fraction of the per-slot bound used
+    return dict(max_abs=float(err.max()) if err.size else 0.0, rel_l2=rel, bound_used=used)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])

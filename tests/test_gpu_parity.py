@@ -256,6 +256,42 @@ def test_decode_split_size_invariance(split):
     pu.compare_step(ds, ref)
 
 
+def test_plan_mismatch_emits_no_attention_work():
+    """Launches are sized from the host copies of the offset arrays; when the
+    device indptr disagrees (here: one row more in the last lane, or a row
+    moved between lanes so a decode lane turns into a prefill lane), the plan
+    sets FP_ST_PLAN_MISMATCH and emits no work item, so fp_attend leaves out
+    and lse untouched instead of indexing past what was sized."""
+    import torch
+
+    wl = W.make_config(3, seed=1, scale="small")
+    ds = pu.gpu_run(wl)
+    assert int(ds.status.cpu()[0]) == 0
+    ip = wl.step.indptr.astype(np.int32)
+    n = np.diff(ip)
+    variants = []
+    bigger = ip.copy()
+    bigger[-1] += 1
+    variants.append(bigger)
+    dec = next(l for l in range(wl.num_lanes - 1) if n[l] == 1 and n[l + 1] > 1)
+    moved = ip.copy()
+    moved[dec + 1] += 1  # lane dec takes a row of lane dec + 1: 2 rows x 4 heads, still decode class...
+    moved[dec + 1] += 8  # ...and 8 more: 10 rows x 4 heads = 40 columns, a prefill lane
+    assert moved[dec + 1] < moved[dec + 2]
+    variants.append(moved)
+    for v in variants:
+        ds.geom.indptr = torch.from_numpy(v).to(ds.device)  # the host copy keeps the original offsets
+        ds.out.fill_(float("nan"))
+        ds.lse.fill_(7.0)
+        ds.status.zero_()
+        ds.attend()
+        torch.cuda.synchronize()
+        from ragged_paged_kv_fp_amd._lib import FP_ST_PLAN_MISMATCH
+
+        assert int(ds.status.cpu()[0]) & FP_ST_PLAN_MISMATCH
+        assert torch.isnan(ds.out).all() and bool((ds.lse == 7.0).all())
+
+
 def test_error_paths_set_status_and_suppress_writes():
     wl = W.make_config(1)
     st = wl.step
