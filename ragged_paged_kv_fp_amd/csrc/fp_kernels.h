@@ -418,6 +418,7 @@ constexpr int kPreCols = 256;    // query row-heads per prefill workgroup (8 wav
 // Rows of one prefill work item: all GQA heads of those rows fill the workgroup.
 __host__ __device__ __forceinline__ int prefill_rows(int G) { return kPreCols / G; }
 
+constexpr int kLastBuckets = 129;  // last-split lengths in 32-slot tiles, 0..128 (splits up to 4096 slots)
 constexpr int kDecodeCols16 = 16;  // passes whose decode lanes have at most this many row-heads run the 16-column kernel
 
 struct PlanArgs {
@@ -506,16 +507,19 @@ __device__ __forceinline__ int block_excl_scan(int v, int *s_w, int *total) {
 // The decode list holds the items of the unmasked decode lanes, then those of
 // the masked ones (a launch each: masked lanes walk tile lists); within each
 // part, first every split but each (lane, KV head)'s last, then the last
-// splits (the partial ones), so that the long items are dispatched first. Split outputs are stored by (lane, KV head, split): lane_info's
+// splits (the partial ones) ordered by the slots they read, longest first, so
+// that the long items are dispatched first and the shortest set the tail. Split outputs are stored by (lane, KV head, split): lane_info's
 // dec_off counts every decode item of the lanes before, in lane order.
 __device__ __forceinline__ void plan_body(const PlanArgs &a) {
     __shared__ int s_pre[kMaxLanes + 1];    // prefill items before lane l
     __shared__ int s_full[2][kMaxLanes + 1];  // non-last decode items of part c (unmasked, masked) before lane l
-    __shared__ int s_nd[2][kMaxLanes + 1];    // decode lanes of part c before lane l
+    __shared__ int s_lane_at[2][kMaxLanes];   // part c's decode lanes by the length of their last split, longest first
+    __shared__ int s_hist[2][kLastBuckets];   // decode lanes of part c per last-split bucket, then bucket offsets
     __shared__ int s_w[kPlanThreads / kWave];
     __shared__ int s_bad;
     const int tid = threadIdx.x;
     if (tid == 0) s_bad = 0;
+    for (int e = tid; e < 2 * kLastBuckets; e += kPlanThreads) s_hist[e / kLastBuckets][e % kLastBuckets] = 0;
     const int per = (a.L + kPlanThreads - 1) / kPlanThreads;
     const int l0 = tid * per, l1 = min(a.L, l0 + per);
     int32_t st = 0;
@@ -541,13 +545,20 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
     int on0 = block_excl_scan(tn0, s_w, &Tn0);
     int on1 = block_excl_scan(tn1, s_w, &Tn1);
     int32_t dummy = 0;
+    // bucket of a decode lane's last split by the slots it reads there, in
+    // 32-slot tiles: 0 for the longest
+    auto last_key = [&](int l, const LaneCounts &c) {
+        const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
+        const int rem = clamp_kv(a.kv_len[l], cap) - (c.nsplit - 1) * a.split;
+        const int t = rem <= 0 ? 0 : (min(rem, a.split) + 31) >> 5;
+        return (kLastBuckets - 1) - min(t, kLastBuckets - 1);
+    };
     for (int l = l0; l < l1; ++l) {
         const LaneCounts c = lane_counts(a, l, &dummy);
         s_pre[l] = op;
         s_full[0][l] = of0;
         s_full[1][l] = of1;
-        s_nd[0][l] = on0;
-        s_nd[1][l] = on1;
+        if (c.dec) atomicAdd(&s_hist[c.cls][last_key(l, c)], 1);
         LaneInfo li;
         li.dec_off = c.dec ? od : -1;
         li.nsplit = c.nsplit;
@@ -561,12 +572,24 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
         }
     }
     const int n0 = Tf0 + a.H * Tn0, n1 = Tf1 + a.H * Tn1;  // decode items of each part
+    __syncthreads();  // the histograms are complete
+    if (tid < 2) {    // bucket offsets, longest last splits first
+        int acc = 0;
+        for (int b = 0; b < kLastBuckets; ++b) {
+            const int cnt = s_hist[tid][b];
+            s_hist[tid][b] = acc;
+            acc += cnt;
+        }
+    }
+    __syncthreads();
+    for (int l = l0; l < l1; ++l) {
+        const LaneCounts c = lane_counts(a, l, &dummy);
+        if (c.dec) s_lane_at[c.cls][atomicAdd(&s_hist[c.cls][last_key(l, c)], 1)] = l;
+    }
     if (tid == 0) {
         s_pre[a.L] = Tp;
         s_full[0][a.L] = Tf0;
         s_full[1][a.L] = Tf1;
-        s_nd[0][a.L] = Tn0;
-        s_nd[1][a.L] = Tn1;
         // Launch grids and workspace were sized from the host copies; device
         // offsets that disagree would index past them, so no work is emitted.
         if (n0 != a.n_dec_host[0] || n1 != a.n_dec_host[1] || Td != n0 + n1 || Tp != a.n_pre_host ||
@@ -595,8 +618,9 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
                 g = j / (ns - 1);
                 sp = j - g * (ns - 1);
             } else {
+                // last splits: lanes by the length of their last split, longest first
                 const int j = local - tf;
-                l = upper_lane(s_nd[cls], a.L, j / a.H);
+                l = s_lane_at[cls][j / a.H];
                 g = j % a.H;
                 sp = a.lane_info[l].nsplit - 1;
             }
