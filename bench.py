@@ -259,6 +259,8 @@ KERNEL_SOURCES = ("ragged_paged_kv_fp_amd/csrc/fp_lib.hip", "ragged_paged_kv_fp_
                   "ragged_paged_kv_fp_amd/csrc/fp_decode.h", "ragged_paged_kv_fp_amd/csrc/fp_prefill.h",
                   "ragged_paged_kv_fp_amd/csrc/fp_device.h", "include/fp.h")
 DOMINANT_KERNEL = {2: "decode_kernel", 3: "prefill_kernel", 4: "decode_kernel", 5: "prefill_kernel", 1: "prefill_kernel"}
+TRAFFIC_KERNELS = {2: ("merge_kernel", "append_kernel"), 3: ("decode_kernel", "append_kernel"),
+                   4: ("merge_kernel",), 5: ("append_kernel",)}
 
 
 def source_hash() -> str:
@@ -271,42 +273,58 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_file(cfg: int) -> str:
-    return os.path.join(ROOT, "profiles", f"{DOMINANT_KERNEL[cfg]}_config{cfg}_hbm_traffic.txt")
+def traffic_file(cfg: int, kernel: str = None) -> str:
+    from workloads import CONFIG_NAMES
+
+    return os.path.join(ROOT, "profiles", f"{kernel or DOMINANT_KERNEL[cfg]}_{CONFIG_NAMES[cfg]}_hbm_traffic.txt")
 
 
-def pmc_summary(fetch_db: str, write_db: str, cfg: int, calib_bytes: int, out: str) -> dict:
-    """Per-launch HBM bytes of the dominant kernel from rocprofv3 FETCH_SIZE and
-    WRITE_SIZE runs (KiB per dispatch), each scaled by what the same counter
-    reads for the plain device copy of calib_bytes run in the same process."""
+def pmc_summary(fetch_db: str, write_db: str, cfg: int, calib_bytes: int, steps: int) -> list:
+    """HBM bytes per step of each library kernel from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs (KiB per dispatch), each counter scaled by what it reads for
+    the plain device copy of calib_bytes run in the same process. A kernel with
+    several template variants (decode's unmasked and masked launches) counts
+    the sum of the variants' per-launch medians: each runs once per step, and
+    the median leaves out the untimed prefix pass's one large append. Writes
+    one record per kernel of DOMINANT_KERNEL and TRAFFIC_KERNELS for the config."""
     import sqlite3
 
-    def per_kernel(db, counter):
+    def rows_of(db, counter):
         c = sqlite3.connect(db)
-        rows = c.execute("select kernel_name, value from counters_collection where counter_name = ?",
+        return c.execute("select kernel_name, value from counters_collection where counter_name = ?",
                          (counter,)).fetchall()
-        return rows
 
-    kern = DOMINANT_KERNEL[cfg]
-    res = {}
+    per = {}  # counter -> (scale, copy_kib, {kernel name: [KiB per dispatch]})
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
-        rows = per_kernel(db, counter)
-        copies = [v for n, v in rows if "copyBuffer" in n]
-        kvals = [v for n, v in rows if f"fpk::{kern}<" in n]  # exact kernel (not mass_decode_kernel)
-        # the calibration copies are the largest copy dispatches of the run
-        copies = sorted(copies)[-5:]
+        rows = rows_of(db, counter)
+        copies = sorted(v for n, v in rows if "copyBuffer" in n)[-5:]  # the calibration copies are the largest
         calib_kib = float(np.median(copies))
-        scale = (calib_bytes / 1024.0) / calib_kib
-        res[counter] = dict(kernel_kib=float(np.mean(kvals)), launches=len(kvals), copy_kib=calib_kib, scale=scale)
-    traffic = sum(v["kernel_kib"] * v["scale"] * 1024.0 for v in res.values())
-    rec = {"kernel": kern, "config": cfg, "source_hash": source_hash(), "calib_copy_bytes": calib_bytes,
-           "counters": res, "traffic_bytes_per_launch": traffic,
-           "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d <dir> -o c -- python3 bench.py "
-                      f"--config {cfg} --no-cpu-baseline --steps 5 --warmup 1 --calib-copy {calib_bytes >> 20}"}
-    with open(out, "w") as f:
-        json.dump(rec, f, indent=1)
-        f.write("\n")
-    return rec
+        by = {}
+        for n, v in rows:
+            if n.startswith("fpk::") or n.startswith("void fpk::"):
+                by.setdefault(n, []).append(float(v))
+        per[counter] = ((calib_bytes / 1024.0) / calib_kib, calib_kib, by)
+    out = []
+    for kern in [DOMINANT_KERNEL[cfg]] + [k for k in TRAFFIC_KERNELS.get(cfg, ()) if k != DOMINANT_KERNEL[cfg]]:
+        res = {}
+        for counter, (scale, calib_kib, by) in per.items():
+            variants = {n: v for n, v in by.items() if f"fpk::{kern}<" in n or n.startswith(f"fpk::{kern}(")}
+            res[counter] = dict(scale=scale, copy_kib=calib_kib,
+                                variants={n: dict(launches=len(v), kib_median=float(np.median(v)),
+                                                  kib_min=float(np.min(v)), kib_max=float(np.max(v)))
+                                          for n, v in variants.items()},
+                                kib_per_step=float(sum(np.median(v) for v in variants.values())))
+        traffic = sum(v["kib_per_step"] * v["scale"] * 1024.0 for v in res.values())
+        rec = {"kernel": kern, "config": cfg, "source_hash": source_hash(), "calib_copy_bytes": calib_bytes,
+               "counters": res, "traffic_bytes_per_step": traffic,
+               "command": [f"rocprofv3 --pmc {c} -d <dir> -o c -- python3 bench.py --config {cfg} --no-extra "
+                           f"--no-peaks --no-cpu-baseline --steps {steps} --warmup 1 --calib-copy {calib_bytes >> 20}"
+                           for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+        with open(traffic_file(cfg, kern), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        out.append(rec)
+    return out
 
 
 def trace_summary(db: str, command: str, last: int = 0) -> str:
@@ -338,17 +356,17 @@ def trace_summary(db: str, command: str, last: int = 0) -> str:
     return "\n".join(lines) + "\n"
 
 
-def measured_traffic(cfg: int):
-    """Committed counter-based traffic for this config, or None if absent or
-    taken on different kernel sources."""
-    path = traffic_file(cfg)
+def measured_traffic(cfg: int, kernel: str = None):
+    """Committed counter-based HBM bytes per step of the config's kernel, or
+    None if absent or taken on different kernel sources."""
+    path = traffic_file(cfg, kernel)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("source_hash") != source_hash():
         return None
-    return float(rec["traffic_bytes_per_launch"])
+    return float(rec["traffic_bytes_per_step"])
 
 
 # --------------------------------------------------------------------------- main
@@ -387,9 +405,10 @@ def main(argv=None):
         print(trace_summary(*args.trace_summary, last=args.trace_last), end="")
         return 0
     if args.pmc_summary:
-        rec = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, (args.calib_copy or 1024) << 20,
-                          traffic_file(args.config))
-        print(json.dumps(rec))
+        recs = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, (args.calib_copy or 1024) << 20,
+                           args.steps)
+        for rec in recs:
+            print(json.dumps({"kernel": rec["kernel"], "traffic_bytes_per_step": rec["traffic_bytes_per_step"]}))
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -437,6 +456,17 @@ def main(argv=None):
     peaks = None if args.no_peaks else measure_peaks()
     pk_hbm = peaks["hbm_read_GB/s"] if peaks else None
     pk_mfma = peaks["mfma_bf16_TFLOP/s"] if peaks else None
+    others, seeds = {}, {}
+    if cfg == 2 and not args.no_extra:
+        # the other configurations and seeds run first, so that the flushed steps
+        # of the main configuration are the last launches of its kernels
+        others = extra_configs(W, runner, args.seed, pk_hbm, pk_mfma)
+        for sd in (1, 2):
+            if sd == args.seed:
+                continue
+            wls, ws_, rs = measure(W, runner, cfg, sd, args.split, 10, 2, None, flush=not args.no_flush)
+            seeds[str(sd)] = round(ws_["kv_bytes_decode"] / (float(np.mean(rs["step_ms"])) * 1e-3) / 1e9, 3)
+            del wls
     mass = {}
     wl, w, r = measure(W, runner, cfg, args.seed, args.split, K, Wm, mass, flush=not args.no_flush, wl=pre_wl)
     pre_wl = None
@@ -488,15 +518,9 @@ def main(argv=None):
         line["roofline"]["prefill"] = prefill_window(w, r, pk_mfma)
     line["attn_mass"] = {"kernel": "mass_kernel (fp_attn_mass after the step's attention), torch events",
                          "this_config": mass_line(wl, w, mass["ms"], cfg)}
-    if cfg == 2 and not args.no_extra:
-        line.update(extra_configs(W, runner, args.seed, pk_hbm, pk_mfma))
-        line["seeds"] = {str(args.seed): round(value, 3)}
-        for sd in (1, 2):
-            if sd == args.seed:
-                continue
-            wls, ws_, rs = measure(W, runner, cfg, sd, args.split, 10, 2, None, flush=not args.no_flush)
-            line["seeds"][str(sd)] = round(ws_["kv_bytes_decode"] / (float(np.mean(rs["step_ms"])) * 1e-3) / 1e9, 3)
-            del wls
+    if others:
+        line.update(others)
+        line["seeds"] = {str(args.seed): round(value, 3), **seeds}
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
@@ -527,7 +551,7 @@ def extra_configs(W, runner, seed, pk_hbm, pk_mfma) -> dict:
                       "t_bound_ms": {"prefill_at_peak": round(t_pre, 4), "decode_at_peak": round(t_dec, 4)},
                       "t_bound_over_t_measured": round(max(t_pre, t_dec) / t3, 4),
                       "t_bound_serial_over_t_measured": round((t_pre + t_dec) / t3, 4),
-                      "traffic": measured_traffic(3)}
+                      "traffic": {"prefill_kernel": measured_traffic(3), "decode_kernel": measured_traffic(3, "decode_kernel")}}
     del wl3
     # a decode wave under a sliding window with sinks: masked decode lanes walk tile lists
     wlw = W.make_window_decode(seed, L=64, kv=32768, window=1024, sinks=4)
