@@ -43,9 +43,12 @@ struct PreLds {
     static constexpr int V_BYTES = D * VROW;
     static constexpr int MW_OFF = K_BYTES + V_BYTES;  // mask words of the block's rows (masked lanes)
     static constexpr int STAGE = MW_OFF + 4 * 256;
-    static constexpr int LUT_OFF = kPreStages * STAGE;  // [16][2] uint32: bf16 keep masks of a mask nibble
+    // the keep-mask table sits at the start of LDS, so a lane's table address
+    // is 8 x the mask nibble with no base added
+    static constexpr int LUT_OFF = 0;                   // [16][2] uint32: bf16 keep masks of a mask nibble
     static constexpr int AOP_OFF = LUT_OFF + 16 * 8;     // [2][64] uint4: A operands of the bias MFMAs
-    static constexpr int TOTAL = AOP_OFF + 2 * 64 * 16;
+    static constexpr int RING_OFF = AOP_OFF + 2 * 64 * 16;
+    static constexpr int TOTAL = RING_OFF + kPreStages * STAGE;
 };
 
 // What this thread brings in for one tile: a 16-byte K chunk and V^T chunk and,
@@ -56,9 +59,17 @@ struct PreStage {
     uint32_t mw;
 };
 
-// Physical pages of the K and V^T chunks this thread moves for one tile (loaded
+// Keeps an index in a vector register, so a load through it is a vector
+// memory load (ordered with the tile loads) rather than a scalar one.
+__device__ __forceinline__ int in_vgpr(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// Physical pages of the K and V^T chunks a wave moves for one tile (loaded
 // one pipeline step before the data, so waiting for them never waits for the
-// data loads still in flight behind them).
+// data loads still in flight behind them). Each is one wave-uniform id, held
+// in a vector register only while its load is in flight.
 struct PrePages {
     int k, v;
 };
@@ -66,16 +77,22 @@ struct PrePages {
 // Per-thread constants of the tile copy. A tile is 32 slots and a page holds
 // P in {8, 16, 32} slots, so a tile starts on a page boundary and the chunk a
 // thread moves sits at the same offset inside the same page of every tile:
-// only the page id changes from tile to tile.
+// only the page id changes from tile to tile. The chunks are dealt out so that
+// all 64 chunks of a wave lie in one page: K by slot (a wave holds 64/KC
+// consecutive slots, at most 8), V^T page by page (a page's D x P block is D*P/8
+// >= 64 chunks, chunk e holding row e / (P/8), slots 8 (e % (P/8)) .. + 7). The
+// address of a chunk is then a wave-uniform page base plus a per-thread 32-bit
+// offset, and only the base is recomputed per tile, in scalar registers.
 template <int D>
 struct PreCopy {
-    const char *kp, *vp;  // chunk address inside physical page 0
+    const char *base;     // pool
+    uint32_t koff, voff;  // byte offsets of the thread's chunks inside a physical page
     uint32_t pbytes;      // bytes per physical page
     int last_page;        // highest physical page id in the pool
-    int kpg, vpg;         // page of the chunk within the tile's pages
+    int kpg, vpg;         // page of the wave's chunks within the tile's pages (wave-uniform)
     int tshift;           // log2(pages per tile)
     int lastpg;           // last working-set page holding a slot below kv_len
-    int k_lds, v_lds;     // LDS byte offsets of the chunk in a stage
+    int k_lds, v_lds;     // LDS byte offsets of the chunks in a stage
     int mw_lds;           // LDS byte offset of the row's mask word
     int ts;               // the tile holding slot kv_len (its tail slots are not part of the sequence)
     int vnv;              // slots of this thread's V^T chunk below kv_len in tile ts
@@ -86,30 +103,34 @@ __device__ __forceinline__ PreCopy<D> pre_copy(const KvView &kv, int rloc) {
     constexpr int KC = PreLds<D>::KC;
     const int tid = threadIdx.x;
     PreCopy<D> c;
-    const int rk = (tid % (32 * KC)) / KC, ck = tid % KC;          // K: slot rk, 16-byte chunk ck
-    const int dv = (tid % (4 * D)) >> 2, cv = tid & 3;             // V^T: row dv, slots 8cv..8cv+7
-    const char *base = reinterpret_cast<const char *>(kv.kbase);
-    c.kp = base + 2 * (((int64_t)kv.g * kv.P + (rk & kv.pmask)) * D + 8 * ck);
-    c.vp = base + 2 * (kv.vblock + (int64_t)kv.g * D * kv.P + (int64_t)dv * kv.P + ((8 * cv) & kv.pmask));
+    const int rk = (tid % (32 * KC)) / KC, ck = tid % KC;  // K: slot rk, 16-byte chunk ck
+    const int cvi = tid % (4 * D);                         // V^T chunk of the tile
+    const int vsh = kv.pshift - 3;                         // log2(chunks per V^T row of a page)
+    const int pgv = cvi >> (__builtin_ctz(D) + vsh);       // page of the chunk within the tile
+    const int e = cvi & ((D << vsh) - 1);
+    const int dv = e >> vsh, slot0 = pgv * kv.P + 8 * (e & ((1 << vsh) - 1));
+    c.base = reinterpret_cast<const char *>(kv.kbase);
+    c.koff = (uint32_t)(2 * (((int64_t)kv.g * kv.P + (rk & kv.pmask)) * D + 8 * ck));
+    c.voff = (uint32_t)(2 * (kv.vblock + (int64_t)kv.g * D * kv.P + (int64_t)dv * kv.P + (slot0 & kv.pmask)));
     c.pbytes = (uint32_t)(2 * kv.page_elems);
     c.last_page = kv.last_page;
-    c.kpg = rk >> kv.pshift;
-    c.vpg = (8 * cv) >> kv.pshift;
+    c.kpg = __builtin_amdgcn_readfirstlane(rk >> kv.pshift);
+    c.vpg = __builtin_amdgcn_readfirstlane(pgv);
     c.tshift = 5 - kv.pshift;
     c.lastpg = kv.eff > 0 ? (kv.eff - 1) >> kv.pshift : 0;
     c.k_lds = rk * PreLds<D>::KROW + 16 * ck;
-    c.v_lds = PreLds<D>::K_BYTES + dv * PreLds<D>::VROW + 16 * cv;
+    c.v_lds = PreLds<D>::K_BYTES + dv * PreLds<D>::VROW + 2 * slot0;
     c.mw_lds = PreLds<D>::MW_OFF + 4 * rloc;
     c.ts = kv.eff >> 5;
-    c.vnv = (kv.eff & 31) - 8 * cv;
+    c.vnv = (kv.eff & 31) - slot0;
     return c;
 }
 
 template <int D>
 __device__ __forceinline__ void pre_pages(const KvView &kv, const PreCopy<D> &c, int t, PrePages &pp) {
     const int base = t << c.tshift;
-    pp.k = kv.pids[min(base + c.kpg, c.lastpg)];
-    pp.v = kv.pids[min(base + c.vpg, c.lastpg)];
+    pp.k = kv.pids[in_vgpr(min(base + c.kpg, c.lastpg))];
+    pp.v = kv.pids[in_vgpr(min(base + c.vpg, c.lastpg))];
 }
 
 // Every load here is unconditional and nothing is done to the loaded values
@@ -121,10 +142,10 @@ template <int D, bool MASKED>
 __device__ __forceinline__ void pre_data(const PreCopy<D> &c, int t, const PrePages &pp, PreStage &st,
                                          const uint32_t *mrow, int wpr) {
     if constexpr (MASKED) st.mw = mrow[t < wpr ? t : 0];
-    const uint32_t pk = (uint32_t)min(max(pp.k, 0), c.last_page);
-    const uint32_t pv = (uint32_t)min(max(pp.v, 0), c.last_page);
-    st.k = *reinterpret_cast<const uint4 *>(c.kp + (uint64_t)pk * c.pbytes);
-    st.v = *reinterpret_cast<const uint4 *>(c.vp + (uint64_t)pv * c.pbytes);
+    const uint32_t pk = (uint32_t)min(max(__builtin_amdgcn_readfirstlane(pp.k), 0), c.last_page);
+    const uint32_t pv = (uint32_t)min(max(__builtin_amdgcn_readfirstlane(pp.v), 0), c.last_page);
+    st.k = *reinterpret_cast<const uint4 *>(c.base + (uint64_t)pk * c.pbytes + c.koff);
+    st.v = *reinterpret_cast<const uint4 *>(c.base + (uint64_t)pv * c.pbytes + c.voff);
 }
 
 // Stores tile t's chunks into an LDS stage. V^T entries of slots at or past
@@ -150,16 +171,15 @@ template <int D>
 struct PreWave {
     uint4 qf[D / 16];
     f32x16 o[D / 32];
-    float m, l;  // running max (log2 units, always a bf16 value) and denominator
-    bool seen;   // the column has had an allowed slot
+    float m, l;      // running max (log2 units, always a bf16 value) and denominator
+    uint32_t negm2;  // -m as two bf16 halves (exact: m is bf16-representable), the bias operand
+    bool seen;       // the column has had an allowed slot
 };
 
 __device__ __forceinline__ float bf16_round(float x) { return __uint_as_float(pack_bf16x2(x, x) << 16); }
 
-// -m of the column as two bf16 halves (exact: m is kept bf16-representable).
-template <int D>
-__device__ __forceinline__ uint32_t neg_m2(const PreWave<D> &w) {
-    const uint32_t hb = __float_as_uint(-w.m) >> 16;
+__device__ __forceinline__ uint32_t neg_m2(float m) {
+    const uint32_t hb = __float_as_uint(-m) >> 16;
     return hb | (hb << 16);
 }
 
@@ -193,25 +213,25 @@ struct RowBias {
 // (load(k), build(), apply(acc, k)), which keeps eight registers free.
 struct MaskBias {
     static constexpr int kDone = 1;  // tail segment after which the scores are complete
-    const char *lds;  // LDS base holding the keep-mask table and the A operands
+    const char *lut;     // the keep-mask table (LDS)
+    const char *aop;     // the A operands (LDS)
     const uint32_t *mw;  // the row's mask word for the tile (LDS)
-    uint32_t lm;      // slots below the row's limit, or all ones when the tile is fully allowed
-    bool full;        // every row may read every slot of the tile
-    uint32_t bits;    // slots of the tile the lane's row may read
+    uint32_t lm;         // slots of the tile below kv_len (wave-uniform)
+    uint32_t fullm;      // all ones when every row may read every slot of the tile (wave-uniform)
+    uint32_t bits;       // slots of the tile the lane's row may read
     uint32_t negm2;
-    int lut_off, aop_off;
     uint4 a, b;
     // issued together with the tile's fragment reads, consumed by load(0)
     __device__ __forceinline__ void fetch() { bits = *mw; }
     __device__ __forceinline__ void load(int k) {
         const int ln = lane_id(), kg = ln >> 5;
-        if (k == 0) bits = full ? 0xFFFFFFFFu : (bits & lm);
-        // B lane (n, kg) of MFMA k holds slots 16k + 8kg .. 16k + 8kg + 7
-        const uint32_t byte = (bits >> (16 * k + 8 * kg)) & 0xFFu;
-        const uint2 lo = *reinterpret_cast<const uint2 *>(lds + lut_off + 8 * (byte & 15u));
-        const uint2 hi = *reinterpret_cast<const uint2 *>(lds + lut_off + 8 * (byte >> 4));
+        // B lane (n, kg) of MFMA k holds slots 16k + 8kg .. 16k + 8kg + 7: after
+        // the shift by 8kg they are bits 16k .. 16k + 7
+        if (k == 0) bits = ((bits & lm) | fullm) >> (8 * kg);
+        const uint2 lo = *reinterpret_cast<const uint2 *>(lut + 8 * ((bits >> (16 * k)) & 15u));
+        const uint2 hi = *reinterpret_cast<const uint2 *>(lut + 8 * ((bits >> (16 * k + 4)) & 15u));
         b = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        a = *reinterpret_cast<const uint4 *>(lds + aop_off + 1024 * k + 16 * ln);
+        a = *reinterpret_cast<const uint4 *>(aop + 1024 * k + 16 * ln);
     }
     __device__ __forceinline__ void build() { b = make_uint4(bfi(b.x), bfi(b.y), bfi(b.z), bfi(b.w)); }
     __device__ __forceinline__ uint32_t bfi(uint32_t keep) const { return (keep & negm2) | (~keep & kBiasOut); }
@@ -301,6 +321,7 @@ __device__ __forceinline__ void pre_rescale(f32x16 &s, float mt, PreWave<D> &w) 
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] -= delta;
         w.m = m_new;
+        w.negm2 = neg_m2(m_new);
         w.seen = w.seen || valid;
     }
 }
@@ -401,13 +422,6 @@ __device__ __forceinline__ uint32_t tile_bits(int j0, int lim, bool masked, uint
     return masked ? (mw & lm) : lm;
 }
 
-// Keeps an index in a vector register, so a load through it is a vector
-// memory load (ordered with the tile loads) rather than a scalar one.
-__device__ __forceinline__ int in_vgpr(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 template <int K>
 using StepK = std::integral_constant<int, K>;
 
@@ -427,7 +441,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char *l
     int cap;
     KvView kv = make_view(a, lane, g, &cap);
     kv.vblock = (int64_t)a.H * a.P * D;
-    auto stage = [&](int k) { return lds + k * PreLds<D>::STAGE; };
+    auto stage = [&](int k) { return lds + PreLds<D>::RING_OFF + k * PreLds<D>::STAGE; };
 
     PreWave<D> w;
     {
@@ -437,6 +451,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char *l
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) w.o[db] = f32x16{};
         w.m = 0.0f;
+        w.negm2 = neg_m2(0.0f);
         w.l = 0.0f;
         w.seen = false;
     }
@@ -514,19 +529,19 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char *l
         auto make_bias = [&](int i, int qe, const char *st) {
             if constexpr (MASKED) {
                 MaskBias b;
-                b.lds = lds;
-                b.lut_off = PreLds<D>::LUT_OFF;
-                b.aop_off = PreLds<D>::AOP_OFF;
+                b.lut = lds + PreLds<D>::LUT_OFF;
+                b.aop = lds + PreLds<D>::AOP_OFF;
                 const int j0 = 32 * tile_at(i, qe);
-                b.full = qe < 0 && j0 + 32 <= kv.eff;  // bit 31: every slot allowed for every row
-                b.lm = tile_bits(j0, lim, false, 0u);
+                // bit 31 of the entry: every slot allowed for every row
+                b.fullm = qe < 0 && j0 + 32 <= kv.eff ? 0xFFFFFFFFu : 0u;
+                b.lm = tile_bits(j0, kv.eff, false, 0u);
                 b.mw = reinterpret_cast<const uint32_t *>(st + cp.mw_lds);
-                b.negm2 = neg_m2(w);
+                b.negm2 = w.negm2;
                 return b;
             } else {
                 RowBias b;
                 b.a0 = h == 0 ? 0x00003F80u : 0u;
-                b.negm2 = neg_m2(w);
+                b.negm2 = w.negm2;
                 return b;
             }
         };
@@ -543,7 +558,7 @@ __device__ __forceinline__ void prefill_item(const AttnArgs &a, int4 it, char *l
             // its drop masks where they are used instead of keeping them live
             // across the loop
             asm volatile("" : "+s"(j0));
-            return pre_max(s, sel, sel ? tile_bits(j0, lim, false, 0u) : 0u);
+            return pre_max(s, sel, sel ? tile_bits(j0, MASKED ? kv.eff : lim, false, 0u) : 0u);
         };
         auto b0 = make_bias(0, q0, stage(0));
         f32x16 sA = pre_qk<D>(stage(0), w, b0), sB = {};
