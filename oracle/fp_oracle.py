@@ -381,6 +381,77 @@ def attn_mass(pool: Pool, indptr, positions, slots, kv_len, q_bits, H_q, theta, 
     return mass
 
 
+def order_key(x32) -> np.ndarray:
+    """Total order of fp32 values as uint32 (negatives below positives, NaN of
+    positive sign above +inf): the key the eviction step compares."""
+    b = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    neg = (b & 0x80000000) != 0
+    return np.where(neg, (~b) & 0xFFFFFFFF, b | 0x80000000).astype(np.uint32)
+
+
+def tova_scores(mass32, page_indptr, P, lane, n):
+    """Eviction score of lane `lane`'s slots 0..n-1: its attention mass summed
+    over the KV heads in head order, in fp32 (the precision the device step
+    decides in). mass32: fp32 [H][S], slot j of the lane at page_indptr[lane]*P + j."""
+    base = int(page_indptr[lane]) * P
+    acc = np.zeros(n, dtype=np.float32)
+    for g in range(mass32.shape[0]):
+        acc = (acc + mass32[g, base:base + n].astype(np.float32)).astype(np.float32)
+    return acc
+
+
+def tova_keep(mass32, page_indptr, P, committed, budget, prev_keep=None, prev_limit=None):
+    """Score-driven eviction (the Docs' Attention masks section: per-row bitmaps
+    express attention-based KV eviction such as TOVA; the review's section 7:
+    the forward pass returns the scores such a policy needs). Reading taken:
+    a lane's old slots are those below its committed length c; a slot is a
+    candidate unless an earlier selection dropped it (prev_keep given, slot
+    below prev_limit, its bit clear); the lane keeps the min(budget, #candidates)
+    candidates with the largest score (order_key of tova_scores), equal keys
+    going to the lower slot. Returns a list of bool arrays, lane l's of length c_l."""
+    out = []
+    for lane in range(len(committed)):
+        c = max(int(committed[lane]), 0)
+        keys = order_key(tova_scores(mass32, page_indptr, P, lane, c))
+        cand = np.ones(c, dtype=bool)
+        if prev_keep is not None:
+            pl = min(max(int(prev_limit[lane]), 0), c)
+            cand[:pl] = np.asarray(prev_keep[lane][:pl], dtype=bool)
+        idx = np.nonzero(cand)[0]
+        k = min(max(int(budget[lane]), 0), len(idx))
+        # larger key first, then lower slot
+        order = sorted(idx.tolist(), key=lambda j: (-int(keys[j]), j))
+        keep = np.zeros(c, dtype=bool)
+        keep[order[:k]] = True
+        out.append(keep)
+    return out
+
+
+def tova_mask(keep, indptr, slots, kv_len, committed, words_per_row):
+    """The pass's per-row bitmaps from the lanes' keep sets: row r of lane l
+    reads old slot j < c_l iff it is kept, and new slot c_l <= j < kv_len_l iff
+    j <= slots[r] (the slot-order rule for the pass's own rows); bits at or past
+    kv_len are 0. words_per_row[l] words per row (fewer than ceil(kv_len/32)
+    drops the tail and flags ST_MASK_SHORT). Returns (list of uint32 arrays,
+    lane l's rows concatenated, status)."""
+    out, status = [], 0
+    for lane in range(len(indptr) - 1):
+        r0, r1 = int(indptr[lane]), int(indptr[lane + 1])
+        c = max(int(committed[lane]), 0)
+        kv = max(int(kv_len[lane]), 0)
+        wpr = int(words_per_row[lane])
+        if r1 > r0 and wpr * 32 < kv:
+            status |= ST_MASK_SHORT
+        words = np.zeros((r1 - r0, wpr), dtype=np.uint32)
+        for t, row in enumerate(range(r0, r1)):
+            for j in range(min(kv, 32 * wpr)):
+                ok = bool(keep[lane][j]) if j < c else j <= int(slots[row])
+                if ok:
+                    words[t, j >> 5] |= np.uint32(1 << (j & 31))
+        out.append(words.reshape(-1))
+    return out, status
+
+
 def fold(committed, indptr, fold_spec, channel=None):
     """committed[l] += k_l with k_l = literal | rows (all) | channel[l], clamped to [0, rows]."""
     out = np.array(committed, dtype=np.int64)

@@ -618,3 +618,98 @@ def test_ia3_matches_exact_rounding_and_closed_forms():
     assert np.array_equal(o2[nz], (y[nz] + 0x80).astype(np.uint16))
     _, st = oracle.ia3(y, np.array([0, 0, 5, 0], np.int32), ip, ones)
     assert st == oracle.ST_ADAPTER
+
+
+# ---- score-driven eviction (TOVA step): selection and bitmaps
+
+def test_order_key_sorts_like_the_floats():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.normal(size=200).astype(np.float32) * 10.0 ** rng.integers(-30, 30, size=200),
+                        np.array([0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45], dtype=np.float32)]).astype(np.float32)
+    keys = oracle.order_key(x)
+    by_key = x[np.argsort(keys, kind="stable")]
+    # equal floats may only differ as -0.0 / +0.0, which the key orders -0 < +0
+    assert np.array_equal(by_key, np.sort(x, kind="stable"))
+    assert oracle.order_key(np.float32(-0.0)) < oracle.order_key(np.float32(0.0))
+
+
+def _keep_by_rank(keys, cand, k):
+    """Brute force: a candidate is kept iff fewer than k candidates beat it
+    (larger key, or equal key at a lower slot)."""
+    keep = np.zeros(len(keys), dtype=bool)
+    for j in np.nonzero(cand)[0]:
+        rank = sum(1 for i in np.nonzero(cand)[0] if keys[i] > keys[j] or (keys[i] == keys[j] and i < j))
+        keep[j] = rank < k
+    return keep
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tova_keep_matches_rank_definition(seed):
+    rng = np.random.default_rng(100 + seed)
+    P, H, L = 8, int(rng.integers(1, 4)), 4
+    pages = rng.integers(1, 6, size=L)
+    page_indptr = np.concatenate([[0], np.cumsum(pages)])
+    S = int(page_indptr[-1]) * P
+    # few distinct levels, so equal keys are common
+    mass = (rng.integers(0, 4, size=(H, S)) * 0.25).astype(np.float32)
+    committed = np.array([rng.integers(0, pages[l] * P + 1) for l in range(L)])
+    budget = rng.integers(-1, 40, size=L)
+    prev_limit = np.array([rng.integers(0, c + 1) for c in committed])
+    prev_keep = [rng.random(c) < 0.6 for c in committed]
+    for pk in (None, prev_keep):
+        got = oracle.tova_keep(mass, page_indptr, P, committed, budget, pk, prev_limit)
+        for lane in range(L):
+            c = int(committed[lane])
+            keys = oracle.order_key(mass[:, page_indptr[lane] * P:page_indptr[lane] * P + c].sum(axis=0, dtype=np.float32))
+            cand = np.ones(c, dtype=bool)
+            if pk is not None:
+                cand[:prev_limit[lane]] = pk[lane][:prev_limit[lane]]
+            k = min(max(int(budget[lane]), 0), int(cand.sum()))
+            assert np.array_equal(got[lane], _keep_by_rank(keys, cand, k)), (seed, lane)
+
+
+def test_tova_keep_special_cases():
+    P = 8
+    page_indptr = np.array([0, 2])
+    mass = np.zeros((2, 16), dtype=np.float32)
+    mass[0, :10] = [3, 1, 4, 1, 5, 9, 2, 6, 5, 3]
+    mass[1, :10] = [0, 0, 0, 0, 0, 0, 0, 0, 0, 1]        # head sums: [3,1,4,1,5,9,2,6,5,4]
+    c = np.array([10])
+    # top 3 by score: 9 (slot 5), 6 (slot 7), then the two 5s -> the lower slot 4
+    keep = oracle.tova_keep(mass, page_indptr, P, c, [3])[0]
+    assert np.nonzero(keep)[0].tolist() == [4, 5, 7]
+    assert oracle.tova_keep(mass, page_indptr, P, c, [0])[0].sum() == 0
+    assert oracle.tova_keep(mass, page_indptr, P, c, [10])[0].all()
+    assert oracle.tova_keep(mass, page_indptr, P, c, [99])[0].all()
+    # equal scores everywhere: the lowest slots
+    flat = np.ones((1, 16), dtype=np.float32)
+    assert np.nonzero(oracle.tova_keep(flat, page_indptr, P, c, [4])[0])[0].tolist() == [0, 1, 2, 3]
+    # a slot dropped earlier stays dropped, however large its score
+    pk = [np.array([1, 1, 1, 1, 1, 0, 1, 1, 1, 1], dtype=bool)]
+    keep = oracle.tova_keep(mass, page_indptr, P, c, [3], pk, [8])[0]
+    assert not keep[5]
+    assert np.nonzero(keep)[0].tolist() == [4, 7, 8]   # scores 6 (slot 7), then 5s at slots 4 and 8
+    # slots at or past prev_limit are candidates even without a keep bit
+    pk0 = [np.zeros(10, dtype=bool)]
+    assert np.nonzero(oracle.tova_keep(mass, page_indptr, P, c, [5], pk0, [8])[0])[0].tolist() == [8, 9]
+
+
+def test_tova_mask_hand_worked_and_causal_when_all_kept():
+    # one lane: 5 old slots, keep {0, 3}; three new rows at slots 5, 6, 7; kv_len 8
+    keep = [np.array([1, 0, 0, 1, 0], dtype=bool)]
+    words, st = oracle.tova_mask(keep, [0, 3], [5, 6, 7], [8], [5], [1])
+    assert st == 0
+    assert words[0].tolist() == [0b00101001, 0b01101001, 0b11101001]
+    # too few words per row for kv_len: flagged
+    _, st = oracle.tova_mask(keep, [0, 3], [5, 6, 7], [40], [5], [1])
+    assert st == oracle.ST_MASK_SHORT
+    # every old slot kept: the bitmap is the slot-order rule attend() applies without a mask
+    rng = np.random.default_rng(7)
+    c, n = 37, 6
+    slots = c + rng.permutation(n)
+    kv = c + n
+    words, _ = oracle.tova_mask([np.ones(c, dtype=bool)], [0, n], slots, [kv], [c], [2])
+    for t in range(n):
+        bits = [j for j in range(kv) if (int(words[0][2 * t + (j >> 5)]) >> (j & 31)) & 1]
+        A, _ = oracle.allowed_slots(0, t, kv, slots, np.array([0, n]))
+        assert bits == list(A)
