@@ -286,6 +286,44 @@ int fp_attn_mass(const fp_kv_pool *pool, const fp_geometry *geom, int32_t num_q_
                  float *slot_mass, hipStream_t stream);
 
 /*
+ * fp_tova_mask - score-driven KV eviction on the device: the next pass's
+ * per-row bitmaps from the attention mass of earlier passes. The Docs'
+ * Attention masks section names attention-based eviction such as TOVA among
+ * the uses of per-row masks, and the review's section 7 has the forward pass
+ * return the scores it needs (fp_attn_mass); the policy itself is not spelled
+ * out there, and this call takes the following reading of it.
+ *   For the pass given by pool and geom (call it before that pass's
+ *   fp_append_kv: committed_len must still be the frozen length), lane l's old
+ *   slots are j < c_l = committed_len[l] (clamped to the lane's capacity), and
+ *     score_l(j) = sum over KV heads g = 0 .. H-1, in that order, in fp32, of
+ *                  slot_mass[g * S + page_indptr[l] * P + j],  S = page_indptr_host[L] * P.
+ *   Old slot j is a candidate unless prev_keep is given, j < prev_limit[l]
+ *   (clamped to [0, c_l]) and bit j of the lane's prev_keep words is clear:
+ *   a slot dropped by an earlier selection stays dropped. The lane keeps the
+ *   min(max(budget[l], 0), #candidates) candidates with the largest score,
+ *   scores compared as the total order of fp32 bit patterns (negatives below
+ *   positives), equal scores going to the lower slot.
+ *   keep: written, lane l's words at keep[keep_word_offset[l] ..]: the first
+ *     ceil(c_l / 32) words, bit j set iff old slot j is kept. keep_word_offset
+ *     (int64 [L+1], device) must give every lane at least ceil(capacity / 32)
+ *     words, the same layout as prev_keep; keep must not overlap prev_keep.
+ *   mask_bits / mask_word_offset: the pass's bitmaps (fp_mask layout), written
+ *     for every lane with a non-empty span: row r of lane l, word w < span / rows,
+ *     bit j = 32w + b is set iff j < kv_len[l] (clamped to capacity) and
+ *       j <  c_l : old slot j is kept;
+ *       j >= c_l : j <= slots[r] (the pass's own slots, by the slot-order rule).
+ *     A span with fewer than ceil(kv_len / 32) words per row sets
+ *     FP_ST_MASK_SHORT. Lanes with an empty span keep the causal rule; their
+ *     keep words are still written.
+ * Deterministic (exact integer selection; every output word has one writer).
+ * Returns FP_ERR_NULL / FP_ERR_SHAPE like fp_attend.
+ */
+int fp_tova_mask(const fp_kv_pool *pool, const fp_geometry *geom, const float *slot_mass, const int32_t *budget,
+                 const uint32_t *prev_keep, const int32_t *prev_limit, const int64_t *keep_word_offset,
+                 uint32_t *keep, uint32_t *mask_bits, const int64_t *mask_word_offset,
+                 const int64_t *mask_word_offset_host, int32_t *status, hipStream_t stream);
+
+/*
  * fp_advance - the StateGeometry of the next pass of a repeating decode loop,
  * written on the device from committed_len, so a loop that keeps its decode
  * pass in flight (Pipelines and frames: run_ahead) never waits on the host for

@@ -432,7 +432,8 @@ def tova_mask(keep, indptr, slots, kv_len, committed, words_per_row):
     reads old slot j < c_l iff it is kept, and new slot c_l <= j < kv_len_l iff
     j <= slots[r] (the slot-order rule for the pass's own rows); bits at or past
     kv_len are 0. words_per_row[l] words per row (fewer than ceil(kv_len/32)
-    drops the tail and flags ST_MASK_SHORT). Returns (list of uint32 arrays,
+    drops the tail and flags ST_MASK_SHORT; none means the lane carries no
+    bitmap and keeps the causal rule, as an empty mask span does). Returns (list of uint32 arrays,
     lane l's rows concatenated, status)."""
     out, status = [], 0
     for lane in range(len(indptr) - 1):
@@ -440,7 +441,7 @@ def tova_mask(keep, indptr, slots, kv_len, committed, words_per_row):
         c = max(int(committed[lane]), 0)
         kv = max(int(kv_len[lane]), 0)
         wpr = int(words_per_row[lane])
-        if r1 > r0 and wpr * 32 < kv:
+        if r1 > r0 and 0 < wpr and wpr * 32 < kv:   # no words at all: the lane keeps the causal rule
             status |= ST_MASK_SHORT
         words = np.zeros((r1 - r0, wpr), dtype=np.uint32)
         for t, row in enumerate(range(r0, r1)):

@@ -40,7 +40,7 @@ FP_FOLD_CHANNEL = -2
 EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_attend_noalloc",
            "fp_attend_noalloc_max_bytes", "fp_hazard_workspace_bytes",
            "fp_check_hazards", "fp_fold", "fp_readout", "fp_attn_mass",
-           "fp_advance", "fp_lora_workspace_bytes", "fp_adapter_lora", "fp_adapter_ia3",
+           "fp_advance", "fp_tova_mask", "fp_lora_workspace_bytes", "fp_adapter_lora", "fp_adapter_ia3",
            "fp_vertical_merge", "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version",
            "fp_source_hash")
 
@@ -141,6 +141,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp_adapter_ia3.restype = c_i32
     lib.fp_advance.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
     lib.fp_advance.restype = c_i32
+    lib.fp_tova_mask.argtypes = [P(FpKvPool), P(FpGeometry)] + [c_ptr] * 10 + [c_ptr]  # ..., status, stream
+    lib.fp_tova_mask.restype = c_i32
     lib.fp_vertical_merge.argtypes = [c_i32] + [c_ptr] * 10 + [c_i32] + [c_ptr] * 6  # L, 10 inputs, page_size, 6 outputs
     lib.fp_vertical_merge.restype = c_i32
     lib.fp_kv_bytes.argtypes = [c_i32, c_i32, c_i32, c_u64, c_i32]

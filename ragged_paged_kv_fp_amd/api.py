@@ -228,6 +228,22 @@ def attn_mass(pool: Pool, geom: Geometry, num_q_heads: int, lse: torch.Tensor, w
                                             _tuning(split), _ptr(slot_mass), _stream(stream)))
 
 
+def tova_mask(pool: Pool, geom: Geometry, slot_mass: torch.Tensor, budget: torch.Tensor,
+              keep_word_offset: torch.Tensor, keep: torch.Tensor, mask: Mask, status: torch.Tensor,
+              prev_keep: Optional[torch.Tensor] = None, prev_limit: Optional[torch.Tensor] = None,
+              stream=None) -> None:
+    """fp_tova_mask: per lane keep the budget old slots (below committed_len) with
+    the largest attention mass summed over KV heads, then write the pass's row
+    bitmaps into mask.bits (kept old slots + the pass's own slots by slot order)."""
+    lib = _lib.load()
+    ps, gs = pool.struct(), geom.struct()
+    ms = mask.struct()
+    _check("fp_tova_mask", lib.fp_tova_mask(ctypes.byref(ps), ctypes.byref(gs), _ptr(slot_mass), _ptr(budget),
+                                            _ptr(prev_keep), _ptr(prev_limit), _ptr(keep_word_offset), _ptr(keep),
+                                            ms.bits, ms.word_offset, ms.word_offset_host, _ptr(status),
+                                            _stream(stream)))
+
+
 @dataclass
 class Lora:
     """Adapters of one projection site: A [n][rank][d_in], B [n][d_out][rank] (bf16), scale [n] (fp32)."""

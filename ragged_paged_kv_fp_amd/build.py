@@ -15,7 +15,7 @@ SOURCES = [os.path.join(HERE, "csrc", "fp_lib.hip")]
 PEAKS_LIB = os.path.join(HERE, "libfp_peaks.so")
 PEAKS_SOURCES = [os.path.join(HERE, "csrc", "fp_peaks.hip")]
 DEPS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("fp_kernels.h", "fp_device.h", "fp_decode.h", "fp_prefill.h",
-                                                                "fp_stats.h", "fp_lora.h")] + [
+                                                                "fp_stats.h", "fp_lora.h", "fp_evict.h")] + [
     os.path.join(ROOT, "include", "fp.h")]
 
 HIPCC_FLAGS = [

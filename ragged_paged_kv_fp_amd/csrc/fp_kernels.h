@@ -817,3 +817,4 @@ __device__ __forceinline__ KvView make_view(const AttnArgs &a, int lane, int g, 
 #include "fp_prefill.h"
 #include "fp_stats.h"
 #include "fp_lora.h"
+#include "fp_evict.h"

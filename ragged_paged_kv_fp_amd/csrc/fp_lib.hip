@@ -717,6 +717,53 @@ int fp_adapter_ia3(const fp_geometry *geom, int32_t num_adapters, int32_t d_out,
     return launch_ok();
 }
 
+int fp_tova_mask(const fp_kv_pool *pool, const fp_geometry *geom, const float *slot_mass, const int32_t *budget,
+                 const uint32_t *prev_keep, const int32_t *prev_limit, const int64_t *keep_word_offset,
+                 uint32_t *keep, uint32_t *mask_bits, const int64_t *mask_word_offset,
+                 const int64_t *mask_word_offset_host, int32_t *status, hipStream_t stream) {
+    int rc = check_pool(pool);
+    if (rc) return rc;
+    if ((rc = check_geom(geom, pool))) return rc;
+    if (!slot_mass || !budget || !keep_word_offset || !keep || !mask_bits || !mask_word_offset ||
+        !mask_word_offset_host || !status)
+        return FP_ERR_NULL;
+    if (prev_keep && !prev_limit) return FP_ERR_NULL;
+    const fp_mask m{mask_bits, mask_word_offset, mask_word_offset_host};
+    if ((rc = check_mask(&m, geom))) return rc;
+    const int L = geom->num_lanes;
+    TovaArgs ta{};
+    ta.mass = slot_mass;
+    ta.S = (int64_t)pool->page_indptr_host[L] * pool->page_size;
+    ta.H = pool->num_kv_heads;
+    ta.P = pool->page_size;
+    ta.L = L;
+    ta.page_indptr = pool->page_indptr;
+    ta.committed = pool->committed_len;
+    ta.budget = budget;
+    ta.prev_limit = prev_limit;
+    ta.prev_keep = prev_keep;
+    ta.keep_off = keep_word_offset;
+    ta.keep = keep;
+    hipLaunchKernelGGL(tova_select_kernel, dim3((unsigned)L), dim3(kTovaThreads), 0, stream, ta);
+    if ((rc = launch_ok())) return rc;
+    if (geom->num_rows == 0) return FP_OK;
+    TovaRowArgs ra{};
+    ra.indptr = geom->indptr;
+    ra.slots = geom->slots;
+    ra.kv_len = geom->kv_len;
+    ra.committed = pool->committed_len;
+    ra.page_indptr = pool->page_indptr;
+    ra.L = L;
+    ra.P = pool->page_size;
+    ra.keep = keep;
+    ra.keep_off = keep_word_offset;
+    ra.mask_off = mask_word_offset;
+    ra.mask = mask_bits;
+    ra.status = status;
+    hipLaunchKernelGGL(tova_rows_kernel, dim3((unsigned)geom->num_rows), dim3(256), 0, stream, ra);
+    return launch_ok();
+}
+
 int fp_advance(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *pos_offset, int32_t *positions,
                int32_t *slots, int32_t *kv_len, hipStream_t stream) {
     if (!pool || !pool->committed_len) return FP_ERR_NULL;

@@ -273,3 +273,22 @@ def test_stale_library_is_refused(lib, tmp_path):
         open(dst, "wb").write(open(src, "rb").read())
     with pytest.raises(_lib.StaleLibraryError):  # file names are part of the hash
         _lib.check_fresh(lib, same)
+
+
+def test_tova_mask_validation(lib):
+    g, p, keep = _structs()
+    st = ctypes.c_int32(0)
+    wo = np.array([0, 3, 3], np.int64)  # lane 0: 3 rows x 1 word, lane 1 keeps the causal rule
+
+    def call(mass=FAKE, budget=FAKE, prev=None, plim=None, koff=FAKE, kept=FAKE, bits=FAKE, woh=wo.ctypes.data,
+             status=ctypes.addressof(st)):
+        return lib.fp_tova_mask(ctypes.byref(p), ctypes.byref(g), mass, budget, prev, plim, koff, kept, bits, FAKE,
+                                woh, status, None)
+
+    for kw in ("mass", "budget", "koff", "kept", "bits", "woh", "status"):
+        assert call(**{kw: None}) == -1, kw
+    assert call(prev=FAKE) == -1  # prev_keep without prev_limit
+    bad = np.array([0, 2, 2], np.int64)  # 2 words over 3 rows
+    assert call(woh=bad.ctypes.data) == -2
+    p.page_size = 12
+    assert call() == -3
