@@ -258,6 +258,7 @@ def cpu_baseline(wl, cfg: int, unit: str):
 KERNEL_SOURCES = ("ragged_paged_kv_fp_amd/csrc/fp_lib.hip", "ragged_paged_kv_fp_amd/csrc/fp_kernels.h",
                   "ragged_paged_kv_fp_amd/csrc/fp_decode.h", "ragged_paged_kv_fp_amd/csrc/fp_prefill.h",
                   "ragged_paged_kv_fp_amd/csrc/fp_device.h", "include/fp.h")
+TOVA_BUDGET = 2048  # old slots a lane keeps in the timed eviction step
 DOMINANT_KERNEL = {2: "decode_kernel", 3: "prefill_kernel", 4: "decode_kernel", 5: "prefill_kernel", 1: "prefill_kernel"}
 TRAFFIC_KERNELS = {2: ("merge_kernel", "append_kernel"), 3: ("decode_kernel", "append_kernel"),
                    4: ("merge_kernel",), 5: ("append_kernel",)}
@@ -518,6 +519,8 @@ def main(argv=None):
         line["roofline"]["prefill"] = prefill_window(w, r, pk_mfma)
     line["attn_mass"] = {"kernel": "mass_kernel (fp_attn_mass after the step's attention), torch events",
                          "this_config": mass_line(wl, w, mass["ms"], cfg)}
+    if "tova_ms" in mass:
+        line["tova_step"] = tova_line(wl, mass)
     if others:
         line.update(others)
         line["seeds"] = {str(args.seed): round(value, 3), **seeds}
@@ -540,6 +543,8 @@ def extra_configs(W, runner, seed, pk_hbm, pk_mfma) -> dict:
                       "peak": BF16_PEAK_TFLOPS, "ms_per_step": round(float(np.mean(r5["step_ms"])), 4),
                       **prefill_window(w5, r5, pk_mfma), "traffic": measured_traffic(5), "steps": 5, "warmup": 1,
                       "attn_mass": mass_line(wl5, w5, mass5["ms"], 5)}
+    if "tova_ms" in mass5:
+        out["prefill"]["tova_step"] = tova_line(wl5, mass5)
     del wl5
     wl3, w3, r3 = measure(W, runner, 3, seed, None, 5, 1)
     t_pre = w3["flops_prefill"] / (BF16_PEAK_TFLOPS * 1e12) * 1e3
@@ -729,6 +734,17 @@ def frame_bench(W, runner, seed, K, Wm) -> dict:
             "steps": K, "warmup": Wm, "status": st, **res}
 
 
+def tova_line(wl, mass) -> dict:
+    """The timed eviction step: bytes are the fp32 mass it reads (every old slot,
+    every KV head) plus the bitmap words it writes."""
+    gbs = mass["tova_bytes"] / (mass["tova_ms"] * 1e-3) / 1e9
+    return {"what": f"fp_tova_mask from this pass's attention mass: keep {TOVA_BUDGET} of each lane's "
+                    f"{mass['tova_old_slots'] // wl.num_lanes} old slots (fp32 mass summed over {wl.H_kv} KV heads, "
+                    "radix select), then write the pass's row bitmaps",
+            "ms": round(mass["tova_ms"], 4), "bytes": mass["tova_bytes"], "GB/s": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def mass_line(wl, w, ms, cfg) -> dict:
     """Roofline of fp_attn_mass: decode-class lanes read each slot's K once
     (HBM-bound: kv_len x H_kv x d x 2 B); prefill lanes run Q.K over every
@@ -873,6 +889,33 @@ def measure(W, runner, cfg, seed, split, K, Wm, mass=None, flush=True, wl=None):
         m1.record(stream)
         torch.cuda.synchronize()
         mass["ms"] = m0.elapsed_time(m1) / K
+        if ds.mask is not None:
+            # score-driven eviction from this mass: re-mask the same pass (rows at
+            # committed_len..) keeping tova_budget old slots per lane
+            ds.reset()
+            L = wl.num_lanes
+            cap = np.diff(wl.page_indptr) * wl.P
+            koff = np.concatenate([[0], np.cumsum((cap + 31) // 32)]).astype(np.int64)
+            keep = torch.zeros(int(koff[-1]), dtype=torch.int32, device="cuda")
+            koff_t = torch.from_numpy(koff).cuda()
+            bits = torch.zeros_like(ds.mask.bits)
+            tmask = api.Mask(bits=bits, word_offset=ds.mask.word_offset, word_offset_host=ds.mask.word_offset_host)
+            budget = torch.full((L,), TOVA_BUDGET, dtype=torch.int32, device="cuda")
+            st = torch.zeros(1, dtype=torch.int32, device="cuda")
+            tcall = lambda: api.tova_mask(ds.pool, ds.geom, buf, budget, koff_t, keep, tmask, st)  # noqa: E731
+            for _ in range(Wm):
+                tcall()
+            torch.cuda.synchronize()
+            m0.record(stream)
+            for _ in range(K):
+                tcall()
+            m1.record(stream)
+            torch.cuda.synchronize()
+            c0 = ds.committed0.cpu().numpy().astype(np.int64)
+            mass["tova_ms"] = m0.elapsed_time(m1) / K
+            mass["tova_bytes"] = int(c0.sum() * wl.H_kv * 4 + ds.mask.bits.numel() * 4)
+            mass["tova_old_slots"] = int(c0.sum())
+            del keep, bits
         del buf
     for evs in hip_ev:
         for e in evs:

@@ -11,12 +11,15 @@
 //    the lane's committed length) is the fp32 sum of its mass over the KV heads
 //    in head order; scores compare by their total-order key (order_key). The
 //    budget-th largest candidate key T is found by a radix select (four 8-bit
-//    digits, most significant first, one LDS histogram per digit); the lane
+//    digits, most significant first; per digit, each wave counts into its own
+//    LDS histogram, since the keys of one lane crowd into few bins and shared
+//    bins would serialise the atomics, and the copies are summed); the lane
 //    then keeps every candidate above T and the lowest-slot candidates equal
 //    to T until the budget is met, found with a block-wide scan in slot order.
 //    The keys of a lane with up to kTovaLdsKeys old slots are computed once
-//    into LDS (coalesced reads of the mass); a longer lane recomputes them from
-//    the mass on every pass over its slots. Either way the step needs no workspace.
+//    into LDS (coalesced reads of the mass), and every pass over them sweeps
+//    the slots with a stride of one per thread; a longer lane recomputes its
+//    keys from the mass on every pass. Either way the step needs no workspace.
 //  tova_rows_kernel: one workgroup per row of the pass, one thread per mask
 //    word: kept old slots, plus the pass's own slots up to the row's slot.
 #pragma once
@@ -50,9 +53,29 @@ __device__ __forceinline__ uint32_t low_bits(int n) {
     return n <= 0 ? 0u : (n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u));
 }
 
+// Inclusive prefix sum over threads 0..255 of the workgroup (every thread of
+// the workgroup calls it; threads from 256 on contribute 0).
+__device__ __forceinline__ int scan256(int v, int *s_w) {
+    const int ln = lane_id(), wv = threadIdx.x / kWave;
+    int x = threadIdx.x < 256 ? v : 0;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (ln >= o) x += y;
+    }
+    if (ln == kWave - 1 && wv < 4) s_w[wv] = x;
+    __syncthreads();
+    for (int w = 0; w < 4; ++w) x += (w < wv && wv < 4) ? s_w[w] : 0;
+    __syncthreads();
+    return x;
+}
+
 __global__ void __launch_bounds__(kTovaThreads) tova_select_kernel(TovaArgs a) {
+    constexpr int PER = kTovaLdsKeys / kTovaThreads;  // slots per thread on the LDS path
+    constexpr int NW = kTovaLdsKeys / 32;
     __shared__ uint32_t s_key[kTovaLdsKeys];
-    __shared__ int s_hist[256];
+    __shared__ uint32_t s_cw[NW];  // candidate words (LDS path)
+    __shared__ uint32_t s_gw[NW];  // words of the kept keys above the threshold (LDS path)
+    __shared__ int s_hist[kTovaThreads / kWave][256];
     __shared__ int s_w[kTovaThreads / kWave];
     __shared__ int s_sel[2];  // digit found, remaining count
     const int l = blockIdx.x, tid = threadIdx.x;
@@ -70,23 +93,55 @@ __global__ void __launch_bounds__(kTovaThreads) tova_select_kernel(TovaArgs a) {
         const uint32_t fresh = ~low_bits(plim - 32 * w);  // at or past prev_limit
         return inside & (pk[w] | fresh);
     };
+    // the sum over heads in head order; four heads' loads in flight at a time
     auto key_of = [&](int j) {
+        const float *m = a.mass + base + j;
         float s = 0.0f;
-        for (int g = 0; g < a.H; ++g) s += a.mass[(int64_t)g * a.S + base + j];
+        int g = 0;
+        for (; g + 4 <= a.H; g += 4) {
+            const float v0 = m[(int64_t)g * a.S], v1 = m[(int64_t)(g + 1) * a.S];
+            const float v2 = m[(int64_t)(g + 2) * a.S], v3 = m[(int64_t)(g + 3) * a.S];
+            s += v0;
+            s += v1;
+            s += v2;
+            s += v3;
+        }
+        for (; g < a.H; ++g) s += m[(int64_t)g * a.S];
         return order_key(s);
     };
+    // LDS path: thread tid owns slots tid + 1024 u, so every LDS access below
+    // is a stride-1 sweep across the workgroup (no bank conflicts) and the
+    // slots' loads are independent of each other
     const bool in_lds = c <= kTovaLdsKeys;  // workgroup-uniform
     if (in_lds) {
-#pragma unroll 4
-        for (int j = tid; j < c; j += kTovaThreads) s_key[j] = key_of(j);
+        float acc[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) acc[u] = 0.0f;
+        for (int g = 0; g < a.H; ++g) {
+            const float *mg = a.mass + (int64_t)g * a.S + base;
+            float v[PER];
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int j = tid + u * kTovaThreads;
+                v[u] = j < c ? mg[j] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < PER; ++u) acc[u] += v[u];
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int j = tid + u * kTovaThreads;
+            if (j < c) s_key[j] = order_key(acc[u]);
+        }
+        for (int w = tid; w < nwords; w += kTovaThreads) s_cw[w] = cand_word(w);
     }
-    auto key_at = [&](int j) { return in_lds ? s_key[j] : key_of(j); };
+    auto cand_bit = [&](int j) { return (s_cw[j >> 5] >> (j & 31)) & 1u; };
 
     // candidates, and the budget clamped to them
     int nc = 0;
     for (int w = tid; w < nwords; w += kTovaThreads) nc += __popc(cand_word(w));
     int ncand;
-    block_excl_scan(nc, s_w, &ncand);
+    block_excl_scan(nc, s_w, &ncand);  // its barriers also publish the LDS keys and words
     const int k = min(max(a.budget[l], 0), ncand);
     if (k == ncand || k == 0) {  // workgroup-uniform: every candidate or none
         for (int w = tid; w < nwords; w += kTovaThreads) kw[w] = k ? cand_word(w) : 0u;
@@ -97,26 +152,39 @@ __global__ void __launch_bounds__(kTovaThreads) tova_select_kernel(TovaArgs a) {
     uint32_t prefix = 0, pmask = 0;
     int rem = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int b = tid; b < 256; b += kTovaThreads) s_hist[b] = 0;
+        for (int b = tid; b < (kTovaThreads / kWave) * 256; b += kTovaThreads) (&s_hist[0][0])[b] = 0;
         __syncthreads();
-        for (int w = tid; w < nwords; w += kTovaThreads) {
-            uint32_t cw = cand_word(w);
-            while (cw) {
-                const int b = __builtin_ctz(cw);
-                cw &= cw - 1;
-                const uint32_t key = key_at(32 * w + b);
-                if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+        int *hist = s_hist[tid / kWave];
+        if (in_lds) {
+#pragma unroll 8
+            for (int u = 0; u < PER; ++u) {
+                const int j = tid + u * kTovaThreads;
+                if (j < c && cand_bit(j)) {
+                    const uint32_t key = s_key[j];
+                    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+                }
+            }
+        } else {
+            for (int w = tid; w < nwords; w += kTovaThreads) {
+                uint32_t cw = cand_word(w);
+                while (cw) {
+                    const int b = __builtin_ctz(cw);
+                    cw &= cw - 1;
+                    const uint32_t key = key_of(32 * w + b);
+                    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+                }
             }
         }
         __syncthreads();
-        if (tid == 0) {
-            int acc = 0, d = 255;
-            for (; d > 0; --d) {
-                if (acc + s_hist[d] >= rem) break;
-                acc += s_hist[d];
-            }
-            s_sel[0] = d;
-            s_sel[1] = rem - acc;
+        // digit d: thread 255 - d sums the wave copies of bin d; a scan over the
+        // threads counts the keys of the digits above d and d itself
+        int cnt = 0;
+        if (tid < 256)
+            for (int v = 0; v < kTovaThreads / kWave; ++v) cnt += s_hist[v][255 - tid];
+        const int incl = scan256(cnt, s_w);
+        if (tid < 256 && incl >= rem && incl - cnt < rem) {
+            s_sel[0] = 255 - tid;
+            s_sel[1] = rem - (incl - cnt);
         }
         __syncthreads();
         prefix |= (uint32_t)s_sel[0] << shift;
@@ -126,6 +194,40 @@ __global__ void __launch_bounds__(kTovaThreads) tova_select_kernel(TovaArgs a) {
     }
     // keep keys above the threshold, and the first `rem` equal ones in slot order
     const uint32_t T = prefix;
+    if (in_lds) {
+        // words of the keys above T and equal to T: the 32 slots of word
+        // (tid >> 5) + 32 u sit in one half of a wave, so a ballot assembles them
+        uint32_t *s_ew = reinterpret_cast<uint32_t *>(&s_hist[0][0]);
+        const int wv = tid / kWave;
+#pragma unroll 8
+        for (int u = 0; u < PER; ++u) {
+            const int j = tid + u * kTovaThreads;
+            const bool cd = j < c && cand_bit(j);
+            const uint32_t key = cd ? s_key[j] : 0u;
+            const uint64_t bg = __ballot(cd && key > T), be = __ballot(cd && key == T);
+            if (lane_id() == 0) {
+                const int w = 2 * wv + 32 * u;
+                s_gw[w] = (uint32_t)bg;
+                s_gw[w + 1] = (uint32_t)(bg >> 32);
+                s_ew[w] = (uint32_t)be;
+                s_ew[w + 1] = (uint32_t)(be >> 32);
+            }
+        }
+        __syncthreads();
+        const uint32_t eq0 = tid < nwords ? s_ew[tid] : 0u;
+        int tot;
+        const int before = block_excl_scan(__popc(eq0), s_w, &tot);
+        int allow = min(max(rem - before, 0), __popc(eq0));
+        uint32_t eq = eq0, kept = 0;
+        while (allow > 0) {  // the lowest `allow` equal slots of the word
+            const uint32_t lowest = eq & (~eq + 1u);
+            kept |= lowest;
+            eq ^= lowest;
+            --allow;
+        }
+        if (tid < nwords) kw[tid] = s_gw[tid] | kept;
+        return;
+    }
     int taken = 0;  // equal keys kept by earlier chunks of words
     for (int w0 = 0; w0 < nwords; w0 += kTovaThreads) {
         const int w = w0 + tid;
@@ -135,7 +237,7 @@ __global__ void __launch_bounds__(kTovaThreads) tova_select_kernel(TovaArgs a) {
             while (cw) {
                 const int b = __builtin_ctz(cw);
                 cw &= cw - 1;
-                const uint32_t key = key_at(32 * w + b);
+                const uint32_t key = key_of(32 * w + b);
                 gt |= (key > T ? 1u : 0u) << b;
                 eq |= (key == T ? 1u : 0u) << b;
             }
