@@ -23,8 +23,12 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-constexpr int kDecWaves = 4;
-constexpr int kDecThreads = 64 * kDecWaves;
+// Waves per decode workgroup: four for the 16-column kernel (two workgroups per
+// CU at two waves per SIMD); two for the 32-column kernel, whose registers allow
+// one wave per SIMD, so that two items still run side by side on each CU and one
+// item's start and end overlap the other's streaming.
+template <int NC>
+constexpr int dec_waves() { return NC == 32 ? 2 : 4; }
 constexpr int kLdsRow = 68;  // padded row of 64 floats: rows land on different LDS banks
 
 // A tile's K/V as loaded from the pool. The K rows are read as whole
@@ -292,11 +296,12 @@ __device__ __forceinline__ void stage_o(const DecState<D, NC> &w, int c, float s
 // and the output combine rows (used after it, past a barrier) share storage.
 template <int D, int NC>
 struct DecShared {
-    float ml[kDecWaves][2][32];
+    static constexpr int W = dec_waves<NC>();
+    float ml[W][2][32];
     float fin[2][32];
     union {
-        float o[kDecWaves][NC][kLdsRow];
-        char k[kDecWaves][DecLds<D>::BYTES];
+        float o[W][NC][kLdsRow];
+        char k[W][DecLds<D>::BYTES];
     } u;
 };
 
@@ -308,6 +313,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs &a, const int4 it, De
     auto &s_fin = sh.fin;
     auto &s_o = sh.u.o;
     auto &s_k = sh.u.k;
+    constexpr int kDecWaves = dec_waves<NC>(), kDecThreads = 64 * kDecWaves;
     const int lane = it.x, g = it.y, s0 = it.z, s1 = it.w;
     const LaneInfo li = a.lane_info[lane];
     const int r0 = a.indptr[lane];
@@ -460,7 +466,7 @@ __device__ __forceinline__ void decode_item(const AttnArgs &a, const int4 it, De
 // starts workgroups in launch order as others finish, so the long items at
 // the head of the list go first and the short partial splits set the tail.
 template <int D, int NC, bool MASKED>
-__global__ void __launch_bounds__(kDecThreads, NC == 16 ? 2 : 1) decode_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * dec_waves<NC>(), NC == 16 ? 2 : 1) decode_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) DecShared<D, NC> sh;
     const int4 it = a.dec_list[blockIdx.x];
     if (it.x >= 0) decode_item<D, NC, MASKED>(a, it, sh);

@@ -141,8 +141,12 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
             const int n = geom->indptr_host[l + 1] - geom->indptr_host[l];
             if (n * G > kDecodeCols16 && n * G <= kDecodeCols) wide = true;
         }
-        const double slots = (double)(wide ? resident_blocks(decode_kernel<128, 32, false>, kDecThreads)
-                                           : resident_blocks(decode_kernel<128, 16, false>, kDecThreads));
+        // counted in four-wave workgroups: a two-wave workgroup streams an item
+        // at half the rate, so it counts as half a slot
+        const double slots = wide ? resident_blocks(decode_kernel<128, 32, false>, 64 * dec_waves<32>()) *
+                                        (dec_waves<32>() / 4.0)
+                                  : resident_blocks(decode_kernel<128, 16, false>, 64 * dec_waves<16>()) *
+                                        (dec_waves<16>() / 4.0);
         for (const int cand : kSplitChoices) {
             split = cand;
             int64_t items = 0;
@@ -367,7 +371,7 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
         if (n == 0) continue;
         AttnArgs ac = a;
         ac.dec_list = dec_items + (part ? p.n_dec_cls[0] : 0);
-        const dim3 grid((unsigned)n), block(kDecThreads);
+        const dim3 grid((unsigned)n), block(64 * (p.wide ? dec_waves<32>() : dec_waves<16>()));
         if (p.D == 128) {
             if (!p.wide) {
                 if (part == 0) hipLaunchKernelGGL((decode_kernel<128, 16, false>), grid, block, 0, stream, ac);
