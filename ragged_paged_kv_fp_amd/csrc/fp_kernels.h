@@ -67,17 +67,25 @@ __device__ __forceinline__ uint4 rotate_chunk(uint4 x, const double2 *cs) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// One workgroup per 2^rshift consecutive rows.
+// One workgroup per 2^rshift consecutive rows. Workgroups are dealt to the 8
+// XCDs in turn, so block b takes row group (b mod 8) * ceil-share + b / 8:
+// each XCD gets a contiguous run of groups, and neighbouring groups, which
+// write the two halves of V^T rows when a page holds more slots than a group
+// has rows, merge their writes in one L2 instead of sending two partial
+// writes of each line to HBM.
 //  1. The rows are validated once (lane, slot, freeze, page).
 //  2. The fp64 (cos, sin) of every (row, RoPE pair) goes to LDS: the KV heads
 //     of a row share them.
 //  3. K: one thread per 16-byte chunk (four pairs) of a (row, head) row, chunk
 //     index fastest, so a wave reads and writes whole 256-byte head rows.
 //  4. V goes through LDS a group of heads at a time (16-byte loads), rows
-//     padded by 16 bytes so the transposed reads below are free of bank
-//     conflicts, then is stored into the V^T block with the row index fastest:
-//     rows of a prefill chunk sit in consecutive slots of a page, so one
-//     wave's 2-byte stores cover consecutive bytes of consecutive V^T rows.
+//     padded by 16 bytes, then is stored into the V^T block. Eight rows at
+//     consecutive slots filling an aligned 8-slot segment of one page (most
+//     of a prefill chunk) are a full segment: per (head, dim) column a thread
+//     gathers its eight values from LDS and writes them with one 16-byte
+//     store. The other rows (decode rows, chunk ends, scattered slots) are
+//     stored per element with the row index fastest, so a wave's 2-byte
+//     stores still cover consecutive bytes of V^T rows.
 template <int D>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     constexpr int PAIRS = D / 2, C8 = D / 8, CSH = D == 128 ? 4 : 3, DSH = D == 128 ? 7 : 6;
@@ -85,8 +93,13 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     __shared__ int s_off[kAppendRows];
     __shared__ double2 s_cs[kAppendRows * PAIRS];
     __shared__ __attribute__((aligned(16))) uint16_t s_v[kAppendVBytes / 2];
+    __shared__ int s_seg[kAppendRows / 8];  // first row of each full segment
+    __shared__ int s_erow[kAppendRows];     // rows stored per element
+    __shared__ int s_nseg, s_nerow;
     const int R = 1 << a.rshift;
-    const int64_t r0 = (int64_t)blockIdx.x << a.rshift;
+    const int nb = gridDim.x, per = nb >> 3, rem = nb & 7, xcd = blockIdx.x & 7;
+    const int grp = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + (blockIdx.x >> 3);
+    const int64_t r0 = (int64_t)grp << a.rshift;
     const int nr = (int)(a.N - r0 < R ? a.N - r0 : R);
     const int tid = threadIdx.x;
     const int H = a.H;
@@ -122,6 +135,29 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
         s_cs[e] = make_double2(c, sn);
     }
     __syncthreads();
+    if (tid < 64) {  // V^T store lists, by the first wave (read after the V staging barrier)
+        // A run starts at a valid row that does not continue the previous
+        // row's slot in the same page, or that begins an aligned segment; a
+        // run of 8 rows is then a full segment.
+        const int j = tid;
+        const bool valid = j < kAppendRows && s_base[j] >= 0;
+        const bool start = valid && (j == 0 || s_base[j - 1] != s_base[j] || s_off[j - 1] + 1 != s_off[j] ||
+                                     (s_off[j] & 7) == 0);
+        const uint64_t starts = __ballot(start);
+        const uint64_t breaks = starts | __ballot(!valid);  // rows past the group are not valid
+        const bool seg = start && __builtin_ctzll(breaks >> (j + 1)) == 7;  // j < 16: a break above it exists
+        const uint64_t segs = __ballot(seg);
+        uint32_t in_seg = 0;
+        for (uint64_t f = segs; f; f &= f - 1) in_seg |= 0xffu << __builtin_ctzll(f);
+        const bool el = valid && !((in_seg >> j) & 1);
+        const uint64_t els = __ballot(el);
+        if (seg) s_seg[__popcll(segs & ((1ull << j) - 1ull))] = j;
+        if (el) s_erow[__popcll(els & ((1ull << j) - 1ull))] = j;
+        if (tid == 0) {
+            s_nseg = __popcll(segs);
+            s_nerow = __popcll(els);
+        }
+    }
     // K chunks kBatch at a time per thread: all loads of a batch are issued
     // before the first rotation, so a thread keeps kBatch loads in flight
     const int nk = nr * H * C8;
@@ -172,12 +208,27 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
             }
         }
         __syncthreads();
-        for (int e = tid; e < (hn * D) << a.rshift; e += blockDim.x) {
-            const int j = e & (R - 1), dh = e >> a.rshift;
-            const int hh = dh >> DSH, d = dh & (D - 1);
-            const int64_t base = s_base[j];
-            if (j < nr && base >= 0)
-                a.pool[base + vblock + ((int64_t)(h0 + hh) * D + d) * a.P + s_off[j]] = s_v[j * rs + hh * D + d];
+        const int nseg = s_nseg, ne = s_nerow;
+        for (int col = tid; col < hn * D; col += blockDim.x) {  // col = hh * D + d
+            const int64_t vrow = vblock + ((int64_t)h0 * D + col) * a.P;  // V^T row (h0 + hh, d) in a page
+            for (int q = 0; q < nseg; ++q) {
+                const int j = s_seg[q];
+                const uint16_t *src = &s_v[j * rs + col];
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = (uint32_t)src[2 * i * rs] | ((uint32_t)src[(2 * i + 1) * rs] << 16);
+                *reinterpret_cast<uint4 *>(a.pool + s_base[j] + vrow + s_off[j]) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        if (ne > 0) {
+            const int lg = ne == 1 ? 0 : 32 - __builtin_clz(ne - 1);  // the element rows, padded to 2^lg
+            for (int e = tid; e < (hn * D) << lg; e += blockDim.x) {
+                const int k = e & ((1 << lg) - 1), col = e >> lg;
+                if (k < ne) {
+                    const int j = s_erow[k];
+                    a.pool[s_base[j] + vblock + ((int64_t)h0 * D + col) * a.P + s_off[j]] = s_v[j * rs + col];
+                }
+            }
         }
         __syncthreads();
     }

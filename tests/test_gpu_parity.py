@@ -80,6 +80,41 @@ def test_explicit_slot_geometry(seed, H_kv, G, d, P, kinds, masked):
     _say(pu.compare_step(ds, ref))
 
 
+@pytest.mark.parametrize("seed,H_kv,d,P,rows", [
+    (40, 2, 64, 8, 2300), (41, 3, 128, 16, 4500), (42, 2, 128, 32, 9000), (43, 1, 64, 32, 17000),
+    (44, 8, 128, 16, 17000),
+])
+def test_append_row_groups(seed, H_kv, d, P, rows):
+    """The KV write of passes large enough that one workgroup takes 2, 4, 8 or
+    16 consecutive rows: contiguous runs from any page offset and across
+    pages, single rows, reversed and gapped runs, rows at frozen or
+    out-of-range slots, lanes of 1 to 300 rows. The whole pool (holes keep the
+    fill) and the status bits equal the oracle's append."""
+    import torch
+
+    wl = W.make_append_mix(seed, H_kv=H_kv, d=d, P=P, rows=rows)
+    st = wl.step
+    _say(f"append mix seed {seed}: H_kv={H_kv} d={d} P={P} rows={st.num_rows} lanes={st.num_lanes}")
+    pool = oracle.Pool(wl.num_pages, wl.P, wl.H_kv, wl.d, wl.page_indptr, wl.page_ids, fill_bits=HOLE_BITS)
+    c = np.zeros(wl.num_lanes, np.int32)
+    p = wl.prefix
+    assert oracle.append(pool, c, p.indptr, p.positions, p.slots, p.k, p.v, wl.theta) == 0
+    c, _ = oracle.fold(c, p.indptr, p.fold)
+    status = oracle.append(pool, c, st.indptr, st.positions, st.slots, st.k, st.v, wl.theta)
+    assert status == oracle.ST_SLOT_RANGE | oracle.ST_FROZEN  # both refusals occur in every case
+
+    from ragged_paged_kv_fp_amd import runner
+
+    ds = runner.DeviceStep(wl, device="cuda", fill_bits=HOLE_BITS)
+    ds.run_prefix()
+    torch.cuda.synchronize()
+    assert int(ds.status.cpu()[0]) == 0
+    ds.append()
+    torch.cuda.synchronize()
+    assert int(ds.status.cpu()[0]) == status
+    pu.compare_pool(ds, dict(pool=pool))
+
+
 @pytest.mark.parametrize("seed,L,kv,window,sinks,P", [(0, 4, 32768, 1024, 4, 16), (1, 3, 30001, 1000, 3, 32),
                                                        (2, 5, 5000, 77, 0, 8)])
 def test_window_decode_lanes_walk_tile_lists(seed, L, kv, window, sinks, P):

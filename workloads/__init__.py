@@ -14,6 +14,7 @@ from .gen import (  # noqa: F401
     Workload,
     bf16_bits_from_f32,
     Lora,
+    make_append_mix,
     make_config,
     make_explicit,
     make_window_decode,

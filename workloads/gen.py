@@ -658,6 +658,39 @@ def make_explicit(seed: int, *, H_kv: int = 2, G: int = 2, d: int = 64, P: int =
     return wl
 
 
+def make_append_mix(seed: int, *, H_kv: int = 2, d: int = 64, P: int = 16, rows: int = 4096) -> Workload:
+    """A pass of at least `rows` rows for the KV write alone, mixing the slot
+    patterns a row group of the append can meet: contiguous runs that start
+    at any offset of a page and cross page boundaries (prefill chunks),
+    single rows (decode), runs in reverse order, runs with gaps, and a few
+    rows aimed at frozen slots (below the folded prefix) or outside the
+    lane's capacity, which the write must refuse and flag. Lane sizes vary
+    from 1 to 300 rows, so row groups straddle lane boundaries. H_q = H_kv."""
+    rngs = _rngs(seed)
+    g = rngs["lengths"]
+    lanes, total = [], 0
+    while total < rows:
+        kind = int(g.integers(0, 5))
+        n = 1 if kind == 1 else int(g.integers(1, 301))
+        c = int(g.integers(0, 6 * P))
+        cap = -(-(c + 2 * n + int(g.integers(0, 2 * P)) + 1) // P) * P
+        if kind in (0, 1):     # contiguous run after the prefix
+            slots = np.arange(c, c + n)
+        elif kind == 2:        # the same run written back to front
+            slots = np.arange(c + n - 1, c - 1, -1)
+        elif kind == 3:        # every other slot
+            slots = c + 2 * np.arange(n)
+        else:                  # contiguous, with a few rows at frozen or out-of-range slots
+            slots = np.arange(c, c + n)
+            bad = g.random(n) < 0.05
+            slots = np.where(bad, g.choice(np.array([-1, cap, cap + P, max(c - 1, -1)]), size=n), slots)
+        lanes.append(dict(c=c, n=n, kv_len=int(min(cap, max(c + 1, int(slots.max()) + 1))), fold=FOLD_ALL,
+                          pos_of_slot=_ident_pos(cap + 2 * P + 1), pages=cap // P, slots=slots))
+        total += n
+    wl = _assemble(f"append_mix_{seed}", rngs, H_q=H_kv, H_kv=H_kv, d=d, P=P, lanes=lanes, extra_pages=2)
+    return wl
+
+
 def make_window_decode(seed: int, *, L: int = 64, kv: int = 32768, window: int = 1024, sinks: int = 4,
                        H_q: int = 32, H_kv: int = 8, d: int = 128, P: int = 16) -> Workload:
     """A decode wave under a sliding window with attention sinks (Docs,
