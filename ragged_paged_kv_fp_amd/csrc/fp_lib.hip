@@ -8,6 +8,7 @@
 #include "fp_kernels.h"
 
 #include <algorithm>
+#include <functional>
 #include <math.h>
 #include <mutex>
 #include <stdint.h>
@@ -112,6 +113,55 @@ int resident_blocks(Kernel kernel, int threads) {
     return cached[dev];
 }
 
+// A second look at the split for unmasked decode passes: an estimate of when
+// the last decode item ends, by list scheduling in the plan's dispatch order
+// (every split but each lane's last, all of one size, then the last splits
+// longest first), each item taken by the first resident workgroup that frees
+// up. An item costs its 32-slot tiles (by capacity) plus a start of
+// kItemStartTiles tiles: page ids and the first K/V loads before it streams,
+// fitted to split sweeps on MI355X. The KV heads of a lane give H equal copies
+// of each of its items in a row, so m = resident workgroups / H slots taking
+// one copy each give the same schedule. With few items per slot this is where
+// the split matters: the longest items set the end. The plan takes a smaller
+// split from kSplitRefine only when the estimate is kRefineGain below the
+// first choice's, which keeps the first choice wherever the two are close.
+constexpr int kSplitRefine[] = {3072, 1536, 1024, 512};
+constexpr double kItemStartTiles = 6.0;
+constexpr double kRefineGain = 0.9;
+constexpr int kRefineSlots = 4096;  // most slots the estimate keeps (more are folded in)
+
+double decode_makespan(const fp_kv_pool *pool, const fp_geometry *geom, int G, int split, int m) {
+    int lasts[kMaxLanes];  // the last split of each decode lane, in tiles
+    double load[kRefineSlots];
+    int nl = 0;
+    int64_t nfull = 0;
+    for (int l = 0; l < geom->num_lanes; ++l) {
+        const int n = geom->indptr_host[l + 1] - geom->indptr_host[l];
+        if (n <= 0 || n * G > kDecodeCols) continue;
+        const int cap = (pool->page_indptr_host[l + 1] - pool->page_indptr_host[l]) * pool->page_size;
+        const int ns = cap > 0 ? (cap + split - 1) / split : 1;
+        nfull += ns - 1;
+        lasts[nl++] = cap > 0 ? (cap - (ns - 1) * split + 31) / 32 : 0;
+    }
+    std::sort(lasts, lasts + nl, std::greater<int>());
+    m = std::max(1, std::min(m, kRefineSlots));
+    const double cf = kItemStartTiles + split / 32;
+    const int64_t per = nfull / m, rem = nfull % m;
+    double end = 0;
+    for (int i = 0; i < m; ++i) {
+        load[i] = (double)(per + (i < rem ? 1 : 0)) * cf;
+        end = std::max(end, load[i]);
+    }
+    std::make_heap(load, load + m, std::greater<double>());  // min-heap: the slot that frees up first
+    for (int i = 0; i < nl; ++i) {
+        std::pop_heap(load, load + m, std::greater<double>());
+        load[m - 1] += kItemStartTiles + lasts[i];
+        end = std::max(end, load[m - 1]);
+        std::push_heap(load, load + m, std::greater<double>());
+    }
+    return end;
+}
+
 // Shape-only plan: mirrors lane_counts() of the device plan from the host copies.
 int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *mask, int32_t Hq,
               const fp_tuning *tun, Plan *pl) {
@@ -137,16 +187,18 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
         // (the 32-column kernel as soon as one decode lane has more than 16
         // query row-heads)
         bool wide = false;  // (Plan::wide, known before the loop below fills it)
+        bool dec_masked = false;
         for (int l = 0; l < geom->num_lanes; ++l) {
             const int n = geom->indptr_host[l + 1] - geom->indptr_host[l];
             if (n * G > kDecodeCols16 && n * G <= kDecodeCols) wide = true;
+            if (n > 0 && n * G <= kDecodeCols && mask && mask->word_offset_host[l + 1] > mask->word_offset_host[l])
+                dec_masked = true;
         }
+        const int resident = wide ? resident_blocks(decode_kernel<128, 32, false>, 64 * dec_waves<32>())
+                                  : resident_blocks(decode_kernel<128, 16, false>, 64 * dec_waves<16>());
         // counted in four-wave workgroups: a two-wave workgroup streams an item
         // at half the rate, so it counts as half a slot
-        const double slots = wide ? resident_blocks(decode_kernel<128, 32, false>, 64 * dec_waves<32>()) *
-                                        (dec_waves<32>() / 4.0)
-                                  : resident_blocks(decode_kernel<128, 16, false>, 64 * dec_waves<16>()) *
-                                        (dec_waves<16>() / 4.0);
+        const double slots = resident * ((wide ? dec_waves<32>() : dec_waves<16>()) / 4.0);
         for (const int cand : kSplitChoices) {
             split = cand;
             int64_t items = 0;
@@ -156,6 +208,22 @@ int make_plan(const fp_kv_pool *pool, const fp_geometry *geom, const fp_mask *ma
                 if (n > 0 && n * G <= kDecodeCols) items += (int64_t)pool->num_kv_heads * (cap > 0 ? (cap + cand - 1) / cand : 1);
             }
             if ((double)items >= kItemsPerSlot * slots) break;
+        }
+        // masked decode items cost their tile lists, not their slot ranges: no estimate for them
+        if (!dec_masked) {
+            const int m = std::max(1, resident / pool->num_kv_heads);
+            const double first = decode_makespan(pool, geom, G, split, m);
+            double best = first;
+            int pick = split;
+            for (const int cand : kSplitRefine) {
+                if (cand >= split) continue;
+                const double e = decode_makespan(pool, geom, G, cand, m);
+                if (e < best) {
+                    best = e;
+                    pick = cand;
+                }
+            }
+            if (best < kRefineGain * first) split = pick;
         }
     }
     Plan p;
