@@ -73,12 +73,15 @@ __device__ __forceinline__ uint4 rotate_chunk(uint4 x, const double2 *cs) {
 // write the two halves of V^T rows when a page holds more slots than a group
 // has rows, merge their writes in one L2 instead of sending two partial
 // writes of each line to HBM.
-//  1. The rows are validated once (lane, slot, freeze, page).
-//  2. The fp64 (cos, sin) of every (row, RoPE pair) goes to LDS: the KV heads
-//     of a row share them.
-//  3. K: one thread per 16-byte chunk (four pairs) of a (row, head) row, chunk
+//  1. Side by side: wave 0 validates the rows (lane, slot, freeze, page),
+//     finding the lanes of the group's first and last rows with a 32-way
+//     search per half wave (one round of loads per factor of 32 lanes) and
+//     each row's lane between those two; the other waves put the fp64
+//     (cos, sin) of every (row, RoPE pair) in LDS, shared by the row's KV
+//     heads. (Issuing the first K and V loads before this was slower.)
+//  2. K: one thread per 16-byte chunk (four pairs) of a (row, head) row, chunk
 //     index fastest, so a wave reads and writes whole 256-byte head rows.
-//  4. V goes through LDS a group of heads at a time (16-byte loads), rows
+//  3. V goes through LDS a group of heads at a time (16-byte loads), rows
 //     padded by 16 bytes, then is stored into the V^T block. Eight rows at
 //     consecutive slots filling an aligned 8-slot segment of one page (most
 //     of a prefill chunk) are a full segment: per (head, dim) column a thread
@@ -88,7 +91,7 @@ __device__ __forceinline__ uint4 rotate_chunk(uint4 x, const double2 *cs) {
 //     stores still cover consecutive bytes of V^T rows.
 template <int D>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
-    constexpr int PAIRS = D / 2, C8 = D / 8, CSH = D == 128 ? 4 : 3, DSH = D == 128 ? 7 : 6;
+    constexpr int PAIRS = D / 2, C8 = D / 8, CSH = D == 128 ? 4 : 3;
     __shared__ int64_t s_base[kAppendRows];  // element offset of the row's page, -1: row not written
     __shared__ int s_off[kAppendRows];
     __shared__ double2 s_cs[kAppendRows * PAIRS];
@@ -103,13 +106,61 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     const int nr = (int)(a.N - r0 < R ? a.N - r0 : R);
     const int tid = threadIdx.x;
     const int H = a.H;
-    if (tid < kAppendRows) {
+    const int nk = nr * H * C8;                                          // K chunks
+    const int hg = max(1, min(H, (kAppendVBytes / 2 - 8 * R) / (R * D)));  // V heads per round
+    // 16-byte chunks of K (e < nk) and of V's head round h0 (e < nr * hn * C8), kBatch per thread
+    auto load_k = [&](int e0, uint4 (&x)[kBatch]) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + 256 * u;
+            const int rh = e >> CSH;  // (row - r0) * H + head: the row's K rows are contiguous
+            x[u] = e < nk ? *reinterpret_cast<const uint4 *>(a.k + (r0 * H + rh) * D + 8 * (e & (C8 - 1)))
+                          : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto load_v = [&](int e0, int h0, int hn, uint4 (&x)[kBatch]) {
+        const int nv = nr * hn * C8;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + 256 * u;
+            const int c = e & (C8 - 1), rh = e >> CSH;
+            const int j = rh / hn, hh = rh - j * hn;
+            x[u] = e < nv ? *reinterpret_cast<const uint4 *>(a.v + (r0 + j) * H * D + (int64_t)(h0 + hh) * D + 8 * c)
+                          : make_uint4(0, 0, 0, 0);
+        }
+    };
+    if (tid < kWave) {
+        // lanes of the group's first row (half wave 0) and last row (half wave 1):
+        // largest lane l with indptr[l] <= row, probing 32 evenly spaced lanes
+        // of the remaining range per round (the probes that hold are a prefix)
+        const int half = tid >> 5, q = tid & 31;
+        const int64_t target = half ? r0 + nr - 1 : r0;
+        const int slot = tid < nr ? a.slots[r0 + tid] : 0;
+        int lo = 0, hi = a.L;  // answer in [lo, hi)
+        while (__ballot(hi - lo > 1)) {
+            const bool busy = hi - lo > 1;
+            const int step = (hi - lo + 31) >> 5;
+            const int pr = lo + q * step;
+            const uint64_t b = __ballot(busy && pr < hi && (int64_t)a.indptr[pr] <= target);
+            if (busy) {
+                // the probe at lo holds when indptr is ordered; at least 1 keeps
+                // [lo, hi) inside the lanes whatever the device copy holds
+                const int k = max(1, __popc(half ? (uint32_t)(b >> 32) : (uint32_t)b));
+                hi = min(hi, lo + k * step);
+                lo += (k - 1) * step;
+            }
+        }
+        const int lane_first = __builtin_amdgcn_readlane(lo, 0), lane_last = __builtin_amdgcn_readlane(lo, 32);
         int64_t base = -1;
         int off = 0;
         if (tid < nr) {
             const int64_t row = r0 + tid;
-            const int lane = find_lane(a.indptr, a.L, row);
-            const int slot = a.slots[row];
+            int l0 = lane_first, l1 = lane_last + 1;  // the row's lane lies in [l0, l1)
+            while (l1 - l0 > 1) {
+                const int mid = (l0 + l1) >> 1;
+                if ((int64_t)a.indptr[mid] <= row) l0 = mid; else l1 = mid;
+            }
+            const int lane = l0;
             const int p0 = a.page_indptr[lane];
             const int cap = (a.page_indptr[lane + 1] - p0) * a.P;
             if (slot < 0 || slot >= cap) {
@@ -126,13 +177,16 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
                 }
             }
         }
-        s_base[tid] = base;
-        s_off[tid] = off;
-    }
-    for (int e = tid; e < nr * PAIRS; e += blockDim.x) {
-        double c, sn;
-        rope_cos_sin(a.positions[r0 + (e / PAIRS)], a.freqs.w[e % PAIRS], &c, &sn);
-        s_cs[e] = make_double2(c, sn);
+        if (tid < kAppendRows) {
+            s_base[tid] = base;
+            s_off[tid] = off;
+        }
+    } else {
+        for (int e = tid - kWave; e < nr * PAIRS; e += blockDim.x - kWave) {
+            double c, sn;
+            rope_cos_sin(a.positions[r0 + (e / PAIRS)], a.freqs.w[e % PAIRS], &c, &sn);
+            s_cs[e] = make_double2(c, sn);
+        }
     }
     __syncthreads();
     if (tid < 64) {  // V^T store lists, by the first wave (read after the V staging barrier)
@@ -160,16 +214,9 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     }
     // K chunks kBatch at a time per thread: all loads of a batch are issued
     // before the first rotation, so a thread keeps kBatch loads in flight
-    const int nk = nr * H * C8;
     for (int e0 = tid; e0 < nk; e0 += kBatch * 256) {
-        uint4 x[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int e = e0 + 256 * u;
-            const int rh = e >> CSH;  // (row - r0) * H + head: the row's K rows are contiguous
-            x[u] = e < nk ? *reinterpret_cast<const uint4 *>(a.k + (r0 * H + rh) * D + 8 * (e & (C8 - 1)))
-                          : make_uint4(0, 0, 0, 0);
-        }
+        uint4 xk[kBatch];
+        load_k(e0, xk);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int e = e0 + 256 * u;
@@ -179,32 +226,24 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
             const int64_t base = s_base[j];
             if (base >= 0)
                 *reinterpret_cast<uint4 *>(a.pool + base + ((int64_t)h * a.P + s_off[j]) * D + 8 * c) =
-                    rotate_chunk(x[u], &s_cs[j * PAIRS + 4 * c]);
+                    rotate_chunk(xk[u], &s_cs[j * PAIRS + 4 * c]);
         }
     }
     const int64_t vblock = (int64_t)H * a.P * D;  // V block [H][D][P] follows the K block
-    const int hg = max(1, min(H, (kAppendVBytes / 2 - 8 * R) / (R * D)));  // heads per round
     for (int h0 = 0; h0 < H; h0 += hg) {
         const int hn = min(hg, H - h0);
         const int rs = hn * D + 8;  // LDS row stride (elements): 16 bytes of padding per row
         const int nv = nr * hn * C8;
         for (int e0 = tid; e0 < nv; e0 += kBatch * 256) {
-            uint4 x[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int e = e0 + 256 * u;
-                const int c = e & (C8 - 1), rh = e >> CSH;
-                const int j = rh / hn, hh = rh - j * hn;
-                x[u] = e < nv ? *reinterpret_cast<const uint4 *>(a.v + (r0 + j) * H * D + (int64_t)(h0 + hh) * D + 8 * c)
-                              : make_uint4(0, 0, 0, 0);
-            }
+            uint4 xv[kBatch];
+            load_v(e0, h0, hn, xv);
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int e = e0 + 256 * u;
                 if (e >= nv) break;
                 const int c = e & (C8 - 1), rh = e >> CSH;
                 const int j = rh / hn, hh = rh - j * hn;
-                *reinterpret_cast<uint4 *>(&s_v[j * rs + hh * D + 8 * c]) = x[u];
+                *reinterpret_cast<uint4 *>(&s_v[j * rs + hh * D + 8 * c]) = xv[u];
             }
         }
         __syncthreads();
