@@ -932,8 +932,8 @@ def rate(units: float, ms_list, scale: float) -> float:
 def decode_windows(w, r, peak_meas=None) -> dict:
     """HBM-bound decode figures of one measurement: algorithmic KV bytes of the
     decode-class lanes over the decode kernel alone, decode + split merge
-    (survey row a4), the whole fp_attend call (plan, Q rotation, tile lists,
-    attention, merge) and the whole step."""
+    (the split-KV decode with its reduction), the whole fp_attend call (plan,
+    Q rotation, tile lists, attention, merge) and the whole step."""
     b = w["kv_bytes_decode"]
     out = {}
     for name, key in (("decode_kernel", "decode_ms"), ("decode_plus_merge", "a4_ms"), ("fp_attend", "call_ms"),
