@@ -569,7 +569,7 @@ def extra_configs(W, runner, seed, pk_hbm, pk_mfma) -> dict:
                                         "H_q=32 H_kv=8 d=128, P=16", "steps": 5, "warmup": 1,
                             "attended_kv_bytes": attended, "kv_bytes_if_unmasked": int(ww["kv_bytes_decode"]),
                             "tile_bytes_upper_bound": tiles,
-                            "decode_ms": _stats(rw["decode_ms"]), "a4_ms": _stats(rw["a4_ms"]),
+                            "decode_ms": _stats(rw["decode_ms"]), "decode_merge_ms": _stats(rw["decode_merge_ms"]),
                             "fp_attend_ms": _stats(rw["call_ms"]), "step_ms": _stats(rw["step_ms"]),
                             "GB/s_attended": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
     del wlw
@@ -869,7 +869,7 @@ def measure(W, runner, cfg, seed, split, K, Wm, mass=None, flush=True, wl=None):
     res["attn_ms"] = [ev.elapsed_ms(b, e) for b, e, _, _ in hip_ev]
     res["prefill_ms"] = [ev.elapsed_ms(b, p) for b, _, p, _ in hip_ev]
     res["decode_ms"] = [ev.elapsed_ms(p, e) for _, e, p, _ in hip_ev]
-    res["a4_ms"] = [ev.elapsed_ms(p, m) for _, _, p, m in hip_ev]  # decode kernel + split merge
+    res["decode_merge_ms"] = [ev.elapsed_ms(p, m) for _, _, p, m in hip_ev]  # decode kernel + split merge
     status = int(ds.status.cpu()[0])
     if status != 0:
         print(f"warning: device status {status} (config {cfg})", file=sys.stderr)
@@ -936,7 +936,7 @@ def decode_windows(w, r, peak_meas=None) -> dict:
     Q rotation, tile lists, attention, merge) and the whole step."""
     b = w["kv_bytes_decode"]
     out = {}
-    for name, key in (("decode_kernel", "decode_ms"), ("decode_plus_merge", "a4_ms"), ("fp_attend", "call_ms"),
+    for name, key in (("decode_kernel", "decode_ms"), ("decode_plus_merge", "decode_merge_ms"), ("fp_attend", "call_ms"),
                       ("step", "step_ms")):
         gbs = rate(b, r[key], 1e9)
         out[name] = {"ms": _stats(r[key]), "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
