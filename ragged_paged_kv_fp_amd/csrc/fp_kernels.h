@@ -749,6 +749,18 @@ constexpr int kRopeThreads = 256;
 template <int D>
 __global__ void __launch_bounds__(kRopeThreads) rope_q_kernel(RopeQArgs ra) { rope_q_body<D>(ra, (int)blockIdx.x); }
 
+// The plan and the Q rotation in one launch, for passes whose rotation needs
+// few workgroups (a decode wave): workgroup 0 plans, workgroup 1 + b rotates
+// row group b. One launch and its gap fewer; the rotation workgroups carry
+// the plan's block size and LDS, which matters only when there are many.
+constexpr int kPrepMaxRopeBlocks = 255;
+
+template <int D>
+__global__ void __launch_bounds__(kPlanThreads) prep_kernel(PlanArgs pa, RopeQArgs ra) {
+    if (blockIdx.x == 0) plan_body(pa);
+    else rope_q_body<D>(ra, (int)blockIdx.x - 1);
+}
+
 // ============================================================================ mask summary
 
 struct SummaryArgs {

@@ -373,12 +373,20 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
     ra.qscale = (double)sm_scale * 1.4426950408889634;  // log2(e)
     ra.freqs = rope_freqs(rope_theta, p.D);
     ra.rshift = row_group_shift(p.N, kQRows);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, pa);
-    if ((rc = launch_ok())) return rc;
-    const dim3 rgrid((unsigned)((p.N + (1 << ra.rshift) - 1) >> ra.rshift));
-    if (p.D == 128) hipLaunchKernelGGL(rope_q_kernel<128>, rgrid, dim3(kRopeThreads), 0, stream, ra);
-    else hipLaunchKernelGGL(rope_q_kernel<64>, rgrid, dim3(kRopeThreads), 0, stream, ra);
-    if ((rc = launch_ok())) return rc;
+    const int64_t rblocks = (p.N + (1 << ra.rshift) - 1) >> ra.rshift;
+    if (rblocks <= kPrepMaxRopeBlocks) {  // plan and Q rotation in one launch
+        const dim3 pgrid((unsigned)(1 + rblocks));
+        if (p.D == 128) hipLaunchKernelGGL(prep_kernel<128>, pgrid, dim3(kPlanThreads), 0, stream, pa, ra);
+        else hipLaunchKernelGGL(prep_kernel<64>, pgrid, dim3(kPlanThreads), 0, stream, pa, ra);
+        if ((rc = launch_ok())) return rc;
+    } else {
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, pa);
+        if ((rc = launch_ok())) return rc;
+        const dim3 rgrid((unsigned)rblocks);
+        if (p.D == 128) hipLaunchKernelGGL(rope_q_kernel<128>, rgrid, dim3(kRopeThreads), 0, stream, ra);
+        else hipLaunchKernelGGL(rope_q_kernel<64>, rgrid, dim3(kRopeThreads), 0, stream, ra);
+        if ((rc = launch_ok())) return rc;
+    }
 
     AttnArgs a;
     a.pool = static_cast<const uint16_t *>(pool->kv);
