@@ -299,10 +299,11 @@ struct DecShared {
     static constexpr int W = dec_waves<NC>();
     float ml[W][2][32];
     float fin[2][32];
-    union {
+    union __attribute__((aligned(16))) {  // 16-byte LDS accesses
         float o[W][NC][kLdsRow];
         char k[W][DecLds<D>::BYTES];
     } u;
+    int steps[W];  // tile steps of each wave (masked launch)
 };
 
 // One work item (lane, KV head, KV split): every barrier inside is reached by
@@ -417,7 +418,29 @@ __device__ __forceinline__ void decode_item(const AttnArgs &a, const int4 it, De
         s_ml[wv][0][col] = w.m;
         s_ml[wv][1][col] = lsum;
     }
+    if constexpr (MASKED) {
+        if (l == 0) sh.steps[wv] = nsteps;
+    }
     __syncthreads();
+    const bool single = li.nsplit <= 1;
+    const int64_t pidx = (int64_t)li.dec_off + (int64_t)g * li.nsplit + s0 / a.split;  // (lane, KV head, split)
+    // A masked lane's split whose share of the tile list is empty for every
+    // wave (most splits of a windowed lane) leaves only its statistics: max
+    // -inf and sum 0, which give it weight 0 in the merge, so its partial
+    // output is neither written nor read. (Unmasked kernels keep one path:
+    // this branch there changed how the compiler schedules the first tile.)
+    if constexpr (MASKED) {
+        int steps = 0;
+#pragma unroll
+        for (int v = 0; v < kDecWaves; ++v) steps += sh.steps[v];
+        if (!single && steps == 0) {  // workgroup-uniform
+            for (int n = threadIdx.x; n < ncols; n += kDecThreads) {
+                a.part_ml[pidx * 64 + n] = kNegInf;
+                a.part_ml[pidx * 64 + 32 + n] = 0.0f;
+            }
+            return;
+        }
+    }
     float M = kNegInf;
 #pragma unroll
     for (int v = 0; v < kDecWaves; ++v) M = fmaxf(M, s_ml[v][0][col]);
@@ -430,8 +453,6 @@ __device__ __forceinline__ void decode_item(const AttnArgs &a, const int4 it, De
         s_fin[0][col] = M;
         s_fin[1][col] = L;
     }
-    const bool single = li.nsplit <= 1;
-    const int64_t pidx = (int64_t)li.dec_off + (int64_t)g * li.nsplit + s0 / a.split;  // (lane, KV head, split)
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) {
         stage_o<D, NC>(w, c, scale, &s_o[wv][col][0]);
@@ -558,17 +579,21 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(AttnArgs a) {
                     const int n = e4 / D4;
                     const float Mn = s_M[n];
                     const float w = Mn == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(s_m[b0 + b][n] - Mn);
-                    const float4 v = pre[b][k];
-                    acc[k].x += w * v.x;
-                    acc[k].y += w * v.y;
-                    acc[k].z += w * v.z;
-                    acc[k].w += w * v.w;
+                    if (w != 0.0f) {  // a split of weight 0 may have left no partial output
+                        const float4 v = pre[b][k];
+                        acc[k].x += w * v.x;
+                        acc[k].y += w * v.y;
+                        acc[k].z += w * v.z;
+                        acc[k].w += w * v.w;
+                    }
                 }
                 const int nx = sp + kMergeBatch;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int e4 = tid + kMergeThreads * k;
-                    if (nx < ns && e4 < n4) pre[b][k] = po[nx * ostride4 + e4];
+                    // splits of this chunk whose column max is -inf are not loaded
+                    if (nx < ns && e4 < n4 && (nx >= c0 + cn || s_m[nx - c0][e4 / D4] != kNegInf))
+                        pre[b][k] = po[nx * ostride4 + e4];
                 }
             }
         }

@@ -129,6 +129,30 @@ def test_window_decode_lanes_walk_tile_lists(seed, L, kv, window, sinks, P):
     _say(pu.compare_step(ds, ref))
 
 
+@pytest.mark.parametrize("split", [64, 512])
+def test_empty_splits_leave_no_partials(split):
+    """Masked decode lanes whose tile lists fall in a few KV splits: the other
+    splits of each (lane, KV head) hold no tile, write only max -inf and sum
+    0, and the merge gives them weight 0 without reading their partial
+    output. The workspace starts as NaN bytes, so any partial output the
+    merge read without it having been written would show."""
+    import torch
+
+    from ragged_paged_kv_fp_amd import runner
+
+    wl = W.make_window_decode(2, L=5, kv=5000, window=77, sinks=2, H_q=16, H_kv=4, d=128, P=8)
+    _say(f"window decode with empty splits: split={split}")
+    ref = pu.oracle_run(wl)
+    ds = runner.DeviceStep(wl, device="cuda", split=split)
+    ds.run_prefix()
+    torch.cuda.synchronize()
+    ds.workspace.fill_(0xFF)
+    ds.status.zero_()
+    ds.step()
+    torch.cuda.synchronize()
+    _say(pu.compare_step(ds, ref))
+
+
 def _hazard_bits(wl):
     """fp_check_hazards on the GPU and oracle.hazards, both after the prefix pass and its fold."""
     import torch
