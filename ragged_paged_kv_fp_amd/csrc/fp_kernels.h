@@ -67,6 +67,22 @@ __device__ __forceinline__ uint4 rotate_chunk(uint4 x, const double2 *cs) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// One 16-byte chunk of a query row (four RoPE pairs) rotated in fp32 by the
+// pairs' prescaled (cos, sin) and rounded to nearest-even bf16. The query is
+// rounded to bf16 for the MFMA in any case; fp32 changes that rounding only
+// where the fp64 product lies within a few fp32 ulps of a bf16 rounding
+// boundary, and then by one bf16 ulp.
+__device__ __forceinline__ uint4 rotate_chunk_f32(uint4 x, const float2 *cs) {
+    uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float x0 = bf16_lo(w[q]), x1 = bf16_hi(w[q]);
+        const float2 r = cs[q];
+        w[q] = pack_bf16x2(fmaf(x0, r.x, -x1 * r.y), fmaf(x0, r.y, x1 * r.x));
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // One workgroup per 2^rshift consecutive rows. Workgroups are dealt to the 8
 // XCDs in turn, so block b takes row group (b mod 8) * ceil-share + b / 8:
 // each XCD gets a contiguous run of groups, and neighbouring groups, which
@@ -456,23 +472,24 @@ struct RopeQArgs {
 
 constexpr int kQRows = 16;  // most rows one Q-rotation workgroup handles
 
-// One workgroup per 2^rshift rows: the fp64 (cos, sin) of every (row, pair),
-// prescaled by qscale, go to LDS (all query heads of a row share them), then
-// one thread per 16-byte chunk (four pairs) of a (row, head) row rotates it
-// and rounds it once to bf16; consecutive threads take consecutive chunks, so
+// One workgroup per 2^rshift rows: the (cos, sin) of every (row, pair),
+// computed in fp64, prescaled by qscale and rounded to fp32, go to LDS (all
+// query heads of a row share them), then one thread per 16-byte chunk (four
+// pairs) of a (row, head) row rotates it in fp32 and rounds it to bf16
+// (rotate_chunk_f32); consecutive threads take consecutive chunks, so
 // a wave reads and writes whole head rows. Output: the rotated, prescaled Q in
 // bf16, same [N][Hq][D] layout as q.
 template <int D>
 __device__ __forceinline__ void rope_q_body(const RopeQArgs &a, int block) {
     constexpr int PAIRS = D / 2, C8 = D / 8, CSH = D == 128 ? 4 : 3;
-    __shared__ double2 s_cs[kQRows * PAIRS];
+    __shared__ float2 s_cs[kQRows * PAIRS];
     const int R = 1 << a.rshift;
     const int64_t r0 = (int64_t)block << a.rshift;
     const int nr = (int)(a.N - r0 < R ? a.N - r0 : R);
     for (int e = threadIdx.x; e < nr * PAIRS; e += blockDim.x) {
         double c, sn;
         rope_cos_sin(a.positions[r0 + (e / PAIRS)], a.freqs.w[e % PAIRS], &c, &sn);
-        s_cs[e] = make_double2(c * a.qscale, sn * a.qscale);
+        s_cs[e] = make_float2((float)(c * a.qscale), (float)(sn * a.qscale));
     }
     __syncthreads();
     const int Hq = a.Hq;
@@ -492,7 +509,7 @@ __device__ __forceinline__ void rope_q_body(const RopeQArgs &a, int block) {
             if (e >= nq) break;
             const int c = e & (C8 - 1), rh = e >> CSH;
             const int j = rh / Hq;
-            *reinterpret_cast<uint4 *>(a.qrot + (r0 * Hq + rh) * D + 8 * c) = rotate_chunk(x[u], &s_cs[j * PAIRS + 4 * c]);
+            *reinterpret_cast<uint4 *>(a.qrot + (r0 * Hq + rh) * D + 8 * c) = rotate_chunk_f32(x[u], &s_cs[j * PAIRS + 4 * c]);
         }
     }
 }
