@@ -767,10 +767,12 @@ template <int D>
 __global__ void __launch_bounds__(kRopeThreads) rope_q_kernel(RopeQArgs ra) { rope_q_body<D>(ra, (int)blockIdx.x); }
 
 // The plan and the Q rotation in one launch, for passes whose rotation needs
-// few workgroups (a decode wave): workgroup 0 plans, workgroup 1 + b rotates
-// row group b. One launch and its gap fewer; the rotation workgroups carry
-// the plan's block size and LDS, which matters only when there are many.
-constexpr int kPrepMaxRopeBlocks = 255;
+// at most about four workgroups per compute unit (decode and verify waves):
+// workgroup 0 plans, workgroup 1 + b rotates row group b on the other compute
+// units while the plan, the longer of the two, runs. One launch and its gap
+// fewer; the rotation workgroups carry the plan's block size and LDS, which
+// matters only when there are many.
+constexpr int kPrepMaxRopeBlocks = 1023;
 
 template <int D>
 __global__ void __launch_bounds__(kPlanThreads) prep_kernel(PlanArgs pa, RopeQArgs ra) {
