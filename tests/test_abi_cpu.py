@@ -121,6 +121,15 @@ def test_bad_arguments_rejected(lib, mut, code):
     assert _ws(lib, p, g, hq=hq) == code
 
 
+def test_lane_limit(lib):
+    """4096 lanes (the plan's limit) are accepted; 4097 are refused before
+    anything is enqueued."""
+    for L, ok in ((4096, True), (4097, False)):
+        g, p, keep = _structs(L=L, rows=[1] * L, pages=[1] * L)
+        n = _ws(lib, p, g)
+        assert (n > 0) if ok else (n == -3), (L, n)
+
+
 def test_workspace_too_small_and_null_pointers(lib):
     g, p, keep = _structs()
     st = ctypes.c_int32(0)

@@ -56,6 +56,19 @@ def test_random_geometry(seed, H_kv, G, d, P):
     _say(pu.compare_step(ds, ref))
 
 
+def test_maximum_lanes():
+    """4096 lanes, the plan's limit (each plan thread then classifies four
+    lanes): decode, verify, prefill and empty lanes, causal and bitmap lanes,
+    every fold mode, against the oracle."""
+    wl = W.make_random(71, H_kv=1, G=2, d=64, P=8, num_lanes=4096, max_rows=24, max_ctx=60, extra_pages=4)
+    n = np.diff(wl.step.indptr)
+    _say(f"maximum lanes: lanes={wl.num_lanes} rows={wl.step.num_rows} decode-class={int(((n > 0) & (n * 2 <= 32)).sum())} "
+         f"prefill-class={int((n * 2 > 32).sum())} empty={int((n == 0).sum())}")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)
+    _say(pu.compare_step(ds, ref))
+
+
 HOLE_BITS = 0x3FC0  # bf16 1.5: what a slot no pass wrote holds (finite, as the step requires below kv_len)
 
 
