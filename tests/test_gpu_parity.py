@@ -328,6 +328,21 @@ def test_decode_split_size_invariance(split):
     pu.compare_step(ds, ref)
 
 
+@pytest.mark.parametrize("seed,split", [(91, 32), (82, 96)])
+def test_merge_over_many_splits(seed, split):
+    """Decode and verify lanes of up to 6000 slots at 32- and 96-slot splits:
+    up to about 190 splits per (lane, KV head), so the merge takes its split
+    statistics in more than one chunk of 128; bitmap lanes among them leave
+    empty splits that the merge must skip in every chunk."""
+    wl = W.make_random(seed, H_kv=2, G=4, d=128, P=16, num_lanes=8, max_rows=9, max_ctx=6000, masked=True)
+    n = np.diff(wl.step.indptr)
+    cap = np.diff(wl.page_indptr) * wl.P
+    _say(f"many splits seed {seed} split {split}: most splits {int((cap[n > 0] + split - 1).max() // split)}")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl, split=split)
+    _say(pu.compare_step(ds, ref))
+
+
 def test_plan_mismatch_emits_no_attention_work():
     """Launches are sized from the host copies of the offset arrays; when the
     device indptr disagrees (here: one row more in the last lane, or a row
