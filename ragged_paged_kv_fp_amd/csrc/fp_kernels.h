@@ -783,8 +783,8 @@ __global__ void __launch_bounds__(kPlanThreads) prep_kernel(PlanArgs pa, RopeQAr
 // ============================================================================ mask summary
 
 struct SummaryArgs {
-    int64_t n_pre;  // prefill items; workgroups past them take decode lane blockIdx.x - n_pre
-    int L;
+    int64_t n_pre;  // prefill items (a multiple of H: each lane's come in groups of its KV heads)
+    int L, H;
     const int4 *pre_items;
     const LaneInfo *lane_info;
     const int32_t *indptr, *page_indptr, *kv_len;
@@ -800,16 +800,20 @@ struct SummaryArgs {
 // has an allowed slot, in increasing order, each entry tagged in bit 31 when
 // every row of the block may read every slot of the tile. Record layout:
 // [count, entry 0, entry 1, ...]. The prefill kernel walks this list, so
-// tiles with no allowed slot are never loaded.
-constexpr int kSumThreads = 256;
+// tiles with no allowed slot are never loaded. The plan lists a lane's prefill
+// items with the KV head fastest, so the KV-head-0 items, one per row block,
+// are items 0, H, 2H, ...: workgroup b < n_pre / H takes item b * H, and the
+// workgroups after them take the masked decode lanes.
+constexpr int kSumThreads = 1024;  // one thread per tile of up to 32768 slots: one pass over the rows
 
 __global__ void __launch_bounds__(kSumThreads) summary_kernel(SummaryArgs a) {
     __shared__ int s_wc[kSumThreads / kWave];
     int l, rstart, nr;
     LaneInfo li;
     int32_t *rec;
-    if ((int64_t)blockIdx.x < a.n_pre) {  // a row block of a masked prefill lane (its KV head 0 item)
-        const int4 it = a.pre_items[blockIdx.x];
+    const int64_t n_blocks = a.n_pre / a.H;
+    if ((int64_t)blockIdx.x < n_blocks) {  // a row block of a masked prefill lane (its KV head 0 item)
+        const int4 it = a.pre_items[(int64_t)blockIdx.x * a.H];
         if (it.x < 0 || it.y != 0) return;
         l = it.x;
         li = a.lane_info[l];
@@ -818,7 +822,7 @@ __global__ void __launch_bounds__(kSumThreads) summary_kernel(SummaryArgs a) {
         nr = it.w;
         rec = a.summary + li.sum_off + (int64_t)(rstart / prefill_rows(a.G)) * li.sum_stride;
     } else {  // a masked decode lane: one list over all its rows
-        l = (int)(blockIdx.x - a.n_pre);
+        l = (int)(blockIdx.x - n_blocks);
         if (l >= a.L) return;
         li = a.lane_info[l];
         if (li.sum_off < 0 || li.dec_off < 0) return;
@@ -841,14 +845,14 @@ __global__ void __launch_bounds__(kSumThreads) summary_kernel(SummaryArgs a) {
         uint32_t any = 0, all = ~0u;
         if (inr) {
             int r = 0;
-            for (; r + 8 <= nr; r += 8) {
-                uint32_t w8[8];
+            for (; r + 16 <= nr; r += 16) {  // 16 rows' words in flight per thread
+                uint32_t w16[16];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) w8[u] = rb[(int64_t)(r + u) * wpr + t];
+                for (int u = 0; u < 16; ++u) w16[u] = rb[(int64_t)(r + u) * wpr + t];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    any |= w8[u];
-                    all &= w8[u];
+                for (int u = 0; u < 16; ++u) {
+                    any |= w16[u];
+                    all &= w16[u];
                 }
             }
             for (; r < nr; ++r) {

@@ -128,11 +128,13 @@ int resident_blocks(Kernel kernel, int threads) {
 constexpr int kSplitRefine[] = {3072, 1536, 1024, 512};
 constexpr double kItemStartTiles = 6.0;
 constexpr double kRefineGain = 0.9;
-constexpr int kRefineSlots = 4096;  // most slots the estimate keeps (more are folded in)
+constexpr int kRefineSlots = 2048;  // most slots the estimate keeps (more are folded in)
 
+// Stack use stays near 12 KB: a last split is at most 128 tiles (splits are at
+// most 4096 slots), and a slot's load, a sum of tile counts, is exact in float.
 double decode_makespan(const fp_kv_pool *pool, const fp_geometry *geom, int G, int split, int m) {
-    int lasts[kMaxLanes];  // the last split of each decode lane, in tiles
-    double load[kRefineSlots];
+    uint8_t lasts[kMaxLanes];  // the last split of each decode lane, in tiles
+    float load[kRefineSlots];
     int nl = 0;
     int64_t nfull = 0;
     for (int l = 0; l < geom->num_lanes; ++l) {
@@ -141,23 +143,23 @@ double decode_makespan(const fp_kv_pool *pool, const fp_geometry *geom, int G, i
         const int cap = (pool->page_indptr_host[l + 1] - pool->page_indptr_host[l]) * pool->page_size;
         const int ns = cap > 0 ? (cap + split - 1) / split : 1;
         nfull += ns - 1;
-        lasts[nl++] = cap > 0 ? (cap - (ns - 1) * split + 31) / 32 : 0;
+        lasts[nl++] = (uint8_t)(cap > 0 ? (cap - (ns - 1) * split + 31) / 32 : 0);
     }
-    std::sort(lasts, lasts + nl, std::greater<int>());
+    std::sort(lasts, lasts + nl, std::greater<uint8_t>());
     m = std::max(1, std::min(m, kRefineSlots));
-    const double cf = kItemStartTiles + split / 32;
+    const float cf = (float)(kItemStartTiles + split / 32);
     const int64_t per = nfull / m, rem = nfull % m;
-    double end = 0;
+    float end = 0.0f;
     for (int i = 0; i < m; ++i) {
-        load[i] = (double)(per + (i < rem ? 1 : 0)) * cf;
+        load[i] = (float)(per + (i < rem ? 1 : 0)) * cf;
         end = std::max(end, load[i]);
     }
-    std::make_heap(load, load + m, std::greater<double>());  // min-heap: the slot that frees up first
+    std::make_heap(load, load + m, std::greater<float>());  // min-heap: the slot that frees up first
     for (int i = 0; i < nl; ++i) {
-        std::pop_heap(load, load + m, std::greater<double>());
-        load[m - 1] += kItemStartTiles + lasts[i];
+        std::pop_heap(load, load + m, std::greater<float>());
+        load[m - 1] += (float)kItemStartTiles + lasts[i];
         end = std::max(end, load[m - 1]);
-        std::push_heap(load, load + m, std::greater<double>());
+        std::push_heap(load, load + m, std::greater<float>());
     }
     return end;
 }
@@ -416,6 +418,7 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
         SummaryArgs sa;
         sa.n_pre = p.n_pre;
         sa.L = p.L;
+        sa.H = p.H;
         sa.pre_items = pre_items;
         sa.lane_info = lane_info;
         sa.indptr = geom->indptr;
@@ -426,8 +429,8 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
         sa.P = p.P;
         sa.G = p.G;
         sa.summary = reinterpret_cast<int32_t *>(ws + p.off_sum);
-        hipLaunchKernelGGL(summary_kernel, dim3((unsigned)(p.n_pre + (p.dec_lists ? p.L : 0))), dim3(kSumThreads), 0,
-                           stream, sa);
+        hipLaunchKernelGGL(summary_kernel, dim3((unsigned)(p.n_pre / p.H + (p.dec_lists ? p.L : 0))), dim3(kSumThreads),
+                           0, stream, sa);
         if ((rc = launch_ok())) return rc;
     }
     if (tuning && tuning->attn_begin && hipEventRecord(tuning->attn_begin, stream) != hipSuccess) return FP_ERR_HIP;
