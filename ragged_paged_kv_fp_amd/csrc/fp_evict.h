@@ -156,12 +156,32 @@ __global__ void __launch_bounds__(kTovaThreads) tova_select_kernel(TovaArgs a) {
         __syncthreads();
         int *hist = s_hist[tid / kWave];
         if (in_lds) {
-#pragma unroll 8
+            // Lanes whose keys share the digit add once: the masses of a lane
+            // mostly share their sign and exponent, so in the first pass nearly
+            // every lane of a wave hits one bin, and an atomic per lane would
+            // serialise on it. A group of fewer than 8 lanes ends the
+            // aggregation; the rest (diverse digits) add one by one.
+#pragma unroll 4
             for (int u = 0; u < PER; ++u) {
                 const int j = tid + u * kTovaThreads;
+                bool has = false;
+                uint32_t d = 0;
                 if (j < c && cand_bit(j)) {
                     const uint32_t key = s_key[j];
-                    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+                    has = (key & pmask) == prefix;
+                    d = (key >> shift) & 255u;
+                }
+                uint64_t todo = __ballot(has);
+                while (todo) {  // wave-uniform
+                    const int leader = __builtin_ctzll(todo);
+                    const uint32_t dl = __shfl(d, leader);
+                    const uint64_t same = __ballot(has && d == dl) & todo;
+                    if (__popcll(same) < 8) {
+                        if (has && ((todo >> lane_id()) & 1ull)) atomicAdd(&hist[d], 1);
+                        break;
+                    }
+                    if (lane_id() == leader) atomicAdd(&hist[dl], (int)__popcll(same));
+                    todo &= ~same;
                 }
             }
         } else {
