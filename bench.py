@@ -498,7 +498,7 @@ def main(argv=None):
                    "lanes": wl.num_lanes, "rows": wl.step.num_rows, "kv_bytes_decode": w["kv_bytes_decode"],
                    "attn_flops": w["flops"], "attended_pairs": w["pairs"]},
         "timing": {"protocol": ("per step: untimed 1 GiB read of other data (evicts L2 and MALL), then events around "
-                                "reset->append->attend->fold->readout; value and ms_per_step are the mean of the K "
+                                "reset->append->attend->fold+readout; value and ms_per_step are the mean of the K "
                                 "flushed steps" if not args.no_flush else "no flush between steps"),
                    "step_ms": _stats(r["step_ms"]),
                    "unflushed_ms_per_step": round(r["unflushed_ms_per_step"], 4),
@@ -860,8 +860,7 @@ def measure(W, runner, cfg, seed, split, K, Wm, mass=None, flush=True, wl=None):
         cb.record(stream)
         ds.attend(events=hip_ev[i])
         ce.record(stream)
-        ds.fold()
-        ds.readout()
+        ds.finish()
         se.record(stream)
     torch.cuda.synchronize()
     res["step_ms"] = [sb.elapsed_time(se) for sb, _, _, se in step_ev]

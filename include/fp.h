@@ -13,7 +13,8 @@
  * Eqs. (1) and (2)); the pages of a lane's working set are listed in slot order.
  *
  * A step is four calls, enqueued in this order on one stream:
- *   fp_append_kv -> fp_attend -> fp_fold -> fp_readout.
+ *   fp_append_kv -> fp_attend -> fp_fold -> fp_readout
+ * (or three, with fp_fold_readout in place of the last two).
  * A repeating decode loop may enqueue fp_advance after fp_fold to write the
  * next pass's geometry on the device.
  *
@@ -231,6 +232,19 @@ int fp_fold(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *chan
  */
 int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, const int32_t *rows,
                int32_t num_readout, float *dst, int32_t *status, hipStream_t stream);
+
+/*
+ * fp_fold_readout - fp_fold and fp_readout of the same pass in one launch (the
+ * two stages read and write disjoint memory, so neither waits on the other).
+ * Arguments, results and status bits are exactly those of
+ * fp_fold(pool, geom, channel, status) followed by
+ * fp_readout(geom, out, row_elems, rows, num_readout, dst, status). Every
+ * check of both calls runs before anything is enqueued: on an error neither
+ * stage runs.
+ */
+int fp_fold_readout(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *channel, const float *out,
+                    int32_t row_elems, const int32_t *rows, int32_t num_readout, float *dst, int32_t *status,
+                    hipStream_t stream);
 
 /* Workspace bytes fp_check_hazards needs: three int32 per KV cell (num_pages * P cells). */
 int64_t fp_hazard_workspace_bytes(const fp_kv_pool *pool);

@@ -39,7 +39,7 @@ FP_FOLD_CHANNEL = -2
 
 EXPORTS = ("fp_append_kv", "fp_attend_workspace_bytes", "fp_attend", "fp_attend_noalloc",
            "fp_attend_noalloc_max_bytes", "fp_hazard_workspace_bytes",
-           "fp_check_hazards", "fp_fold", "fp_readout", "fp_attn_mass",
+           "fp_check_hazards", "fp_fold", "fp_readout", "fp_fold_readout", "fp_attn_mass",
            "fp_advance", "fp_tova_mask", "fp_lora_workspace_bytes", "fp_adapter_lora", "fp_adapter_ia3",
            "fp_vertical_merge", "fp_kv_bytes", "fp_pages_for", "fp_page_waste", "fp_page_bytes", "fp_version",
            "fp_source_hash")
@@ -129,6 +129,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp_fold.restype = c_i32
     lib.fp_readout.argtypes = [P(FpGeometry), c_ptr, c_i32, c_ptr, c_i32, c_ptr, c_ptr, c_ptr]
     lib.fp_readout.restype = c_i32
+    lib.fp_fold_readout.argtypes = [P(FpKvPool), P(FpGeometry), c_ptr, c_ptr, c_i32, c_ptr, c_i32, c_ptr, c_ptr,
+                                    c_ptr]
+    lib.fp_fold_readout.restype = c_i32
     lib.fp_attn_mass.argtypes = [P(FpKvPool), P(FpGeometry), c_i32, P(FpMask), c_ptr, c_ptr, ctypes.c_size_t, P(FpTuning),
                                  c_ptr, c_ptr]
     lib.fp_attn_mass.restype = c_i32

@@ -213,6 +213,18 @@ def readout(geom: Geometry, out: torch.Tensor, dst: torch.Tensor, status: torch.
                                         _ptr(status), _stream(stream)))
 
 
+def fold_readout(pool: Pool, geom: Geometry, out: torch.Tensor, dst: torch.Tensor, status: torch.Tensor,
+                 channel: Optional[torch.Tensor] = None, rows: Optional[torch.Tensor] = None, stream=None) -> None:
+    """fp_fold_readout: fold() then readout() of the same pass, in one launch."""
+    lib = _lib.load()
+    ps, gs = pool.struct(), geom.struct()
+    row_elems = int(out.numel() // max(1, geom.num_rows)) if geom.num_rows else int(dst.shape[-1])
+    num = int(dst.shape[0])
+    _check("fp_fold_readout", lib.fp_fold_readout(ctypes.byref(ps), ctypes.byref(gs), _ptr(channel), _ptr(out),
+                                                  row_elems, _ptr(rows), num, _ptr(dst), _ptr(status),
+                                                  _stream(stream)))
+
+
 def attn_mass(pool: Pool, geom: Geometry, num_q_heads: int, lse: torch.Tensor, workspace: torch.Tensor,
               slot_mass: torch.Tensor, mask: Optional[Mask] = None, split: Optional[int] = None,
               stream=None) -> None:

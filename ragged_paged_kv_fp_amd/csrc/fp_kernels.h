@@ -365,9 +365,10 @@ __global__ void __launch_bounds__(256) hazard_reads_kernel(HazardArgs a) {
 
 // ============================================================================ fold
 
-__global__ void __launch_bounds__(256) fold_kernel(const int32_t *indptr, const int32_t *fold, const int32_t *channel,
-                                                    int32_t *committed, int L, int32_t *status) {
-    const int l = blockIdx.x * blockDim.x + threadIdx.x;
+// Lane l = 256 b + t of workgroup b: committed_len += its fold count.
+__device__ __forceinline__ void fold_body(const int32_t *indptr, const int32_t *fold, const int32_t *channel,
+                                          int32_t *committed, int L, int32_t *status, int b) {
+    const int l = b * blockDim.x + threadIdx.x;
     if (l >= L) return;
     const int n = indptr[l + 1] - indptr[l];
     const int f = fold[l];
@@ -388,6 +389,11 @@ __global__ void __launch_bounds__(256) fold_kernel(const int32_t *indptr, const 
     if (k > n) { k = n; clamped = true; }
     committed[l] += k;
     if (clamped) atomicOr(status, FP_ST_FOLD_CLAMP);
+}
+
+__global__ void __launch_bounds__(256) fold_kernel(const int32_t *indptr, const int32_t *fold, const int32_t *channel,
+                                                    int32_t *committed, int L, int32_t *status) {
+    fold_body(indptr, fold, channel, committed, L, status, (int)blockIdx.x);
 }
 
 // ============================================================================ advance
@@ -411,11 +417,10 @@ __global__ void __launch_bounds__(256) advance_kernel(const int32_t *indptr, con
 
 // Block b copies one readout row: rows[b] if a list is given, else the last row
 // of lane b (its destination index counts the non-empty lanes before it).
-__global__ void __launch_bounds__(256) readout_kernel(const int32_t *indptr, int L, int64_t N, const float *out,
-                                                       int row_elems, const int32_t *rows, int num_readout, float *dst,
-                                                       int32_t *status) {
+__device__ __forceinline__ void readout_body(const int32_t *indptr, int L, int64_t N, const float *out,
+                                             int row_elems, const int32_t *rows, int num_readout, float *dst,
+                                             int32_t *status, int b) {
     __shared__ int s_cnt[256 / kWave];
-    const int b = blockIdx.x;
     int64_t src, di;
     if (rows) {
         di = b;
@@ -455,6 +460,27 @@ __global__ void __launch_bounds__(256) readout_kernel(const int32_t *indptr, int
     } else {
         for (int e = threadIdx.x; e < row_elems; e += blockDim.x) d[e] = s[e];
     }
+}
+
+__global__ void __launch_bounds__(256) readout_kernel(const int32_t *indptr, int L, int64_t N, const float *out,
+                                                       int row_elems, const int32_t *rows, int num_readout, float *dst,
+                                                       int32_t *status) {
+    readout_body(indptr, L, N, out, row_elems, rows, num_readout, dst, status, (int)blockIdx.x);
+}
+
+// Fold and readout in one launch: the first fold_blocks workgroups fold, the
+// rest copy readout rows. The two touch disjoint memory (committed lengths
+// against the output rows), so their order inside the launch does not matter.
+__global__ void __launch_bounds__(256) fold_readout_kernel(const int32_t *indptr, const int32_t *fold,
+                                                            const int32_t *channel, int32_t *committed, int L,
+                                                            int fold_blocks, int64_t N, const float *out,
+                                                            int row_elems, const int32_t *rows, int num_readout,
+                                                            float *dst, int32_t *status) {
+    const int b = (int)blockIdx.x;
+    if (b < fold_blocks)
+        fold_body(indptr, fold, channel, committed, L, status, b);
+    else
+        readout_body(indptr, L, N, out, row_elems, rows, num_readout, dst, status, b - fold_blocks);
 }
 
 // ============================================================================ Q rotation

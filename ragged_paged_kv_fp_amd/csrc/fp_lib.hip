@@ -604,20 +604,20 @@ int fp_check_hazards(const fp_kv_pool *pool, const fp_geometry *geom, void *work
     return FP_OK;
 }
 
-int fp_fold(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *channel, int32_t *status,
-            hipStream_t stream) {
+// Checks of a fold call; on success *blocks is its workgroup count.
+static int fold_check(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *status, unsigned *blocks) {
     if (!pool || !pool->committed_len) return FP_ERR_NULL;
     if (!geom || !geom->indptr || !geom->fold || !geom->indptr_host) return FP_ERR_NULL;
     if (!status) return FP_ERR_NULL;
     if (geom->num_lanes < 1) return FP_ERR_SHAPE;
-    const int L = geom->num_lanes;
-    hipLaunchKernelGGL(fold_kernel, dim3((L + 255) / 256), dim3(256), 0, stream, geom->indptr, geom->fold, channel,
-                       pool->committed_len, L, status);
-    return launch_ok();
+    *blocks = (unsigned)((geom->num_lanes + 255) / 256);
+    return FP_OK;
 }
 
-int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, const int32_t *rows, int32_t num_readout,
-               float *dst, int32_t *status, hipStream_t stream) {
+// Checks of a readout call; on success *blocks is its workgroup count (zero
+// when there is nothing to copy).
+static int readout_check(const fp_geometry *geom, const float *out, int32_t row_elems, const int32_t *rows,
+                         int32_t num_readout, const float *dst, const int32_t *status, unsigned *blocks) {
     if (!geom || !geom->indptr || !geom->indptr_host) return FP_ERR_NULL;
     if (geom->num_lanes < 1 || row_elems < 1 || num_readout < 0) return FP_ERR_SHAPE;
     if (!status) return FP_ERR_NULL;
@@ -632,11 +632,44 @@ int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, con
         }
         if (nonempty != num_readout) return FP_ERR_SHAPE;
     }
+    *blocks = 0;
     if (num_readout == 0) return FP_OK;
     if (!out || !dst) return FP_ERR_NULL;
-    const unsigned grid = rows ? (unsigned)num_readout : (unsigned)L;
-    hipLaunchKernelGGL(readout_kernel, dim3(grid), dim3(256), 0, stream, geom->indptr, L, (int64_t)geom->num_rows, out,
-                       row_elems, rows, num_readout, dst, status);
+    *blocks = rows ? (unsigned)num_readout : (unsigned)L;
+    return FP_OK;
+}
+
+int fp_fold(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *channel, int32_t *status,
+            hipStream_t stream) {
+    unsigned fb = 0;
+    int rc = fold_check(pool, geom, status, &fb);
+    if (rc) return rc;
+    hipLaunchKernelGGL(fold_kernel, dim3(fb), dim3(256), 0, stream, geom->indptr, geom->fold, channel,
+                       pool->committed_len, geom->num_lanes, status);
+    return launch_ok();
+}
+
+int fp_readout(const fp_geometry *geom, const float *out, int32_t row_elems, const int32_t *rows, int32_t num_readout,
+               float *dst, int32_t *status, hipStream_t stream) {
+    unsigned rb = 0;
+    int rc = readout_check(geom, out, row_elems, rows, num_readout, dst, status, &rb);
+    if (rc) return rc;
+    if (rb == 0) return FP_OK;
+    hipLaunchKernelGGL(readout_kernel, dim3(rb), dim3(256), 0, stream, geom->indptr, geom->num_lanes,
+                       (int64_t)geom->num_rows, out, row_elems, rows, num_readout, dst, status);
+    return launch_ok();
+}
+
+int fp_fold_readout(const fp_kv_pool *pool, const fp_geometry *geom, const int32_t *channel, const float *out,
+                    int32_t row_elems, const int32_t *rows, int32_t num_readout, float *dst, int32_t *status,
+                    hipStream_t stream) {
+    unsigned fb = 0, rb = 0;
+    int rc = fold_check(pool, geom, status, &fb);
+    if (rc) return rc;
+    if ((rc = readout_check(geom, out, row_elems, rows, num_readout, dst, status, &rb))) return rc;
+    hipLaunchKernelGGL(fold_readout_kernel, dim3(fb + rb), dim3(256), 0, stream, geom->indptr, geom->fold, channel,
+                       pool->committed_len, geom->num_lanes, (int)fb, (int64_t)geom->num_rows, out, row_elems, rows,
+                       num_readout, dst, status);
     return launch_ok();
 }
 

@@ -106,11 +106,15 @@ class DeviceStep:
     def readout(self, stream=None):
         api.readout(self.geom, self.out, self.dst, self.status, self.readout_rows, stream)
 
+    def finish(self, stream=None):
+        """fold() and readout() of the pass, in one launch."""
+        api.fold_readout(self.pool, self.geom, self.out, self.dst, self.status, self.channel, self.readout_rows,
+                         stream)
+
     def step(self, stream=None, events=None) -> None:
         self.append(stream)
         self.attend(stream, events=events)
-        self.fold(stream)
-        self.readout(stream)
+        self.finish(stream)
 
     # ------------------------------------------------------------------ views
     def pool_logical(self):
@@ -186,8 +190,7 @@ class RunAheadLoop:
         api.append_kv(self.pool, self.geom, self.k, self.v, ra.theta, self.status, stream)
         api.attend(self.pool, self.geom, self.q, ra.H_q, ra.theta, ra.sm_scale, self.out, self.workspace,
                    self.status, self.lse, None, self.split, stream)
-        api.fold(self.pool, self.geom, self.status, self.channel, stream)
-        api.readout(self.geom, self.out, self.dst, self.status, None, stream)
+        api.fold_readout(self.pool, self.geom, self.out, self.dst, self.status, self.channel, None, stream)
 
     def pool_logical(self):
         ra = self.ra

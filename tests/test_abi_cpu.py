@@ -169,6 +169,13 @@ def test_readout_default_count_checked(lib):
     st = ctypes.c_int32(0)
     assert lib.fp_readout(ctypes.byref(g), FAKE, 8, None, 3, FAKE, ctypes.addressof(st), None) == -2
     assert lib.fp_readout(ctypes.byref(g), FAKE, 8, None, 2, FAKE, None, None) == -1
+    # the one-launch fold+readout runs both calls' checks before enqueueing anything
+    assert lib.fp_fold_readout(ctypes.byref(p), ctypes.byref(g), None, FAKE, 8, None, 3, FAKE,
+                               ctypes.addressof(st), None) == -2
+    assert lib.fp_fold_readout(ctypes.byref(p), ctypes.byref(g), None, FAKE, 8, None, 2, FAKE, None, None) == -1
+    assert lib.fp_fold_readout(None, ctypes.byref(g), None, FAKE, 8, None, 2, FAKE, ctypes.addressof(st), None) == -1
+    assert lib.fp_fold_readout(ctypes.byref(p), ctypes.byref(g), None, None, 8, None, 2, FAKE,
+                               ctypes.addressof(st), None) == -1
 
 
 def test_attn_mass_and_advance_validation(lib):

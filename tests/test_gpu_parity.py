@@ -438,6 +438,50 @@ def test_channel_fold_out_of_range_clamped():
     pu.compare_step(ds, ref)
 
 
+def _fold_readout_case(case):
+    if case == "channel_clamp":
+        wl = W.make_config(4, seed=2, scale="small")
+        wl.channel = wl.channel.copy()
+        verify = [i for i, f in enumerate(wl.step.fold) if f == W.FOLD_CHANNEL]
+        wl.channel[verify[0]] = 99
+        wl.channel[verify[-1]] = -3
+        return wl
+    if case == "row_list":
+        wl = W.make_random(41, H_kv=2, G=4, d=128, P=16, num_lanes=300, max_rows=12, max_ctx=90)
+        n = wl.step.num_rows
+        wl.readout_rows = np.concatenate([np.arange(n - 1, -1, -7), [-1, n, 0]]).astype(np.int32)
+        return wl
+    return W.make_config(2, seed=3, scale="small")  # default readout, one row per lane
+
+
+@pytest.mark.parametrize("case", ["channel_clamp", "row_list", "default"])
+def test_fold_readout_one_launch_matches_two(case):
+    # fp_fold_readout must leave committed_len, the readout rows and the status
+    # word exactly as fp_fold followed by fp_readout does (and as the oracle says).
+    import torch
+
+    wl = _fold_readout_case(case)
+    _say(f"fold+readout {case}: lanes={wl.num_lanes} rows={wl.step.num_rows}")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)  # the step ends in fp_fold_readout
+    pu.compare_step(ds, ref)
+    one = (ds.pool.committed_len.cpu().clone(), ds.dst.cpu().clone(), int(ds.status.cpu()[0]))
+    ds.reset()
+    ds.status.zero_()
+    ds.dst.fill_(float("nan"))
+    torch.cuda.synchronize()
+    ds.fold()
+    ds.readout()
+    torch.cuda.synchronize()
+    assert torch.equal(ds.pool.committed_len.cpu(), one[0])
+    assert np.array_equal(ds.dst.cpu().numpy().view(np.uint32), one[1].numpy().view(np.uint32))
+    assert int(ds.status.cpu()[0]) == one[2]
+    if case == "row_list":
+        assert one[2] & oracle.ST_READOUT_RANGE
+    if case == "channel_clamp":
+        assert one[2] & oracle.ST_FOLD_CLAMP
+
+
 def test_empty_rows_and_mask_short():
     wl = W.make_random(33, H_kv=2, G=4, d=128, P=16, num_lanes=6, max_rows=60, max_ctx=200)
     # an all-zero bitmap lane: every row empty -> O = 0, LSE = -inf
