@@ -107,7 +107,7 @@ def compare_step(ds, ref, lanes=None):
     assert ds.pool.committed_len.cpu().numpy().tolist() == ref["committed"].tolist(), "fold lengths differ"
     assert int(ds.status.cpu()[0]) == ref["status"], f"status {int(ds.status.cpu()[0])} != {ref['status']}"
     rl = ref["readout_rows"]
-    out = ds.out.cpu().numpy().reshape(ds.out.shape[0], -1)
+    out = ds.out.cpu().numpy().reshape(ds.out.shape[0], int(np.prod(ds.out.shape[1:])))  # also for a pass of 0 rows
     dst = ds.dst.cpu().numpy()
     assert dst.shape[0] == len(rl)
     ok = (rl >= 0) & (rl < out.shape[0])

@@ -482,6 +482,18 @@ def test_fold_readout_one_launch_matches_two(case):
         assert one[2] & oracle.ST_FOLD_CLAMP
 
 
+def test_pass_without_rows():
+    # lanes with cached history and no new rows: append and attend have
+    # nothing to do, the fold clamps the channel count and the literal count to
+    # the lanes' zero rows (status 8) and the default readout lists no row
+    wl = W.make_empty_pass(5)
+    _say(f"empty pass: lanes={wl.num_lanes} rows={wl.step.num_rows}")
+    ref = pu.oracle_run(wl)
+    ds = pu.gpu_run(wl)
+    pu.compare_step(ds, ref)
+    assert ref["status"] == oracle.ST_FOLD_CLAMP and ds.dst.shape[0] == 0
+
+
 def test_empty_rows_and_mask_short():
     wl = W.make_random(33, H_kv=2, G=4, d=128, P=16, num_lanes=6, max_rows=60, max_ctx=200)
     # an all-zero bitmap lane: every row empty -> O = 0, LSE = -inf

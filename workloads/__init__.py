@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     Lora,
     make_append_mix,
     make_config,
+    make_empty_pass,
     make_explicit,
     make_window_decode,
     make_lora,

@@ -719,3 +719,18 @@ def make_window_decode(seed: int, *, L: int = 64, kv: int = 32768, window: int =
                      v=_normal_bf16(rngs["prefix_kv"], (L * n_pre, H_kv, d)))
     wl.meta.update(window=window, sinks=sinks)
     return wl
+
+
+def make_empty_pass(seed: int, *, H_q: int = 32, H_kv: int = 8, d: int = 128, P: int = 16) -> Workload:
+    """A pass with lanes but no rows: five lanes with cached prefixes of 0, 17,
+    64, 300 and 5 slots and no new rows. Their folds are all, none, a device
+    channel count of 2 and a literal 3 (both more than the lane's zero rows)
+    and all; the default readout then lists no row."""
+    rngs = _rngs(seed)
+    cs = [0, 17, 64, 300, 5]
+    folds = [FOLD_ALL, 0, FOLD_CHANNEL, 3, FOLD_ALL]
+    lanes = [dict(c=c, n=0, kv_len=c, fold=f, pos_of_slot=_ident_pos(max(c, 1)), pages=-(-max(c, 1) // P))
+             for c, f in zip(cs, folds)]
+    return _assemble(f"empty_pass_{len(lanes)}", rngs, H_q=H_q, H_kv=H_kv, d=d, P=P, lanes=lanes,
+                     channel_fn=lambda rng, ls: np.full(len(ls), 2, dtype=np.int32))
+
