@@ -588,7 +588,7 @@ def run_ahead_bench(W, runner, seed, K, Wm) -> dict:
     """A repeating decode loop at the decode-wave shape (64 lanes, prompts up to
     8192 slots, 32/8 heads, d=128, P=16, each lane drafting 0/1/2/4/8 rows per
     pass and the fold committing a device-channel count), every pass taking
-    its geometry from fp_advance. K passes enqueued eagerly (five ABI calls per
+    its geometry from fp_advance. K passes enqueued eagerly (four ABI calls per
     pass) and K as one HIP-graph replay per pass, each after the copies of that
     pass's inputs into the loop's buffers: device and host ms per pass."""
     import torch
@@ -695,7 +695,7 @@ def lora_bench(W, seed, K, Wm) -> dict:
 def frame_bench(W, runner, seed, K, Wm) -> dict:
     """A frame of two passes (config 3 with each lane's rows split at a random
     point: prefix pass folded all, then the continuation) submitted K times
-    eagerly (eight ABI calls per frame from the host) and K times as one HIP
+    eagerly (six ABI calls per frame from the host) and K times as one HIP
     graph replay: device ms per frame from torch events and host ms per frame."""
     import torch
 

@@ -1,8 +1,9 @@
-"""Device buffers for one pass and the four ABI calls in order.
+"""Device buffers for one pass and the ABI calls in order.
 
 Uploads a host-side description of a pass (offset arrays, slots, positions,
 bf16 bit patterns, page table, masks, channel) into caller-owned torch
-tensors and issues append -> attend -> fold -> readout on one stream.
+tensors and issues append -> attend -> fold + readout (one launch) on one
+stream; fold() and readout() remain for callers that want them apart.
 """
 
 from __future__ import annotations
@@ -318,8 +319,7 @@ class Frame:
             api.append_kv(self.pool, g, it["k"], it["v"], self.theta, self.status)
             api.attend(self.pool, g, it["q"], self.H_q, self.theta, self.sm_scale, it["out"], it["ws"], self.status,
                        it["lse"])
-            api.fold(self.pool, g, self.status)
-            api.readout(g, it["out"], it["dst"][:it["nro"]], self.status, it["readout_rows"])
+            api.fold_readout(self.pool, g, it["out"], it["dst"][:it["nro"]], self.status, None, it["readout_rows"])
 
     def parts(self):
         """(original pass index, its rows' out, its rows' lse) for every original pass, in frame order."""
