@@ -613,26 +613,56 @@ __device__ __forceinline__ int upper_lane(const int *offs, int L, int idx) {
     return lo;
 }
 
-// Exclusive prefix sum over the workgroup's threads (in thread order); *total
-// gets the sum of all. s_w: one int per wave.
+// Inclusive prefix sum over the 64 lanes of a wave in registers (DPP): within
+// each 16-lane row by shifts of 1, 2, 4 and 8 lanes, then each row's total
+// carried into the rows after it by broadcasts of lanes 15 and 31. A lane whose
+// source lies outside its row, or a row the step does not write, adds 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Exclusive prefix sums over the workgroup's threads (in thread order) of K
+// values at once, in place; tot[k] gets the sum of all. One pair of barriers
+// for all K: each wave scans its values in registers and leaves its totals in
+// s_w (K ints per wave); then lanes 0..15 of every wave read the 16 wave
+// totals of a value and scan them the same way, and each wave takes its
+// offset and the grand total from that scan by lane reads.
+template <int K>
+__device__ __forceinline__ void block_excl_scan_n(int (&v)[K], int (&tot)[K], int *s_w) {
+    constexpr int NW = kPlanThreads / kWave;
+    static_assert(NW <= 16, "the wave totals are scanned within one 16-lane row");
+    const int ln = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    int x[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) x[k] = wave_incl_scan(v[k]);
+    if (ln == kWave - 1) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) s_w[k * NW + wv] = x[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int inc = wave_incl_scan(ln < NW ? s_w[k * NW + ln] : 0);
+        const int before = wv > 0 ? __builtin_amdgcn_readlane(inc, wv - 1) : 0;
+        tot[k] = __builtin_amdgcn_readlane(inc, NW - 1);
+        v[k] = before + x[k] - v[k];
+    }
+    __syncthreads();
+}
+
+// Exclusive prefix sum of one value per thread; *total gets the sum of all.
+// s_w: one int per wave.
 __device__ __forceinline__ int block_excl_scan(int v, int *s_w, int *total) {
-    const int ln = lane_id(), wv = threadIdx.x / kWave;
-    int x = v;
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (ln >= o) x += y;
-    }
-    if (ln == kWave - 1) s_w[wv] = x;
-    __syncthreads();
-    int before = 0, tot = 0;
-    for (int w = 0; w < kPlanThreads / kWave; ++w) {
-        const int t = s_w[w];
-        before += w < wv ? t : 0;
-        tot += t;
-    }
-    __syncthreads();
-    *total = tot;
-    return before + x - v;
+    int vv[1] = {v}, tt[1];
+    block_excl_scan_n<1>(vv, tt, s_w);
+    *total = tt[0];
+    return vv[0];
 }
 
 // Single workgroup: per-lane classification (decode if all rows x GQA heads fit
@@ -648,17 +678,41 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
     __shared__ int s_full[2][kMaxLanes + 1];  // non-last decode items of part c (unmasked, masked) before lane l
     __shared__ int s_lane_at[2][kMaxLanes];   // part c's decode lanes by the length of their last split, longest first
     __shared__ int s_hist[2][kLastBuckets];   // decode lanes of part c per last-split bucket, then bucket offsets
-    __shared__ int s_w[kPlanThreads / kWave];
+    __shared__ int s_nsplit[kMaxLanes];       // decode splits of lane l
+    __shared__ int s_cap[kMaxLanes];          // slot capacity of lane l
+    __shared__ int s_w[7 * (kPlanThreads / kWave)];
     __shared__ int s_bad;
     const int tid = threadIdx.x;
     if (tid == 0) s_bad = 0;
     for (int e = tid; e < 2 * kLastBuckets; e += kPlanThreads) s_hist[e / kLastBuckets][e % kLastBuckets] = 0;
     const int per = (a.L + kPlanThreads - 1) / kPlanThreads;
     const int l0 = tid * per, l1 = min(a.L, l0 + per);
-    int32_t st = 0;
+    // bucket of a decode lane's last split by the slots it reads there, in
+    // 32-slot tiles: 0 for the longest
+    auto last_key = [&](int l, const LaneCounts &c) {
+        const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
+        const int rem = clamp_kv(a.kv_len[l], cap) - (c.nsplit - 1) * a.split;
+        const int t = rem <= 0 ? 0 : (min(rem, a.split) + 31) >> 5;
+        return (kLastBuckets - 1) - min(t, kLastBuckets - 1);
+    };
+    // A thread keeps its first lane's counts and key in registers for the
+    // later passes (with at most 1024 lanes, its only lane); further lanes are
+    // read again. Split counts and capacities go to LDS for the item lists.
+    LaneCounts c0 = {0, 0, 0, 0, 0, 0, 0, 0};
+    int key0 = 0;
+    int32_t st = 0, dummy = 0;
+    auto counts_of = [&](int l) { return l == l0 ? c0 : lane_counts(a, l, &dummy); };
+    auto key_of = [&](int l, const LaneCounts &c) { return l == l0 ? key0 : last_key(l, c); };
     int td = 0, tp = 0, ts = 0, tc = 0, tf0 = 0, tf1 = 0, tn0 = 0, tn1 = 0;
     for (int l = l0; l < l1; ++l) {
         const LaneCounts c = lane_counts(a, l, &st);
+        const int key = last_key(l, c);
+        if (l == l0) {
+            c0 = c;
+            key0 = key;
+        }
+        s_nsplit[l] = c.nsplit;
+        s_cap[l] = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
         td += c.dec; tp += c.pre; ts += c.sum;
         if (c.dec) {
             if (c.cls == 0) { tf0 += c.dec - a.H; tn0 += 1; }
@@ -668,30 +722,17 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
         if (c.nsplit > 1 && !a.merge_host) tc = kDecodeCols + 1;  // forces the mismatch path
     }
     if (st) atomicOr(a.status, st);
-    int Td, Tp, Ts, Tf0, Tf1, Tn0, Tn1;
-    int od = block_excl_scan(td, s_w, &Td);  // its barriers also order s_bad's initialisation
+    int sc[7] = {td, tp, ts, tf0, tf1, tn0, tn1}, tot[7];
+    block_excl_scan_n<7>(sc, tot, s_w);  // its barriers also order s_bad's initialisation
     if (tc > a.ncols_host) atomicOr(&s_bad, 1);
-    int op = block_excl_scan(tp, s_w, &Tp);
-    int os = block_excl_scan(ts, s_w, &Ts);
-    int of0 = block_excl_scan(tf0, s_w, &Tf0);
-    int of1 = block_excl_scan(tf1, s_w, &Tf1);
-    int on0 = block_excl_scan(tn0, s_w, &Tn0);
-    int on1 = block_excl_scan(tn1, s_w, &Tn1);
-    int32_t dummy = 0;
-    // bucket of a decode lane's last split by the slots it reads there, in
-    // 32-slot tiles: 0 for the longest
-    auto last_key = [&](int l, const LaneCounts &c) {
-        const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
-        const int rem = clamp_kv(a.kv_len[l], cap) - (c.nsplit - 1) * a.split;
-        const int t = rem <= 0 ? 0 : (min(rem, a.split) + 31) >> 5;
-        return (kLastBuckets - 1) - min(t, kLastBuckets - 1);
-    };
+    int od = sc[0], op = sc[1], os = sc[2], of0 = sc[3], of1 = sc[4], on0 = sc[5], on1 = sc[6];
+    const int Td = tot[0], Tp = tot[1], Ts = tot[2], Tf0 = tot[3], Tf1 = tot[4], Tn0 = tot[5], Tn1 = tot[6];
     for (int l = l0; l < l1; ++l) {
-        const LaneCounts c = lane_counts(a, l, &dummy);
+        const LaneCounts c = counts_of(l);
         s_pre[l] = op;
         s_full[0][l] = of0;
         s_full[1][l] = of1;
-        if (c.dec) atomicAdd(&s_hist[c.cls][last_key(l, c)], 1);
+        if (c.dec) atomicAdd(&s_hist[c.cls][key_of(l, c)], 1);
         LaneInfo li;
         li.dec_off = c.dec ? od : -1;
         li.nsplit = c.nsplit;
@@ -706,18 +747,26 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
     }
     const int n0 = Tf0 + a.H * Tn0, n1 = Tf1 + a.H * Tn1;  // decode items of each part
     __syncthreads();  // the histograms are complete
-    if (tid < 2) {    // bucket offsets, longest last splits first
-        int acc = 0;
-        for (int b = 0; b < kLastBuckets; ++b) {
-            const int cnt = s_hist[tid][b];
-            s_hist[tid][b] = acc;
-            acc += cnt;
+    if (tid < 2 * kWave) {  // bucket offsets, longest last splits first: wave c scans part c's buckets
+        static_assert(kLastBuckets <= 3 * kWave, "three buckets per lane");
+        const int c = tid / kWave, b0 = 3 * lane_id();
+        int cnt[3], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            cnt[j] = b0 + j < kLastBuckets ? s_hist[c][b0 + j] : 0;
+            sum += cnt[j];
+        }
+        int acc = wave_incl_scan(sum) - sum;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            if (b0 + j < kLastBuckets) s_hist[c][b0 + j] = acc;
+            acc += cnt[j];
         }
     }
     __syncthreads();
     for (int l = l0; l < l1; ++l) {
-        const LaneCounts c = lane_counts(a, l, &dummy);
-        if (c.dec) s_lane_at[c.cls][atomicAdd(&s_hist[c.cls][last_key(l, c)], 1)] = l;
+        const LaneCounts c = counts_of(l);
+        if (c.dec) s_lane_at[c.cls][atomicAdd(&s_hist[c.cls][key_of(l, c)], 1)] = l;
     }
     if (tid == 0) {
         s_pre[a.L] = Tp;
@@ -747,7 +796,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
                 // a non-last split: the largest lane whose first such item is at or before local
                 l = upper_lane(s_full[cls], a.L, local);
                 const int j = local - s_full[cls][l];
-                const int ns = a.lane_info[l].nsplit;
+                const int ns = s_nsplit[l];
                 g = j / (ns - 1);
                 sp = j - g * (ns - 1);
             } else {
@@ -755,9 +804,9 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
                 const int j = local - tf;
                 l = s_lane_at[cls][j / a.H];
                 g = j % a.H;
-                sp = a.lane_info[l].nsplit - 1;
+                sp = s_nsplit[l] - 1;
             }
-            const int cap = (a.page_indptr[l + 1] - a.page_indptr[l]) * a.P;
+            const int cap = s_cap[l];
             it = make_int4(l, g, sp * a.split, min((sp + 1) * a.split, cap));
         }
         a.dec_items[idx] = it;
