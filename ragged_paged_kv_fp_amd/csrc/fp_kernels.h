@@ -43,7 +43,7 @@ struct AppendArgs {
 
 constexpr int kAppendRows = 16;        // most consecutive rows one append workgroup writes
 constexpr int kBatch = 8;              // 16-byte loads a thread of the row kernels issues before using them
-constexpr int kAppendVBytes = 33024;   // LDS staging V: 16 rows x (8 heads x 128 dims + 8 padding) bf16
+constexpr int kAppendVBytes = 16640;   // LDS staging V: 16 rows x (4 heads x 128 dims + 8 padding) bf16
 
 // log2 of the rows per workgroup of the row-grouped kernels (append, Q
 // rotation): many rows share a workgroup when there are enough rows to fill
@@ -110,8 +110,14 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
     constexpr int PAIRS = D / 2, C8 = D / 8, CSH = D == 128 ? 4 : 3;
     __shared__ int64_t s_base[kAppendRows];  // element offset of the row's page, -1: row not written
     __shared__ int s_off[kAppendRows];
-    __shared__ double2 s_cs[kAppendRows * PAIRS];
-    __shared__ __attribute__((aligned(16))) uint16_t s_v[kAppendVBytes / 2];
+    // The angle table serves the K rotation and the V staging buffer the V
+    // transpose after it (a barrier between), so they share LDS: at about
+    // 17 KB a workgroup, enough workgroups stay resident per compute unit for
+    // a 20,000-row pass to run in one round.
+    constexpr int kCsBytes = kAppendRows * PAIRS * (int)sizeof(double2);
+    __shared__ __attribute__((aligned(16))) char s_u[kCsBytes > kAppendVBytes ? kCsBytes : kAppendVBytes];
+    double2 *s_cs = reinterpret_cast<double2 *>(s_u);
+    uint16_t *s_v = reinterpret_cast<uint16_t *>(s_u);
     __shared__ int s_seg[kAppendRows / 8];  // first row of each full segment
     __shared__ int s_erow[kAppendRows];     // rows stored per element
     __shared__ int s_nseg, s_nerow;
@@ -246,6 +252,7 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
         }
     }
     const int64_t vblock = (int64_t)H * a.P * D;  // V block [H][D][P] follows the K block
+    __syncthreads();  // every K rotation has read the angle table before V overwrites it
     for (int h0 = 0; h0 < H; h0 += hg) {
         const int hn = min(hg, H - h0);
         const int rs = hn * D + 8;  // LDS row stride (elements): 16 bytes of padding per row
