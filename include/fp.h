@@ -21,8 +21,8 @@
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless the name ends in `_host`.
  *  - bf16 values are passed as 16-bit storage (bit patterns). The pool, Q, K
- *    and V arrays must be 16-byte aligned (FP_ERR_UNSUPPORTED otherwise): the
- *    kernels move them in 16-byte vectors.
+ *    and V arrays and fp_attend's `out` must be 16-byte aligned
+ *    (FP_ERR_UNSUPPORTED otherwise): the kernels move them in 16-byte vectors.
  *  - The caller owns every buffer; the library allocates no memory, keeps no
  *    state between calls (apart from the static device scratch of
  *    fp_attend_noalloc) and never synchronizes. Buffers must stay valid until

@@ -457,21 +457,27 @@ __device__ __forceinline__ void decode_item(const AttnArgs &a, const int4 it, De
     for (int c = 0; c < D / 64; ++c) {
         stage_o<D, NC>(w, c, scale, &s_o[wv][col][0]);
         __syncthreads();
-        for (int e = threadIdx.x; e < NC * 64; e += kDecThreads) {
-            const int n = e >> 6, dl = e & 63;
+        // four consecutive dims per thread: 16-byte LDS reads and stores
+        for (int e = threadIdx.x; e < NC * 16; e += kDecThreads) {
+            const int n = e >> 4, dl = 4 * (e & 15);
             if (n >= ncols) continue;
-            float acc = 0.0f;
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int v = 0; v < kDecWaves; ++v) acc += s_o[v][n][dl];
+            for (int v = 0; v < kDecWaves; ++v) {
+                const float4 x = *reinterpret_cast<const float4 *>(&s_o[v][n][dl]);
+                acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+            }
             const float Lt = s_fin[1][n];
             if (single) {
                 const int64_t orow = r0 + n / a.G;
                 const int ohead = g * a.G + n % a.G;
-                a.out[(orow * a.Hq + ohead) * D + 64 * c + dl] = Lt > 0.0f ? acc / Lt : 0.0f;
+                const float4 o = Lt > 0.0f ? make_float4(acc.x / Lt, acc.y / Lt, acc.z / Lt, acc.w / Lt)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+                *reinterpret_cast<float4 *>(&a.out[(orow * a.Hq + ohead) * D + 64 * c + dl]) = o;
                 if (c == 0 && dl == 0 && a.lse)
                     a.lse[orow * a.Hq + ohead] = Lt > 0.0f ? (s_fin[0][n] + __log2f(Lt)) * 0.69314718055994531f : kNegInf;
             } else {
-                a.part_o[(pidx * a.ncols_max + n) * D + 64 * c + dl] = acc;
+                *reinterpret_cast<float4 *>(&a.part_o[(pidx * a.ncols_max + n) * D + 64 * c + dl]) = acc;
                 if (c == 0 && dl == 0) {
                     a.part_ml[pidx * 64 + n] = s_fin[0][n];
                     a.part_ml[pidx * 64 + 32 + n] = Lt;

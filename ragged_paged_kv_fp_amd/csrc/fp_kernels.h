@@ -460,7 +460,7 @@ __device__ __forceinline__ void readout_body(const int32_t *indptr, int L, int64
         return;
     }
     const float *s = out + src * (int64_t)row_elems;
-    if ((row_elems & 3) == 0) {
+    if ((row_elems & 3) == 0 && ((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(d)) & 15) == 0) {
         const float4 *s4 = reinterpret_cast<const float4 *>(s);
         float4 *d4 = reinterpret_cast<float4 *>(d);
         for (int e = threadIdx.x; e < (row_elems >> 2); e += blockDim.x) d4[e] = s4[e];

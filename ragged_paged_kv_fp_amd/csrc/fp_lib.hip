@@ -339,7 +339,7 @@ int attend_impl(const fp_kv_pool *pool, const fp_geometry *geom, const void *q, 
     if (!status) return FP_ERR_NULL;
     if (p.N == 0) return FP_OK;
     if (!q || !out) return FP_ERR_NULL;
-    if (!aligned16(q)) return FP_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(out)) return FP_ERR_UNSUPPORTED;
     if (!workspace) return FP_ERR_NULL;
     if (workspace_bytes < p.total) return FP_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);

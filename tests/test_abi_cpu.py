@@ -136,6 +136,10 @@ def test_workspace_too_small_and_null_pointers(lib):
     rc = lib.fp_attend(ctypes.byref(p), ctypes.byref(g), FAKE, 4, 10000.0, 0.125, None, FAKE, None, FAKE, 16, None,
                        ctypes.addressof(st), None)
     assert rc == -4
+    # out must be 16-byte aligned like Q (the kernels store it in 16-byte vectors)
+    rc = lib.fp_attend(ctypes.byref(p), ctypes.byref(g), FAKE, 4, 10000.0, 0.125, None, FAKE + 4, None, FAKE, 1 << 30,
+                       None, ctypes.addressof(st), None)
+    assert rc == -3
     rc = lib.fp_attend(ctypes.byref(p), ctypes.byref(g), None, 4, 10000.0, 0.125, None, FAKE, None, FAKE, 1 << 30,
                        None, ctypes.addressof(st), None)
     assert rc == -1
