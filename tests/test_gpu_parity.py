@@ -482,6 +482,27 @@ def test_fold_readout_one_launch_matches_two(case):
         assert one[2] & oracle.ST_FOLD_CLAMP
 
 
+def test_readout_into_unaligned_rows():
+    # a destination 4 bytes off 16-byte alignment takes the scalar copy and
+    # still receives every row exactly
+    import torch
+
+    from ragged_paged_kv_fp_amd import api
+
+    wl = W.make_config(4, seed=3, scale="small")
+    ds = pu.gpu_run(wl)
+    want = ds.dst.cpu().numpy().copy()
+    n, e = ds.dst.shape
+    raw = torch.full((n * e + 1,), float("nan"), dtype=torch.float32, device=ds.dst.device)
+    dst = raw[1:].view(n, e)
+    assert dst.data_ptr() % 16 == 4
+    ds.status.zero_()
+    api.readout(ds.geom, ds.out, dst, ds.status, ds.readout_rows)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    assert int(ds.status.cpu()[0]) == 0
+
+
 def test_pass_without_rows():
     # lanes with cached history and no new rows: append and attend have
     # nothing to do, the fold clamps the channel count and the literal count to
